@@ -1,0 +1,256 @@
+"""Plain float64 oracle for the AdaFlash fused block-verification + OPD pass.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): nothing on the product
+path may import it.
+
+Sources (the pages, cited by title and section):
+  [P1] Pith verdict record for arXiv 2607.19223 (JSON): skeptic critique,
+       "load-bearing attack" (length-head loss, truncated verification).
+  [P2] ResearchPod summary "AdaFlash: Adaptive Speculative Decoding via
+       On-Policy Distilled Diffusion Drafters", components 1 (OPD with
+       reverse KL and entry-wise clipping) and 2 (adaptive length head).
+  [P3] Pith review page of the same paper: "What carries the argument";
+       Referee Report major comments 1-2 (paper Sec. 3.1-3.3) and minor
+       comments 1, 2, 4 (Sec. 2.1 Eq. (1), Sec. 3.2, Sec. B.1);
+       "Axiom & Free-Parameter Ledger".
+
+What the oracle computes, in the pages' order:
+  length head  z_b = w.h_b + bias, rate_b = sigmoid(z_b),
+               b_k = clamp(round(gamma * rate_b * k), 1, k)      [P3 minor 2; ledger gamma]
+  argmax       a_r = first index of max_j zp_{r,j}                [P3 major 2: target
+                                                                    distribution per position]
+  acceptance   acc_b = length of the leading run of positions i < b_k whose
+               draft token equals a_{b,i}                          [P1; P3 Sec. 2.1 context]
+  OPD loss     loss_r = lam * CE_r + (1 - lam) * sum_j clip(q_j (log q_j - log p_j), -tau, tau)
+               with CE_r = -log q_{a_r}, p = softmax(zp_r), q = softmax(zq_r)
+                                                                    [P3 "What carries the argument";
+                                                                     P2 component 1; ledger]
+  gradient     d loss_r / d zq_r (the target is a fixed teacher)
+
+Readings where the pages leave a step open (each is listed in the design
+notes with its reason):
+  * rounding of b_k: ceil by default; floor (the referee's quotation of the
+    paper) on request.  gamma scales the predicted rate before rounding.
+  * clipping acts on each entry's value r_j = q_j (log q_j - log p_j); the
+    interval [-tau, tau] is closed and a clipped entry passes no gradient.
+  * lam weights the cross-entropy term; temperature 1 (plain softmax).
+  * only verified positions (i < b_k) carry loss; the loss is a plain sum.
+  * argmax ties go to the lowest index.
+  * acc counts accepted draft tokens, so the pages' tau_accept = acc + 1.
+
+Every function here is pinned by tests/test_oracle_pins.py against values
+that do not come from this file (closed forms, library routines, finite
+differences, invariants, brute force, the pages' Eq. (1)).
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 encodings -> float64 values.  A bfloat16 value is the float32
+    whose upper 16 bits are the encoding and whose lower 16 bits are zero."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# length head  [P3 minor comment 2 (Sec. 3.2); ledger: gamma; P2 component 2]
+# ---------------------------------------------------------------------------
+
+def _sigmoid(z: float) -> float:
+    if z >= 0.0:
+        return 1.0 / (1.0 + math.exp(-z))
+    e = math.exp(z)
+    return e / (1.0 + e)
+
+
+def length_head(h: np.ndarray, w: np.ndarray, bias: float, gamma: float, k: int,
+                round_mode: str = "ceil"):
+    """Adaptive length head.
+
+    A pooled drafter state h_b is mapped to one scalar, the predicted
+    acceptance rate rate_b = sigmoid(w . h_b + bias); gamma * rate_b * k is
+    rounded (ceil by default, floor optionally) and clamped to [1, k].
+
+    Returns (rate [B] float64, bk [B] int64, margin [B] float64), where margin
+    is the distance of gamma*rate*k to the nearest integer: a decision within
+    ~1e-9 of an integer can legitimately flip under a different (still
+    float64) summation order, and callers treat it as ambiguous.
+    """
+    if round_mode not in ("ceil", "floor"):
+        raise ValueError(round_mode)
+    h = np.asarray(h, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    B = h.shape[0]
+    rate = np.empty(B)
+    bk = np.empty(B, dtype=np.int64)
+    margin = np.empty(B)
+    for b in range(B):
+        z = math.fsum((w * h[b]).tolist()) + float(bias)
+        s = _sigmoid(z)
+        x = float(gamma) * s * k
+        n = math.ceil(x) if round_mode == "ceil" else math.floor(x)
+        bk[b] = min(max(n, 1), k)
+        rate[b] = s
+        margin[b] = abs(x - round(x))
+    return rate, bk, margin
+
+
+# ---------------------------------------------------------------------------
+# target argmax and acceptance  [P3 major 2 (Sec. 3.1/3.3); P1 skeptic critique]
+# ---------------------------------------------------------------------------
+
+def target_argmax(zp_row: np.ndarray) -> int:
+    """Greedy target choice at one position: the first index of the largest
+    target logit (softmax is monotone, so this is the argmax of p)."""
+    return int(np.argmax(zp_row))
+
+
+def accepted_length(draft: Sequence[int], target: Sequence[int], b: int) -> int:
+    """Greedy block verification: walk the first b positions and stop at the
+    first draft token that differs from the target's choice."""
+    n = 0
+    while n < b and int(draft[n]) == int(target[n]):
+        n += 1
+    return n
+
+
+# ---------------------------------------------------------------------------
+# OPD loss and gradient of one verified row
+# [P3 "What carries the argument"; P2 component 1; ledger: alpha, delta,
+#  reverse-KL temperature]
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class RowTerms:
+    argmax: int
+    lse_p: float
+    lse_q: float
+    ce: float
+    klc: float
+    S: float
+    loss: float
+    grad: np.ndarray      # d loss / d zq, already multiplied by grad_scale
+    q: np.ndarray
+    ell: np.ndarray       # log q - log p
+    r: np.ndarray         # q * ell (entry-wise reverse-KL terms)
+    c: np.ndarray         # bool: entry inside [-tau, tau]
+
+
+def _logsumexp(z: np.ndarray) -> float:
+    m = float(np.max(z))
+    return m + math.log(float(np.sum(np.exp(z - m))))
+
+
+def row_terms(zp_row: np.ndarray, zq_row: np.ndarray, lam: float, tau: float,
+              grad_scale: float = 1.0,
+              clip_override: Optional[Dict[int, bool]] = None) -> RowTerms:
+    """Loss and gradient of one verified position.
+
+    p = softmax(zp), q = softmax(zq) at temperature 1; the hard label is the
+    target's greedy choice a.  With ell_j = log q_j - log p_j and
+    r_j = q_j * ell_j (taken as 0 where q_j underflows to 0):
+        loss = lam * (-log q_a) + (1 - lam) * sum_j clip(r_j, -tau, tau).
+    Differentiating with d log q_j / d zq_m = [j = m] - q_m:
+        d r_j / d zq_m = q_j ([j = m] - q_m) (ell_j + 1),
+    so with c_j = [-tau <= r_j <= tau] and S = sum_j c_j q_j (ell_j + 1):
+        d loss / d zq_m = lam (q_m - [m = a]) + (1 - lam) q_m (c_m (ell_m + 1) - S).
+
+    clip_override forces c_j for chosen entries (used only to accept either
+    branch for entries whose |r_j| sits on tau to within rounding).
+    """
+    zp = np.asarray(zp_row, dtype=np.float64)
+    zq = np.asarray(zq_row, dtype=np.float64)
+    a = target_argmax(zp)
+    lse_p = _logsumexp(zp)
+    lse_q = _logsumexp(zq)
+    logp = zp - lse_p
+    logq = zq - lse_q
+    q = np.exp(logq)
+    ell = logq - logp
+    r = np.where(q > 0.0, q * ell, 0.0)
+    c = (r >= -tau) & (r <= tau)
+    if clip_override:
+        c = c.copy()
+        for j, v in clip_override.items():
+            c[j] = bool(v)
+    ce = -float(logq[a])
+    clipped = np.where(c, r, np.clip(r, -tau, tau))
+    klc = math.fsum(clipped.tolist())
+    S = math.fsum(np.where(c, q * (ell + 1.0), 0.0).tolist())
+    loss = lam * ce + (1.0 - lam) * klc
+    onehot = np.zeros_like(q)
+    onehot[a] = 1.0
+    grad = grad_scale * (lam * (q - onehot) + (1.0 - lam) * q * (np.where(c, ell + 1.0, 0.0) - S))
+    return RowTerms(argmax=a, lse_p=lse_p, lse_q=lse_q, ce=ce, klc=klc, S=S, loss=loss,
+                    grad=grad, q=q, ell=ell, r=r, c=c)
+
+
+def clip_margin(r: np.ndarray, tau: float) -> np.ndarray:
+    """Relative distance of |r_j| to the clip threshold (0 means on it)."""
+    return np.abs(np.abs(r) - tau) / tau
+
+
+# ---------------------------------------------------------------------------
+# the whole pass over a batch of draft blocks
+# ---------------------------------------------------------------------------
+
+def verify_opd(zp: np.ndarray, zq: np.ndarray, draft: np.ndarray, *, k: int,
+               lam: float, tau: float, grad_scale: float = 1.0,
+               bk: Optional[np.ndarray] = None, row_off: Optional[np.ndarray] = None,
+               want_grad: bool = True) -> dict:
+    """Reference results for B draft blocks.
+
+    Dense layout (row_off is None): row b*k+i holds position i of request b;
+    it is verified when i < clamp(bk[b], 1, k).  Ragged layout: request b
+    owns rows row_off[b]..row_off[b+1]-1, all verified, and its b_k is the
+    row count.  zp/zq are float64 [R, V].
+
+    Unverified rows get the target argmax (the greedy choice is still
+    defined) but no loss and a zero gradient; only verified positions enter
+    the OPD sum and the acceptance scan.
+    """
+    zp = np.asarray(zp, dtype=np.float64)
+    zq = np.asarray(zq, dtype=np.float64)
+    R, V = zp.shape
+    if row_off is None:
+        B = R // k
+        assert B * k == R
+        spans = [(b * k, k, min(max(int(bk[b]), 1), k)) for b in range(B)]
+    else:
+        B = len(row_off) - 1
+        spans = []
+        for b in range(B):
+            n = int(row_off[b + 1] - row_off[b])
+            spans.append((int(row_off[b]), n, n))
+    tgt = np.empty(R, dtype=np.int64)
+    row_loss = np.zeros(R)
+    row_stats = np.zeros((R, 4))
+    verified = np.zeros(R, dtype=bool)
+    grad = np.zeros((R, V)) if want_grad else None
+    acc = np.empty(B, dtype=np.int64)
+    req_loss = np.empty(B)
+    for b, (r0, n, bkb) in enumerate(spans):
+        for i in range(n):
+            r = r0 + i
+            if i < bkb:
+                t = row_terms(zp[r], zq[r], lam, tau, grad_scale)
+                tgt[r] = t.argmax
+                row_loss[r] = t.loss
+                row_stats[r] = (t.lse_p, t.lse_q, t.S, t.klc)
+                verified[r] = True
+                if want_grad:
+                    grad[r] = t.grad
+            else:
+                tgt[r] = target_argmax(zp[r])
+        acc[b] = accepted_length(draft[r0:r0 + n], tgt[r0:r0 + n], bkb)
+        req_loss[b] = math.fsum(row_loss[r0:r0 + n].tolist())
+    total = math.fsum(req_loss.tolist())
+    return dict(tgt_argmax=tgt, acc_len=acc, row_loss=row_loss, req_loss=req_loss,
+                total_loss=total, row_stats=row_stats, grad=grad, verified=verified)
