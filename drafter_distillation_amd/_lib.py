@@ -1,0 +1,232 @@
+"""ctypes binding of libav.so (include/av.h).
+
+Argument marshalling only: every step of the pass runs in the HIP library.
+Tensors are torch CUDA (HIP) tensors; their data pointers and the current
+torch stream are handed to the C ABI.  If the library has not been built, or a
+tensor is not on a GPU, the calls raise instead of falling back to anything.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libav.so")
+
+AV_OK, AV_EINVAL, AV_EUNSUPPORTED, AV_EHIP = 0, -1, -2, -3
+AV_F32, AV_BF16 = 0, 1
+AV_ROUND_CEIL, AV_ROUND_FLOOR = 0, 1
+AV_DEV_TIMEOUT, AV_DEV_BAD_OFFSETS = 1, 2
+AV_MAX_K = 64
+
+
+class AVError(RuntimeError):
+    def __init__(self, fn: str, code: int, detail: str = ""):
+        self.code = code
+        msg = f"{fn} failed: {av_status_str(code)}"
+        if detail:
+            msg += f" ({detail})"
+        super().__init__(msg)
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_SIGS = {
+    "av_length_head": (_i, [_vp, _vp, _f, _f, _i, _i, _i, _i, _vp, _vp, _vp]),
+    "av_workspace_bytes": (_sz, [_i, _i, _i]),
+    "av_workspace_init": (_i, [_vp, _sz, _vp]),
+    "av_verify_opd_fwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _f, _f, _f,
+                               _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i, _vp]),
+    "av_verify_opd_bwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _f, _f, _f,
+                               _vp, _i, _vp]),
+    "av_status_str": (ctypes.c_char_p, [_i]),
+    "av_last_hip_error": (ctypes.c_char_p, []),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libav.so (once).  Raises if it has not been built."""
+    global _lib
+    with _lib_lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build it with `python -m drafter_distillation_amd.build`")
+            h = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in _SIGS.items():
+                fn = getattr(h, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = h
+    return _lib
+
+
+def av_status_str(code: int) -> str:
+    return lib().av_status_str(int(code)).decode()
+
+
+def _check(fn: str, code: int) -> None:
+    if code != AV_OK:
+        detail = lib().av_last_hip_error().decode() if code == AV_EHIP else ""
+        raise AVError(fn, code, detail)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need_gpu(name: str, t: torch.Tensor, dtype=None) -> None:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+# ---------------------------------------------------------------------------
+# workspace cache: one zero-initialised scratch buffer per (device, stream)
+# ---------------------------------------------------------------------------
+
+_ws: dict = {}
+
+
+def av_workspace_bytes(B: int, k: int, R: int) -> int:
+    return int(lib().av_workspace_bytes(int(B), int(k), int(R)))
+
+
+def workspace(dev: torch.device, nbytes: int) -> torch.Tensor:
+    """A workspace of at least nbytes for calls on the current stream of dev."""
+    key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
+    buf = _ws.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        _check("av_workspace_init", lib().av_workspace_init(_ptr(buf), buf.numel(), _stream(dev)))
+        _ws[key] = buf
+    return buf
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+
+def av_length_head(h: torch.Tensor, w: torch.Tensor, bias: float, gamma: float, k: int,
+                   round_mode: int = AV_ROUND_CEIL, rate_out: Optional[torch.Tensor] = None,
+                   bk_out: Optional[torch.Tensor] = None):
+    """Length head (see include/av.h).  Returns (rate [B] float32, bk [B] int32)."""
+    _need_gpu("h", h, torch.float32)
+    _need_gpu("w", w, torch.float32)
+    B, H = h.shape
+    if w.shape != (H,):
+        raise ValueError("w must have shape [H]")
+    dev = h.device
+    rate = rate_out if rate_out is not None else torch.empty(B, dtype=torch.float32, device=dev)
+    bk = bk_out if bk_out is not None else torch.empty(B, dtype=torch.int32, device=dev)
+    with torch.cuda.device(dev):
+        rc = lib().av_length_head(_ptr(h), _ptr(w), float(bias), float(gamma), B, H, int(k),
+                                  int(round_mode), _ptr(rate), _ptr(bk), _stream(dev))
+    _check("av_length_head", rc)
+    return rate, bk
+
+
+def _dtype_code(zp: torch.Tensor) -> int:
+    if zp.dtype == torch.bfloat16:
+        return AV_BF16
+    if zp.dtype == torch.float32:
+        return AV_F32
+    raise ValueError(f"logits must be bfloat16 or float32, got {zp.dtype}")
+
+
+def av_verify_opd_fwd(zp: torch.Tensor, zq: torch.Tensor, draft: torch.Tensor, *, k: int,
+                      bk: Optional[torch.Tensor] = None, row_off: Optional[torch.Tensor] = None,
+                      lam: float, tau: float, grad_scale: float = 1.0, want_grad: bool = True,
+                      want_stats: bool = True, vecs_per_thread: int = 0,
+                      out: Optional[dict] = None) -> dict:
+    """Fused verify + OPD pass (see include/av.h).
+
+    zp, zq: [R, V] bf16/f32; draft: [R] int32; dense layout with bk [B] int32,
+    or ragged layout with row_off [B+1] int32.  Returns a dict of output
+    tensors (tgt_argmax, acc_len, row_loss, req_loss, total_loss, row_stats,
+    grad, status); `out` may supply preallocated tensors under those names.
+    """
+    _need_gpu("zp", zp)
+    _need_gpu("zq", zq, zp.dtype)
+    _need_gpu("draft", draft, torch.int32)
+    if zp.dim() != 2 or zq.shape != zp.shape or draft.shape != (zp.shape[0],):
+        raise ValueError("zp, zq must be [R, V] and draft [R]")
+    R, V = zp.shape
+    dev = zp.device
+    if row_off is not None:
+        _need_gpu("row_off", row_off, torch.int32)
+        B = row_off.numel() - 1
+    else:
+        if bk is None:
+            raise ValueError("dense layout needs bk")
+        _need_gpu("bk", bk, torch.int32)
+        B = bk.numel()
+    o = dict(out or {})
+
+    def get(name, shape, dtype):
+        t = o.get(name)
+        if t is None:
+            t = torch.empty(shape, dtype=dtype, device=dev)
+            o[name] = t
+        return t
+
+    tgt = get("tgt_argmax", (R,), torch.int32)
+    acc = get("acc_len", (B,), torch.int32)
+    row_loss = get("row_loss", (R,), torch.float32)
+    req_loss = get("req_loss", (B,), torch.float32)
+    total = get("total_loss", (1,), torch.float32)
+    stats = get("row_stats", (R, 4), torch.float32) if want_stats else None
+    grad = get("grad", (R, V), torch.float32) if want_grad else None
+    status = get("status", (1,), torch.int32)
+    nbytes = av_workspace_bytes(B, k, R) if B >= 1 and R >= 1 else 0
+    with torch.cuda.device(dev):
+        ws = workspace(dev, nbytes)
+        rc = lib().av_verify_opd_fwd(
+            _dtype_code(zp), B, int(k), V, R, _ptr(row_off), _ptr(zp), _ptr(zq), _ptr(draft),
+            _ptr(bk), float(lam), float(tau), float(grad_scale), _ptr(tgt), _ptr(acc),
+            _ptr(row_loss), _ptr(req_loss), _ptr(total), _ptr(stats), _ptr(grad), _ptr(status),
+            _ptr(ws), ws.numel(), int(vecs_per_thread), _stream(dev))
+    _check("av_verify_opd_fwd", rc)
+    return o
+
+
+def av_verify_opd_bwd(zp: torch.Tensor, zq: torch.Tensor, tgt_argmax: torch.Tensor,
+                      row_stats: torch.Tensor, *, k: int, bk: Optional[torch.Tensor] = None,
+                      row_off: Optional[torch.Tensor] = None, lam: float, tau: float,
+                      grad_scale: float = 1.0, vecs_per_thread: int = 0,
+                      grad: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Gradient alone from saved statistics (see include/av.h)."""
+    _need_gpu("zp", zp)
+    _need_gpu("zq", zq, zp.dtype)
+    _need_gpu("tgt_argmax", tgt_argmax, torch.int32)
+    _need_gpu("row_stats", row_stats, torch.float32)
+    R, V = zp.shape
+    dev = zp.device
+    if row_off is not None:
+        _need_gpu("row_off", row_off, torch.int32)
+        B = row_off.numel() - 1
+    else:
+        _need_gpu("bk", bk, torch.int32)
+        B = bk.numel()
+    if grad is None:
+        grad = torch.empty((R, V), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        rc = lib().av_verify_opd_bwd(
+            _dtype_code(zp), B, int(k), V, R, _ptr(row_off), _ptr(zp), _ptr(zq), _ptr(bk),
+            _ptr(tgt_argmax), _ptr(row_stats), float(lam), float(tau), float(grad_scale),
+            _ptr(grad), int(vecs_per_thread), _stream(dev))
+    _check("av_verify_opd_bwd", rc)
+    return grad

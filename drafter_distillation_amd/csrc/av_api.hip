@@ -1,0 +1,241 @@
+// C ABI of the verify + OPD library: host-side argument checks, launch
+// configuration, error reporting.  Semantics are documented in include/av.h.
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "av.h"
+#include "av_internal.h"
+
+namespace {
+
+thread_local char g_hip_err[256] = "";
+
+int hip_fail(hipError_t e) {
+  snprintf(g_hip_err, sizeof(g_hip_err), "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
+  return AV_EHIP;
+}
+
+// Per-device launch facts, queried once per device and variant.
+struct DeviceInfo {
+  int cus = 0;
+  long long ticks_per_ms = 0;  // wall-clock counter rate
+  int occ[4] = {0, 0, 0, 0};   // fused-kernel workgroups per CU, per variant (no dynamic LDS)
+};
+constexpr int kMaxDevices = 64;
+DeviceInfo g_dev[kMaxDevices];
+std::once_flag g_dev_once[kMaxDevices];
+hipError_t g_dev_err[kMaxDevices];
+
+hipError_t device_info(const DeviceInfo** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_dev_once[dev], [dev]() {
+    DeviceInfo& d = g_dev[dev];
+    hipError_t err = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    int khz = 0;
+    if (err == hipSuccess) err = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+    d.ticks_per_ms = khz > 0 ? (long long)khz : 100000;
+    for (int v = 0; v < 4 && err == hipSuccess; ++v)
+      err = avk::fused_blocks_per_cu((avk::Variant)v, 0, &d.occ[v]);
+    g_dev_err[dev] = err;
+  });
+  if (g_dev_err[dev] != hipSuccess) return g_dev_err[dev];
+  *out = &g_dev[dev];
+  return hipSuccess;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shared validation of the verify entry points.  Fills the layout facts.
+struct Plan {
+  avk::Variant var;
+  int vec, nvmax, nv, nvec, C;
+  bool ragged;
+};
+
+int plan_rows(int dtype, int B, int k, int V, int R, const int32_t* row_off, const void* zp,
+              const void* zq, const float* grad, int vecs_per_thread, Plan* p) {
+  if (dtype != AV_F32 && dtype != AV_BF16) return AV_EUNSUPPORTED;
+  if (B < 1 || k < 1 || k > AV_MAX_K || V < 1 || R < 1) return AV_EINVAL;
+  p->ragged = row_off != nullptr;
+  if (!p->ragged && (long long)R != (long long)B * k) return AV_EINVAL;
+  if (p->ragged && ((long long)R < B || (long long)R > (long long)B * k)) return AV_EINVAL;
+  if (vecs_per_thread < 0) return AV_EINVAL;
+  const int vec = dtype == AV_BF16 ? 8 : 4;
+  const bool vec_ok = V % vec == 0 && aligned16(zp) && aligned16(zq) && (grad == nullptr || aligned16(grad));
+  if (dtype == AV_BF16) p->var = vec_ok ? avk::kBf16x8 : avk::kBf16x1;
+  else p->var = vec_ok ? avk::kF32x4 : avk::kF32x1;
+  p->vec = avk::variant_vec(p->var);
+  p->nvmax = avk::variant_nvmax(p->var);
+  p->nv = (vecs_per_thread == 0 || vecs_per_thread > p->nvmax) ? p->nvmax : vecs_per_thread;
+  p->nvec = V / p->vec;
+  const long long per_chunk = (long long)avk::kBlock * p->nv;
+  const long long C = (p->nvec + per_chunk - 1) / per_chunk;
+  if (C > avk::kMaxChunks) return AV_EUNSUPPORTED;
+  p->C = (int)C;
+  if ((long long)R * C > 0x7fffffffLL) return AV_EUNSUPPORTED;
+  return AV_OK;
+}
+
+bool finite(float x) { return isfinite(x); }
+
+}  // namespace
+
+extern "C" {
+
+const char* av_status_str(int status) {
+  switch (status) {
+    case AV_OK: return "AV_OK";
+    case AV_EINVAL: return "AV_EINVAL: invalid argument";
+    case AV_EUNSUPPORTED: return "AV_EUNSUPPORTED: outside the implemented range";
+    case AV_EHIP: return "AV_EHIP: HIP runtime error";
+    default: return "unknown av_status";
+  }
+}
+
+const char* av_last_hip_error(void) { return g_hip_err; }
+
+size_t av_workspace_bytes(int B, int k, int R) {
+  if (B < 1 || k < 1 || k > AV_MAX_K || R < 1 || (long long)R > (long long)B * k) return 0;
+  return avk::ws_total(B, R);
+}
+
+int av_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace || workspace_bytes < avk::kCtlBytes || !aligned16(workspace)) return AV_EINVAL;
+  hipError_t e = avk::launch_zero((uint64_t*)workspace, workspace_bytes / 8, (hipStream_t)stream);
+  return e == hipSuccess ? AV_OK : hip_fail(e);
+}
+
+int av_length_head(const float* h, const float* w, float bias, float gamma, int B, int H, int k,
+                   int round_mode, float* rate_out, int32_t* bk_out, void* stream) {
+  if (!h || !w || !bk_out) return AV_EINVAL;
+  if (B < 1 || H < 1 || k < 1 || k > AV_MAX_K) return AV_EINVAL;
+  if (round_mode != AV_ROUND_CEIL && round_mode != AV_ROUND_FLOOR) return AV_EINVAL;
+  if (!finite(bias) || !finite(gamma) || gamma < 0.0f) return AV_EINVAL;
+  avk::HeadArgs a;
+  a.h = h;
+  a.w = w;
+  a.rate = rate_out;
+  a.bk = bk_out;
+  a.bias = bias;
+  a.gamma = gamma;
+  a.B = B;
+  a.H = H;
+  a.k = k;
+  a.mode = round_mode;
+  hipError_t e = avk::launch_head(a, (hipStream_t)stream);
+  return e == hipSuccess ? AV_OK : hip_fail(e);
+}
+
+int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_off,
+                      const void* zp, const void* zq, const int32_t* draft, const int32_t* bk,
+                      float lambda, float tau, float grad_scale, int32_t* tgt_argmax,
+                      int32_t* acc_len, float* row_loss, float* req_loss, float* total_loss,
+                      float* row_stats, float* grad_zq, int32_t* status, void* workspace,
+                      size_t workspace_bytes, int vecs_per_thread, void* stream) {
+  if (!zp || !zq || !draft || !tgt_argmax || !acc_len || !row_loss || !workspace) return AV_EINVAL;
+  if (!row_off && !bk) return AV_EINVAL;
+  if (!(lambda >= 0.0f && lambda <= 1.0f)) return AV_EINVAL;
+  if (!(tau > 0.0f)) return AV_EINVAL;
+  if (!finite(grad_scale)) return AV_EINVAL;
+  if (row_stats && !aligned16(row_stats)) return AV_EINVAL;
+  if (!aligned16(workspace)) return AV_EINVAL;
+  Plan p;
+  int rc = plan_rows(dtype, B, k, V, R, row_off, zp, zq, grad_zq, vecs_per_thread, &p);
+  if (rc != AV_OK) return rc;
+  if (p.ragged && B + 1 > 16384) return AV_EUNSUPPORTED;  // offsets are cached in LDS
+  if (workspace_bytes < avk::ws_total(B, R)) return AV_EINVAL;
+
+  const DeviceInfo* dev = nullptr;
+  hipError_t e = device_info(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+
+  const size_t lds = p.ragged ? (size_t)(B + 1) * sizeof(int32_t) : 0;
+  int occ = dev->occ[p.var];
+  if (lds) {
+    e = avk::fused_blocks_per_cu(p.var, lds, &occ);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  if (occ < 1) return AV_EUNSUPPORTED;
+  const long long n_items = (long long)R * p.C;
+  long long grid = (long long)occ * dev->cus;
+  if (grid > n_items) grid = n_items;
+  if (n_items + grid > 0xffffffffLL) return AV_EUNSUPPORTED;
+
+  char* ws = (char*)workspace;
+  avk::FwdArgs a;
+  a.zp = zp;
+  a.zq = zq;
+  a.draft = draft;
+  a.bk = bk;
+  a.row_off = row_off;
+  a.tgt = tgt_argmax;
+  a.acc = acc_len;
+  a.row_loss = row_loss;
+  a.req_loss = req_loss;
+  a.total = total_loss;
+  a.stats = row_stats;
+  a.grad = grad_zq;
+  a.status_out = status;
+  a.ctl = (uint64_t*)ws;
+  a.slots = (uint64_t*)(ws + avk::ws_slots_off());
+  a.rowres = (uint64_t*)(ws + avk::ws_rowres_off(R));
+  a.reqres = (uint64_t*)(ws + avk::ws_reqres_off(R));
+  a.timeout_ticks = dev->ticks_per_ms * 2000;  // 2 s per wait
+  a.B = B;
+  a.k = k;
+  a.V = V;
+  a.R = R;
+  a.C = p.C;
+  a.nvec = p.nvec;
+  a.ragged = p.ragged ? 1 : 0;
+  a.n_items = (uint32_t)n_items;
+  a.lam = lambda;
+  a.tau = tau;
+  a.gs = grad_scale;
+  e = avk::launch_fused(p.var, a, (int)grid, lds, (hipStream_t)stream);
+  return e == hipSuccess ? AV_OK : hip_fail(e);
+}
+
+int av_verify_opd_bwd(int dtype, int B, int k, int V, int R, const int32_t* row_off,
+                      const void* zp, const void* zq, const int32_t* bk,
+                      const int32_t* tgt_argmax, const float* row_stats, float lambda,
+                      float tau, float grad_scale, float* grad_zq, int vecs_per_thread,
+                      void* stream) {
+  if (!zp || !zq || !tgt_argmax || !row_stats || !grad_zq) return AV_EINVAL;
+  if (!row_off && !bk) return AV_EINVAL;
+  if (!(lambda >= 0.0f && lambda <= 1.0f)) return AV_EINVAL;
+  if (!(tau > 0.0f)) return AV_EINVAL;
+  if (!finite(grad_scale)) return AV_EINVAL;
+  if (!aligned16(row_stats)) return AV_EINVAL;
+  Plan p;
+  int rc = plan_rows(dtype, B, k, V, R, row_off, zp, zq, grad_zq, vecs_per_thread, &p);
+  if (rc != AV_OK) return rc;
+  avk::BwdArgs a;
+  a.zp = zp;
+  a.zq = zq;
+  a.bk = bk;
+  a.tgt = tgt_argmax;
+  a.stats = row_stats;
+  a.grad = grad_zq;
+  a.B = B;
+  a.k = k;
+  a.V = V;
+  a.R = R;
+  a.C = p.C;
+  a.nvec = p.nvec;
+  a.ragged = p.ragged ? 1 : 0;
+  a.lam = lambda;
+  a.tau = tau;
+  a.gs = grad_scale;
+  hipError_t e = avk::launch_bwd(p.var, a, (hipStream_t)stream);
+  return e == hipSuccess ? AV_OK : hip_fail(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// Internal interface between the C ABI (av_api.hip) and the gfx950 kernels
+// (av_kernels.hip).  Not installed; callers use include/av.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace avk {
+
+constexpr int kBlock = 256;      // threads per workgroup: 4 wave64s
+constexpr int kMaxChunks = 64;   // chunks per row; one lane of wave 0 each
+constexpr int kSlotWords = 8;    // tagged 64-bit words per (row, chunk) slot
+
+// Workspace layout (all 64-bit words):
+//   ctl[0]   status (high 32 bits) | dispense counter (low 32 bits)
+//   ctl[1]   launch epoch (low 32 bits)
+//   slots    [R][kMaxChunks][kSlotWords]  per-chunk partial statistics
+//   rowres   [R][2]                       per-row target argmax and loss
+//   reqres   [B][2]                       per-request loss sum (float64 halves)
+constexpr size_t kCtlBytes = 256;
+
+inline size_t ws_slots_off() { return kCtlBytes; }
+inline size_t ws_rowres_off(int R) { return ws_slots_off() + (size_t)R * kMaxChunks * kSlotWords * 8; }
+inline size_t ws_reqres_off(int R) { return ws_rowres_off(R) + (size_t)R * 16; }
+inline size_t ws_total(int B, int R) {
+  size_t n = ws_reqres_off(R) + (size_t)B * 16;
+  return (n + 255) & ~(size_t)255;
+}
+
+// Kernel variants: element type and 16-byte vector width (or scalar access
+// for rows that are not 16-byte aligned).
+enum Variant { kBf16x8 = 0, kBf16x1 = 1, kF32x4 = 2, kF32x1 = 3 };
+
+inline int variant_vec(Variant v) { return v == kBf16x8 ? 8 : v == kF32x4 ? 4 : 1; }
+// Most vectors (of variant_vec elements) one thread holds per chunk.
+inline int variant_nvmax(Variant v) { return v == kBf16x8 ? 4 : v == kF32x4 ? 8 : 16; }
+
+struct FwdArgs {
+  const void* zp;
+  const void* zq;
+  const int32_t* draft;
+  const int32_t* bk;
+  const int32_t* row_off;
+  int32_t* tgt;
+  int32_t* acc;
+  float* row_loss;
+  float* req_loss;
+  float* total;
+  float* stats;
+  float* grad;
+  int32_t* status_out;
+  uint64_t* ctl;
+  uint64_t* slots;
+  uint64_t* rowres;
+  uint64_t* reqres;
+  long long timeout_ticks;
+  int B, k, V, R;
+  int C;         // chunks per row
+  int nvec;      // vectors per row (V / vec)
+  int ragged;
+  uint32_t n_items;  // R * C
+  float lam, tau, gs;
+};
+
+struct BwdArgs {
+  const void* zp;
+  const void* zq;
+  const int32_t* bk;
+  const int32_t* tgt;
+  const float* stats;
+  float* grad;
+  int B, k, V, R, C, nvec, ragged;
+  float lam, tau, gs;
+};
+
+struct HeadArgs {
+  const float* h;
+  const float* w;
+  float* rate;
+  int32_t* bk;
+  float bias, gamma;
+  int B, H, k, mode;
+};
+
+hipError_t launch_fused(Variant v, const FwdArgs& a, int grid, size_t lds, hipStream_t s);
+hipError_t fused_blocks_per_cu(Variant v, size_t lds, int* out);
+hipError_t launch_bwd(Variant v, const BwdArgs& a, hipStream_t s);
+hipError_t launch_head(const HeadArgs& a, hipStream_t s);
+hipError_t launch_zero(uint64_t* p, size_t words, hipStream_t s);
+
+}  // namespace avk

@@ -38,8 +38,10 @@ Nothing here computes a verification result, a loss or a gradient.
 
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 from typing import Dict, Optional, Tuple
 
 import numpy as np
@@ -232,9 +234,19 @@ def _head_inputs(c: dict, seed: int):
     return h.astype(np.float32), w.astype(np.float32)
 
 
-def make(name: str, seed: int = 0, **overrides) -> Workload:
+def _default_workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def make(name: str, seed: int = 0, workers: Optional[int] = None, **overrides) -> Workload:
     """Build a whole workload.  Overrides (B, k, V, H, dtype, sigma, lam, tau,
-    ...) give smaller or edge-case variants of the same recipe."""
+    ...) give smaller or edge-case variants of the same recipe.  Requests are
+    generated on `workers` threads; each request has its own random stream,
+    so the result does not depend on the thread count."""
     c = _cfg(name, overrides)
     B, k, V = c["B"], c["k"], c["V"]
     if c["layout"] == "ragged":
@@ -249,13 +261,22 @@ def make(name: str, seed: int = 0, **overrides) -> Workload:
     zp = np.empty((R, V), dtype=sdt)
     zq = np.empty((R, V), dtype=sdt)
     draft = np.empty(R, dtype=np.int32)
-    r0 = 0
-    for b in range(B):
+    starts = np.concatenate([[0], np.cumsum(n)[:-1]]).astype(np.int64)
+
+    def fill(b: int) -> None:
         p_s, q_s, d = _gen_request(c, seed, b, int(n[b]))
+        r0 = int(starts[b])
         zp[r0:r0 + n[b]] = p_s
         zq[r0:r0 + n[b]] = q_s
         draft[r0:r0 + n[b]] = d
-        r0 += int(n[b])
+
+    nw = workers or _default_workers()
+    if nw <= 1 or B == 1:
+        for b in range(B):
+            fill(b)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=nw) as ex:
+            list(ex.map(fill, range(B)))
     if c["bk"] in ("head", "planted"):
         h, w = _head_inputs(c, seed)
     else:

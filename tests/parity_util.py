@@ -1,0 +1,185 @@
+"""Helpers shared by the GPU parity tests: move seeded workloads to the GPU,
+run the HIP path through the binding, and compare with the float64 oracle.
+
+Acceptance rule (the arithmetic behind it is written out in the design notes):
+  * bit-exact: target argmax, accepted lengths, b_k (except b_k decisions the
+    oracle flags as within 1e-9 of an integer);
+  * row loss, clipped-KL sum, S: |gpu - ref| <= 1e-3 |ref| + 1e-5;
+  * lse_p, lse_q: |gpu - ref| <= 2e-6 |ref| + 2e-6;
+  * gradient, per entry: |gpu - ref| <= 1e-3 |ref| + 2e-5 gs q_j (1 + |ell_j| + |S|)
+    -- the second term bounds float32 rounding of q_j, ell_j and S where the
+    reference itself cancels to near zero;
+  * an entry whose |r_j| lies within 1e-4 tau of tau may be classified either
+    way by float32; rows with such entries are accepted if they match the
+    oracle with any combination of those indicators flipped (at most 3).
+"""
+
+from __future__ import annotations
+
+import itertools
+import math
+from typing import Iterable, Optional
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+
+LOSS_RTOL, LOSS_ATOL = 1e-3, 1e-5
+LSE_RTOL, LSE_ATOL = 2e-6, 2e-6
+GRAD_RTOL, GRAD_QTOL = 1e-3, 2e-5
+CLIP_AMBIG = 1e-4
+
+
+def logits_tensor(a: np.ndarray, dtype: str, dev="cuda") -> torch.Tensor:
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+
+def decode_rows(w: synth.Workload, which: str, rows) -> np.ndarray:
+    a = (w.zp if which == "zp" else w.zq)[rows]
+    if w.dtype == "bf16":
+        return oracle.bf16_bits_to_f64(a)
+    return a.astype(np.float64)
+
+
+def gpu_inputs(w: synth.Workload, dev="cuda") -> dict:
+    d = dict(zp=logits_tensor(w.zp, w.dtype, dev), zq=logits_tensor(w.zq, w.dtype, dev),
+             draft=torch.from_numpy(w.draft.astype(np.int32)).to(dev))
+    if w.row_off is not None:
+        d["row_off"] = torch.from_numpy(w.row_off.astype(np.int32)).to(dev)
+    return d
+
+
+def run_fwd(av, inp: dict, w: synth.Workload, *, bk: Optional[np.ndarray], lam: float, tau: float,
+            gs: float = 1.0, vecs: int = 0, want_grad: bool = True) -> dict:
+    kw = dict(k=w.k, lam=lam, tau=tau, grad_scale=gs, vecs_per_thread=vecs, want_grad=want_grad)
+    if w.row_off is not None:
+        kw["row_off"] = inp["row_off"]
+    else:
+        kw["bk"] = torch.from_numpy(np.asarray(bk, dtype=np.int32)).to(inp["zp"].device)
+    out = av.av_verify_opd_fwd(inp["zp"], inp["zq"], inp["draft"], **kw)
+    torch.cuda.synchronize()
+    return {k: (v.cpu().numpy() if isinstance(v, torch.Tensor) else v) for k, v in out.items()}
+
+
+def spans(w: synth.Workload, bk: Optional[np.ndarray]):
+    """(first row, stored rows, effective b_k) per request."""
+    if w.row_off is not None:
+        n = np.diff(w.row_off)
+        return [(int(w.row_off[b]), int(n[b]), int(n[b])) for b in range(w.B)]
+    return [(b * w.k, w.k, min(max(int(bk[b]), 1), w.k)) for b in range(w.B)]
+
+
+def close(a, b, rtol, atol) -> bool:
+    return abs(float(a) - float(b)) <= rtol * abs(float(b)) + atol
+
+
+def grad_row_ok(g: np.ndarray, t: oracle.RowTerms, gs: float) -> np.ndarray:
+    tol = GRAD_RTOL * np.abs(t.grad) + GRAD_QTOL * abs(gs) * t.q * (1.0 + np.abs(t.ell) + abs(t.S))
+    return np.abs(g.astype(np.float64) - t.grad) <= tol
+
+
+def check_row(r: int, out: dict, zp_row, zq_row, lam, tau, gs, verified: bool, errors: list):
+    """Compare one row of GPU output with the oracle; append messages to errors."""
+    a_ref = oracle.target_argmax(zp_row)
+    if int(out["tgt_argmax"][r]) != a_ref:
+        errors.append(f"row {r}: argmax {out['tgt_argmax'][r]} != {a_ref}")
+    grad = out.get("grad")
+    stats = out.get("row_stats")
+    if not verified:
+        if out["row_loss"][r] != 0.0:
+            errors.append(f"row {r}: unverified loss {out['row_loss'][r]}")
+        if grad is not None and np.any(grad[r] != 0.0):
+            errors.append(f"row {r}: unverified row has a nonzero gradient")
+        if stats is not None and np.any(stats[r] != 0.0):
+            errors.append(f"row {r}: unverified row has nonzero stats")
+        return
+    t = oracle.row_terms(zp_row, zq_row, lam, tau, gs)
+    variants = [t]
+    amb = np.nonzero(oracle.clip_margin(t.r, tau) <= CLIP_AMBIG)[0] if math.isfinite(tau) else []
+    if 0 < len(amb) <= 3:
+        for flips in itertools.product([False, True], repeat=len(amb)):
+            if any(flips):
+                ov = {int(j): (not bool(t.c[j])) if f else bool(t.c[j]) for j, f in zip(amb, flips)}
+                variants.append(oracle.row_terms(zp_row, zq_row, lam, tau, gs, clip_override=ov))
+    msgs = None
+    for v in variants:
+        m = []
+        if not close(out["row_loss"][r], v.loss, LOSS_RTOL, LOSS_ATOL):
+            m.append(f"loss {out['row_loss'][r]} vs {v.loss}")
+        if stats is not None:
+            s = stats[r]
+            if not close(s[0], v.lse_p, LSE_RTOL, LSE_ATOL):
+                m.append(f"lse_p {s[0]} vs {v.lse_p}")
+            if not close(s[1], v.lse_q, LSE_RTOL, LSE_ATOL):
+                m.append(f"lse_q {s[1]} vs {v.lse_q}")
+            if not close(s[2], v.S, LOSS_RTOL, LOSS_ATOL):
+                m.append(f"S {s[2]} vs {v.S}")
+            if not close(s[3], v.klc, LOSS_RTOL, LOSS_ATOL):
+                m.append(f"KLc {s[3]} vs {v.klc}")
+        if grad is not None:
+            ok = grad_row_ok(grad[r], v, gs)
+            if not ok.all():
+                j = int(np.argmin(ok))
+                m.append(f"grad: {np.count_nonzero(~ok)} entries off, e.g. j={j} {grad[r][j]} vs {v.grad[j]}")
+        if not m:
+            return
+        if msgs is None:
+            msgs = m
+    errors.append(f"row {r}: " + "; ".join(msgs))
+
+
+def check_workload(out: dict, w: synth.Workload, bk: Optional[np.ndarray], lam: float, tau: float,
+                   gs: float = 1.0, rows: Optional[Iterable[int]] = None, max_errors: int = 10):
+    """Full comparison (rows=None) or comparison on sampled rows; argmax and
+    acceptance are always checked on every row and request."""
+    errors: list = []
+    sp = spans(w, bk)
+    verified = np.zeros(w.R, dtype=bool)
+    for r0, n, bkb in sp:
+        verified[r0:r0 + bkb] = True
+    # argmax of every row and acceptance of every request: exact
+    tgt_ref = np.empty(w.R, dtype=np.int64)
+    for r in range(w.R):
+        tgt_ref[r] = oracle.target_argmax(decode_rows(w, "zp", r))
+    bad = np.nonzero(out["tgt_argmax"] != tgt_ref)[0]
+    if len(bad):
+        errors.append(f"argmax differs on {len(bad)} rows, e.g. row {bad[0]}: "
+                      f"{out['tgt_argmax'][bad[0]]} vs {tgt_ref[bad[0]]}")
+    for b, (r0, n, bkb) in enumerate(sp):
+        acc = oracle.accepted_length(w.draft[r0:r0 + n], tgt_ref[r0:r0 + n], bkb)
+        if int(out["acc_len"][b]) != acc:
+            errors.append(f"request {b}: acc {out['acc_len'][b]} vs {acc}")
+    # per-row loss / stats / gradient
+    check = range(w.R) if rows is None else rows
+    for r in check:
+        check_row(r, out, decode_rows(w, "zp", r), decode_rows(w, "zq", r), lam, tau, gs,
+                  bool(verified[r]), errors)
+        if len(errors) >= max_errors:
+            break
+    # reductions: per request from the (already checked) row losses, in float64
+    rl = out["row_loss"].astype(np.float64)
+    for b, (r0, n, bkb) in enumerate(sp):
+        ref = math.fsum(rl[r0:r0 + bkb].tolist())
+        if not close(out["req_loss"][b], ref, 1e-6, 1e-6):
+            errors.append(f"request {b}: req_loss {out['req_loss'][b]} vs sum of rows {ref}")
+    tot = math.fsum(out["req_loss"].astype(np.float64).tolist())
+    if not close(out["total_loss"][0], tot, 1e-6, 1e-5):
+        errors.append(f"total {out['total_loss'][0]} vs {tot}")
+    if int(out["status"][0]) != 0:
+        errors.append(f"device status {out['status'][0]}")
+    return errors
+
+
+def oracle_reductions(w: synth.Workload, bk, lam, tau, gs=1.0) -> dict:
+    """Whole-batch oracle (small workloads only)."""
+    zp = decode_rows(w, "zp", slice(None))
+    zq = decode_rows(w, "zq", slice(None))
+    if w.row_off is not None:
+        return oracle.verify_opd(zp, zq, w.draft, k=w.k, lam=lam, tau=tau, grad_scale=gs,
+                                 row_off=w.row_off, want_grad=False)
+    return oracle.verify_opd(zp, zq, w.draft, k=w.k, lam=lam, tau=tau, grad_scale=gs, bk=bk,
+                             want_grad=False)

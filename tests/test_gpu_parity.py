@@ -1,0 +1,340 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on
+the same seeded inputs.  Small shapes are compared entry by entry on every
+row; the full-size workloads, in the launch configuration the benchmark
+uses, are compared on every argmax and acceptance length and on sampled rows
+of loss, statistics and gradient."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity_util import (check_workload, gpu_inputs, logits_tensor, oracle_reductions, run_fwd,
+                         spans)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def av():
+    import drafter_distillation_amd as dd
+    dd.lib()
+    return dd
+
+
+def head_bk(w):
+    _, bk, _ = oracle.length_head(w.h, w.w, w.bias, w.gamma, w.k)
+    return bk
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def assert_no_errors(errors):
+    assert not errors, "\n".join(errors[:10])
+
+
+# ---------------------------------------------------------------------------
+# length head
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "single", "concurrent", "long"])
+@pytest.mark.parametrize("mode", ["ceil", "floor"])
+def test_length_head(av, name, mode):
+    w = synth.make(name, V=64)  # only the head inputs matter here
+    say(f"length head {name} {mode}")
+    for gamma, bias in [(1.0, 0.0), (0.75, 0.3), (1.6, -2.0)]:
+        rate, bk = av.av_length_head(torch.from_numpy(w.h).cuda(), torch.from_numpy(w.w).cuda(),
+                                     bias, gamma, w.k,
+                                     av.AV_ROUND_CEIL if mode == "ceil" else av.AV_ROUND_FLOOR)
+        ref_rate, ref_bk, margin = oracle.length_head(w.h, w.w, bias, gamma, w.k, mode)
+        rate, bk = rate.cpu().numpy(), bk.cpu().numpy()
+        sure = margin > 1e-9
+        assert np.array_equal(bk[sure], ref_bk[sure])
+        assert np.all(np.abs(bk[~sure] - ref_bk[~sure]) <= 1)
+        np.testing.assert_allclose(rate, ref_rate, rtol=1e-6, atol=1e-30)
+
+
+def test_length_head_extremes(av):
+    H = 300
+    w = np.full(H, 1.0, np.float32)
+    h = np.stack([np.zeros(H), np.full(H, 0.5), np.full(H, -0.5), np.full(H, 1e-3)]).astype(np.float32)
+    for mode, code in (("ceil", av.AV_ROUND_CEIL), ("floor", av.AV_ROUND_FLOOR)):
+        rate, bk = av.av_length_head(torch.from_numpy(h).cuda(), torch.from_numpy(w).cuda(),
+                                     0.0, 1.0, 16, code)
+        _, ref, _ = oracle.length_head(h, w, 0.0, 1.0, 16, mode)
+        assert list(bk.cpu().numpy()) == list(ref)
+        assert rate.cpu().numpy()[0] == 0.5
+
+
+# ---------------------------------------------------------------------------
+# whole-batch parity on small shapes (every row, every entry)
+# ---------------------------------------------------------------------------
+
+def full_parity(av, w, bk, lam, tau, gs=1.0, vecs=0):
+    say(f"parity {w.name} B={w.B} k={w.k} V={w.V} {w.dtype} {w.layout} lam={lam} tau={tau} "
+        f"gs={gs} vecs={vecs}")
+    inp = gpu_inputs(w)
+    out = run_fwd(av, inp, w, bk=bk, lam=lam, tau=tau, gs=gs, vecs=vecs)
+    assert_no_errors(check_workload(out, w, bk, lam, tau, gs))
+    ref = oracle_reductions(w, bk, lam, tau, gs)
+    np.testing.assert_allclose(out["req_loss"], ref["req_loss"], rtol=1e-3, atol=1e-4)
+    assert math.isclose(out["total_loss"][0], ref["total_loss"], rel_tol=1e-3, abs_tol=1e-4)
+    return out
+
+
+@pytest.mark.parametrize("vecs", [0, 1])
+def test_tiny_workload(av, vecs):
+    w = synth.make("tiny")
+    full_parity(av, w, head_bk(w), w.lam, w.tau, vecs=vecs)
+
+
+def test_single_request_full_vocab(av):
+    w = synth.make("single")
+    full_parity(av, w, head_bk(w), w.lam, w.tau)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V", [1, 7, 8, 37, 64, 1000, 2056, 10000, 10001, 65544])
+@pytest.mark.parametrize("vecs", [0, 1])
+def test_small_shapes(av, dtype, V, vecs):
+    w = synth.make("concurrent", B=3, V=V, dtype=dtype)
+    bk = np.array([1, 16, 7])
+    full_parity(av, w, bk, 0.5, 0.1, gs=0.25, vecs=vecs)
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.5, 1.0])
+@pytest.mark.parametrize("tau", [0.01, 0.05, 0.1, 1e9, float("inf")])
+def test_lambda_tau_branches(av, lam, tau):
+    w = synth.make("long", B=2, V=3000)
+    full_parity(av, w, np.array([32, 17]), lam, tau, vecs=1)
+
+
+@pytest.mark.parametrize("vecs", [0, 1])
+def test_ragged_small(av, vecs):
+    w = synth.make("ragged", B=10, V=5000)
+    full_parity(av, w, None, 0.5, 0.1, gs=1.0 / w.R, vecs=vecs)
+
+
+def test_verification_length_edges_and_acceptance(av):
+    # b_k outside [1, k] is clamped; all-accepted, none-accepted and
+    # out-of-range drafts.
+    w = synth.make("concurrent", B=6, V=2000)
+    zp = oracle.bf16_bits_to_f64(w.zp)
+    tgt = np.argmax(zp, axis=1).astype(np.int32)
+    d = w.draft.copy()
+    d[0:16] = tgt[0:16]                 # request 0 accepts everything
+    d[16:32] = tgt[16:32]
+    d[16] = (tgt[16] + 1) % w.V         # request 1 rejects the first token
+    d[32:48] = tgt[32:48]
+    d[35] = -5                          # request 2: out-of-range draft
+    d[48:64] = tgt[48:64]
+    d[50] = w.V                         # request 3: out-of-range draft (= V)
+    d[64:80] = tgt[64:80]               # request 4 accepts all but b_k = 0 -> 1
+    w.draft = d
+    bk = np.array([16, 16, 16, 99, 0, -3])
+    out = full_parity(av, w, bk, 0.5, 0.1)
+    assert list(out["acc_len"][:5]) == [16, 0, 3, 2, 1]
+
+
+def test_ties_across_thread_chunk_and_vector_boundaries(av):
+    # bf16 exact ties placed so that the lowest index is in a later thread,
+    # a later vector, an earlier chunk, or the same 8-wide vector.
+    w = synth.make("concurrent", B=1, V=12000, dtype="bf16")
+    zp = w.zp.copy()
+    big = synth.to_bf16_bits(np.array([40.0]))[0]
+    pairs = [(5, 9), (7, 2047), (2048, 4000), (100, 11999), (3, 4), (8191, 8192), (0, 11998),
+             (6000, 6001), (2047, 2048), (11990, 11991), (1, 2), (4095, 4096), (123, 4567),
+             (10000, 10001), (9, 10), (2, 11999)]
+    for i, (j1, j2) in enumerate(pairs):
+        zp[i, j1] = big
+        zp[i, j2] = big
+    zp[15, 50] = big                    # three-way tie
+    w.zp = zp
+    for vecs in (0, 1, 2):
+        out = full_parity(av, w, np.array([16]), 0.5, 0.1, vecs=vecs)
+        assert list(out["tgt_argmax"][:15]) == [min(p) for p in pairs[:15]]
+        assert out["tgt_argmax"][15] == 2
+
+
+def test_negative_clip_branch(av):
+    # Target mass concentrated on one token the drafter under-weights gives
+    # r_j = q_j log(q_j / p_j) < -tau (never produced by the seeded workloads).
+    rng = np.random.default_rng(7)
+    B, k, V = 2, 4, 4096
+    zp = rng.normal(0, 1, (B * k, V))
+    zq = zp + rng.normal(0, 0.5, (B * k, V))
+    for r in range(B * k):
+        j = 17 * (r + 1)
+        zp[r, j] = 14.0                 # p_j ~ 0.97
+        zq[r, j] = 10.5 + 0.3 * r       # q_j ~ 0.3-0.9
+    w = synth.make("concurrent", B=B, V=V, dtype="f32")
+    w.k = k
+    w.zp = zp.astype(np.float32)
+    w.zq = zq.astype(np.float32)
+    w.draft = np.argmax(w.zq, axis=1).astype(np.int32)
+    t = oracle.row_terms(w.zp[0].astype(np.float64), w.zq[0].astype(np.float64), 0.5, 0.1)
+    assert t.r.min() < -0.1             # the negative branch is exercised
+    full_parity(av, w, np.array([4, 3]), 0.5, 0.1)
+    full_parity(av, w, np.array([4, 3]), 0.0, 0.05, vecs=1)
+
+
+# ---------------------------------------------------------------------------
+# standalone backward, determinism, device-side status
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,kw", [("concurrent", dict(B=4, V=10000)),
+                                      ("concurrent", dict(B=2, V=1001, dtype="f32")),
+                                      ("ragged", dict(B=6, V=4096))])
+def test_bwd_matches_fused_bits(av, name, kw):
+    w = synth.make(name, **kw)
+    bk = None if w.row_off is not None else np.array([1, 16, 9, 4][:w.B])
+    inp = gpu_inputs(w)
+    say(f"bwd vs fused {name} {kw}")
+    for lam, tau in [(0.5, 0.1), (0.0, 1e9), (1.0, 0.05)]:
+        out = run_fwd(av, inp, w, bk=bk, lam=lam, tau=tau, gs=0.5)
+        kwb = dict(k=w.k, lam=lam, tau=tau, grad_scale=0.5)
+        if w.row_off is not None:
+            kwb["row_off"] = inp["row_off"]
+        else:
+            kwb["bk"] = torch.from_numpy(bk.astype(np.int32)).cuda()
+        g = av.av_verify_opd_bwd(inp["zp"], inp["zq"], torch.from_numpy(out["tgt_argmax"]).cuda(),
+                                 torch.from_numpy(out["row_stats"]).cuda(), **kwb)
+        g = g.cpu().numpy()
+        assert np.array_equal(g.view(np.uint32), out["grad"].view(np.uint32))
+
+
+def test_repeat_calls_are_bit_identical(av):
+    w = synth.make("concurrent", B=8, V=30000)
+    bk = head_bk(w)
+    inp = gpu_inputs(w)
+    a = run_fwd(av, inp, w, bk=bk, lam=0.5, tau=0.1)
+    for _ in range(3):
+        b = run_fwd(av, inp, w, bk=bk, lam=0.5, tau=0.1)
+        for key in ("tgt_argmax", "acc_len", "row_loss", "req_loss", "total_loss", "row_stats",
+                    "grad"):
+            assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), key
+
+
+def test_forward_only_matches_fused(av):
+    w = synth.make("concurrent", B=3, V=9000)
+    bk = np.array([5, 16, 1])
+    inp = gpu_inputs(w)
+    a = run_fwd(av, inp, w, bk=bk, lam=0.5, tau=0.1)
+    b = run_fwd(av, inp, w, bk=bk, lam=0.5, tau=0.1, want_grad=False)
+    for key in ("tgt_argmax", "acc_len", "row_loss", "req_loss", "total_loss", "row_stats"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_bad_ragged_offsets_are_reported_not_computed(av):
+    w = synth.make("ragged", B=5, V=512)
+    inp = gpu_inputs(w)
+    bad = w.row_off.copy()
+    bad[2] = bad[1]                      # request 1 with zero rows
+    inp["row_off"] = torch.from_numpy(bad.astype(np.int32)).cuda()
+    out = av.av_verify_opd_fwd(inp["zp"], inp["zq"], inp["draft"], k=w.k, row_off=inp["row_off"],
+                               lam=0.5, tau=0.1)
+    torch.cuda.synchronize()
+    assert int(out["status"].item()) & av.AV_DEV_BAD_OFFSETS
+    # the workspace is left ready for the next call
+    good = run_fwd(av, gpu_inputs(w), w, bk=None, lam=0.5, tau=0.1)
+    assert int(good["status"][0]) == 0
+
+
+def test_graph_replay(av):
+    # Each replay of a captured launch must see a fresh epoch.
+    w = synth.make("concurrent", B=4, V=20000)
+    bk = torch.from_numpy(head_bk(w).astype(np.int32)).cuda()
+    inp = gpu_inputs(w)
+    ref = av.av_verify_opd_fwd(inp["zp"], inp["zq"], inp["draft"], k=w.k, bk=bk, lam=0.5, tau=0.1)
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in ref.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        out = av.av_verify_opd_fwd(inp["zp"], inp["zq"], inp["draft"], k=w.k, bk=bk, lam=0.5,
+                                   tau=0.1)  # warm-up: allocates the stream's workspace
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        av.av_verify_opd_fwd(inp["zp"], inp["zq"], inp["draft"], k=w.k, bk=bk, lam=0.5, tau=0.1,
+                             out=out)
+    for _ in range(4):
+        for t in out.values():
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for key in ref:
+            assert torch.equal(out[key], ref[key]), key
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads in the benchmark's launch configuration
+# ---------------------------------------------------------------------------
+
+def sample_rows(w, bk, n_per_kind=6, seed=0):
+    rng = np.random.default_rng(seed)
+    ver, unv = [], []
+    for r0, n, bkb in spans(w, bk):
+        ver.extend(range(r0, r0 + bkb))
+        unv.extend(range(r0 + bkb, r0 + n))
+    rows = list(rng.choice(ver, size=min(n_per_kind, len(ver)), replace=False))
+    rows += [ver[0], ver[-1]]
+    if unv:
+        rows += list(rng.choice(unv, size=min(n_per_kind // 2, len(unv)), replace=False))
+    return sorted(set(int(r) for r in rows))
+
+
+def grad_row_sums_vanish(out, w, bk):
+    # softmax shift invariance: each verified gradient row sums to zero
+    g = out["grad"]
+    sums = np.abs(g.astype(np.float64).sum(axis=1))
+    scale = np.abs(g).max(axis=1) + 1e-30
+    assert np.all(sums <= 1e-4 * scale * math.sqrt(w.V)), sums.max()
+
+
+@pytest.fixture(scope="module")
+def concurrent_full():
+    say("generating concurrent workload (B=128, k=16, V=151936, bf16)")
+    return synth.make("concurrent")
+
+
+def test_full_concurrent(av, concurrent_full):
+    w = concurrent_full
+    bk = head_bk(w)
+    say(f"full concurrent: verified rows {int(np.clip(bk, 1, w.k).sum())}")
+    rate, bkg = av.av_length_head(torch.from_numpy(w.h).cuda(), torch.from_numpy(w.w).cuda(),
+                                  w.bias, w.gamma, w.k)
+    assert np.array_equal(bkg.cpu().numpy(), bk)
+    inp = gpu_inputs(w)
+    out = run_fwd(av, inp, w, bk=bk, lam=w.lam, tau=w.tau, gs=1.0 / bk.sum())
+    assert_no_errors(check_workload(out, w, bk, w.lam, w.tau, 1.0 / bk.sum(),
+                                    rows=sample_rows(w, bk)))
+    grad_row_sums_vanish(out, w, bk)
+
+
+def test_full_ragged(av):
+    say("generating ragged workload")
+    w = synth.make("ragged")
+    inp = gpu_inputs(w)
+    out = run_fwd(av, inp, w, bk=None, lam=w.lam, tau=w.tau)
+    assert_no_errors(check_workload(out, w, None, w.lam, w.tau, rows=sample_rows(w, None)))
+    grad_row_sums_vanish(out, w, None)
+
+
+def test_full_long_block_sweep(av):
+    say("generating long workload (B=64, k=32, V=262144, bf16)")
+    w = synth.make("long")
+    bk = head_bk(w)
+    inp = gpu_inputs(w)
+    for lam in (0.0, 0.5, 1.0):
+        for tau in (0.05, 0.1, 1e9):
+            say(f"long: lam={lam} tau={tau}")
+            out = run_fwd(av, inp, w, bk=bk, lam=lam, tau=tau)
+            rows = sample_rows(w, bk, n_per_kind=3, seed=int(lam * 10 + tau * 100) % 1000)
+            assert_no_errors(check_workload(out, w, bk, lam, tau, rows=rows))
