@@ -73,8 +73,13 @@ int plan_rows(int dtype, int B, int k, int V, int R, const int32_t* row_off, con
   else p->var = vec_ok ? avk::kF32x4 : avk::kF32x1;
   p->vec = avk::variant_vec(p->var);
   p->nvmax = avk::variant_nvmax(p->var);
-  p->nv = (vecs_per_thread == 0 || vecs_per_thread > p->nvmax) ? p->nvmax : vecs_per_thread;
   p->nvec = V / p->vec;
+  // A requested chunk size is raised as far as needed to keep <= 64 chunks.
+  const long long per_block = (long long)avk::kBlock * avk::kMaxChunks;
+  const int nv_min = (int)((p->nvec + per_block - 1) / per_block);
+  p->nv = (vecs_per_thread == 0 || vecs_per_thread > p->nvmax) ? p->nvmax : vecs_per_thread;
+  if (p->nv < nv_min) p->nv = nv_min;
+  if (p->nv > p->nvmax) return AV_EUNSUPPORTED;
   const long long per_chunk = (long long)avk::kBlock * p->nv;
   const long long C = (p->nvec + per_chunk - 1) / per_chunk;
   if (C > avk::kMaxChunks) return AV_EUNSUPPORTED;

@@ -144,8 +144,10 @@ int av_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
  *   status       [1] int32 out or NULL: 0, or AV_DEV_* bits found on device
  *   workspace    >= av_workspace_bytes(B, k, R) bytes, zeroed once by
  *                av_workspace_init before first use
- *   vecs_per_thread  0 = automatic; 1..8 forces smaller row chunks (tuning
- *                and tests); values above the variant's maximum are clamped
+ *   vecs_per_thread  0 = automatic (largest chunks); a positive value asks
+ *                for smaller row chunks (tuning and tests).  It is clamped to
+ *                the variant's maximum and raised where needed so that a row
+ *                never has more than 64 chunks.
  * Errors (AV_EINVAL): NULL required pointer, B < 1, k < 1 or > AV_MAX_K,
  * V < 1, R inconsistent with the layout, lambda outside [0, 1] or NaN, tau
  * <= 0 or NaN, grad_scale non-finite, workspace too small, bad
