@@ -150,7 +150,7 @@ def _dtype_code(zp: torch.Tensor) -> int:
 def av_verify_opd_fwd(zp: torch.Tensor, zq: torch.Tensor, draft: torch.Tensor, *, k: int,
                       bk: Optional[torch.Tensor] = None, row_off: Optional[torch.Tensor] = None,
                       lam: float, tau: float, grad_scale: float = 1.0, want_grad: bool = True,
-                      want_stats: bool = True, vecs_per_thread: int = 0,
+                      want_stats: bool = True, onchip_limit: int = 0,
                       out: Optional[dict] = None) -> dict:
     """Fused verify + OPD pass (see include/av.h).
 
@@ -198,7 +198,7 @@ def av_verify_opd_fwd(zp: torch.Tensor, zq: torch.Tensor, draft: torch.Tensor, *
             _dtype_code(zp), B, int(k), V, R, _ptr(row_off), _ptr(zp), _ptr(zq), _ptr(draft),
             _ptr(bk), float(lam), float(tau), float(grad_scale), _ptr(tgt), _ptr(acc),
             _ptr(row_loss), _ptr(req_loss), _ptr(total), _ptr(stats), _ptr(grad), _ptr(status),
-            _ptr(ws), ws.numel(), int(vecs_per_thread), _stream(dev))
+            _ptr(ws), ws.numel(), int(onchip_limit), _stream(dev))
     _check("av_verify_opd_fwd", rc)
     return o
 

@@ -55,36 +55,39 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // Shared validation of the verify entry points.  Fills the layout facts.
 struct Plan {
   avk::Variant var;
-  int vec, nvmax, nv, nvec, C;
+  int vec, nvec;
   bool ragged;
 };
 
 int plan_rows(int dtype, int B, int k, int V, int R, const int32_t* row_off, const void* zp,
-              const void* zq, const float* grad, int vecs_per_thread, Plan* p) {
+              const void* zq, const float* grad, Plan* p) {
   if (dtype != AV_F32 && dtype != AV_BF16) return AV_EUNSUPPORTED;
   if (B < 1 || k < 1 || k > AV_MAX_K || V < 1 || R < 1) return AV_EINVAL;
   p->ragged = row_off != nullptr;
   if (!p->ragged && (long long)R != (long long)B * k) return AV_EINVAL;
   if (p->ragged && ((long long)R < B || (long long)R > (long long)B * k)) return AV_EINVAL;
-  if (vecs_per_thread < 0) return AV_EINVAL;
   const int vec = dtype == AV_BF16 ? 8 : 4;
   const bool vec_ok = V % vec == 0 && aligned16(zp) && aligned16(zq) && (grad == nullptr || aligned16(grad));
   if (dtype == AV_BF16) p->var = vec_ok ? avk::kBf16x8 : avk::kBf16x1;
   else p->var = vec_ok ? avk::kF32x4 : avk::kF32x1;
   p->vec = avk::variant_vec(p->var);
-  p->nvmax = avk::variant_nvmax(p->var);
   p->nvec = V / p->vec;
-  // A requested chunk size is raised as far as needed to keep <= 64 chunks.
+  if ((long long)R * V >= (1LL << 46)) return AV_EUNSUPPORTED;
+  return AV_OK;
+}
+
+// Chunks of the streaming backward: up to vecs_per_thread vectors per thread
+// (raised as needed to keep <= 64 chunks per row).
+int plan_chunks(const Plan& p, int vecs_per_thread, int* C) {
+  if (vecs_per_thread < 0) return AV_EINVAL;
+  const int nvmax = avk::variant_nvmax(p.var);
   const long long per_block = (long long)avk::kBlock * avk::kMaxChunks;
-  const int nv_min = (int)((p->nvec + per_block - 1) / per_block);
-  p->nv = (vecs_per_thread == 0 || vecs_per_thread > p->nvmax) ? p->nvmax : vecs_per_thread;
-  if (p->nv < nv_min) p->nv = nv_min;
-  if (p->nv > p->nvmax) return AV_EUNSUPPORTED;
-  const long long per_chunk = (long long)avk::kBlock * p->nv;
-  const long long C = (p->nvec + per_chunk - 1) / per_chunk;
-  if (C > avk::kMaxChunks) return AV_EUNSUPPORTED;
-  p->C = (int)C;
-  if ((long long)R * C > 0x7fffffffLL) return AV_EUNSUPPORTED;
+  const int nv_min = (int)((p.nvec + per_block - 1) / per_block);
+  int nv = (vecs_per_thread == 0 || vecs_per_thread > nvmax) ? nvmax : vecs_per_thread;
+  if (nv < nv_min) nv = nv_min;
+  if (nv > nvmax) return AV_EUNSUPPORTED;
+  const long long per_chunk = (long long)avk::kBlock * nv;
+  *C = (int)((p.nvec + per_chunk - 1) / per_chunk);
   return AV_OK;
 }
 
@@ -143,7 +146,7 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_
                       float lambda, float tau, float grad_scale, int32_t* tgt_argmax,
                       int32_t* acc_len, float* row_loss, float* req_loss, float* total_loss,
                       float* row_stats, float* grad_zq, int32_t* status, void* workspace,
-                      size_t workspace_bytes, int vecs_per_thread, void* stream) {
+                      size_t workspace_bytes, int onchip_limit, void* stream) {
   if (!zp || !zq || !draft || !tgt_argmax || !acc_len || !row_loss || !workspace) return AV_EINVAL;
   if (!row_off && !bk) return AV_EINVAL;
   if (!(lambda >= 0.0f && lambda <= 1.0f)) return AV_EINVAL;
@@ -152,10 +155,18 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_
   if (row_stats && !aligned16(row_stats)) return AV_EINVAL;
   if (!aligned16(workspace)) return AV_EINVAL;
   Plan p;
-  int rc = plan_rows(dtype, B, k, V, R, row_off, zp, zq, grad_zq, vecs_per_thread, &p);
+  int rc = plan_rows(dtype, B, k, V, R, row_off, zp, zq, grad_zq, &p);
   if (rc != AV_OK) return rc;
-  if (p.ragged && B + 1 > 16384) return AV_EUNSUPPORTED;  // offsets are cached in LDS
+  if (onchip_limit < 0) return AV_EINVAL;
+  if (p.ragged && B + 1 > 4096) return AV_EUNSUPPORTED;  // offsets are cached in LDS
   if (workspace_bytes < avk::ws_total(B, R)) return AV_EINVAL;
+  int nr = avk::variant_row_regs(p.var), nl = avk::variant_row_lds(p.var);
+  if (onchip_limit > 0) {
+    nr = onchip_limit & 0xff;
+    nl = (onchip_limit >> 8) & 0xff;
+    if (nr > avk::variant_row_regs(p.var)) nr = avk::variant_row_regs(p.var);
+    if (nl > avk::variant_row_lds(p.var)) nl = avk::variant_row_lds(p.var);
+  }
 
   const DeviceInfo* dev = nullptr;
   hipError_t e = device_info(&dev);
@@ -168,10 +179,8 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_
     if (e != hipSuccess) return hip_fail(e);
   }
   if (occ < 1) return AV_EUNSUPPORTED;
-  const long long n_items = (long long)R * p.C;
   long long grid = (long long)occ * dev->cus;
-  if (grid > n_items) grid = n_items;
-  if (n_items + grid > 0xffffffffLL) return AV_EUNSUPPORTED;
+  if (grid > R) grid = R;
 
   char* ws = (char*)workspace;
   avk::FwdArgs a;
@@ -189,18 +198,17 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_
   a.grad = grad_zq;
   a.status_out = status;
   a.ctl = (uint64_t*)ws;
-  a.slots = (uint64_t*)(ws + avk::ws_slots_off());
-  a.rowres = (uint64_t*)(ws + avk::ws_rowres_off(R));
+  a.rowres = (uint64_t*)(ws + avk::ws_rowres_off());
   a.reqres = (uint64_t*)(ws + avk::ws_reqres_off(R));
   a.timeout_ticks = dev->ticks_per_ms * 2000;  // 2 s per wait
   a.B = B;
   a.k = k;
   a.V = V;
   a.R = R;
-  a.C = p.C;
   a.nvec = p.nvec;
+  a.nr = nr;
+  a.nl = nl;
   a.ragged = p.ragged ? 1 : 0;
-  a.n_items = (uint32_t)n_items;
   a.lam = lambda;
   a.tau = tau;
   a.gs = grad_scale;
@@ -220,8 +228,12 @@ int av_verify_opd_bwd(int dtype, int B, int k, int V, int R, const int32_t* row_
   if (!finite(grad_scale)) return AV_EINVAL;
   if (!aligned16(row_stats)) return AV_EINVAL;
   Plan p;
-  int rc = plan_rows(dtype, B, k, V, R, row_off, zp, zq, grad_zq, vecs_per_thread, &p);
+  int rc = plan_rows(dtype, B, k, V, R, row_off, zp, zq, grad_zq, &p);
   if (rc != AV_OK) return rc;
+  int C = 0;
+  rc = plan_chunks(p, vecs_per_thread, &C);
+  if (rc != AV_OK) return rc;
+  if ((long long)R * C > 0x7fffffffLL) return AV_EUNSUPPORTED;
   avk::BwdArgs a;
   a.zp = zp;
   a.zq = zq;
@@ -233,7 +245,7 @@ int av_verify_opd_bwd(int dtype, int B, int k, int V, int R, const int32_t* row_
   a.k = k;
   a.V = V;
   a.R = R;
-  a.C = p.C;
+  a.C = C;
   a.nvec = p.nvec;
   a.ragged = p.ragged ? 1 : 0;
   a.lam = lambda;

@@ -7,21 +7,20 @@
 
 namespace avk {
 
-constexpr int kBlock = 256;      // threads per workgroup: 4 wave64s
-constexpr int kMaxChunks = 64;   // chunks per row; one lane of wave 0 each
-constexpr int kSlotWords = 8;    // tagged 64-bit words per (row, chunk) slot
+constexpr int kBlock = 256;      // threads per workgroup of the streaming kernels
+constexpr int kRowBlock = 1024;  // threads per workgroup of the fused row kernel (1 per CU)
+constexpr int kMaxChunks = 64;   // chunks per row of the standalone backward
 
-// Workspace layout (all 64-bit words):
-//   ctl[0]   status (high 32 bits) | dispense counter (low 32 bits)
+// Fused-pass workspace (64-bit words):
+//   ctl[0]   row dispense counter
 //   ctl[1]   launch epoch (low 32 bits)
-//   slots    [R][kMaxChunks][kSlotWords]  per-chunk partial statistics
-//   rowres   [R][2]                       per-row target argmax and loss
-//   reqres   [B][2]                       per-request loss sum (float64 halves)
+//   ctl[2]   status bits (high 32 bits) | workgroups finished (low 32 bits)
+//   rowres   [R][2]   per-row target argmax and loss (tagged)
+//   reqres   [B][2]   per-request loss sum, float64 halves (tagged)
 constexpr size_t kCtlBytes = 256;
 
-inline size_t ws_slots_off() { return kCtlBytes; }
-inline size_t ws_rowres_off(int R) { return ws_slots_off() + (size_t)R * kMaxChunks * kSlotWords * 8; }
-inline size_t ws_reqres_off(int R) { return ws_rowres_off(R) + (size_t)R * 16; }
+inline size_t ws_rowres_off() { return kCtlBytes; }
+inline size_t ws_reqres_off(int R) { return ws_rowres_off() + (size_t)R * 16; }
 inline size_t ws_total(int B, int R) {
   size_t n = ws_reqres_off(R) + (size_t)B * 16;
   return (n + 255) & ~(size_t)255;
@@ -32,8 +31,11 @@ inline size_t ws_total(int B, int R) {
 enum Variant { kBf16x8 = 0, kBf16x1 = 1, kF32x4 = 2, kF32x1 = 3 };
 
 inline int variant_vec(Variant v) { return v == kBf16x8 ? 8 : v == kF32x4 ? 4 : 1; }
-// Most vectors (of variant_vec elements) one thread holds per chunk.
-inline int variant_nvmax(Variant v) { return v == kBf16x8 ? 4 : v == kF32x4 ? 8 : 16; }
+// Streaming backward: most vectors one thread holds per chunk.
+inline int variant_nvmax(Variant v) { return v == kBf16x8 ? 8 : v == kF32x4 ? 8 : 16; }
+// Fused row kernel: vectors per thread kept in registers and in LDS.
+inline int variant_row_regs(Variant v) { return (v == kBf16x8 || v == kF32x4) ? 9 : 32; }
+inline int variant_row_lds(Variant v) { return (v == kBf16x8 || v == kF32x4) ? 4 : 0; }
 
 struct FwdArgs {
   const void* zp;
@@ -50,15 +52,13 @@ struct FwdArgs {
   float* grad;
   int32_t* status_out;
   uint64_t* ctl;
-  uint64_t* slots;
   uint64_t* rowres;
   uint64_t* reqres;
   long long timeout_ticks;
   int B, k, V, R;
-  int C;         // chunks per row
   int nvec;      // vectors per row (V / vec)
+  int nr, nl;    // vectors per thread held in registers / in LDS
   int ragged;
-  uint32_t n_items;  // R * C
   float lam, tau, gs;
 };
 

@@ -6,30 +6,33 @@
 // minor comment 2, the free-parameter ledger).  This file is about how.
 //
 // fused_kernel -- the whole forward (+ gradient) pass in one launch.
-//   A row's statistics (lse_p, lse_q, argmax, then the clipped-KL sum and S)
-//   depend on the entire V-long row, and the gradient of every entry depends
-//   on S.  Streaming a row twice from HBM would cost 12 bytes per verified
-//   bf16 entry instead of 8 (4 read + 4 written), so a row is split into C
-//   chunks that C workgroups hold in registers while they exchange per-chunk
-//   partials, twice, through the workspace; every byte of zp/zq is read from
-//   HBM exactly once and every gradient byte is written once.
+//   One 1024-thread workgroup per CU, persistent, takes whole rows from an
+//   atomic counter.  Sweep 1 streams a row's zp and zq from HBM once and
+//   keeps as much of it as fits on chip (per thread NR vectors in registers
+//   and NL in LDS, filled by direct-to-LDS loads: about 70% of a 151936-wide
+//   bf16 row) while folding every entry into online statistics:
+//     max / sum exp / first argmax of zp, max / sum exp of zq, and
+//     K = sum exp(zq - m_q)(zq - zp), which gives the unclipped reverse KL.
+//   The clip interval is entry-wise, so S (the softmax-gradient correction)
+//   and the clipped-KL sum differ from their unclipped values only through
+//   entries with |q_j log(q_j/p_j)| > tau.  A per-thread bound
+//     exp(max zq - lse_q) (max |zq - zp| + |lse_q - lse_p|)  <=  tau / 2
+//   certifies most regions clip-free; only regions that fail it are
+//   evaluated entry by entry (on chip, or re-read).  Sweep 2 writes the
+//   fp32 gradient, re-reading only the streamed part of the row.  HBM
+//   traffic per verified bf16 entry: 4 bytes read, 4 written, plus ~1.2
+//   bytes of re-read for the part that did not fit on chip.
 //
-//   Work items (row, chunk) are handed out in row-major order by an atomic
-//   counter to a persistent grid.  Only running workgroups take items, and
-//   every item before the one a workgroup waits on has already been taken,
-//   so the lowest unfinished row always has all of its chunks held by
-//   running workgroups: the waits cannot deadlock as long as C workgroups
-//   fit on the device at once (C <= 64, far below one per CU).
-//
-//   Every exchanged value is one 64-bit word {tag, 32-bit payload} written
-//   and read with agent-scope atomics, so each word is coherent across XCDs
-//   on its own and no cache-wide fence is needed.  The tag is the launch
-//   epoch (kept in the workspace, advanced by the last workgroup), so stale
-//   words of earlier launches never match and nothing is cleared between
-//   launches; graph replays see a fresh epoch too.
-//
-//   Each wait is bounded (wall clock); on expiry the launch raises
-//   AV_DEV_TIMEOUT, every other wait gives up at once, and the grid drains.
+//   Rows never wait on each other.  The per-request reductions (accepted
+//   length, request and total loss) are done by the workgroup that
+//   processed a request's last row: it polls the tagged result words of the
+//   request's rows.  Rows are handed out in order, so every row it waits
+//   for is done or held by a running workgroup that waits only on earlier
+//   rows.  Every such word is {tag, 32-bit payload} written and read with
+//   agent-scope atomics (coherent across XCDs on its own, no cache-wide
+//   fence); the tag is the launch epoch kept in the workspace, so stale
+//   words of earlier launches never match and graph replays see a fresh
+//   epoch.  Waits are bounded; on expiry the launch reports AV_DEV_TIMEOUT.
 //
 // bwd_kernel -- gradient only, from saved row statistics; one streaming
 //   sweep, the same float32 entry math as the fused pass (bit-identical).
@@ -46,6 +49,7 @@ namespace {
 
 constexpr int kWaves = kBlock / 64;
 constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -70,22 +74,25 @@ __device__ __forceinline__ void raise_status(uint64_t* ctl, uint32_t bits) {
   __hip_atomic_fetch_or(ctl, (uint64_t)bits << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Bounded wait: sleeps a little between polls, and every few polls gives
-// up if the launch already failed or the wall-clock bound is exceeded.
+// Bounded wait: sleeps between polls (backing off up to ~0.4 us), and every
+// few polls gives up if the launch already failed or the wall-clock bound is
+// exceeded.  `st` is the launch's status word (status bits in the high half).
 struct Waiter {
   long long t0, limit;
-  uint64_t* ctl;
+  uint64_t* st;
   int it;
-  __device__ Waiter(uint64_t* c, long long lim) : t0(wall_clock64()), limit(lim), ctl(c), it(0) {}
+  __device__ Waiter(uint64_t* c, long long lim) : t0(wall_clock64()), limit(lim), st(c), it(0) {}
   __device__ bool keep_going() {
-    if ((++it & 7) == 0) {
-      if ((uint32_t)(tget(ctl) >> 32) != 0u) return false;
+    ++it;
+    if ((it & 7) == 0) {
+      if ((uint32_t)(tget(st) >> 32) != 0u) return false;
       if (wall_clock64() - t0 > limit) {
-        raise_status(ctl, AV_DEV_TIMEOUT);
+        raise_status(st, AV_DEV_TIMEOUT);
         return false;
       }
     }
-    __builtin_amdgcn_s_sleep(1);
+    const int n = it < 8 ? it : 8;
+    for (int j = 0; j < n; ++j) __builtin_amdgcn_s_sleep(2);
     return true;
   }
 };
@@ -134,9 +141,10 @@ struct Tr;
 
 template <>
 struct Tr<kBf16x8> {  // 8 bfloat16 per 16-byte load
-  static constexpr int VEC = 8, NVMAX = 4;
+  static constexpr int VEC = 8, NVMAX = 8;
   using S = u32x4;
-  __device__ static S load(const void* base, long long vi) { return ((const u32x4*)base)[vi]; }
+  __device__ static const void* row(const void* base, long long r) { return (const u32x4*)base + r; }
+  __device__ static S load(const void* row, unsigned vi) { return ((const u32x4*)row)[vi]; }
   __device__ static float at(const S& s, int e) {
     const uint32_t w = s[e >> 1];
     return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
@@ -150,7 +158,8 @@ template <>
 struct Tr<kBf16x1> {  // one bfloat16 per access (rows not 16-byte aligned)
   static constexpr int VEC = 1, NVMAX = 16;
   using S = uint32_t;
-  __device__ static S load(const void* base, long long vi) { return ((const uint16_t*)base)[vi]; }
+  __device__ static const void* row(const void* base, long long r) { return (const uint16_t*)base + r; }
+  __device__ static S load(const void* row, unsigned vi) { return ((const uint16_t*)row)[vi]; }
   __device__ static float at(const S& s, int) { return __uint_as_float(s << 16); }
   __device__ static float elem(const void* base, long long j) {
     return __uint_as_float((uint32_t)((const uint16_t*)base)[j] << 16);
@@ -161,7 +170,8 @@ template <>
 struct Tr<kF32x4> {  // 4 float32 per 16-byte load
   static constexpr int VEC = 4, NVMAX = 8;
   using S = f32x4;
-  __device__ static S load(const void* base, long long vi) { return ((const f32x4*)base)[vi]; }
+  __device__ static const void* row(const void* base, long long r) { return (const f32x4*)base + r; }
+  __device__ static S load(const void* row, unsigned vi) { return ((const f32x4*)row)[vi]; }
   __device__ static float at(const S& s, int e) { return s[e]; }
   __device__ static float elem(const void* base, long long j) { return ((const float*)base)[j]; }
 };
@@ -170,13 +180,16 @@ template <>
 struct Tr<kF32x1> {
   static constexpr int VEC = 1, NVMAX = 16;
   using S = float;
-  __device__ static S load(const void* base, long long vi) { return ((const float*)base)[vi]; }
+  __device__ static const void* row(const void* base, long long r) { return (const float*)base + r; }
+  __device__ static S load(const void* row, unsigned vi) { return ((const float*)row)[vi]; }
   __device__ static float at(const S& s, int) { return s; }
   __device__ static float elem(const void* base, long long j) { return ((const float*)base)[j]; }
 };
 
+// Stores VEC gradient entries at element vi*VEC of a row (g = row start).
 template <int VEC>
-__device__ __forceinline__ void store_vec(float* g, long long off, const float* v) {
+__device__ __forceinline__ void store_vec(float* g, unsigned vi, const float* v) {
+  const unsigned off = vi * (unsigned)VEC;
   if constexpr (VEC == 8) {
     const f32x4 a = {v[0], v[1], v[2], v[3]};
     const f32x4 b = {v[4], v[5], v[6], v[7]};
@@ -231,23 +244,164 @@ __device__ __forceinline__ float grad_entry(float q, float g, const GradK& c) {
 }
 
 // ---------------------------------------------------------------------------
-// fused pass
+// fused pass: one 1024-thread workgroup per row
 // ---------------------------------------------------------------------------
 
-struct Smem {
-  float f[kWaves][4];
-  int i[kWaves];
-  double d[kWaves];
-  float rf[4];
-  int ri;
-  double rd[2];
+constexpr int kRowWaves = kRowBlock / 64;
+
+template <int VAR>
+struct RowCfg;
+template <>
+struct RowCfg<kBf16x8> {  // 9 register + 4 LDS vectors: 104 bf16 pairs per thread
+  static constexpr int NR = 9, NL = 4;
+};
+template <>
+struct RowCfg<kF32x4> {
+  static constexpr int NR = 9, NL = 4;
+};
+template <>
+struct RowCfg<kBf16x1> {
+  static constexpr int NR = 32, NL = 0;
+};
+template <>
+struct RowCfg<kF32x1> {
+  static constexpr int NR = 32, NL = 0;
+};
+
+struct RowSmem {
+  float f[kRowWaves][5];  // per-wave mp, sp, mq, sq, kq
+  int i[kRowWaves];       // per-wave first vector holding mp
+  double d[kRowWaves][2];
+  float rf[4];  // row lse_p, lse_q, S, clipped-KL
+  int ri;       // row target argmax
+  double rd;    // row reverse KL (unclipped)
+  int any;
   uint32_t item, stat, tag;
 };
 
-// Request `req` is complete once every one of its rows has published its
-// result word; called by the workgroup that finished the request's last item.
-__device__ __forceinline__ void finish_request(const FwdArgs& a, const int* s_off, int req,
+// Running statistics of one thread's part of a row.
+struct RowAcc {
+  float mp, sp;  // max of zp, sum exp(zp - mp)
+  int bv;        // first vector holding mp
+  float mq, sq;  // max of zq, sum exp(zq - mq)
+  float kq;      // sum exp(zq - mq) (zq - zp): the reverse KL, once normalised
+  float mq_on, d_on, mq_st, d_st;  // per region: max zq and max |zq - zp|
+};
+
+__device__ __forceinline__ void acc_init(RowAcc& A) {
+  A.mp = -INFINITY;
+  A.sp = 0.0f;
+  A.bv = INT_MAX;
+  A.mq = -INFINITY;
+  A.sq = 0.0f;
+  A.kq = 0.0f;
+  A.mq_on = -INFINITY;
+  A.d_on = 0.0f;
+  A.mq_st = -INFINITY;
+  A.d_st = 0.0f;
+}
+
+// Folds one vector into the running statistics (online normaliser: the sums
+// are rescaled when a larger maximum appears).  `onchip` selects which
+// clip-bound region the vector belongs to.
+template <int VAR>
+__device__ __forceinline__ void acc_vec(const typename Tr<VAR>::S& xp, const typename Tr<VAR>::S& xq,
+                                        int vi, RowAcc& A, bool onchip) {
+  using T = Tr<VAR>;
+  constexpr int VEC = T::VEC;
+  float vp = T::at(xp, 0), vq = T::at(xq, 0);
+#pragma unroll
+  for (int e = 1; e < VEC; ++e) {
+    vp = fmaxf(vp, T::at(xp, e));
+    vq = fmaxf(vq, T::at(xq, e));
+  }
+  if (vp > A.mp || (vp == A.mp && vi < A.bv)) A.bv = vi;
+  const float np = fmaxf(A.mp, vp);
+  A.sp *= __builtin_amdgcn_exp2f((A.mp - np) * kLog2e);
+  A.mp = np;
+  const float npL = np * kLog2e;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e)
+    A.sp += __builtin_amdgcn_exp2f(__builtin_fmaf(T::at(xp, e), kLog2e, -npL));
+  const float nq = fmaxf(A.mq, vq);
+  const float sc = __builtin_amdgcn_exp2f((A.mq - nq) * kLog2e);
+  A.sq *= sc;
+  A.kq *= sc;
+  A.mq = nq;
+  const float nqL = nq * kLog2e;
+  float dm = 0.0f;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    const float q = T::at(xq, e), p = T::at(xp, e);
+    const float eq = __builtin_amdgcn_exp2f(__builtin_fmaf(q, kLog2e, -nqL));
+    const float d = q - p;
+    A.sq += eq;
+    A.kq = __builtin_fmaf(eq, d, A.kq);
+    dm = fmaxf(dm, __builtin_fabsf(d));
+  }
+  if (onchip) {
+    A.mq_on = fmaxf(A.mq_on, vq);
+    A.d_on = fmaxf(A.d_on, dm);
+  } else {
+    A.mq_st = fmaxf(A.mq_st, vq);
+    A.d_st = fmaxf(A.d_st, dm);
+  }
+}
+
+// (m, s) <- log-sum-exp merge; commutative, so xor butterflies leave the same
+// bits in every lane.  Empty parts (s == 0) contribute nothing.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float& k, float om, float os,
+                                          float ok) {
+  const float M = fmaxf(m, om);
+  const float fa = (s == 0.0f) ? 0.0f : __builtin_amdgcn_exp2f((m - M) * kLog2e);
+  const float fb = (os == 0.0f) ? 0.0f : __builtin_amdgcn_exp2f((om - M) * kLog2e);
+  m = M;
+  s = s * fa + os * fb;
+  k = k * fa + ok * fb;
+}
+
+__device__ __forceinline__ void wave_merge_acc(RowAcc& A) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float omp = __shfl_xor(A.mp, o), osp = __shfl_xor(A.sp, o);
+    const int obv = __shfl_xor(A.bv, o);
+    const float omq = __shfl_xor(A.mq, o), osq = __shfl_xor(A.sq, o), okq = __shfl_xor(A.kq, o);
+    if (omp > A.mp || (omp == A.mp && obv < A.bv)) A.bv = obv;
+    float dummy = 0.0f;
+    lse_merge(A.mp, A.sp, dummy, omp, osp, 0.0f);
+    lse_merge(A.mq, A.sq, A.kq, omq, osq, okq);
+  }
+}
+
+// First index of `m` inside the vector that starts at element vi*VEC.
+template <int VAR>
+__device__ __forceinline__ int first_in_vector(const void* zp_row, int vi, float m) {
+  using T = Tr<VAR>;
+  const typename T::S x = T::load(zp_row, (unsigned)vi);
+  int e0 = T::VEC - 1;
+#pragma unroll
+  for (int e = T::VEC - 1; e >= 0; --e)
+    if (T::at(x, e) == m) e0 = e;
+  return vi * T::VEC + e0;
+}
+
+// Row r is complete; publish its argmax and loss for the request finisher.
+__device__ __forceinline__ void publish_row(const FwdArgs& a, int row, int A, float loss,
+                                            float lse_p, float lse_q, float S, float klc,
                                             uint32_t tag) {
+  a.row_loss[row] = loss;
+  a.tgt[row] = A;
+  if (a.stats) *(f32x4*)(a.stats + 4 * (long long)row) = (f32x4){lse_p, lse_q, S, klc};
+  tput(a.rowres + 2 * (long long)row, tag, (uint32_t)A);
+  tput(a.rowres + 2 * (long long)row + 1, tag, __float_as_uint(loss));
+}
+
+// Request `req` is complete once every one of its rows has published its
+// argmax and loss; called by the workgroup that processed the request's last
+// row (rows are handed out in order, so every other row of the request is
+// done or held by a running workgroup that waits on nothing later).
+__device__ __forceinline__ void finish_request(const FwdArgs& a, const int* s_off, int req,
+                                               uint32_t tag) {
   const int lane = threadIdx.x & 63;
   if ((threadIdx.x >> 6) != 0) return;
   int r0, n, bkb;
@@ -261,7 +415,7 @@ __device__ __forceinline__ void finish_request(const FwdArgs& a, const int* s_of
     bkb = min(max(a.bk[req], 1), a.k);
   }
   uint64_t w0 = 0, w1 = 0;
-  Waiter wt(a.ctl, a.timeout_ticks);
+  Waiter wt(a.ctl + 2, a.timeout_ticks);
   for (;;) {
     bool ok = true;
     if (lane < n) {
@@ -289,13 +443,13 @@ __device__ __forceinline__ void finish_request(const FwdArgs& a, const int* s_of
 }
 
 // Sum of the request totals in a fixed order; run by the workgroup that
-// holds the last item, after its own request has been finished.
-__device__ __forceinline__ void finish_total(const FwdArgs& a, Smem& sm, uint32_t tag) {
+// processed the last row, after its own request has been finished.
+__device__ __forceinline__ void finish_total(const FwdArgs& a, RowSmem& sm, uint32_t tag) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   double part = 0.0;
-  for (int b = tid; b < a.B; b += kBlock) {
+  for (int b = tid; b < a.B; b += kRowBlock) {
     uint64_t h = 0, l = 0;
-    Waiter wt(a.ctl, a.timeout_ticks);
+    Waiter wt(a.ctl + 2, a.timeout_ticks);
     do {
       h = tget(a.reqres + 2 * (long long)b);
       l = tget(a.reqres + 2 * (long long)b + 1);
@@ -304,343 +458,323 @@ __device__ __forceinline__ void finish_total(const FwdArgs& a, Smem& sm, uint32_
     part += __longlong_as_double((long long)(((uint64_t)(uint32_t)h << 32) | (uint32_t)l));
   }
   part = wsumd(part);
-  if (lane == 0) sm.d[wid] = part;
+  if (lane == 0) sm.d[wid][0] = part;
   __syncthreads();
-  if (tid == 0 && a.total) a.total[0] = (float)((sm.d[0] + sm.d[1]) + (sm.d[2] + sm.d[3]));
+  if (wid == 0) {
+    double t = (lane < kRowWaves) ? sm.d[lane][0] : 0.0;
+    t = wsumd(t);
+    if (lane == 0 && a.total) a.total[0] = (float)t;
+  }
+}
+
+// Claims the workgroup's next row (called once per row, after the row's last
+// wait on anything but rows handed out before it).
+__device__ __forceinline__ void take_next(const FwdArgs& a, RowSmem& sm) {
+  if (threadIdx.x == 0) {
+    sm.item = (uint32_t)__hip_atomic_fetch_add(a.ctl, 1ull, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+    sm.stat = (uint32_t)(tget(a.ctl + 2) >> 32);
+  }
 }
 
 template <int VAR>
-__device__ __forceinline__ void process_item(const FwdArgs& a, Smem& sm, const int* s_off,
-                                             uint32_t item, uint32_t tag) {
+__device__ __forceinline__ void zero_row(const FwdArgs& a, long long rowv) {
+  constexpr int VEC = Tr<VAR>::VEC;
+  float* g_r = a.grad + rowv * VEC;
+  float z[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) z[e] = 0.0f;
+  for (int vi = threadIdx.x; vi < a.nvec; vi += kRowBlock) store_vec<VEC>(g_r, (unsigned)vi, z);
+}
+
+// Unverified row: target argmax only, zero gradient.
+template <int VAR>
+__device__ __forceinline__ void unverified_row(const FwdArgs& a, RowSmem& sm, int row, uint32_t tag) {
   using T = Tr<VAR>;
   using S = typename T::S;
-  constexpr int VEC = T::VEC, NVMAX = T::NVMAX;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-
-  const int row = (int)(item / (uint32_t)a.C);
-  const int chunk = (int)(item - (uint32_t)row * (uint32_t)a.C);
-  const bool owner = chunk == a.C - 1;  // publishes the row's result
-  int req, pos, bkb;
-  bool last_of_req;
-  if (a.ragged) {
-    int lo = 0, hi = a.B - 1;  // last request whose first row is <= row
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_off[mid] <= row) lo = mid;
-      else hi = mid - 1;
-    }
-    req = lo;
-    pos = row - s_off[req];
-    bkb = s_off[req + 1] - s_off[req];
-    last_of_req = owner && row == s_off[req + 1] - 1;
-  } else {
-    req = row / a.k;
-    pos = row - req * a.k;
-    bkb = min(max(a.bk[req], 1), a.k);
-    last_of_req = owner && pos == a.k - 1;
-  }
-  const bool verified = pos < bkb;
+  constexpr int VEC = T::VEC;
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wid = tid >> 6;
   const long long rowv = (long long)row * a.nvec;
-  const int vlo = (int)((long long)chunk * a.nvec / a.C);
-  const int vhi = (int)((long long)(chunk + 1) * a.nvec / a.C);
-  uint64_t* slot_row = a.slots + (long long)row * kMaxChunks * kSlotWords;
-  uint64_t* my_slot = slot_row + chunk * kSlotWords;
-
-  // ---- stream the chunk into registers (one HBM read of each byte) ----
-  S xp[NVMAX], xq[NVMAX];
+  const void* zp_r = T::row(a.zp, rowv);
+  float m = -INFINITY;
+  int bv = INT_MAX;
+#pragma unroll 4
+  for (int vi = tid; vi < a.nvec; vi += kRowBlock) {  // increasing vi: strict > keeps the first
+    const S x = T::load(zp_r, (unsigned)vi);
+    float vm = T::at(x, 0);
 #pragma unroll
-  for (int v = 0; v < NVMAX; ++v) {
-    const int vi = vlo + v * kBlock + tid;
-    if (vi < vhi) {
-      xp[v] = T::load(a.zp, rowv + vi);
-      if (verified) xq[v] = T::load(a.zq, rowv + vi);
+    for (int e = 1; e < VEC; ++e) vm = fmaxf(vm, T::at(x, e));
+    if (vm > m) {
+      m = vm;
+      bv = vi;
     }
   }
-
-  // ---- round 1, local: max + first argmax of zp, max of zq ----
-  float mp = -INFINITY, mq = -INFINITY;
-  int ip = INT_MAX;
-#pragma unroll
-  for (int v = 0; v < NVMAX; ++v) {
-    const int vi = vlo + v * kBlock + tid;
-    if (vi < vhi) {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const float x = T::at(xp[v], e);
-        if (x > mp) {
-          mp = x;
-          ip = vi * VEC + e;
-        }
-      }
-      if (verified) {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) mq = fmaxf(mq, T::at(xq[v], e));
-      }
-    }
-  }
-  wargmax(mp, ip);
-  mq = wmax(mq);
+  wargmax(m, bv);
   if (lane == 0) {
-    sm.f[wid][0] = mp;
-    sm.i[wid] = ip;
-    sm.f[wid][1] = mq;
+    sm.f[wid][0] = m;
+    sm.i[wid] = bv;
   }
   __syncthreads();
-  float Mp = sm.f[0][0], Mq = sm.f[0][1];
-  int Ap = sm.i[0];
+  if (wid == 0) {  // before the zero stores: a load behind them would wait for them
+    float M = -INFINITY;
+    int B = INT_MAX;
+    if (lane < kRowWaves) {
+      M = sm.f[lane][0];
+      B = sm.i[lane];
+    }
+    wargmax(M, B);
+    if (lane == 0) {
+      const int A = first_in_vector<VAR>(zp_r, B, M);
+      publish_row(a, row, A, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, tag);
+    }
+  }
+  take_next(a, sm);
+  if (a.grad) zero_row<VAR>(a, rowv);
+}
+
+// Gradient of one vector of entries (label entry Arg gets -gs*lam) -> store.
+template <int VAR>
+__device__ __forceinline__ void grad_vec(const typename Tr<VAR>::S& xp, const typename Tr<VAR>::S& xq,
+                                         int vi, const RowK& rk, const GradK& gk, int Arg, float* g_r) {
+  using T = Tr<VAR>;
+  constexpr int VEC = T::VEC;
+  float out[VEC];
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) {
-    amax_merge(Mp, Ap, sm.f[w][0], sm.i[w]);
-    Mq = fmaxf(Mq, sm.f[w][1]);
+  for (int e = 0; e < VEC; ++e) {
+    float q, r, g;
+    opd_entry(T::at(xp, e), T::at(xq, e), rk, q, r, g);
+    out[e] = grad_entry(q, g, gk);
+  }
+  const int rel = Arg - vi * VEC;
+  if ((unsigned)rel < (unsigned)VEC) {  // this vector holds the label
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+      if (e == rel) out[e] = out[e] - gk.fix;
+  }
+  store_vec<VEC>(g_r, (unsigned)vi, out);
+}
+
+// Verified row: statistics, loss, and (optionally) the gradient.
+template <int VAR>
+__device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
+                                             typename Tr<VAR>::S (*lp)[kRowBlock],
+                                             typename Tr<VAR>::S (*lq)[kRowBlock], int row,
+                                             uint32_t tag) {
+  using T = Tr<VAR>;
+  using S = typename T::S;
+  constexpr int VEC = T::VEC, NR = RowCfg<VAR>::NR, NL = RowCfg<VAR>::NL;
+  // Opaque per row: keeps the compiler from hoisting the many tid-derived
+  // per-vector indices out of the row loop (they would sit in registers or
+  // scratch for the whole kernel).
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wid = tid >> 6;
+  const long long rowv = (long long)row * a.nvec;
+  const void* zp_r = T::row(a.zp, rowv);
+  const void* zq_r = T::row(a.zq, rowv);
+  const int nvec = a.nvec, nr = a.nr, nl = a.nl;
+  const int von = nr + nl;  // first streamed vector slot
+  const float tau = a.tau;
+
+  // ---- sweep 1: read the row once; keep its first (nr + nl) vectors per
+  // thread on chip (registers, then LDS), fold every vector into the running
+  // statistics ----
+  if constexpr (NL > 0) {
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      const int vi = (nr + l) * kRowBlock + tid;
+      if (l < nl && vi < nvec) {
+        __builtin_amdgcn_global_load_lds((const void*)((const S*)zp_r + (unsigned)vi),
+                                         (__attribute__((address_space(3))) void*)&lp[l][wid * 64],
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)((const S*)zq_r + (unsigned)vi),
+                                         (__attribute__((address_space(3))) void*)&lq[l][wid * 64],
+                                         16, 0, 0);
+      }
+    }
+  }
+  S rp[NR], rq[NR];
+#pragma unroll
+  for (int v = 0; v < NR; ++v) {
+    const int vi = v * kRowBlock + tid;
+    if (v < nr && vi < nvec) {
+      rp[v] = T::load(zp_r, (unsigned)vi);
+      rq[v] = T::load(zq_r, (unsigned)vi);
+    }
+  }
+  RowAcc A;
+  acc_init(A);
+#pragma unroll 2
+  for (int vi = von * kRowBlock + tid; vi < nvec; vi += kRowBlock) {
+    const S xp = T::load(zp_r, (unsigned)vi), xq = T::load(zq_r, (unsigned)vi);
+    acc_vec<VAR>(xp, xq, vi, A, false);
+  }
+#pragma unroll
+  for (int v = 0; v < NR; ++v) {
+    const int vi = v * kRowBlock + tid;
+    if (v < nr && vi < nvec) acc_vec<VAR>(rp[v], rq[v], vi, A, true);
+  }
+  if constexpr (NL > 0) {
+    __builtin_amdgcn_s_waitcnt(0);  // the LDS copies of this wave have landed
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      const int vi = (nr + l) * kRowBlock + tid;
+      if (l < nl && vi < nvec) acc_vec<VAR>(lp[l][tid], lq[l][tid], vi, A, true);
+    }
   }
 
-  if (!verified) {
-    if (tid == 0) {
-      tput(my_slot + 0, tag, __float_as_uint(Mp));
-      tput(my_slot + 1, tag, (uint32_t)Ap);
+  // ---- combine the statistics of the 1024 threads ----
+  const float mq_on = A.mq_on, d_on = A.d_on, mq_st = A.mq_st, d_st = A.d_st;
+  wave_merge_acc(A);
+  if (lane == 0) {
+    sm.f[wid][0] = A.mp;
+    sm.f[wid][1] = A.sp;
+    sm.f[wid][2] = A.mq;
+    sm.f[wid][3] = A.sq;
+    sm.f[wid][4] = A.kq;
+    sm.i[wid] = A.bv;
+  }
+  __syncthreads();
+  if (wid == 0) {  // lane w merges wave w's partials
+    RowAcc W;
+    acc_init(W);
+    if (lane < kRowWaves) {
+      W.mp = sm.f[lane][0];
+      W.sp = sm.f[lane][1];
+      W.mq = sm.f[lane][2];
+      W.sq = sm.f[lane][3];
+      W.kq = sm.f[lane][4];
+      W.bv = sm.i[lane];
     }
-    if (a.grad) {
-      float z[VEC];
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) z[e] = 0.0f;
-#pragma unroll
-      for (int v = 0; v < NVMAX; ++v) {
-        const int vi = vlo + v * kBlock + tid;
-        if (vi < vhi) store_vec<VEC>(a.grad, (rowv + vi) * VEC, z);
-      }
+    wave_merge_acc(W);
+    if (lane == 0) {
+      const float lse_p = W.mp + kLn2 * __builtin_amdgcn_logf(W.sp);
+      const float lse_q = W.mq + kLn2 * __builtin_amdgcn_logf(W.sq);
+      sm.rf[0] = lse_p;
+      sm.rf[1] = lse_q;
+      sm.ri = first_in_vector<VAR>(zp_r, W.bv, W.mp);
+      // sum_j q_j (log q_j - log p_j) = sum_j q_j (zq_j - zp_j) - (lse_q - lse_p)
+      sm.rd = (double)W.kq / (double)W.sq - (double)(lse_q - lse_p);
     }
-    if (owner && wid == 0) {  // combine the row's argmax partials
-      uint64_t w0 = 0, w1 = 0;
-      Waiter wt(a.ctl, a.timeout_ticks);
-      for (;;) {
-        bool ok = true;
-        if (lane < a.C) {
-          w0 = tget(slot_row + lane * kSlotWords + 0);
-          w1 = tget(slot_row + lane * kSlotWords + 1);
-          ok = tag_ok(w0, tag) && tag_ok(w1, tag);
-        }
-        if (__all(ok)) break;
-        if (!__all(wt.keep_going())) break;
-      }
-      float m = -INFINITY;
-      int ix = INT_MAX;
-      if (lane < a.C) {
-        m = lo_f(w0);
-        ix = (int)(uint32_t)w1;
-      }
-      wargmax(m, ix);
-      if (lane == 0) {
-        a.tgt[row] = ix;
-        a.row_loss[row] = 0.0f;
-        if (a.stats) *(f32x4*)(a.stats + 4 * (long long)row) = (f32x4){0.f, 0.f, 0.f, 0.f};
-        tput(a.rowres + 2 * (long long)row, tag, (uint32_t)ix);
-        tput(a.rowres + 2 * (long long)row + 1, tag, 0u);
-      }
-    }
-  } else {
-    // ---- round 1, local sums of exp relative to the chunk maxima ----
-    {
-      const float mpL = Mp * kLog2e, mqL = Mq * kLog2e;
-      float sp = 0.0f, sq = 0.0f;
+  }
+  __syncthreads();
+  const float lse_p32 = sm.rf[0], lse_q32 = sm.rf[1];
+  const int Arg = sm.ri;
+  const double KL = sm.rd;
+  const RowK rk = row_consts(lse_p32, lse_q32, tau);
+
+  // ---- clipping: every entry of a region whose bound
+  //   q_j |ell_j| <= exp(max zq - lse_q) (max |zq - zp| + |lse_q - lse_p|)
+  // stays below tau / 2 is inside the clip interval, so only regions that
+  // fail the bound are evaluated entry by entry, and the row's S and
+  // clipped-KL follow from the unclipped sums minus those corrections ----
+  const float adelta = __builtin_fabsf(rk.delta);
+  const bool flag_on = __builtin_amdgcn_exp2f((mq_on - lse_q32) * kLog2e) * (d_on + adelta) > 0.5f * tau;
+  const bool flag_st = __builtin_amdgcn_exp2f((mq_st - lse_q32) * kLog2e) * (d_st + adelta) > 0.5f * tau;
+  double S64 = KL + 1.0, KLc64 = KL;
+  if (__syncthreads_or(flag_on || flag_st)) {
+    float cs = 0.0f, ck = 0.0f;
+    if (flag_on) {
 #pragma unroll
-      for (int v = 0; v < NVMAX; ++v) {
-        const int vi = vlo + v * kBlock + tid;
-        if (vi < vhi) {
+      for (int v = 0; v < NR; ++v) {
+        const int vi = v * kRowBlock + tid;
+        if (v < nr && vi < nvec) {
 #pragma unroll
           for (int e = 0; e < VEC; ++e) {
-            sp += __builtin_amdgcn_exp2f(__builtin_fmaf(T::at(xp[v], e), kLog2e, -mpL));
-            sq += __builtin_amdgcn_exp2f(__builtin_fmaf(T::at(xq[v], e), kLog2e, -mqL));
+            float q, r, g;
+            opd_entry(T::at(rp[v], e), T::at(rq[v], e), rk, q, r, g);
+            cs += (r + q) - g;
+            ck += r - __builtin_amdgcn_fmed3f(r, -tau, tau);
           }
         }
       }
-      sp = wsum(sp);
-      sq = wsum(sq);
-      if (lane == 0) {
-        sm.f[wid][2] = sp;
-        sm.f[wid][3] = sq;
-      }
-      __syncthreads();
-      if (tid == 0) {
-        const float Sp = (sm.f[0][2] + sm.f[1][2]) + (sm.f[2][2] + sm.f[3][2]);
-        const float Sq = (sm.f[0][3] + sm.f[1][3]) + (sm.f[2][3] + sm.f[3][3]);
-        tput(my_slot + 0, tag, __float_as_uint(Mp));
-        tput(my_slot + 1, tag, (uint32_t)Ap);
-        tput(my_slot + 2, tag, __float_as_uint(Sp));
-        tput(my_slot + 3, tag, __float_as_uint(Mq));
-        tput(my_slot + 4, tag, __float_as_uint(Sq));
-      }
-    }
-
-    // ---- round 1, exchange: row lse_p, lse_q and argmax ----
-    if (wid == 0) {
-      uint64_t w[5] = {0, 0, 0, 0, 0};
-      Waiter wt(a.ctl, a.timeout_ticks);
-      for (;;) {
-        bool ok = true;
-        if (lane < a.C) {
+      if constexpr (NL > 0) {
 #pragma unroll
-          for (int j = 0; j < 5; ++j) {
-            w[j] = tget(slot_row + lane * kSlotWords + j);
-            ok = ok && tag_ok(w[j], tag);
+        for (int l = 0; l < NL; ++l) {
+          const int vi = (nr + l) * kRowBlock + tid;
+          if (l < nl && vi < nvec) {
+            const S xp = lp[l][tid], xq = lq[l][tid];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+              float q, r, g;
+              opd_entry(T::at(xp, e), T::at(xq, e), rk, q, r, g);
+              cs += (r + q) - g;
+              ck += r - __builtin_amdgcn_fmed3f(r, -tau, tau);
+            }
           }
         }
-        if (__all(ok)) break;
-        if (!__all(wt.keep_going())) break;
-      }
-      float pm = -INFINITY, qm = -INFINITY, ps = 0.0f, qs = 0.0f;
-      int pi = INT_MAX;
-      if (lane < a.C) {
-        pm = lo_f(w[0]);
-        pi = (int)(uint32_t)w[1];
-        ps = lo_f(w[2]);
-        qm = lo_f(w[3]);
-        qs = lo_f(w[4]);
-      }
-      float Mpr = pm;
-      int A = pi;
-      wargmax(Mpr, A);
-      const float Mqr = wmax(qm);
-      double tp = (lane < a.C) ? (double)ps * exp((double)pm - (double)Mpr) : 0.0;
-      double tq = (lane < a.C) ? (double)qs * exp((double)qm - (double)Mqr) : 0.0;
-      tp = wsumd(tp);
-      tq = wsumd(tq);
-      if (lane == 0) {
-        const double lse_p = (double)Mpr + log(tp);
-        const double lse_q = (double)Mqr + log(tq);
-        sm.rf[0] = (float)lse_p;
-        sm.rf[1] = (float)lse_q;
-        sm.ri = A;
-        sm.rd[0] = lse_q;
       }
     }
-    __syncthreads();
-    const float lse_p32 = sm.rf[0], lse_q32 = sm.rf[1];
-    const int A = sm.ri;
-
-    // ---- round 2, local: clipped reverse-KL terms and S ----
-    const RowK rk = row_consts(lse_p32, lse_q32, a.tau);
-    float qv[NVMAX][VEC], gv[NVMAX][VEC];
-    float klc = 0.0f, ss = 0.0f;
-#pragma unroll
-    for (int v = 0; v < NVMAX; ++v) {
-      const int vi = vlo + v * kBlock + tid;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        qv[v][e] = 0.0f;
-        gv[v][e] = 0.0f;
-      }
-      if (vi < vhi) {
+    if (flag_st) {
+      for (int vi = von * kRowBlock + tid; vi < nvec; vi += kRowBlock) {
+        const S xp = T::load(zp_r, (unsigned)vi), xq = T::load(zq_r, (unsigned)vi);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
           float q, r, g;
-          opd_entry(T::at(xp[v], e), T::at(xq[v], e), rk, q, r, g);
-          qv[v][e] = q;
-          gv[v][e] = g;
-          klc += __builtin_amdgcn_fmed3f(r, -a.tau, a.tau);
-          ss += g;
+          opd_entry(T::at(xp, e), T::at(xq, e), rk, q, r, g);
+          cs += (r + q) - g;
+          ck += r - __builtin_amdgcn_fmed3f(r, -tau, tau);
         }
       }
     }
-    klc = wsum(klc);
-    ss = wsum(ss);
+    double dcs = wsumd((double)cs), dck = wsumd((double)ck);
     if (lane == 0) {
-      sm.f[wid][0] = klc;
-      sm.f[wid][1] = ss;
+      sm.d[wid][0] = dcs;
+      sm.d[wid][1] = dck;
     }
     __syncthreads();
-    if (tid == 0) {
-      const float kc = (sm.f[0][0] + sm.f[1][0]) + (sm.f[2][0] + sm.f[3][0]);
-      const float sc = (sm.f[0][1] + sm.f[1][1]) + (sm.f[2][1] + sm.f[3][1]);
-      tput(my_slot + 5, tag, __float_as_uint(kc));
-      tput(my_slot + 6, tag, __float_as_uint(sc));
-    }
+    double tcs = (lane < kRowWaves) ? sm.d[lane][0] : 0.0;
+    double tck = (lane < kRowWaves) ? sm.d[lane][1] : 0.0;
+    tcs = wsumd(tcs);  // every wave forms the same fixed-order sum
+    tck = wsumd(tck);
+    S64 -= tcs;
+    KLc64 -= tck;
+  }
+  const float S32 = (float)S64;
+  take_next(a, sm);
 
-    // ---- round 2, exchange: row KLc and S ----
-    if (a.grad || owner) {
-      if (wid == 0) {
-        uint64_t w5 = 0, w6 = 0;
-        Waiter wt(a.ctl, a.timeout_ticks);
-        for (;;) {
-          bool ok = true;
-          if (lane < a.C) {
-            w5 = tget(slot_row + lane * kSlotWords + 5);
-            w6 = tget(slot_row + lane * kSlotWords + 6);
-            ok = tag_ok(w5, tag) && tag_ok(w6, tag);
-          }
-          if (__all(ok)) break;
-          if (!__all(wt.keep_going())) break;
-        }
-        double kk = (lane < a.C) ? (double)lo_f(w5) : 0.0;
-        double s2 = (lane < a.C) ? (double)lo_f(w6) : 0.0;
-        kk = wsumd(kk);
-        s2 = wsumd(s2);
-        if (lane == 0) {
-          sm.rd[1] = kk;
-          sm.rf[2] = (float)s2;
-        }
-      }
-      __syncthreads();
+  // ---- sweep 2: the gradient; streamed vectors are read a second time ----
+  if (a.grad) {
+    const GradK gk = grad_consts(a.lam, a.gs, S32);
+    float* g_r = a.grad + rowv * VEC;
+#pragma unroll 2
+    for (int vi = von * kRowBlock + tid; vi < nvec; vi += kRowBlock) {
+      const S xp = T::load(zp_r, (unsigned)vi), xq = T::load(zq_r, (unsigned)vi);
+      grad_vec<VAR>(xp, xq, vi, rk, gk, Arg, g_r);
     }
-
-    // ---- gradient from the register-resident q and g ----
-    if (a.grad) {
-      const GradK gk = grad_consts(a.lam, a.gs, sm.rf[2]);
-      const int va = A / VEC, ea = A - va * VEC;
-      const int rel = va - vlo;
-      const bool mine = va >= vlo && va < vhi && (rel & (kBlock - 1)) == tid;
-      const int vown = rel / kBlock;
 #pragma unroll
-      for (int v = 0; v < NVMAX; ++v) {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) qv[v][e] = grad_entry(qv[v][e], gv[v][e], gk);
-      }
-      if (mine) {
-#pragma unroll
-        for (int v = 0; v < NVMAX; ++v) {
-#pragma unroll
-          for (int e = 0; e < VEC; ++e)
-            if (v == vown && e == ea) qv[v][e] = qv[v][e] - gk.fix;
-        }
-      }
-#pragma unroll
-      for (int v = 0; v < NVMAX; ++v) {
-        const int vi = vlo + v * kBlock + tid;
-        if (vi < vhi) store_vec<VEC>(a.grad, (rowv + vi) * VEC, qv[v]);
-      }
+    for (int v = 0; v < NR; ++v) {
+      const int vi = v * kRowBlock + tid;
+      if (v < nr && vi < nvec) grad_vec<VAR>(rp[v], rq[v], vi, rk, gk, Arg, g_r);
     }
-
-    if (owner && tid == 0) {
-      // A is in [0, V) unless a wait timed out on stale words; keep the read
-      // inside the row either way.
-      const int Ain = min(max(A, 0), a.V - 1);
-      const float zqa = T::elem(a.zq, (long long)row * a.V + Ain);
-      const double ce = sm.rd[0] - (double)zqa;
-      const double kl = sm.rd[1];
-      const double loss = (double)a.lam * ce + (1.0 - (double)a.lam) * kl;
-      const float lf = (float)loss;
-      a.row_loss[row] = lf;
-      a.tgt[row] = A;
-      if (a.stats)
-        *(f32x4*)(a.stats + 4 * (long long)row) = (f32x4){lse_p32, lse_q32, sm.rf[2], (float)kl};
-      tput(a.rowres + 2 * (long long)row, tag, (uint32_t)A);
-      tput(a.rowres + 2 * (long long)row + 1, tag, __float_as_uint(lf));
+    if constexpr (NL > 0) {
+#pragma unroll
+      for (int l = 0; l < NL; ++l) {
+        const int vi = (nr + l) * kRowBlock + tid;
+        if (l < nl && vi < nvec) grad_vec<VAR>(lp[l][tid], lq[l][tid], vi, rk, gk, Arg, g_r);
+      }
     }
   }
 
-  if (last_of_req) {
-    __syncthreads();
-    finish_request(a, s_off, req, tag);
-  }
-  if (item == a.n_items - 1u) {
-    __syncthreads();
-    finish_total(a, sm, tag);
+  if (tid == 0) {
+    // Arg is in [0, V): first_in_vector returns an index inside the row.
+    const float zqa = T::elem(a.zq, (long long)row * a.V + Arg);
+    const double ce = (double)lse_q32 - (double)zqa;
+    const double loss = (double)a.lam * ce + (1.0 - (double)a.lam) * KLc64;
+    publish_row(a, row, Arg, (float)loss, lse_p32, lse_q32, S32, (float)KLc64, tag);
   }
 }
 
 template <int VAR>
-__global__ __launch_bounds__(kBlock) void fused_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kRowBlock) void fused_kernel(FwdArgs a) {
+  using S = typename Tr<VAR>::S;
+  constexpr int NLA = RowCfg<VAR>::NL > 0 ? RowCfg<VAR>::NL : 1;
+  __shared__ S lp[NLA][kRowBlock];
+  __shared__ S lq[NLA][kRowBlock];
+  __shared__ RowSmem sm;
   extern __shared__ int s_off[];  // ragged row offsets [B + 1]
-  __shared__ Smem sm;
   const int tid = threadIdx.x;
   if (tid == 0) {
     const uint32_t epoch =
@@ -649,43 +783,74 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(FwdArgs a) {
   }
   int bad = 0;
   if (a.ragged) {
-    for (int j = tid; j <= a.B; j += kBlock) s_off[j] = a.row_off[j];
+    for (int j = tid; j <= a.B; j += kRowBlock) s_off[j] = a.row_off[j];
     __syncthreads();
     int okl = 1;
-    for (int j = tid; j < a.B; j += kBlock) {
+    for (int j = tid; j < a.B; j += kRowBlock) {
       const int n = s_off[j + 1] - s_off[j];
       if (n < 1 || n > a.k) okl = 0;
     }
     if (tid == 0 && (s_off[0] != 0 || s_off[a.B] != a.R)) okl = 0;
     bad = !__syncthreads_and(okl);
-    if (bad && tid == 0) raise_status(a.ctl, AV_DEV_BAD_OFFSETS);
+    if (bad && tid == 0) raise_status(a.ctl + 2, AV_DEV_BAD_OFFSETS);
   }
-  __syncthreads();
-  const uint32_t tag = sm.tag;
+  take_next(a, sm);
   for (;;) {
-    if (tid == 0) {
-      const uint64_t old =
-          __hip_atomic_fetch_add(a.ctl, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      sm.item = (uint32_t)old;
-      sm.stat = (uint32_t)(old >> 32);
+    __syncthreads();
+    const uint32_t item = sm.item, stat = sm.stat, tag = sm.tag;
+    __syncthreads();
+    if (item >= (uint32_t)a.R) break;
+    if (bad || stat != 0u) {  // failed launch: drain without work
+      take_next(a, sm);
+      continue;
     }
-    __syncthreads();
-    const uint32_t item = sm.item, stat = sm.stat;
-    __syncthreads();
-    if (item >= a.n_items) {
-      // The last take of the launch: every other workgroup has finished, so
-      // the counter, the status and the epoch can be reset for the next one.
-      if (tid == 0 && item == a.n_items + gridDim.x - 1u) {
-        if (a.status_out) a.status_out[0] = (int32_t)(stat | (bad ? AV_DEV_BAD_OFFSETS : 0u));
-        __hip_atomic_store(a.ctl, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t epoch = tag - 1u;
-        const uint32_t next = (epoch + 1u == 0xFFFFFFFFu) ? 0u : epoch + 1u;
-        __hip_atomic_store(a.ctl + 1, (uint64_t)next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int row = (int)item;
+    int req, pos, bkb;
+    bool last_of_req;
+    if (a.ragged) {
+      int lo = 0, hi = a.B - 1;  // last request whose first row is <= row
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_off[mid] <= row) lo = mid;
+        else hi = mid - 1;
       }
-      return;
+      req = lo;
+      pos = row - s_off[req];
+      bkb = s_off[req + 1] - s_off[req];
+      last_of_req = row == s_off[req + 1] - 1;
+    } else {
+      req = row / a.k;
+      pos = row - req * a.k;
+      bkb = min(max(a.bk[req], 1), a.k);
+      last_of_req = pos == a.k - 1;
     }
-    if (bad || stat != 0u) continue;  // failed launch: drain without work
-    process_item<VAR>(a, sm, s_off, item, tag);
+    if (pos < bkb) verified_row<VAR>(a, sm, lp, lq, row, tag);
+    else unverified_row<VAR>(a, sm, row, tag);
+    if (last_of_req) {
+      __syncthreads();
+      finish_request(a, s_off, req, tag);
+    }
+    if (row == a.R - 1) {
+      __syncthreads();
+      finish_total(a, sm, tag);
+    }
+  }
+  // The last workgroup to leave resets the dispenser, the status and the
+  // done count and advances the epoch.  Status bits and the done count share
+  // one word, so every status raised before a workgroup left is seen by the
+  // one that leaves last.
+  if (tid == 0) {
+    const uint64_t old =
+        __hip_atomic_fetch_add(a.ctl + 2, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)old == gridDim.x - 1u) {
+      const uint32_t stat = (uint32_t)(old >> 32) | (bad ? (uint32_t)AV_DEV_BAD_OFFSETS : 0u);
+      if (a.status_out) a.status_out[0] = (int32_t)stat;
+      __hip_atomic_store(a.ctl, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.ctl + 2, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t epoch = sm.tag - 1u;
+      const uint32_t next = (epoch + 1u == 0xFFFFFFFFu) ? 0u : epoch + 1u;
+      __hip_atomic_store(a.ctl + 1, (uint64_t)next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -708,8 +873,11 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(BwdArgs a) {
     verified = pos < min(max(a.bk[req], 1), a.k);
   }
   const long long rowv = (long long)row * a.nvec;
-  const int vlo = (int)((long long)chunk * a.nvec / a.C);
-  const int vhi = (int)((long long)(chunk + 1) * a.nvec / a.C);
+  const int vlo = (int)((uint32_t)chunk * (uint32_t)a.nvec / (uint32_t)a.C);
+  const int vhi = (int)((uint32_t)(chunk + 1) * (uint32_t)a.nvec / (uint32_t)a.C);
+  const void* zp_r = T::row(a.zp, rowv);
+  const void* zq_r = T::row(a.zq, rowv);
+  float* g_r = a.grad + rowv * VEC;
   if (!verified) {
     float z[VEC];
 #pragma unroll
@@ -717,7 +885,7 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(BwdArgs a) {
 #pragma unroll
     for (int v = 0; v < NVMAX; ++v) {
       const int vi = vlo + v * kBlock + tid;
-      if (vi < vhi) store_vec<VEC>(a.grad, (rowv + vi) * VEC, z);
+      if (vi < vhi) store_vec<VEC>(g_r, (unsigned)vi, z);
     }
     return;
   }
@@ -730,8 +898,8 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(BwdArgs a) {
   for (int v = 0; v < NVMAX; ++v) {
     const int vi = vlo + v * kBlock + tid;
     if (vi < vhi) {
-      xp[v] = T::load(a.zp, rowv + vi);
-      xq[v] = T::load(a.zq, rowv + vi);
+      xp[v] = T::load(zp_r, (unsigned)vi);
+      xq[v] = T::load(zq_r, (unsigned)vi);
     }
   }
 #pragma unroll
@@ -746,7 +914,7 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(BwdArgs a) {
         out[e] = grad_entry(q, g, gk);
         if (vi * VEC + e == A) out[e] = out[e] - gk.fix;
       }
-      store_vec<VEC>(a.grad, (rowv + vi) * VEC, out);
+      store_vec<VEC>(g_r, (unsigned)vi, out);
     }
   }
 }
@@ -788,12 +956,12 @@ __global__ __launch_bounds__(kBlock) void zero_kernel(uint64_t* p, size_t n) {
 
 template <int VAR>
 hipError_t launch_fused_t(const FwdArgs& a, int grid, size_t lds, hipStream_t s) {
-  hipLaunchKernelGGL(fused_kernel<VAR>, dim3(grid), dim3(kBlock), lds, s, a);
+  hipLaunchKernelGGL(fused_kernel<VAR>, dim3(grid), dim3(kRowBlock), lds, s, a);
   return hipGetLastError();
 }
 template <int VAR>
 hipError_t occ_t(size_t lds, int* out) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, fused_kernel<VAR>, kBlock, lds);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, fused_kernel<VAR>, kRowBlock, lds);
 }
 template <int VAR>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {

@@ -144,15 +144,17 @@ int av_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
  *   status       [1] int32 out or NULL: 0, or AV_DEV_* bits found on device
  *   workspace    >= av_workspace_bytes(B, k, R) bytes, zeroed once by
  *                av_workspace_init before first use
- *   vecs_per_thread  0 = automatic (largest chunks); a positive value asks
- *                for smaller row chunks (tuning and tests).  It is clamped to
- *                the variant's maximum and raised where needed so that a row
- *                never has more than 64 chunks.
+ *   onchip_limit 0 = automatic.  Otherwise (regs | lds << 8): how many
+ *                16-byte vectors per thread of each row the pass keeps in
+ *                registers and in LDS (each clamped to what the build
+ *                provides); the rest of the row is read from HBM a second
+ *                time for the gradient.  A tuning and test knob.
  * Errors (AV_EINVAL): NULL required pointer, B < 1, k < 1 or > AV_MAX_K,
  * V < 1, R inconsistent with the layout, lambda outside [0, 1] or NaN, tau
- * <= 0 or NaN, grad_scale non-finite, workspace too small, bad
- * vecs_per_thread.  AV_EUNSUPPORTED: dtype other than AV_F32/AV_BF16, or a
- * row too long for 64 chunks (V > 524288 on the vector path).
+ * <= 0 or NaN, grad_scale non-finite, workspace too small, negative
+ * onchip_limit, row_stats or workspace not 16-byte aligned.
+ * AV_EUNSUPPORTED: dtype other than AV_F32/AV_BF16; ragged with B > 4095
+ * (the offsets are cached on chip); R*V >= 2^46.
  */
 int av_verify_opd_fwd(int dtype, int B, int k, int V, int R,
                       const int32_t* row_off, const void* zp, const void* zq,
@@ -162,7 +164,7 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R,
                       float* req_loss, float* total_loss, float* row_stats,
                       float* grad_zq, int32_t* status,
                       void* workspace, size_t workspace_bytes,
-                      int vecs_per_thread, void* stream);
+                      int onchip_limit, void* stream);
 
 /*
  * av_verify_opd_bwd -- gradient alone, from saved row statistics.
@@ -174,8 +176,14 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R,
  *   row_off, zp, zq, bk, dtype, B, k, V, R: as for av_verify_opd_fwd
  *   tgt_argmax [R] int32, row_stats [R, 4] float32: from the forward call
  *   grad_zq    [R, V] float32 out (unverified dense rows are zeroed)
- * Errors as for av_verify_opd_fwd.  Needs no workspace; row_off is only used
- * to select the ragged layout (every stored row verified).
+ *   vecs_per_thread  0 = automatic; otherwise the most 16-byte vectors one
+ *              thread handles per work item (raised where needed so that a
+ *              row has at most 64 items)
+ * Errors as for av_verify_opd_fwd (AV_EINVAL also for a negative
+ * vecs_per_thread).  AV_EUNSUPPORTED also for rows longer than 64 items:
+ * V > 1048576 (bf16, V % 8 == 0, 16-byte aligned rows), V > 524288 (f32,
+ * V % 4 == 0, aligned), V > 262144 otherwise.  Needs no workspace; row_off
+ * only selects the ragged layout (every stored row verified).
  */
 int av_verify_opd_bwd(int dtype, int B, int k, int V, int R,
                       const int32_t* row_off, const void* zp, const void* zq,

@@ -44,7 +44,7 @@ def test_status_strings():
 def test_workspace_bytes():
     n = dd.av_workspace_bytes(128, 16, 2048)
     assert n % 256 == 0
-    assert n >= 2048 * 64 * 64  # one 64-byte slot per (row, chunk), up to 64 chunks
+    assert n >= 2048 * 16 + 128 * 16  # a tagged (argmax, loss) pair per row, a loss sum per request
     assert dd.av_workspace_bytes(128, 16, 2048) == dd.av_workspace_bytes(128, 16, 2048)
     assert dd.av_workspace_bytes(0, 16, 10) == 0
     assert dd.av_workspace_bytes(4, 65, 10) == 0
@@ -87,12 +87,13 @@ def fwd(**kw):
     (dict(tau=float("nan")), dd.AV_EINVAL),
     (dict(gs=float("inf")), dd.AV_EINVAL),
     (dict(gs=float("nan")), dd.AV_EINVAL),
-    (dict(ws_bytes=1024), dd.AV_EINVAL),                 # workspace too small
+    (dict(ws_bytes=256), dd.AV_EINVAL),                  # workspace too small
     (dict(vecs=-1), dd.AV_EINVAL),
     (dict(stats=ctypes.c_void_p(0x10004)), dd.AV_EINVAL),  # row_stats not 16-byte aligned
     (dict(ws=ctypes.c_void_p(0x10008)), dd.AV_EINVAL),
     (dict(dtype=2), dd.AV_EUNSUPPORTED),
-    (dict(V=64 * 256 * 32 + 8), dd.AV_EUNSUPPORTED),     # more than 64 chunks per row
+    (dict(row_off=P, B=5000, R=5000), dd.AV_EUNSUPPORTED),  # ragged offsets cached on chip
+    (dict(B=1 << 16, k=64, R=1 << 22, V=1 << 24), dd.AV_EUNSUPPORTED),  # R*V >= 2^46
 ])
 def test_fwd_rejects_bad_arguments_on_host(kw, code):
     assert fwd(**kw) == code
@@ -128,7 +129,10 @@ def test_length_head_rejects_bad_arguments_on_host(kw, code):
     (dict(lam=2.0), dd.AV_EINVAL),
     (dict(tau=0.0), dd.AV_EINVAL),
     (dict(R=7), dd.AV_EINVAL),
+    (dict(vecs=-2), dd.AV_EINVAL),
     (dict(dtype=5), dd.AV_EUNSUPPORTED),
+    (dict(V=64 * 256 * 64 + 8), dd.AV_EUNSUPPORTED),     # more than 64 items per row
+    (dict(dtype=0, V=64 * 256 * 32 + 4), dd.AV_EUNSUPPORTED),
 ])
 def test_bwd_rejects_bad_arguments_on_host(kw, code):
     a = dict(dtype=1, B=2, k=4, V=64, R=8, row_off=NULL, zp=P, zq=P, bk=P, tgt=P, stats=P,

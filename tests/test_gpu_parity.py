@@ -38,6 +38,11 @@ def assert_no_errors(errors):
     assert not errors, "\n".join(errors[:10])
 
 
+# onchip: 0 = automatic; else (vectors per thread in registers) | (in LDS) << 8,
+# the rest of the row streamed twice -- small values exercise every path.
+ONCHIP = [0, 1, 1 | (1 << 8), 2 | (3 << 8)]
+
+
 # ---------------------------------------------------------------------------
 # length head
 # ---------------------------------------------------------------------------
@@ -87,7 +92,7 @@ def full_parity(av, w, bk, lam, tau, gs=1.0, vecs=0):
     return out
 
 
-@pytest.mark.parametrize("vecs", [0, 1])
+@pytest.mark.parametrize("vecs", ONCHIP)
 def test_tiny_workload(av, vecs):
     w = synth.make("tiny")
     full_parity(av, w, head_bk(w), w.lam, w.tau, vecs=vecs)
@@ -100,7 +105,7 @@ def test_single_request_full_vocab(av):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("V", [1, 7, 8, 37, 64, 1000, 2056, 10000, 10001, 65544])
-@pytest.mark.parametrize("vecs", [0, 1])
+@pytest.mark.parametrize("vecs", ONCHIP)
 def test_small_shapes(av, dtype, V, vecs):
     w = synth.make("concurrent", B=3, V=V, dtype=dtype)
     bk = np.array([1, 16, 7])
@@ -110,11 +115,12 @@ def test_small_shapes(av, dtype, V, vecs):
 @pytest.mark.parametrize("lam", [0.0, 0.5, 1.0])
 @pytest.mark.parametrize("tau", [0.01, 0.05, 0.1, 1e9, float("inf")])
 def test_lambda_tau_branches(av, lam, tau):
-    w = synth.make("long", B=2, V=3000)
-    full_parity(av, w, np.array([32, 17]), lam, tau, vecs=1)
+    w = synth.make("long", B=2, V=24000)
+    for vecs in (0, 1 | (1 << 8)):
+        full_parity(av, w, np.array([32, 17]), lam, tau, vecs=vecs)
 
 
-@pytest.mark.parametrize("vecs", [0, 1])
+@pytest.mark.parametrize("vecs", ONCHIP)
 def test_ragged_small(av, vecs):
     w = synth.make("ragged", B=10, V=5000)
     full_parity(av, w, None, 0.5, 0.1, gs=1.0 / w.R, vecs=vecs)
@@ -155,7 +161,7 @@ def test_ties_across_thread_chunk_and_vector_boundaries(av):
         zp[i, j2] = big
     zp[15, 50] = big                    # three-way tie
     w.zp = zp
-    for vecs in (0, 1, 2):
+    for vecs in ONCHIP:
         out = full_parity(av, w, np.array([16]), 0.5, 0.1, vecs=vecs)
         assert list(out["tgt_argmax"][:15]) == [min(p) for p in pairs[:15]]
         assert out["tgt_argmax"][15] == 2
@@ -228,6 +234,22 @@ def test_forward_only_matches_fused(av):
     b = run_fwd(av, inp, w, bk=bk, lam=0.5, tau=0.1, want_grad=False)
     for key in ("tgt_argmax", "acc_len", "row_loss", "req_loss", "total_loss", "row_stats"):
         assert np.array_equal(a[key], b[key]), key
+
+
+def test_workspace_reuse_across_shapes(av):
+    # One workspace, calls of different shapes and layouts in turn: every
+    # structure a call keeps in it must ignore what earlier calls left there.
+    cases = [(synth.make("concurrent", B=8, V=30000), np.array([16, 1, 8, 3, 16, 5, 2, 9])),
+             (synth.make("concurrent", B=2, V=5000, dtype="f32"), np.array([4, 16])),
+             (synth.make("ragged", B=9, V=7000), None),
+             (synth.make("long", B=3, V=20000), np.array([32, 7, 19])),
+             (synth.make("concurrent", B=8, V=30000), np.array([2, 16, 4, 9, 1, 16, 6, 11]))]
+    for rep in range(2):
+        for w, bk in cases:
+            say(f"reuse rep={rep} {w.name} B={w.B} V={w.V} {w.dtype} {w.layout}")
+            for vecs in (0, 1 | (1 << 8)):
+                out = run_fwd(av, gpu_inputs(w), w, bk=bk, lam=0.5, tau=0.1, vecs=vecs)
+                assert_no_errors(check_workload(out, w, bk, 0.5, 0.1))
 
 
 def test_bad_ragged_offsets_are_reported_not_computed(av):
