@@ -28,13 +28,17 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fused verify+OPD fwd/bwd GB/s and % HBM peak at B=128,k=16,V=151936 bf16"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "drafter_distillation_amd", "csrc", "av_kernels.hip")
+KERNEL_SRC_DIR = os.path.join(ROOT, "drafter_distillation_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_concurrent_traffic.json")
 
 
 def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel and launch sources: counter readings are stale once it changes."""
+    hsh = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_SRC_DIR)):
+        with open(os.path.join(KERNEL_SRC_DIR, name), "rb") as f:
+            hsh.update(name.encode() + b"\0" + f.read())
+    return hsh.hexdigest()[:16]
 
 
 def algorithmic_bytes(B, k, V, H, R, Rv, elem=2):
@@ -66,6 +70,62 @@ def measured_traffic():
     return t.get("bytes_per_launch")
 
 
+FUSED_KERNEL_PREFIX = "void avk::(anonymous namespace)::fused_kernel<"
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def _counter_rows(csv_path: str, counter: str):
+    import csv
+
+    with open(csv_path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") == counter:
+                yield row["Kernel_Name"], int(row["Grid_Size"]), float(row["Counter_Value"])
+
+
+def summarize_traffic(fetch_csv: str, write_csv: str, copy_mib: int) -> dict:
+    """HBM bytes per fused launch from two rocprofv3 --pmc runs (FETCH_SIZE,
+    WRITE_SIZE; KiB per dispatch) of `bench.py --copy-calibration-mib N`.
+
+    Each counter is scaled by known bytes / counter bytes of the plain
+    device-to-device copy of N MiB that run performs (the copy reads N MiB and
+    writes N MiB).  Only the largest copy dispatches (the calibration copy)
+    are used for the factor.
+    """
+    known = copy_mib * 1024.0  # KiB read (and written) by the calibration copy
+    out = {"kernel_sha": kernel_sha(), "copy_calibration_mib": copy_mib}
+    total = 0.0
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = list(_counter_rows(path, name))
+        fused = [v for k, g, v in rows if k.startswith(FUSED_KERNEL_PREFIX)]
+        copies = [(g, v) for k, g, v in rows if k == COPY_KERNEL]
+        if not fused or not copies:
+            raise SystemExit(f"{path}: no {name} rows for the fused kernel or the copy")
+        gmax = max(g for g, _ in copies)
+        cal = [v for g, v in copies if g == gmax]
+        cal_kib = sum(cal) / len(cal)
+        factor = known / cal_kib
+        fused_kib = sum(fused) / len(fused)
+        out[name] = {"fused_kib_per_dispatch": round(fused_kib, 3), "dispatches": len(fused),
+                     "copy_kib_per_dispatch": round(cal_kib, 3), "copy_dispatches": len(cal),
+                     "factor": round(factor, 6)}
+        total += fused_kib * 1024.0 * factor
+    out["bytes_per_launch"] = int(round(total))
+    return out
+
+
+def copy_calibration(torch, dev, mib: int, reps: int = 3) -> None:
+    """A plain device-to-device copy of `mib` MiB, run `reps` times outside the
+    timed region, as the known-size reference for the HBM byte counters."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def cpu_baseline(n_requests: int):
     """The float64 oracle, untuned, on the first n_requests of the same
     workload, single-threaded; reported in the same unit (algorithmic GB/s)."""
@@ -74,14 +134,17 @@ def cpu_baseline(n_requests: int):
     import oracle
     import synth
 
+    from threadpoolctl import threadpool_limits
+
     w = synth.make("concurrent", B=n_requests)
     _, bk, _ = oracle.length_head(w.h, w.w, w.bias, w.gamma, w.k)
-    t0 = time.perf_counter()
-    zp = oracle.bf16_bits_to_f64(w.zp)
-    zq = oracle.bf16_bits_to_f64(w.zq)
-    oracle.length_head(w.h, w.w, w.bias, w.gamma, w.k)
-    oracle.verify_opd(zp, zq, w.draft, k=w.k, lam=w.lam, tau=w.tau, grad_scale=1.0, bk=bk)
-    dt = time.perf_counter() - t0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        zp = oracle.bf16_bits_to_f64(w.zp)
+        zq = oracle.bf16_bits_to_f64(w.zq)
+        oracle.length_head(w.h, w.w, w.bias, w.gamma, w.k)
+        oracle.verify_opd(zp, zq, w.draft, k=w.k, lam=w.lam, tau=w.tau, grad_scale=1.0, bk=bk)
+        dt = time.perf_counter() - t0
     Rv = int(np.clip(bk, 1, w.k).sum())
     fused, head = algorithmic_bytes(w.B, w.k, w.V, w.H, w.R, Rv)
     return {
@@ -103,7 +166,19 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=64)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run a plain copy of this many MiB before warmup (counter calibration)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic file from two rocprofv3 --pmc counter CSVs and exit")
     args = ap.parse_args()
+
+    if args.summarize_traffic:
+        t = summarize_traffic(*args.summarize_traffic, args.copy_calibration_mib or 1024)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(t, f, indent=1)
+            f.write("\n")
+        print(json.dumps(t))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -121,6 +196,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     dd.lib()
+
+    if args.copy_calibration_mib > 0:
+        copy_calibration(torch, dev, args.copy_calibration_mib)
 
     w = synth.make("concurrent", seed=args.seed)
     zp = torch.from_numpy(w.zp.view(np.int16)).view(torch.bfloat16).to(dev)

@@ -31,6 +31,10 @@ HIPCC_FLAGS = [
     "-fPIC",
     "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Keep the per-thread register copies of a row as separate registers: the
+    # pass that turns small private arrays into one vector value makes the
+    # register allocator spill whole arrays to scratch in the row kernel.
+    "-mllvm", "-amdgpu-promote-alloca-to-vector-limit=8",
     "-Wall",
     "-Wno-unused-result",
     "-I", INCLUDE,

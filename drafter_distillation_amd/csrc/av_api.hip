@@ -172,7 +172,12 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_
   hipError_t e = device_info(&dev);
   if (e != hipSuccess) return hip_fail(e);
 
-  const size_t lds = p.ragged ? (size_t)(B + 1) * sizeof(int32_t) : 0;
+  // Dynamic LDS: ragged row offsets, or the longest-first schedule of the
+  // dense layout (b_k as bytes and request indices as 16-bit words).
+  const bool lpt = !p.ragged && B <= avk::kMaxLptRequests;
+  size_t lds = 0;
+  if (p.ragged) lds = (size_t)(B + 1) * sizeof(int32_t);
+  else if (lpt) lds = ((size_t)B * 3 + 3) & ~(size_t)3;
   int occ = dev->occ[p.var];
   if (lds) {
     e = avk::fused_blocks_per_cu(p.var, lds, &occ);
@@ -200,6 +205,7 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_
   a.ctl = (uint64_t*)ws;
   a.rowres = (uint64_t*)(ws + avk::ws_rowres_off());
   a.reqres = (uint64_t*)(ws + avk::ws_reqres_off(R));
+  a.arrive = (uint64_t*)(ws + avk::ws_arrive_off(B, R));
   a.timeout_ticks = dev->ticks_per_ms * 2000;  // 2 s per wait
   a.B = B;
   a.k = k;
@@ -209,6 +215,7 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_
   a.nr = nr;
   a.nl = nl;
   a.ragged = p.ragged ? 1 : 0;
+  a.lpt = lpt ? 1 : 0;
   a.lam = lambda;
   a.tau = tau;
   a.gs = grad_scale;

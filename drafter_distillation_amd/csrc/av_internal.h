@@ -12,19 +12,25 @@ constexpr int kRowBlock = 1024;  // threads per workgroup of the fused row kerne
 constexpr int kMaxChunks = 64;   // chunks per row of the standalone backward
 
 // Fused-pass workspace (64-bit words):
-//   ctl[0]   row dispense counter
+//   ctl[0]   status bits (high 32 bits) | row dispense counter (low 32 bits)
 //   ctl[1]   launch epoch (low 32 bits)
 //   ctl[2]   status bits (high 32 bits) | workgroups finished (low 32 bits)
 //   rowres   [R][2]   per-row target argmax and loss (tagged)
 //   reqres   [B][2]   per-request loss sum, float64 halves (tagged)
+//   arrive   [B]      per-request count of completed verified rows (tagged)
 constexpr size_t kCtlBytes = 256;
 
 inline size_t ws_rowres_off() { return kCtlBytes; }
 inline size_t ws_reqres_off(int R) { return ws_rowres_off() + (size_t)R * 16; }
+inline size_t ws_arrive_off(int B, int R) { return ws_reqres_off(R) + (size_t)B * 16; }
 inline size_t ws_total(int B, int R) {
-  size_t n = ws_reqres_off(R) + (size_t)B * 16;
+  size_t n = ws_arrive_off(B, R) + (size_t)B * 8;
   return (n + 255) & ~(size_t)255;
 }
+
+// Longest-first row order of the dense layout needs B bytes of b_k and B
+// 16-bit request indices in LDS; above this many requests rows go in index order.
+constexpr int kMaxLptRequests = 4095;
 
 // Kernel variants: element type and 16-byte vector width (or scalar access
 // for rows that are not 16-byte aligned).
@@ -33,9 +39,16 @@ enum Variant { kBf16x8 = 0, kBf16x1 = 1, kF32x4 = 2, kF32x1 = 3 };
 inline int variant_vec(Variant v) { return v == kBf16x8 ? 8 : v == kF32x4 ? 4 : 1; }
 // Streaming backward: most vectors one thread holds per chunk.
 inline int variant_nvmax(Variant v) { return v == kBf16x8 ? 8 : v == kF32x4 ? 8 : 16; }
-// Fused row kernel: vectors per thread kept in registers and in LDS.
-inline int variant_row_regs(Variant v) { return (v == kBf16x8 || v == kF32x4) ? 9 : 32; }
-inline int variant_row_lds(Variant v) { return (v == kBf16x8 || v == kF32x4) ? 4 : 0; }
+// Fused row kernel: vectors per thread kept in registers and in LDS (16-byte
+// vectors: 9 in registers use 72 of the 128 VGPRs a 1024-thread workgroup
+// allows; 4 in LDS, for zp and zq, use 128 KB of the 160 KB).
+#ifndef AV_NR
+#define AV_NR 9
+#endif
+constexpr int kRowRegs16 = AV_NR, kRowLds16 = 4;
+constexpr int kRowRegs1 = 32, kRowLds1 = 0;  // scalar variants
+inline int variant_row_regs(Variant v) { return (v == kBf16x8 || v == kF32x4) ? kRowRegs16 : kRowRegs1; }
+inline int variant_row_lds(Variant v) { return (v == kBf16x8 || v == kF32x4) ? kRowLds16 : kRowLds1; }
 
 struct FwdArgs {
   const void* zp;
@@ -54,11 +67,13 @@ struct FwdArgs {
   uint64_t* ctl;
   uint64_t* rowres;
   uint64_t* reqres;
+  uint64_t* arrive;
   long long timeout_ticks;
   int B, k, V, R;
   int nvec;      // vectors per row (V / vec)
   int nr, nl;    // vectors per thread held in registers / in LDS
   int ragged;
+  int lpt;       // dense layout, rows handed out longest first
   float lam, tau, gs;
 };
 

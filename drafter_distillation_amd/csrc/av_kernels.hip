@@ -7,32 +7,35 @@
 //
 // fused_kernel -- the whole forward (+ gradient) pass in one launch.
 //   One 1024-thread workgroup per CU, persistent, takes whole rows from an
-//   atomic counter.  Sweep 1 streams a row's zp and zq from HBM once and
-//   keeps as much of it as fits on chip (per thread NR vectors in registers
-//   and NL in LDS, filled by direct-to-LDS loads: about 70% of a 151936-wide
-//   bf16 row) while folding every entry into online statistics:
-//     max / sum exp / first argmax of zp, max / sum exp of zq, and
-//     K = sum exp(zq - m_q)(zq - zp), which gives the unclipped reverse KL.
+//   atomic counter, longest first: in the dense layout every verified row is
+//   handed out before any unverified one (they only need the argmax and a
+//   zero gradient), so the last rows of the launch are the short ones.
+//   Sweep 1 streams a row's zp and zq from HBM once and keeps as much of it
+//   as fits on chip (per thread NR vectors in registers and NL in LDS, filled
+//   by direct-to-LDS loads: about 70% of a 151936-wide bf16 row) while
+//   folding every entry into online statistics:
+//     max / sum exp / first argmax of zp (and zq there), max / sum exp of zq,
+//     and K = sum exp(zq - m_q)(zq - zp), which gives the unclipped reverse KL.
 //   The clip interval is entry-wise, so S (the softmax-gradient correction)
 //   and the clipped-KL sum differ from their unclipped values only through
-//   entries with |q_j log(q_j/p_j)| > tau.  A per-thread bound
-//     exp(max zq - lse_q) (max |zq - zp| + |lse_q - lse_p|)  <=  tau / 2
-//   certifies most regions clip-free; only regions that fail it are
-//   evaluated entry by entry (on chip, or re-read).  Sweep 2 writes the
-//   fp32 gradient, re-reading only the streamed part of the row.  HBM
-//   traffic per verified bf16 entry: 4 bytes read, 4 written, plus ~1.2
-//   bytes of re-read for the part that did not fit on chip.
+//   entries with |q_j log(q_j/p_j)| > tau.  A per-thread bound on q_j |ell_j|
+//   (kept as running maxima of exp(zq_j - m) |zq_j - zp_j| and of zq_j)
+//   certifies most regions clip-free; only regions that fail it are evaluated
+//   entry by entry (on chip, or re-read).  Sweep 2 writes the fp32 gradient,
+//   re-reading only the streamed part of the row.  HBM traffic per verified
+//   bf16 entry: 4 bytes read, 4 written, plus ~1.2 bytes of re-read for the
+//   part that did not fit on chip.
 //
-//   Rows never wait on each other.  The per-request reductions (accepted
-//   length, request and total loss) are done by the workgroup that
-//   processed a request's last row: it polls the tagged result words of the
-//   request's rows.  Rows are handed out in order, so every row it waits
-//   for is done or held by a running workgroup that waits only on earlier
-//   rows.  Every such word is {tag, 32-bit payload} written and read with
-//   agent-scope atomics (coherent across XCDs on its own, no cache-wide
-//   fence); the tag is the launch epoch kept in the workspace, so stale
-//   words of earlier launches never match and graph replays see a fresh
-//   epoch.  Waits are bounded; on expiry the launch reports AV_DEV_TIMEOUT.
+//   Rows never wait on each other.  A completed verified row publishes its
+//   argmax and loss and counts itself on its request's arrival counter; the
+//   workgroup whose count completes the request computes the accepted length
+//   and the request loss, and the workgroup that leaves the kernel last sums
+//   the request losses.  Every shared word is {tag, 32-bit payload} written
+//   and read with agent-scope atomics (coherent across XCDs on its own, no
+//   cache-wide fence); the tag is the launch epoch kept in the workspace, so
+//   stale words of earlier launches never match and graph replays see a
+//   fresh epoch.  A reader polls until the tag shows (bounded; on expiry the
+//   launch reports AV_DEV_TIMEOUT).
 //
 // bwd_kernel -- gradient only, from saved row statistics; one streaming
 //   sweep, the same float32 entry math as the fused pass (bit-identical).
@@ -70,24 +73,29 @@ __device__ __forceinline__ bool tag_ok(uint64_t w, uint32_t tag) {
 }
 __device__ __forceinline__ float lo_f(uint64_t w) { return __uint_as_float((uint32_t)w); }
 
+// Status bits live in the high halves of the dispenser word ctl[0] (so every
+// later claim sees them) and of the exit word ctl[2] (so the workgroup that
+// leaves last sees them).
 __device__ __forceinline__ void raise_status(uint64_t* ctl, uint32_t bits) {
-  __hip_atomic_fetch_or(ctl, (uint64_t)bits << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t v = (uint64_t)bits << 32;
+  __hip_atomic_fetch_or(ctl, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_fetch_or(ctl + 2, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Bounded wait: sleeps between polls (backing off up to ~0.4 us), and every
 // few polls gives up if the launch already failed or the wall-clock bound is
-// exceeded.  `st` is the launch's status word (status bits in the high half).
+// exceeded.  `ctl` is the launch's control block.
 struct Waiter {
   long long t0, limit;
-  uint64_t* st;
+  uint64_t* ctl;
   int it;
-  __device__ Waiter(uint64_t* c, long long lim) : t0(wall_clock64()), limit(lim), st(c), it(0) {}
+  __device__ Waiter(uint64_t* c, long long lim) : t0(wall_clock64()), limit(lim), ctl(c), it(0) {}
   __device__ bool keep_going() {
     ++it;
     if ((it & 7) == 0) {
-      if ((uint32_t)(tget(st) >> 32) != 0u) return false;
+      if ((uint32_t)(tget(ctl + 2) >> 32) != 0u) return false;
       if (wall_clock64() - t0 > limit) {
-        raise_status(st, AV_DEV_TIMEOUT);
+        raise_status(ctl, AV_DEV_TIMEOUT);
         return false;
       }
     }
@@ -136,15 +144,26 @@ __device__ __forceinline__ void wargmax(float& v, int& i) {
 // element access per variant
 // ---------------------------------------------------------------------------
 
+// Buffer resource of one row (raw addressing, `bytes` long): loads and stores
+// then take a 32-bit per-lane byte offset plus a wave-uniform one, so a
+// thread's many vectors of a row cost no per-vector 64-bit address.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc row_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 template <int VAR>
 struct Tr;
 
 template <>
 struct Tr<kBf16x8> {  // 8 bfloat16 per 16-byte load
-  static constexpr int VEC = 8, NVMAX = 8;
+  static constexpr int VEC = 8, NVMAX = 8, EB = 2;
   using S = u32x4;
   __device__ static const void* row(const void* base, long long r) { return (const u32x4*)base + r; }
   __device__ static S load(const void* row, unsigned vi) { return ((const u32x4*)row)[vi]; }
+  __device__ static S bload(Rsrc r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  }
   __device__ static float at(const S& s, int e) {
     const uint32_t w = s[e >> 1];
     return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
@@ -156,10 +175,13 @@ struct Tr<kBf16x8> {  // 8 bfloat16 per 16-byte load
 
 template <>
 struct Tr<kBf16x1> {  // one bfloat16 per access (rows not 16-byte aligned)
-  static constexpr int VEC = 1, NVMAX = 16;
+  static constexpr int VEC = 1, NVMAX = 16, EB = 2;
   using S = uint32_t;
   __device__ static const void* row(const void* base, long long r) { return (const uint16_t*)base + r; }
   __device__ static S load(const void* row, unsigned vi) { return ((const uint16_t*)row)[vi]; }
+  __device__ static S bload(Rsrc r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+  }
   __device__ static float at(const S& s, int) { return __uint_as_float(s << 16); }
   __device__ static float elem(const void* base, long long j) {
     return __uint_as_float((uint32_t)((const uint16_t*)base)[j] << 16);
@@ -168,20 +190,27 @@ struct Tr<kBf16x1> {  // one bfloat16 per access (rows not 16-byte aligned)
 
 template <>
 struct Tr<kF32x4> {  // 4 float32 per 16-byte load
-  static constexpr int VEC = 4, NVMAX = 8;
+  static constexpr int VEC = 4, NVMAX = 8, EB = 4;
   using S = f32x4;
   __device__ static const void* row(const void* base, long long r) { return (const f32x4*)base + r; }
   __device__ static S load(const void* row, unsigned vi) { return ((const f32x4*)row)[vi]; }
+  __device__ static S bload(Rsrc r, uint32_t voff, uint32_t soff) {
+    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return __builtin_bit_cast(f32x4, w);
+  }
   __device__ static float at(const S& s, int e) { return s[e]; }
   __device__ static float elem(const void* base, long long j) { return ((const float*)base)[j]; }
 };
 
 template <>
 struct Tr<kF32x1> {
-  static constexpr int VEC = 1, NVMAX = 16;
+  static constexpr int VEC = 1, NVMAX = 16, EB = 4;
   using S = float;
   __device__ static const void* row(const void* base, long long r) { return (const float*)base + r; }
   __device__ static S load(const void* row, unsigned vi) { return ((const float*)row)[vi]; }
+  __device__ static S bload(Rsrc r, uint32_t voff, uint32_t soff) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+  }
   __device__ static float at(const S& s, int) { return s; }
   __device__ static float elem(const void* base, long long j) { return ((const float*)base)[j]; }
 };
@@ -200,6 +229,24 @@ __device__ __forceinline__ void store_vec(float* g, unsigned vi, const float* v)
     __builtin_nontemporal_store(a, (f32x4*)(g + off));
   } else {
     __builtin_nontemporal_store(v[0], g + off);
+  }
+}
+
+// Same through a row's buffer resource: VEC entries at byte offset voff + soff
+// (nontemporal: the gradient is not read again by this pass).
+template <int VEC>
+__device__ __forceinline__ void bstore_vec(Rsrc g, uint32_t voff, uint32_t soff, const float* v) {
+  constexpr int kNT = 2;
+  if constexpr (VEC == 8) {
+    const f32x4 a = {v[0], v[1], v[2], v[3]};
+    const f32x4 b = {v[4], v[5], v[6], v[7]};
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, a), g, voff, soff, kNT);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, b), g, voff + 16u, soff, kNT);
+  } else if constexpr (VEC == 4) {
+    const f32x4 a = {v[0], v[1], v[2], v[3]};
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, a), g, voff, soff, kNT);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[0]), g, voff, soff, kNT);
   }
 }
 
@@ -248,62 +295,66 @@ __device__ __forceinline__ float grad_entry(float q, float g, const GradK& c) {
 // ---------------------------------------------------------------------------
 
 constexpr int kRowWaves = kRowBlock / 64;
+constexpr int kLastWave = kRowWaves - 1;  // publishes rows and finishes requests
+// Floor of the factor that rescales the clip-bound maxima when a thread's
+// running max of zq grows: keeps them upper bounds instead of letting them
+// underflow (an entry that small relative to the max has q_j |ell_j| far
+// below any tau for finite logits).
+constexpr float kRescaleFloor = 0x1p-100f;
 
 template <int VAR>
-struct RowCfg;
-template <>
-struct RowCfg<kBf16x8> {  // 9 register + 4 LDS vectors: 104 bf16 pairs per thread
-  static constexpr int NR = 9, NL = 4;
-};
-template <>
-struct RowCfg<kF32x4> {
-  static constexpr int NR = 9, NL = 4;
-};
-template <>
-struct RowCfg<kBf16x1> {
-  static constexpr int NR = 32, NL = 0;
-};
-template <>
-struct RowCfg<kF32x1> {
-  static constexpr int NR = 32, NL = 0;
+struct RowCfg {  // vectors per thread kept in registers (NR) and in LDS (NL)
+  static constexpr bool kWide = VAR == kBf16x8 || VAR == kF32x4;
+  static constexpr int NR = kWide ? kRowRegs16 : kRowRegs1;
+  static constexpr int NL = kWide ? kRowLds16 : kRowLds1;
 };
 
+// Workgroup state.  Per-wave partials and the claimed item are double-buffered
+// by the parity of the row iteration.  Every row passes at least one barrier,
+// so a buffer is rewritten two rows later only after every wave has read it,
+// and the waves need not meet at the start of a row: a wave that is done with
+// one row's gradient starts loading the next row.
 struct RowSmem {
-  float f[kRowWaves][5];  // per-wave mp, sp, mq, sq, kq
-  int i[kRowWaves];       // per-wave first vector holding mp
-  double d[kRowWaves][2];
-  float rf[4];  // row lse_p, lse_q, S, clipped-KL
-  int ri;       // row target argmax
-  double rd;    // row reverse KL (unclipped)
-  int any;
-  uint32_t item, stat, tag;
+  float f[2][kRowWaves][6];   // mp, sp, mq, sq, kq, zq at the argmax
+  int i[2][kRowWaves];        // first index of mp
+  double d[2][kRowWaves][2];  // clip corrections of S and of the KL sum
+  uint64_t item[2];           // claimed dispenser word (status bits << 32 | item)
+  int hist[AV_MAX_K + 1];     // longest-first schedule of the dense layout:
+  int cnt[AV_MAX_K + 1];      //   requests with b_k > p
+  int cum[AV_MAX_K + 1];      //   verified rows at positions < p
+  int cumu[AV_MAX_K + 1];     //   unverified rows at positions < p
+  uint64_t exitw;
+  uint32_t tag;
 };
 
 // Running statistics of one thread's part of a row.
 struct RowAcc {
   float mp, sp;  // max of zp, sum exp(zp - mp)
-  int bv;        // first vector holding mp
+  int bi;        // first index of mp
+  float za;      // zq at that index
   float mq, sq;  // max of zq, sum exp(zq - mq)
   float kq;      // sum exp(zq - mq) (zq - zp): the reverse KL, once normalised
-  float mq_on, d_on, mq_st, d_st;  // per region: max zq and max |zq - zp|
+  float mq_on, mq_st;  // per region (on chip / streamed): max zq
+  float pm_on, pm_st;  // per region: max exp(zq - mq) |zq - zp| (mq: running max)
 };
 
 __device__ __forceinline__ void acc_init(RowAcc& A) {
   A.mp = -INFINITY;
   A.sp = 0.0f;
-  A.bv = INT_MAX;
+  A.bi = INT_MAX;
+  A.za = 0.0f;
   A.mq = -INFINITY;
   A.sq = 0.0f;
   A.kq = 0.0f;
   A.mq_on = -INFINITY;
-  A.d_on = 0.0f;
   A.mq_st = -INFINITY;
-  A.d_st = 0.0f;
+  A.pm_on = 0.0f;
+  A.pm_st = 0.0f;
 }
 
-// Folds one vector into the running statistics (online normaliser: the sums
-// are rescaled when a larger maximum appears).  `onchip` selects which
-// clip-bound region the vector belongs to.
+// Folds one vector (elements vi*VEC ...) into the running statistics (online
+// normaliser: sums are rescaled when a larger maximum appears).  `onchip`
+// selects the clip-bound region of the vector.
 template <int VAR>
 __device__ __forceinline__ void acc_vec(const typename Tr<VAR>::S& xp, const typename Tr<VAR>::S& xq,
                                         int vi, RowAcc& A, bool onchip) {
@@ -315,7 +366,19 @@ __device__ __forceinline__ void acc_vec(const typename Tr<VAR>::S& xp, const typ
     vp = fmaxf(vp, T::at(xp, e));
     vq = fmaxf(vq, T::at(xq, e));
   }
-  if (vp > A.mp || (vp == A.mp && vi < A.bv)) A.bv = vi;
+  const int base = vi * VEC;
+  if (__builtin_expect(vp > A.mp || (vp == A.mp && base < A.bi), 0)) {  // new first maximum
+    int e0 = VEC - 1;
+    float z0 = T::at(xq, VEC - 1);
+#pragma unroll
+    for (int e = VEC - 2; e >= 0; --e)
+      if (T::at(xp, e) == vp) {
+        e0 = e;
+        z0 = T::at(xq, e);
+      }
+    A.bi = base + e0;
+    A.za = z0;
+  }
   const float np = fmaxf(A.mp, vp);
   A.sp *= __builtin_amdgcn_exp2f((A.mp - np) * kLog2e);
   A.mp = np;
@@ -327,9 +390,12 @@ __device__ __forceinline__ void acc_vec(const typename Tr<VAR>::S& xp, const typ
   const float sc = __builtin_amdgcn_exp2f((A.mq - nq) * kLog2e);
   A.sq *= sc;
   A.kq *= sc;
+  const float scb = fmaxf(sc, kRescaleFloor);
+  A.pm_on *= scb;
+  A.pm_st *= scb;
   A.mq = nq;
   const float nqL = nq * kLog2e;
-  float dm = 0.0f;
+  float pm = 0.0f;
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
     const float q = T::at(xq, e), p = T::at(xp, e);
@@ -337,14 +403,14 @@ __device__ __forceinline__ void acc_vec(const typename Tr<VAR>::S& xp, const typ
     const float d = q - p;
     A.sq += eq;
     A.kq = __builtin_fmaf(eq, d, A.kq);
-    dm = fmaxf(dm, __builtin_fabsf(d));
+    pm = fmaxf(pm, eq * __builtin_fabsf(d));
   }
   if (onchip) {
     A.mq_on = fmaxf(A.mq_on, vq);
-    A.d_on = fmaxf(A.d_on, dm);
+    A.pm_on = fmaxf(A.pm_on, pm);
   } else {
     A.mq_st = fmaxf(A.mq_st, vq);
-    A.d_st = fmaxf(A.d_st, dm);
+    A.pm_st = fmaxf(A.pm_st, pm);
   }
 }
 
@@ -360,65 +426,119 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float& k, float om
   k = k * fa + ok * fb;
 }
 
-__device__ __forceinline__ void wave_merge_acc(RowAcc& A) {
+// One butterfly step over the row statistics (not the per-thread bounds).
+__device__ __forceinline__ void merge_step(RowAcc& A, int o) {
+  const float omp = __shfl_xor(A.mp, o), osp = __shfl_xor(A.sp, o);
+  const int obi = __shfl_xor(A.bi, o);
+  const float oza = __shfl_xor(A.za, o);
+  const float omq = __shfl_xor(A.mq, o), osq = __shfl_xor(A.sq, o), okq = __shfl_xor(A.kq, o);
+  if (omp > A.mp || (omp == A.mp && obi < A.bi)) {
+    A.bi = obi;
+    A.za = oza;
+  }
+  float dummy = 0.0f;
+  lse_merge(A.mp, A.sp, dummy, omp, osp, 0.0f);
+  lse_merge(A.mq, A.sq, A.kq, omq, osq, okq);
+}
+
+// Sum of the first 16 lanes, in a fixed order, broadcast from lane 0.
+__device__ __forceinline__ double wsumd16(double v) {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float omp = __shfl_xor(A.mp, o), osp = __shfl_xor(A.sp, o);
-    const int obv = __shfl_xor(A.bv, o);
-    const float omq = __shfl_xor(A.mq, o), osq = __shfl_xor(A.sq, o), okq = __shfl_xor(A.kq, o);
-    if (omp > A.mp || (omp == A.mp && obv < A.bv)) A.bv = obv;
-    float dummy = 0.0f;
-    lse_merge(A.mp, A.sp, dummy, omp, osp, 0.0f);
-    lse_merge(A.mq, A.sq, A.kq, omq, osq, okq);
+  for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return __shfl(v, 0);
+}
+
+// Claims the next dispense index; the high half carries the launch's status.
+__device__ __forceinline__ uint64_t claim(const FwdArgs& a) {
+  return __hip_atomic_fetch_add(a.ctl, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Counts one more completed row of a request; returns the new count.  The
+// counter word is {tag, count}: a word from an earlier launch counts as 0.
+__device__ __forceinline__ uint32_t arrive(uint64_t* p, uint32_t tag) {
+  uint64_t old = tget(p);
+  for (;;) {
+    const uint32_t n = tag_ok(old, tag) ? (uint32_t)old + 1u : 1u;
+    const uint64_t nw = ((uint64_t)tag << 32) | (uint64_t)n;
+    if (__hip_atomic_compare_exchange_strong(p, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      return n;
   }
 }
 
-// First index of `m` inside the vector that starts at element vi*VEC.
-template <int VAR>
-__device__ __forceinline__ int first_in_vector(const void* zp_row, int vi, float m) {
-  using T = Tr<VAR>;
-  const typename T::S x = T::load(zp_row, (unsigned)vi);
-  int e0 = T::VEC - 1;
-#pragma unroll
-  for (int e = T::VEC - 1; e >= 0; --e)
-    if (T::at(x, e) == m) e0 = e;
-  return vi * T::VEC + e0;
+// Work item: a row, its request, and whether it is verified.
+struct Item {
+  int row, req, r0, bkb;  // r0: first row of the request; bkb: its verified rows
+  bool verified;
+};
+
+// Dense layout, longest first: verified rows position-major (position p holds
+// the cnt[p] requests with b_k > p, which lead `order`, sorted by b_k
+// descending), then unverified rows position-major (the requests with
+// b_k <= p, which trail `order`).
+__device__ __forceinline__ Item map_item(const FwdArgs& a, const RowSmem& sm, const int* s_off,
+                                         const uint16_t* order, const uint8_t* key, int idx) {
+  Item m;
+  if (a.ragged) {
+    int lo = 0, hi = a.B - 1;  // last request whose first row is <= idx
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_off[mid] <= idx) lo = mid;
+      else hi = mid - 1;
+    }
+    m.row = idx;
+    m.req = lo;
+    m.r0 = s_off[lo];
+    m.bkb = s_off[lo + 1] - m.r0;
+    m.verified = true;
+  } else if (a.lpt) {
+    const int k = a.k, rv = sm.cum[k];
+    int p, j, lo = 0, hi = k - 1;
+    if (idx < rv) {
+      while (lo < hi) {  // last position whose first verified row is <= idx
+        const int mid = (lo + hi + 1) >> 1;
+        if (sm.cum[mid] <= idx) lo = mid;
+        else hi = mid - 1;
+      }
+      p = lo;
+      j = idx - sm.cum[p];
+      m.verified = true;
+    } else {
+      const int u = idx - rv;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (sm.cumu[mid] <= u) lo = mid;
+        else hi = mid - 1;
+      }
+      p = lo;
+      j = sm.cnt[p] + (u - sm.cumu[p]);
+      m.verified = false;
+    }
+    m.req = order[j];
+    m.r0 = m.req * k;
+    m.row = m.r0 + p;
+    m.bkb = key[m.req];
+  } else {
+    m.row = idx;
+    m.req = idx / a.k;
+    m.r0 = m.req * a.k;
+    m.bkb = min(max(a.bk[m.req], 1), a.k);
+    m.verified = idx - m.r0 < m.bkb;
+  }
+  return m;
 }
 
-// Row r is complete; publish its argmax and loss for the request finisher.
-__device__ __forceinline__ void publish_row(const FwdArgs& a, int row, int A, float loss,
-                                            float lse_p, float lse_q, float S, float klc,
-                                            uint32_t tag) {
-  a.row_loss[row] = loss;
-  a.tgt[row] = A;
-  if (a.stats) *(f32x4*)(a.stats + 4 * (long long)row) = (f32x4){lse_p, lse_q, S, klc};
-  tput(a.rowres + 2 * (long long)row, tag, (uint32_t)A);
-  tput(a.rowres + 2 * (long long)row + 1, tag, __float_as_uint(loss));
-}
-
-// Request `req` is complete once every one of its rows has published its
-// argmax and loss; called by the workgroup that processed the request's last
-// row (rows are handed out in order, so every other row of the request is
-// done or held by a running workgroup that waits on nothing later).
-__device__ __forceinline__ void finish_request(const FwdArgs& a, const int* s_off, int req,
+// Request `req` (rows r0 .. r0+bkb-1 verified) is complete: accepted length
+// and request loss.  Run by one wave of the workgroup that counted the
+// request's last row; the other rows' words carry the tag once visible.
+__device__ __forceinline__ void finish_request(const FwdArgs& a, int req, int r0, int bkb,
                                                uint32_t tag) {
   const int lane = threadIdx.x & 63;
-  if ((threadIdx.x >> 6) != 0) return;
-  int r0, n, bkb;
-  if (a.ragged) {
-    r0 = s_off[req];
-    n = s_off[req + 1] - r0;
-    bkb = n;
-  } else {
-    r0 = req * a.k;
-    n = a.k;
-    bkb = min(max(a.bk[req], 1), a.k);
-  }
   uint64_t w0 = 0, w1 = 0;
-  Waiter wt(a.ctl + 2, a.timeout_ticks);
+  Waiter wt(a.ctl, a.timeout_ticks);
   for (;;) {
     bool ok = true;
-    if (lane < n) {
+    if (lane < bkb) {
       w0 = tget(a.rowres + 2 * (long long)(r0 + lane));
       w1 = tget(a.rowres + 2 * (long long)(r0 + lane) + 1);
       ok = tag_ok(w0, tag) && tag_ok(w1, tag);
@@ -442,110 +562,136 @@ __device__ __forceinline__ void finish_request(const FwdArgs& a, const int* s_of
   }
 }
 
-// Sum of the request totals in a fixed order; run by the workgroup that
-// processed the last row, after its own request has been finished.
-__device__ __forceinline__ void finish_total(const FwdArgs& a, RowSmem& sm, uint32_t tag) {
+// Sum of the request losses in a fixed order; run by the workgroup that
+// leaves last, when every request has been finished.  False on a timeout.
+__device__ __forceinline__ bool finish_total(const FwdArgs& a, RowSmem& sm, uint32_t tag) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   double part = 0.0;
+  bool ok = true;
   for (int b = tid; b < a.B; b += kRowBlock) {
     uint64_t h = 0, l = 0;
-    Waiter wt(a.ctl + 2, a.timeout_ticks);
-    do {
+    Waiter wt(a.ctl, a.timeout_ticks);
+    for (;;) {
       h = tget(a.reqres + 2 * (long long)b);
       l = tget(a.reqres + 2 * (long long)b + 1);
       if (tag_ok(h, tag) && tag_ok(l, tag)) break;
-    } while (wt.keep_going());
+      if (!wt.keep_going()) {
+        ok = false;
+        break;
+      }
+    }
     part += __longlong_as_double((long long)(((uint64_t)(uint32_t)h << 32) | (uint32_t)l));
   }
   part = wsumd(part);
-  if (lane == 0) sm.d[wid][0] = part;
-  __syncthreads();
+  if (lane == 0) sm.d[0][wid][0] = part;
+  ok = __syncthreads_and(ok);
   if (wid == 0) {
-    double t = (lane < kRowWaves) ? sm.d[lane][0] : 0.0;
-    t = wsumd(t);
+    double t = (lane < kRowWaves) ? sm.d[0][lane][0] : 0.0;
+    t = wsumd16(t);
     if (lane == 0 && a.total) a.total[0] = (float)t;
   }
+  return ok;
 }
 
-// Claims the workgroup's next row (called once per row, after the row's last
-// wait on anything but rows handed out before it).
-__device__ __forceinline__ void take_next(const FwdArgs& a, RowSmem& sm) {
-  if (threadIdx.x == 0) {
-    sm.item = (uint32_t)__hip_atomic_fetch_add(a.ctl, 1ull, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-    sm.stat = (uint32_t)(tget(a.ctl + 2) >> 32);
-  }
-}
+// Byte sizes of one slot of a row: kRowBlock vectors of logits / of gradient.
+template <int VAR>
+struct Slot {
+  static constexpr uint32_t IN = kRowBlock * (uint32_t)(Tr<VAR>::VEC * Tr<VAR>::EB);
+  static constexpr uint32_t OUT = kRowBlock * Tr<VAR>::VEC * 4u;
+};
 
 template <int VAR>
-__device__ __forceinline__ void zero_row(const FwdArgs& a, long long rowv) {
+__device__ __forceinline__ void zero_row(const FwdArgs& a, long long rowv, int tid) {
   constexpr int VEC = Tr<VAR>::VEC;
-  float* g_r = a.grad + rowv * VEC;
+  const Rsrc g = row_rsrc(a.grad + rowv * VEC, (uint32_t)a.V * 4u);
+  const uint32_t goff = (uint32_t)tid * (VEC * 4u);
   float z[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) z[e] = 0.0f;
-  for (int vi = threadIdx.x; vi < a.nvec; vi += kRowBlock) store_vec<VEC>(g_r, (unsigned)vi, z);
+  const int nvec = a.nvec, nfull = nvec / kRowBlock;
+#pragma unroll 4
+  for (int s = 0; s < nfull; ++s) bstore_vec<VEC>(g, goff, (uint32_t)s * Slot<VAR>::OUT, z);
+  if (nfull * kRowBlock + tid < nvec) bstore_vec<VEC>(g, goff, (uint32_t)nfull * Slot<VAR>::OUT, z);
+}
+
+// Folds one zp vector into a running (max, first index) pair; vectors come in
+// increasing order, so a strict > keeps the first maximum.
+template <int VAR>
+__device__ __forceinline__ void argmax_vec(const typename Tr<VAR>::S& x, int vi, float& m, int& bi) {
+  using T = Tr<VAR>;
+  constexpr int VEC = T::VEC;
+  float vm = T::at(x, 0);
+#pragma unroll
+  for (int e = 1; e < VEC; ++e) vm = fmaxf(vm, T::at(x, e));
+  if (vm > m) {
+    int e0 = VEC - 1;
+#pragma unroll
+    for (int e = VEC - 2; e >= 0; --e)
+      if (T::at(x, e) == vm) e0 = e;
+    m = vm;
+    bi = vi * VEC + e0;
+  }
 }
 
 // Unverified row: target argmax only, zero gradient.
 template <int VAR>
-__device__ __forceinline__ void unverified_row(const FwdArgs& a, RowSmem& sm, int row, uint32_t tag) {
+__device__ __forceinline__ void unverified_row(const FwdArgs& a, RowSmem& sm, int row, int par) {
   using T = Tr<VAR>;
   using S = typename T::S;
-  constexpr int VEC = T::VEC;
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   const int lane = tid & 63, wid = tid >> 6;
+  uint64_t nxt = 0;
+  if (tid == 0) nxt = claim(a);  // answered with this row's first loads
   const long long rowv = (long long)row * a.nvec;
-  const void* zp_r = T::row(a.zp, rowv);
+  const Rsrc rzp = row_rsrc(T::row(a.zp, rowv), (uint32_t)a.V * (uint32_t)T::EB);
+  const uint32_t voff = (uint32_t)tid * (uint32_t)(T::VEC * T::EB);  // bytes of one vector
+  const int nvec = a.nvec, nfull = nvec / kRowBlock;
   float m = -INFINITY;
-  int bv = INT_MAX;
+  int bi = INT_MAX;
 #pragma unroll 4
-  for (int vi = tid; vi < a.nvec; vi += kRowBlock) {  // increasing vi: strict > keeps the first
-    const S x = T::load(zp_r, (unsigned)vi);
-    float vm = T::at(x, 0);
-#pragma unroll
-    for (int e = 1; e < VEC; ++e) vm = fmaxf(vm, T::at(x, e));
-    if (vm > m) {
-      m = vm;
-      bv = vi;
-    }
-  }
-  wargmax(m, bv);
+  for (int s = 0; s < nfull; ++s)
+    argmax_vec<VAR>(T::bload(rzp, voff, (uint32_t)s * Slot<VAR>::IN), s * kRowBlock + tid, m, bi);
+  if (nfull * kRowBlock + tid < nvec)
+    argmax_vec<VAR>(T::bload(rzp, voff, (uint32_t)nfull * Slot<VAR>::IN), nfull * kRowBlock + tid,
+                    m, bi);
+  wargmax(m, bi);
   if (lane == 0) {
-    sm.f[wid][0] = m;
-    sm.i[wid] = bv;
+    sm.f[par][wid][0] = m;
+    sm.i[par][wid] = bi;
   }
+  if (tid == 0) sm.item[par ^ 1] = nxt;
   __syncthreads();
-  if (wid == 0) {  // before the zero stores: a load behind them would wait for them
+  if (wid == kLastWave) {
     float M = -INFINITY;
-    int B = INT_MAX;
+    int I = INT_MAX;
     if (lane < kRowWaves) {
-      M = sm.f[lane][0];
-      B = sm.i[lane];
+      M = sm.f[par][lane][0];
+      I = sm.i[par][lane];
     }
-    wargmax(M, B);
+    wargmax(M, I);
     if (lane == 0) {
-      const int A = first_in_vector<VAR>(zp_r, B, M);
-      publish_row(a, row, A, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, tag);
+      a.row_loss[row] = 0.0f;
+      a.tgt[row] = I;
+      if (a.stats) *(f32x4*)(a.stats + 4 * (long long)row) = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
     }
   }
-  take_next(a, sm);
-  if (a.grad) zero_row<VAR>(a, rowv);
+  if (a.grad) zero_row<VAR>(a, rowv, tid);
 }
 
 // Gradient of one vector of entries (label entry Arg gets -gs*lam) -> store.
 template <int VAR>
 __device__ __forceinline__ void grad_vec(const typename Tr<VAR>::S& xp, const typename Tr<VAR>::S& xq,
-                                         int vi, const RowK& rk, const GradK& gk, int Arg, float* g_r) {
+                                         int vi, const RowK& rk, const GradK& gk, int Arg, Rsrc g,
+                                         uint32_t goff, uint32_t gsoff) {
   using T = Tr<VAR>;
   constexpr int VEC = T::VEC;
   float out[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
-    float q, r, g;
-    opd_entry(T::at(xp, e), T::at(xq, e), rk, q, r, g);
-    out[e] = grad_entry(q, g, gk);
+    float q, r, gg;
+    opd_entry(T::at(xp, e), T::at(xq, e), rk, q, r, gg);
+    out[e] = grad_entry(q, gg, gk);
   }
   const int rel = Arg - vi * VEC;
   if ((unsigned)rel < (unsigned)VEC) {  // this vector holds the label
@@ -553,217 +699,269 @@ __device__ __forceinline__ void grad_vec(const typename Tr<VAR>::S& xp, const ty
     for (int e = 0; e < VEC; ++e)
       if (e == rel) out[e] = out[e] - gk.fix;
   }
-  store_vec<VEC>(g_r, (unsigned)vi, out);
+  bstore_vec<VEC>(g, goff, gsoff, out);
+}
+
+// Clip corrections of one vector: cs += (r + q) - g, ck += r - clip(r).
+template <int VAR>
+__device__ __forceinline__ void clip_vec(const typename Tr<VAR>::S& xp, const typename Tr<VAR>::S& xq,
+                                         const RowK& rk, float& cs, float& ck) {
+  using T = Tr<VAR>;
+#pragma unroll
+  for (int e = 0; e < T::VEC; ++e) {
+    float q, r, g;
+    opd_entry(T::at(xp, e), T::at(xq, e), rk, q, r, g);
+    cs += (r + q) - g;
+    ck += r - __builtin_amdgcn_fmed3f(r, -rk.tau, rk.tau);
+  }
+}
+
+// Returns x through an empty asm statement: the compiler must treat the result
+// as a new value, so indices derived from it are recomputed in each phase of
+// a row instead of being kept (in registers or scratch) across phases.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
 
 // Verified row: statistics, loss, and (optionally) the gradient.
+//
+// A row is split into slots of kRowBlock vectors; thread t owns vector
+// s * kRowBlock + t of slot s.  Slots 0 .. nr-1 stay in registers, nr ..
+// nr+nl-1 in LDS, the rest are streamed (and read again for the gradient).
 template <int VAR>
 __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
                                              typename Tr<VAR>::S (*lp)[kRowBlock],
-                                             typename Tr<VAR>::S (*lq)[kRowBlock], int row,
-                                             uint32_t tag) {
+                                             typename Tr<VAR>::S (*lq)[kRowBlock], const Item& it,
+                                             int par, uint32_t tag) {
   using T = Tr<VAR>;
   using S = typename T::S;
   constexpr int VEC = T::VEC, NR = RowCfg<VAR>::NR, NL = RowCfg<VAR>::NL;
-  // Opaque per row: keeps the compiler from hoisting the many tid-derived
-  // per-vector indices out of the row loop (they would sit in registers or
-  // scratch for the whole kernel).
+  constexpr uint32_t SIN = Slot<VAR>::IN, SOUT = Slot<VAR>::OUT;
+  // Opaque per row: keeps the compiler from hoisting tid-derived values out
+  // of the row loop (they would sit in registers or scratch for the whole
+  // kernel).
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   const int lane = tid & 63, wid = tid >> 6;
+  const int row = it.row;
   const long long rowv = (long long)row * a.nvec;
-  const void* zp_r = T::row(a.zp, rowv);
-  const void* zq_r = T::row(a.zq, rowv);
+  const uint32_t rbytes = (uint32_t)a.V * (uint32_t)T::EB;
+  const Rsrc rzp = row_rsrc(T::row(a.zp, rowv), rbytes);
+  const Rsrc rzq = row_rsrc(T::row(a.zq, rowv), rbytes);
+  const uint32_t voff = (uint32_t)tid * (uint32_t)(T::VEC * T::EB);  // bytes of one vector
   const int nvec = a.nvec, nr = a.nr, nl = a.nl;
-  const int von = nr + nl;  // first streamed vector slot
+  const int von = nr + nl;                 // first streamed slot
+  const int nfull = nvec / kRowBlock;      // slots in which every thread has a vector
+  const bool tail = nfull >= von && nfull * kRowBlock + tid < nvec;  // streamed partial slot
   const float tau = a.tau;
 
-  // ---- sweep 1: read the row once; keep its first (nr + nl) vectors per
-  // thread on chip (registers, then LDS), fold every vector into the running
-  // statistics ----
+  // ---- sweep 1: read the row once; keep its on-chip slots, fold every
+  // vector into the running statistics ----
   if constexpr (NL > 0) {
 #pragma unroll
     for (int l = 0; l < NL; ++l) {
-      const int vi = (nr + l) * kRowBlock + tid;
-      if (l < nl && vi < nvec) {
-        __builtin_amdgcn_global_load_lds((const void*)((const S*)zp_r + (unsigned)vi),
-                                         (__attribute__((address_space(3))) void*)&lp[l][wid * 64],
-                                         16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)((const S*)zq_r + (unsigned)vi),
-                                         (__attribute__((address_space(3))) void*)&lq[l][wid * 64],
-                                         16, 0, 0);
+      const int sl = nr + l;
+      if (l < nl && sl * kRowBlock + tid < nvec) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rzp, (__attribute__((address_space(3))) void*)&lp[l][wid * 64], 16, voff,
+            (uint32_t)sl * SIN, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rzq, (__attribute__((address_space(3))) void*)&lq[l][wid * 64], 16, voff,
+            (uint32_t)sl * SIN, 0, 0);
       }
     }
   }
+  // Defined in every lane (zero where unused), so the register copies never
+  // carry values from one row to the next.
   S rp[NR], rq[NR];
 #pragma unroll
   for (int v = 0; v < NR; ++v) {
-    const int vi = v * kRowBlock + tid;
-    if (v < nr && vi < nvec) {
-      rp[v] = T::load(zp_r, (unsigned)vi);
-      rq[v] = T::load(zq_r, (unsigned)vi);
+    rp[v] = S{};
+    rq[v] = S{};
+    if (v < nr && v * kRowBlock + tid < nvec) {
+      rp[v] = T::bload(rzp, voff, (uint32_t)v * SIN);
+      rq[v] = T::bload(rzq, voff, (uint32_t)v * SIN);
     }
   }
   RowAcc A;
   acc_init(A);
-#pragma unroll 2
-  for (int vi = von * kRowBlock + tid; vi < nvec; vi += kRowBlock) {
-    const S xp = T::load(zp_r, (unsigned)vi), xq = T::load(zq_r, (unsigned)vi);
-    acc_vec<VAR>(xp, xq, vi, A, false);
+#ifndef AV_SU
+#define AV_SU 2
+#endif
+#pragma unroll AV_SU
+  for (int s = von; s < nfull; ++s) {
+    const S xp = T::bload(rzp, voff, (uint32_t)s * SIN), xq = T::bload(rzq, voff, (uint32_t)s * SIN);
+    acc_vec<VAR>(xp, xq, s * kRowBlock + tid, A, false);
   }
+  if (tail) {
+    const S xp = T::bload(rzp, voff, (uint32_t)nfull * SIN);
+    const S xq = T::bload(rzq, voff, (uint32_t)nfull * SIN);
+    acc_vec<VAR>(xp, xq, nfull * kRowBlock + tid, A, false);
+  }
+  uint64_t nxt = 0;
+  if (tid == 0) nxt = claim(a);  // its reply returns behind this row's loads
+  {
+    const int t = opaque(tid);
 #pragma unroll
-  for (int v = 0; v < NR; ++v) {
-    const int vi = v * kRowBlock + tid;
-    if (v < nr && vi < nvec) acc_vec<VAR>(rp[v], rq[v], vi, A, true);
+    for (int v = 0; v < NR; ++v) {
+      const int vi = v * kRowBlock + t;
+      if (v < nr && vi < nvec) acc_vec<VAR>(rp[v], rq[v], vi, A, true);
+    }
   }
   if constexpr (NL > 0) {
     __builtin_amdgcn_s_waitcnt(0);  // the LDS copies of this wave have landed
+    const int t = opaque(tid);
 #pragma unroll
     for (int l = 0; l < NL; ++l) {
-      const int vi = (nr + l) * kRowBlock + tid;
-      if (l < nl && vi < nvec) acc_vec<VAR>(lp[l][tid], lq[l][tid], vi, A, true);
+      const int vi = (nr + l) * kRowBlock + t;
+      if (l < nl && vi < nvec) acc_vec<VAR>(lp[l][t], lq[l][t], vi, A, true);
     }
   }
 
-  // ---- combine the statistics of the 1024 threads ----
-  const float mq_on = A.mq_on, d_on = A.d_on, mq_st = A.mq_st, d_st = A.d_st;
-  wave_merge_acc(A);
+  // ---- combine the statistics of the 1024 threads: wave butterflies, then
+  // every wave merges the 16 wave partials the same way ----
+  RowAcc W = A;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) merge_step(W, o);
   if (lane == 0) {
-    sm.f[wid][0] = A.mp;
-    sm.f[wid][1] = A.sp;
-    sm.f[wid][2] = A.mq;
-    sm.f[wid][3] = A.sq;
-    sm.f[wid][4] = A.kq;
-    sm.i[wid] = A.bv;
+    sm.f[par][wid][0] = W.mp;
+    sm.f[par][wid][1] = W.sp;
+    sm.f[par][wid][2] = W.mq;
+    sm.f[par][wid][3] = W.sq;
+    sm.f[par][wid][4] = W.kq;
+    sm.f[par][wid][5] = W.za;
+    sm.i[par][wid] = W.bi;
   }
+  if (tid == 0) sm.item[par ^ 1] = nxt;
   __syncthreads();
-  if (wid == 0) {  // lane w merges wave w's partials
-    RowAcc W;
-    acc_init(W);
-    if (lane < kRowWaves) {
-      W.mp = sm.f[lane][0];
-      W.sp = sm.f[lane][1];
-      W.mq = sm.f[lane][2];
-      W.sq = sm.f[lane][3];
-      W.kq = sm.f[lane][4];
-      W.bv = sm.i[lane];
-    }
-    wave_merge_acc(W);
-    if (lane == 0) {
-      const float lse_p = W.mp + kLn2 * __builtin_amdgcn_logf(W.sp);
-      const float lse_q = W.mq + kLn2 * __builtin_amdgcn_logf(W.sq);
-      sm.rf[0] = lse_p;
-      sm.rf[1] = lse_q;
-      sm.ri = first_in_vector<VAR>(zp_r, W.bv, W.mp);
-      // sum_j q_j (log q_j - log p_j) = sum_j q_j (zq_j - zp_j) - (lse_q - lse_p)
-      sm.rd = (double)W.kq / (double)W.sq - (double)(lse_q - lse_p);
-    }
+  acc_init(W);
+  if (lane < kRowWaves) {
+    W.mp = sm.f[par][lane][0];
+    W.sp = sm.f[par][lane][1];
+    W.mq = sm.f[par][lane][2];
+    W.sq = sm.f[par][lane][3];
+    W.kq = sm.f[par][lane][4];
+    W.za = sm.f[par][lane][5];
+    W.bi = sm.i[par][lane];
   }
-  __syncthreads();
-  const float lse_p32 = sm.rf[0], lse_q32 = sm.rf[1];
-  const int Arg = sm.ri;
-  const double KL = sm.rd;
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) merge_step(W, o);
+  const float mp = __shfl(W.mp, 0), sp = __shfl(W.sp, 0);
+  const float mq = __shfl(W.mq, 0), sq = __shfl(W.sq, 0), kq = __shfl(W.kq, 0);
+  const float zqa = __shfl(W.za, 0);
+  const int Arg = __shfl(W.bi, 0);
+  const float lse_p32 = mp + kLn2 * __builtin_amdgcn_logf(sp);
+  const float lse_q32 = mq + kLn2 * __builtin_amdgcn_logf(sq);
+  // sum_j q_j (log q_j - log p_j) = sum_j q_j (zq_j - zp_j) - (lse_q - lse_p)
+  const double KL = (double)kq / (double)sq - (double)(lse_q32 - lse_p32);
   const RowK rk = row_consts(lse_p32, lse_q32, tau);
 
-  // ---- clipping: every entry of a region whose bound
-  //   q_j |ell_j| <= exp(max zq - lse_q) (max |zq - zp| + |lse_q - lse_p|)
-  // stays below tau / 2 is inside the clip interval, so only regions that
-  // fail the bound are evaluated entry by entry, and the row's S and
-  // clipped-KL follow from the unclipped sums minus those corrections ----
+  // ---- clipping: an entry's |r_j| = q_j |ell_j| is at most
+  //   exp(m_t - lse_q) exp(zq_j - m_t) |zq_j - zp_j| + exp(zq_j - lse_q) |lse_q - lse_p|
+  // (m_t: the thread's max zq).  Every entry of a region whose bound stays
+  // below tau / 2 lies inside the clip interval; only regions that fail it
+  // are evaluated entry by entry, and S and the clipped KL follow from the
+  // unclipped sums minus those corrections ----
   const float adelta = __builtin_fabsf(rk.delta);
-  const bool flag_on = __builtin_amdgcn_exp2f((mq_on - lse_q32) * kLog2e) * (d_on + adelta) > 0.5f * tau;
-  const bool flag_st = __builtin_amdgcn_exp2f((mq_st - lse_q32) * kLog2e) * (d_st + adelta) > 0.5f * tau;
-  double S64 = KL + 1.0, KLc64 = KL;
-  if (__syncthreads_or(flag_on || flag_st)) {
-    float cs = 0.0f, ck = 0.0f;
-    if (flag_on) {
-#pragma unroll
-      for (int v = 0; v < NR; ++v) {
-        const int vi = v * kRowBlock + tid;
-        if (v < nr && vi < nvec) {
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            float q, r, g;
-            opd_entry(T::at(rp[v], e), T::at(rq[v], e), rk, q, r, g);
-            cs += (r + q) - g;
-            ck += r - __builtin_amdgcn_fmed3f(r, -tau, tau);
-          }
-        }
-      }
-      if constexpr (NL > 0) {
-#pragma unroll
-        for (int l = 0; l < NL; ++l) {
-          const int vi = (nr + l) * kRowBlock + tid;
-          if (l < nl && vi < nvec) {
-            const S xp = lp[l][tid], xq = lq[l][tid];
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-              float q, r, g;
-              opd_entry(T::at(xp, e), T::at(xq, e), rk, q, r, g);
-              cs += (r + q) - g;
-              ck += r - __builtin_amdgcn_fmed3f(r, -tau, tau);
-            }
-          }
-        }
-      }
-    }
-    if (flag_st) {
-      for (int vi = von * kRowBlock + tid; vi < nvec; vi += kRowBlock) {
-        const S xp = T::load(zp_r, (unsigned)vi), xq = T::load(zq_r, (unsigned)vi);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          float q, r, g;
-          opd_entry(T::at(xp, e), T::at(xq, e), rk, q, r, g);
-          cs += (r + q) - g;
-          ck += r - __builtin_amdgcn_fmed3f(r, -tau, tau);
-        }
-      }
-    }
-    double dcs = wsumd((double)cs), dck = wsumd((double)ck);
-    if (lane == 0) {
-      sm.d[wid][0] = dcs;
-      sm.d[wid][1] = dck;
-    }
-    __syncthreads();
-    double tcs = (lane < kRowWaves) ? sm.d[lane][0] : 0.0;
-    double tck = (lane < kRowWaves) ? sm.d[lane][1] : 0.0;
-    tcs = wsumd(tcs);  // every wave forms the same fixed-order sum
-    tck = wsumd(tck);
-    S64 -= tcs;
-    KLc64 -= tck;
-  }
-  const float S32 = (float)S64;
-  take_next(a, sm);
-
-  // ---- sweep 2: the gradient; streamed vectors are read a second time ----
-  if (a.grad) {
-    const GradK gk = grad_consts(a.lam, a.gs, S32);
-    float* g_r = a.grad + rowv * VEC;
-#pragma unroll 2
-    for (int vi = von * kRowBlock + tid; vi < nvec; vi += kRowBlock) {
-      const S xp = T::load(zp_r, (unsigned)vi), xq = T::load(zq_r, (unsigned)vi);
-      grad_vec<VAR>(xp, xq, vi, rk, gk, Arg, g_r);
-    }
+  const float et = __builtin_amdgcn_exp2f((A.mq - lse_q32) * kLog2e);
+  const bool flag_on =
+      __builtin_fmaf(et, A.pm_on, adelta * __builtin_amdgcn_exp2f((A.mq_on - lse_q32) * kLog2e)) >
+      0.5f * tau;
+  const bool flag_st =
+      __builtin_fmaf(et, A.pm_st, adelta * __builtin_amdgcn_exp2f((A.mq_st - lse_q32) * kLog2e)) >
+      0.5f * tau;
+  float cs = 0.0f, ck = 0.0f;
+  if (flag_on) {
+    const int t = opaque(tid);
 #pragma unroll
     for (int v = 0; v < NR; ++v) {
-      const int vi = v * kRowBlock + tid;
-      if (v < nr && vi < nvec) grad_vec<VAR>(rp[v], rq[v], vi, rk, gk, Arg, g_r);
+      if (v < nr && v * kRowBlock + t < nvec) clip_vec<VAR>(rp[v], rq[v], rk, cs, ck);
     }
     if constexpr (NL > 0) {
 #pragma unroll
       for (int l = 0; l < NL; ++l) {
-        const int vi = (nr + l) * kRowBlock + tid;
-        if (l < nl && vi < nvec) grad_vec<VAR>(lp[l][tid], lq[l][tid], vi, rk, gk, Arg, g_r);
+        if (l < nl && (nr + l) * kRowBlock + t < nvec) clip_vec<VAR>(lp[l][t], lq[l][t], rk, cs, ck);
       }
     }
   }
+  if (flag_st) {
+    for (int s = von; s < nfull; ++s)
+      clip_vec<VAR>(T::bload(rzp, voff, (uint32_t)s * SIN), T::bload(rzq, voff, (uint32_t)s * SIN), rk,
+                    cs, ck);
+    if (tail)
+      clip_vec<VAR>(T::bload(rzp, voff, (uint32_t)nfull * SIN),
+                    T::bload(rzq, voff, (uint32_t)nfull * SIN), rk, cs, ck);
+  }
+  double dcs = 0.0, dck = 0.0;
+  if (__any(flag_on || flag_st)) {
+    dcs = wsumd((double)cs);
+    dck = wsumd((double)ck);
+  }
+  if (lane == 0) {
+    sm.d[par][wid][0] = dcs;
+    sm.d[par][wid][1] = dck;
+  }
+  __syncthreads();
+  const double tcs = wsumd16((lane < kRowWaves) ? sm.d[par][lane][0] : 0.0);
+  const double tck = wsumd16((lane < kRowWaves) ? sm.d[par][lane][1] : 0.0);
+  const double S64 = (KL + 1.0) - tcs, KLc64 = KL - tck;
+  const float S32 = (float)S64;
 
-  if (tid == 0) {
-    // Arg is in [0, V): first_in_vector returns an index inside the row.
-    const float zqa = T::elem(a.zq, (long long)row * a.V + Arg);
-    const double ce = (double)lse_q32 - (double)zqa;
-    const double loss = (double)a.lam * ce + (1.0 - (double)a.lam) * KLc64;
-    publish_row(a, row, Arg, (float)loss, lse_p32, lse_q32, S32, (float)KLc64, tag);
+  // ---- the row is complete: one wave publishes it; if it is the request's
+  // last verified row to complete, that wave also finishes the request ----
+  if (wid == kLastWave) {
+    uint32_t n = 0;
+    if (lane == 0) {
+      const double ce = (double)lse_q32 - (double)zqa;
+      const float loss = (float)((double)a.lam * ce + (1.0 - (double)a.lam) * KLc64);
+      a.row_loss[row] = loss;
+      a.tgt[row] = Arg;
+      if (a.stats)
+        *(f32x4*)(a.stats + 4 * (long long)row) = (f32x4){lse_p32, lse_q32, S32, (float)KLc64};
+      tput(a.rowres + 2 * (long long)row, tag, (uint32_t)Arg);
+      tput(a.rowres + 2 * (long long)row + 1, tag, __float_as_uint(loss));
+      n = arrive(a.arrive + it.req, tag);
+    }
+    n = __shfl(n, 0);
+    if (n == (uint32_t)it.bkb) finish_request(a, it.req, it.r0, it.bkb, tag);
+  }
+
+  // ---- sweep 2: the gradient; streamed vectors are read a second time ----
+  if (a.grad) {
+    const GradK gk = grad_consts(a.lam, a.gs, S32);
+    const Rsrc rg = row_rsrc(a.grad + rowv * VEC, (uint32_t)a.V * 4u);
+    const uint32_t goff = (uint32_t)tid * (VEC * 4u);
+#ifndef AV_GU
+#define AV_GU 2
+#endif
+#pragma unroll AV_GU
+    for (int s = von; s < nfull; ++s) {
+      const S xp = T::bload(rzp, voff, (uint32_t)s * SIN), xq = T::bload(rzq, voff, (uint32_t)s * SIN);
+      grad_vec<VAR>(xp, xq, s * kRowBlock + tid, rk, gk, Arg, rg, goff, (uint32_t)s * SOUT);
+    }
+    if (tail) {
+      const S xp = T::bload(rzp, voff, (uint32_t)nfull * SIN);
+      const S xq = T::bload(rzq, voff, (uint32_t)nfull * SIN);
+      grad_vec<VAR>(xp, xq, nfull * kRowBlock + tid, rk, gk, Arg, rg, goff, (uint32_t)nfull * SOUT);
+    }
+    {
+      const int t = opaque(tid);
+#pragma unroll
+      for (int v = 0; v < NR; ++v) {
+        const int vi = v * kRowBlock + t;
+        if (v < nr && vi < nvec) grad_vec<VAR>(rp[v], rq[v], vi, rk, gk, Arg, rg, goff, (uint32_t)v * SOUT);
+      }
+    }
+    if constexpr (NL > 0) {
+      const int t = opaque(tid);
+#pragma unroll
+      for (int l = 0; l < NL; ++l) {
+        const int sl = nr + l, vi = sl * kRowBlock + t;
+        if (l < nl && vi < nvec)
+          grad_vec<VAR>(lp[l][t], lq[l][t], vi, rk, gk, Arg, rg, goff, (uint32_t)sl * SOUT);
+      }
+    }
   }
 }
 
@@ -774,16 +972,21 @@ __global__ __launch_bounds__(kRowBlock) void fused_kernel(FwdArgs a) {
   __shared__ S lp[NLA][kRowBlock];
   __shared__ S lq[NLA][kRowBlock];
   __shared__ RowSmem sm;
-  extern __shared__ int s_off[];  // ragged row offsets [B + 1]
+  // ragged: row offsets [B + 1]; dense longest-first: order [B] (uint16), b_k [B] (uint8)
+  extern __shared__ int s_dyn[];
+  const int* s_off = s_dyn;
+  uint16_t* order = (uint16_t*)s_dyn;
+  uint8_t* key = (uint8_t*)(order + (a.lpt ? a.B : 0));
   const int tid = threadIdx.x;
   if (tid == 0) {
     const uint32_t epoch =
         (uint32_t)__hip_atomic_load(a.ctl + 1, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
     sm.tag = epoch + 1u;  // epochs stay below 0xFFFFFFFF, so tags are never 0
+    sm.item[0] = claim(a);
   }
   int bad = 0;
   if (a.ragged) {
-    for (int j = tid; j <= a.B; j += kRowBlock) s_off[j] = a.row_off[j];
+    for (int j = tid; j <= a.B; j += kRowBlock) s_dyn[j] = a.row_off[j];
     __syncthreads();
     int okl = 1;
     for (int j = tid; j < a.B; j += kRowBlock) {
@@ -792,62 +995,74 @@ __global__ __launch_bounds__(kRowBlock) void fused_kernel(FwdArgs a) {
     }
     if (tid == 0 && (s_off[0] != 0 || s_off[a.B] != a.R)) okl = 0;
     bad = !__syncthreads_and(okl);
-    if (bad && tid == 0) raise_status(a.ctl + 2, AV_DEV_BAD_OFFSETS);
+    if (bad && tid == 0) raise_status(a.ctl, AV_DEV_BAD_OFFSETS);
+  } else if (a.lpt) {  // counting sort of the requests by b_k, descending
+    if (tid <= a.k) sm.hist[tid] = 0;
+    __syncthreads();
+    for (int b = tid; b < a.B; b += kRowBlock) {
+      const int kb = min(max(a.bk[b], 1), a.k);
+      key[b] = (uint8_t)kb;
+      atomicAdd(&sm.hist[kb], 1);
+    }
+    __syncthreads();
+    if (tid <= a.k) {
+      int c = 0;
+      for (int v = tid + 1; v <= a.k; ++v) c += sm.hist[v];
+      sm.cnt[tid] = c;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int cv = 0, cu = 0;
+      for (int p = 0; p <= a.k; ++p) {
+        sm.cum[p] = cv;
+        sm.cumu[p] = cu;
+        if (p < a.k) {
+          cv += sm.cnt[p];
+          cu += a.B - sm.cnt[p];
+        }
+      }
+    }
+    for (int b = tid; b < a.B; b += kRowBlock) {  // stable: rank among equal b_k
+      const int kb = key[b];
+      int rank = 0;
+      for (int j = 0; j < b; ++j) rank += key[j] == kb;
+      order[sm.cnt[kb] + rank] = (uint16_t)b;
+    }
   }
-  take_next(a, sm);
-  for (;;) {
-    __syncthreads();
-    const uint32_t item = sm.item, stat = sm.stat, tag = sm.tag;
-    __syncthreads();
-    if (item >= (uint32_t)a.R) break;
+  __syncthreads();
+  const uint32_t tag = sm.tag;
+  for (int iter = 0;; ++iter) {
+    const int par = iter & 1;
+    const uint64_t w = sm.item[par];
+    const uint32_t idx = __builtin_amdgcn_readfirstlane((uint32_t)w);
+    const uint32_t stat = __builtin_amdgcn_readfirstlane((uint32_t)(w >> 32));
+    if (idx >= (uint32_t)a.R) break;
     if (bad || stat != 0u) {  // failed launch: drain without work
-      take_next(a, sm);
+      if (tid == 0) sm.item[par ^ 1] = claim(a);
+      __syncthreads();
       continue;
     }
-    const int row = (int)item;
-    int req, pos, bkb;
-    bool last_of_req;
-    if (a.ragged) {
-      int lo = 0, hi = a.B - 1;  // last request whose first row is <= row
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_off[mid] <= row) lo = mid;
-        else hi = mid - 1;
-      }
-      req = lo;
-      pos = row - s_off[req];
-      bkb = s_off[req + 1] - s_off[req];
-      last_of_req = row == s_off[req + 1] - 1;
-    } else {
-      req = row / a.k;
-      pos = row - req * a.k;
-      bkb = min(max(a.bk[req], 1), a.k);
-      last_of_req = pos == a.k - 1;
-    }
-    if (pos < bkb) verified_row<VAR>(a, sm, lp, lq, row, tag);
-    else unverified_row<VAR>(a, sm, row, tag);
-    if (last_of_req) {
-      __syncthreads();
-      finish_request(a, s_off, req, tag);
-    }
-    if (row == a.R - 1) {
-      __syncthreads();
-      finish_total(a, sm, tag);
-    }
+    const Item it = map_item(a, sm, s_off, order, key, (int)idx);
+    if (it.verified) verified_row<VAR>(a, sm, lp, lq, it, par, tag);
+    else unverified_row<VAR>(a, sm, it.row, par);
   }
-  // The last workgroup to leave resets the dispenser, the status and the
-  // done count and advances the epoch.  Status bits and the done count share
-  // one word, so every status raised before a workgroup left is seen by the
-  // one that leaves last.
-  if (tid == 0) {
-    const uint64_t old =
-        __hip_atomic_fetch_add(a.ctl + 2, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((uint32_t)old == gridDim.x - 1u) {
-      const uint32_t stat = (uint32_t)(old >> 32) | (bad ? (uint32_t)AV_DEV_BAD_OFFSETS : 0u);
+  // The workgroup that leaves last sums the request losses, reports the
+  // status, resets the dispenser and the done count, and advances the epoch.
+  // Status bits and the done count share one word, so every status raised
+  // before a workgroup left is seen by the one that leaves last.
+  __syncthreads();
+  if (tid == 0)
+    sm.exitw = __hip_atomic_fetch_add(a.ctl + 2, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const uint64_t old = sm.exitw;
+  if ((uint32_t)old == gridDim.x - 1u) {
+    uint32_t stat = (uint32_t)(old >> 32) | (bad ? (uint32_t)AV_DEV_BAD_OFFSETS : 0u);
+    if (stat == 0u && !finish_total(a, sm, tag)) stat |= (uint32_t)AV_DEV_TIMEOUT;
+    if (tid == 0) {
       if (a.status_out) a.status_out[0] = (int32_t)stat;
       __hip_atomic_store(a.ctl, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(a.ctl + 2, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t epoch = sm.tag - 1u;
+      const uint32_t epoch = tag - 1u;
       const uint32_t next = (epoch + 1u == 0xFFFFFFFFu) ? 0u : epoch + 1u;
       __hip_atomic_store(a.ctl + 1, (uint64_t)next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
