@@ -23,8 +23,12 @@ int hip_fail(hipError_t e) {
 struct DeviceInfo {
   int cus = 0;
   long long ticks_per_ms = 0;  // wall-clock counter rate
-  int occ[4] = {0, 0, 0, 0};   // fused-kernel workgroups per CU, per variant (no dynamic LDS)
+  int occ[4][2] = {};          // fused-kernel workgroups per CU, per variant and full/general
+                               // form, with the most dynamic LDS a launch uses
 };
+// Most dynamic LDS of a fused launch: ragged offsets of 4095 requests, or the
+// longest-first schedule of avk::kMaxLptRequests requests.
+constexpr size_t kMaxDynLds = 4096 * sizeof(int32_t);
 constexpr int kMaxDevices = 64;
 DeviceInfo g_dev[kMaxDevices];
 std::once_flag g_dev_once[kMaxDevices];
@@ -42,7 +46,8 @@ hipError_t device_info(const DeviceInfo** out) {
     if (err == hipSuccess) err = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
     d.ticks_per_ms = khz > 0 ? (long long)khz : 100000;
     for (int v = 0; v < 4 && err == hipSuccess; ++v)
-      err = avk::fused_blocks_per_cu((avk::Variant)v, 0, &d.occ[v]);
+      for (int f = 0; f < 2 && err == hipSuccess; ++f)
+        err = avk::fused_blocks_per_cu((avk::Variant)v, f != 0, kMaxDynLds, &d.occ[v][f]);
     g_dev_err[dev] = err;
   });
   if (g_dev_err[dev] != hipSuccess) return g_dev_err[dev];
@@ -178,12 +183,12 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_
   size_t lds = 0;
   if (p.ragged) lds = (size_t)(B + 1) * sizeof(int32_t);
   else if (lpt) lds = ((size_t)B * 3 + 3) & ~(size_t)3;
-  int occ = dev->occ[p.var];
-  if (lds) {
-    e = avk::fused_blocks_per_cu(p.var, lds, &occ);
-    if (e != hipSuccess) return hip_fail(e);
-  }
-  if (occ < 1) return AV_EUNSUPPORTED;
+  // The fast form needs every on-chip slot filled and the default split.
+  const int nr_max = avk::variant_row_regs(p.var), nl_max = avk::variant_row_lds(p.var);
+  const bool full = nr == nr_max && nl == nl_max &&
+                    (long long)p.nvec >= (long long)(nr_max + nl_max) * avk::kRowBlock;
+  const int occ = dev->occ[p.var][full ? 1 : 0];
+  if (occ < 1 || lds > kMaxDynLds) return AV_EUNSUPPORTED;
   long long grid = (long long)occ * dev->cus;
   if (grid > R) grid = R;
 
@@ -219,7 +224,7 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_
   a.lam = lambda;
   a.tau = tau;
   a.gs = grad_scale;
-  e = avk::launch_fused(p.var, a, (int)grid, lds, (hipStream_t)stream);
+  e = avk::launch_fused(p.var, full, a, (int)grid, lds, (hipStream_t)stream);
   return e == hipSuccess ? AV_OK : hip_fail(e);
 }
 

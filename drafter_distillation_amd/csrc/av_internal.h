@@ -45,7 +45,10 @@ inline int variant_nvmax(Variant v) { return v == kBf16x8 ? 8 : v == kF32x4 ? 8 
 #ifndef AV_NR
 #define AV_NR 9
 #endif
-constexpr int kRowRegs16 = AV_NR, kRowLds16 = 4;
+#ifndef AV_NL
+#define AV_NL 4
+#endif
+constexpr int kRowRegs16 = AV_NR, kRowLds16 = AV_NL;
 constexpr int kRowRegs1 = 32, kRowLds1 = 0;  // scalar variants
 inline int variant_row_regs(Variant v) { return (v == kBf16x8 || v == kF32x4) ? kRowRegs16 : kRowRegs1; }
 inline int variant_row_lds(Variant v) { return (v == kBf16x8 || v == kF32x4) ? kRowLds16 : kRowLds1; }
@@ -97,8 +100,10 @@ struct HeadArgs {
   int B, H, k, mode;
 };
 
-hipError_t launch_fused(Variant v, const FwdArgs& a, int grid, size_t lds, hipStream_t s);
-hipError_t fused_blocks_per_cu(Variant v, size_t lds, int* out);
+// full: every on-chip slot of a row is filled (nvec >= (regs + lds) * kRowBlock)
+// and the default on-chip split is used.
+hipError_t launch_fused(Variant v, bool full, const FwdArgs& a, int grid, size_t lds, hipStream_t s);
+hipError_t fused_blocks_per_cu(Variant v, bool full, size_t lds, int* out);
 hipError_t launch_bwd(Variant v, const BwdArgs& a, hipStream_t s);
 hipError_t launch_head(const HeadArgs& a, hipStream_t s);
 hipError_t launch_zero(uint64_t* p, size_t words, hipStream_t s);

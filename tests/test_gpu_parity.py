@@ -340,6 +340,28 @@ def test_full_concurrent(av, concurrent_full):
     grad_row_sums_vanish(out, w, bk)
 
 
+@pytest.mark.parametrize("name", ["concurrent", "long", "ragged"])
+def test_full_size_fused_grad_matches_bwd_bits(av, name):
+    """Every gradient entry of a full-size workload, checked against the
+    standalone backward (separate kernel, separate store pattern) bit for bit;
+    the oracle checks above cover sampled rows."""
+    say(f"full-size fused vs bwd: {name}")
+    w = synth.make(name)
+    inp = gpu_inputs(w)
+    kw = dict(k=w.k, lam=w.lam, tau=w.tau, grad_scale=0.25)
+    if w.row_off is not None:
+        kw["row_off"] = inp["row_off"]
+    else:
+        kw["bk"] = torch.from_numpy(head_bk(w).astype(np.int32)).cuda()
+    out = av.av_verify_opd_fwd(inp["zp"], inp["zq"], inp["draft"], **kw)
+    g = av.av_verify_opd_bwd(inp["zp"], inp["zq"], out["tgt_argmax"], out["row_stats"], **kw)
+    torch.cuda.synchronize()
+    assert int(out["status"].item()) == 0
+    a, b = out["grad"].view(torch.int32), g.view(torch.int32)
+    diff = (a != b).nonzero()
+    assert diff.numel() == 0, f"{diff.shape[0]} entries differ, first at {diff[:4].tolist()}"
+
+
 def test_full_ragged(av):
     say("generating ragged workload")
     w = synth.make("ragged")
