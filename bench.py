@@ -164,7 +164,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-requests", type=int, default=64)
+    ap.add_argument("--cpu-requests", type=int, default=128)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run a plain copy of this many MiB before warmup (counter calibration)")
