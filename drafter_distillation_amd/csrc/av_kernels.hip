@@ -887,6 +887,31 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
+// Explicit waits on this wave's outstanding memory operations.  They are also
+// compiler barriers: direct-to-LDS loads are not tracked by the compiler, so
+// every LDS read of such data sits behind one of these.
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void wait_vmem_but() {  // all but the N most recent
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Direct loads of slot s of a row's zp and zq into LDS slot position l.
+template <int VAR>
+__device__ __forceinline__ void dma_slot(const RowIO<VAR>& io, Rsrc rzp, Rsrc rzq,
+                                         typename Tr<VAR>::S (*lp)[kRowBlock],
+                                         typename Tr<VAR>::S (*lq)[kRowBlock], int l, int s, int nvec,
+                                         int tid) {
+  if (io.has(io.nb(s, nvec))) {
+    const uint32_t so = (uint32_t)s * RowIO<VAR>::SIN;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rzp, (__attribute__((address_space(3))) void*)&lp[l][io.wid * 64], 16, (uint32_t)tid * 16u, so, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rzq, (__attribute__((address_space(3))) void*)&lq[l][io.wid * 64], 16, (uint32_t)tid * 16u, so, 0, 0);
+  }
+}
+
 // Verified row: statistics, loss, and (optionally) the gradient.
 //
 // Slots 0 .. nr-1 of the row stay in registers, nr .. nr+nl-1 in LDS, the
@@ -918,23 +943,16 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   const float tau = opaque_s(a.tau);
 
   // ---- sweep 1: read the row once; keep its on-chip slots, fold every
-  // vector into the running statistics ----
-  {
+  // vector into the running statistics.  Fast form: the streamed slots pass
+  // through the LDS slots NL at a time (direct loads, no registers held
+  // while in flight), then the LDS slots take their resident data. ----
+  constexpr bool RING = FULL && NL > 0;
+  const int ns = nfull + (nfull * kRowBlock < nvec ? 1 : 0);  // slots, the partial one included
+  if constexpr (!RING && NL > 0) {
     const IO io(tid);
-    if constexpr (NL > 0) {
 #pragma unroll
-      for (int l = 0; l < NL; ++l) {
-        const int sl = nr + l;
-        if (l < nl && io.has(io.nb(sl, nvec))) {
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rzp, (__attribute__((address_space(3))) void*)&lp[l][wid * 64], 16, (uint32_t)tid * 16u,
-              (uint32_t)sl * SIN, 0, 0);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rzq, (__attribute__((address_space(3))) void*)&lq[l][wid * 64], 16, (uint32_t)tid * 16u,
-              (uint32_t)sl * SIN, 0, 0);
-        }
-      }
-    }
+    for (int l = 0; l < NL; ++l)
+      if (l < nl) dma_slot<VAR>(io, rzp, rzq, lp, lq, l, nr + l, nvec, tid);
   }
   // Defined in every lane (zero where unused), so the register copies never
   // carry values from one row to the next.
@@ -954,7 +972,65 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   }
   RowAcc A;
   acc_init(A);
-  {
+  if constexpr (RING) {
+    // Streamed slots go in pairs through the two halves of the LDS slots,
+    // double-buffered: pair p+1 is in flight while pair p is folded in.
+    // Each half takes its resident slots after its last streamed pair.  A
+    // wait for pair p leaves outstanding only what was issued after it (the
+    // next pair, or a half's resident slots), counted for slots every wave
+    // loads (partial slots are not counted).
+    static_assert(NL == 4, "two halves of two LDS slots");
+    const IO io(opaque(tid));
+    const int npair = (ns - von + 1) >> 1;
+    auto full_ops = [&](int q) {  // loads of pair q that every wave issues
+      const int s0 = von + 2 * q;
+      return (s0 < nfull ? 2 : 0) + (s0 + 1 < nfull ? 2 : 0);
+    };
+    if (npair == 0) {
+#pragma unroll
+      for (int l = 0; l < NL; ++l) dma_slot<VAR>(io, rzp, rzq, lp, lq, l, nr + l, nvec, tid);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        if (von + j < ns) dma_slot<VAR>(io, rzp, rzq, lp, lq, j, von + j, nvec, tid);
+      if (npair >= 2) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          if (von + 2 + j < ns) dma_slot<VAR>(io, rzp, rzq, lp, lq, 2 + j, von + 2 + j, nvec, tid);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) dma_slot<VAR>(io, rzp, rzq, lp, lq, 2 + j, nr + 2 + j, nvec, tid);
+      }
+    }
+    for (int q = 0; q < npair; ++q) {
+      const int h = q & 1;
+      const int after = (q + 1 < npair) ? full_ops(q + 1) : 4;
+      if (after >= 4) wait_vmem_but<4>();
+      else if (after >= 2) wait_vmem_but<2>();
+      else wait_vmem_all();
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int sl = von + 2 * q + j;
+        if (sl < ns) {
+          const int nbv = io.nb(sl, nvec);
+          if (io.has(nbv))
+            acc_vec<VAR>(io.lds(lp[2 * h + j], nbv), io.lds(lq[2 * h + j], nbv), io.lo(sl), io.H(nbv), A,
+                         false);
+        }
+      }
+      wait_lds_reads();  // this half is free again
+      if (q + 2 < npair) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int sl = von + 2 * (q + 2) + j;
+          if (sl < ns) dma_slot<VAR>(io, rzp, rzq, lp, lq, 2 * h + j, sl, nvec, tid);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) dma_slot<VAR>(io, rzp, rzq, lp, lq, 2 * h + j, nr + 2 * h + j, nvec, tid);
+      }
+    }
+  } else {
     const IO io(opaque(tid));
 #ifndef AV_SU
 #define AV_SU 1
@@ -984,7 +1060,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
     }
   }
   if constexpr (NL > 0) {
-    __builtin_amdgcn_s_waitcnt(0);  // the LDS copies of this wave have landed
+    wait_vmem_all();  // the LDS copies of this wave have landed
     const IO io(opaque(tid));
 #pragma unroll
     for (int l = 0; l < NL; ++l) {
@@ -1107,45 +1183,86 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
     if (n == (uint32_t)it.bkb) finish_request(a, it.req, it.r0, it.bkb, tag);
   }
 
-  // ---- sweep 2: the gradient; streamed vectors are read a second time ----
+  // ---- sweep 2: the gradient; streamed vectors are read a second time
+  // (fast form: through the LDS slots once their resident data is done) ----
   if (a.grad) {
     const GradK gk = grad_consts(opaque_s(a.lam), opaque_s(a.gs), S32);
     const Rsrc rg = row_rsrc(a.grad + rowv * IO::VEC, (uint32_t)opaque_s(a.V) * 4u);
-    {
+    if constexpr (RING) {
+      // Stores of one full register slot's vector (all register slots are full).
+      constexpr int kRegStores = NR * (IO::kHalves ? 2 : 1);
+      static_assert(kRegStores <= 63, "vmcnt range");
       const IO io(opaque(tid));
+#pragma unroll
+      for (int l = 0; l < NL; ++l)
+        grad_vec<VAR>(io.lds(lp[l], 64), io.lds(lq[l], 64), io, nr + l, 64, rk, gk, Arg, rg);
+      bool regs_done = false;
+      for (int s0 = von; s0 < ns; s0 += NL) {
+        wait_lds_reads();
+#pragma unroll
+        for (int l = 0; l < NL; ++l)
+          if (s0 + l < ns) dma_slot<VAR>(io, rzp, rzq, lp, lq, l, s0 + l, nvec, tid);
+        if (!regs_done) {  // the register slots' gradient overlaps the first loads
+#pragma unroll
+          for (int v = 0; v < NR; ++v) grad_vec<VAR>(rp[v], rq[v], io, v, 64, rk, gk, Arg, rg);
+          wait_vmem_but<kRegStores>();
+          regs_done = true;
+        } else {
+          wait_vmem_all();
+        }
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+          const int sl = s0 + l;
+          if (sl < ns) {
+            const int nbv = io.nb(sl, nvec);
+            if (io.has(nbv))
+              grad_vec<VAR>(io.lds(lp[l], nbv), io.lds(lq[l], nbv), io, sl, nbv, rk, gk, Arg, rg);
+          }
+        }
+      }
+      if (!regs_done) {
+#pragma unroll
+        for (int v = 0; v < NR; ++v) grad_vec<VAR>(rp[v], rq[v], io, v, 64, rk, gk, Arg, rg);
+      }
+      wait_lds_reads();  // the next row's direct loads may overwrite the LDS slots
+    } else {
+      {
+        const IO io(opaque(tid));
 #ifndef AV_GU
 #define AV_GU 2
 #endif
 #pragma unroll AV_GU
-      for (int s = von; s < nfull; ++s) {
-        const S xp = io.load(rzp, s, 64), xq = io.load(rzq, s, 64);
-        grad_vec<VAR>(xp, xq, io, s, 64, rk, gk, Arg, rg);
-      }
-      if (tail) {
-        const int nbv = io.nb(nfull, nvec);
-        if (io.has(nbv)) {
-          const S xp = io.load(rzp, nfull, nbv), xq = io.load(rzq, nfull, nbv);
-          grad_vec<VAR>(xp, xq, io, nfull, nbv, rk, gk, Arg, rg);
+        for (int s = von; s < nfull; ++s) {
+          const S xp = io.load(rzp, s, 64), xq = io.load(rzq, s, 64);
+          grad_vec<VAR>(xp, xq, io, s, 64, rk, gk, Arg, rg);
+        }
+        if (tail) {
+          const int nbv = io.nb(nfull, nvec);
+          if (io.has(nbv)) {
+            const S xp = io.load(rzp, nfull, nbv), xq = io.load(rzq, nfull, nbv);
+            grad_vec<VAR>(xp, xq, io, nfull, nbv, rk, gk, Arg, rg);
+          }
         }
       }
-    }
-    {
-      const IO io(opaque(tid));
+      {
+        const IO io(opaque(tid));
 #pragma unroll
-      for (int v = 0; v < NR; ++v) {
-        const int nbv = io.nb(v, nvec);
-        if (v < nr && io.has(nbv))
-          grad_vec<VAR>(rp[v], rq[v], io, v, nbv, rk, gk, Arg, rg);
+        for (int v = 0; v < NR; ++v) {
+          const int nbv = io.nb(v, nvec);
+          if (v < nr && io.has(nbv))
+            grad_vec<VAR>(rp[v], rq[v], io, v, nbv, rk, gk, Arg, rg);
+        }
       }
-    }
-    if constexpr (NL > 0) {
-      const IO io(opaque(tid));
+      if constexpr (NL > 0) {
+        const IO io(opaque(tid));
 #pragma unroll
-      for (int l = 0; l < NL; ++l) {
-        const int sl = nr + l, nbv = io.nb(sl, nvec);
-        if (l < nl && io.has(nbv))
-          grad_vec<VAR>(io.lds(lp[l], nbv), io.lds(lq[l], nbv), io, sl, nbv, rk, gk, Arg, rg);
+        for (int l = 0; l < NL; ++l) {
+          const int sl = nr + l, nbv = io.nb(sl, nvec);
+          if (l < nl && io.has(nbv))
+            grad_vec<VAR>(io.lds(lp[l], nbv), io.lds(lq[l], nbv), io, sl, nbv, rk, gk, Arg, rg);
+        }
       }
+      wait_lds_reads();
     }
   }
 }
