@@ -211,6 +211,8 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_
   a.rowres = (uint64_t*)(ws + avk::ws_rowres_off());
   a.reqres = (uint64_t*)(ws + avk::ws_reqres_off(R));
   a.arrive = (uint64_t*)(ws + avk::ws_arrive_off(B, R));
+  a.halfres = (uint64_t*)(ws + avk::ws_halfres_off(B, R));
+  a.harrive = (uint64_t*)(ws + avk::ws_harrive_off(B, R));
   a.timeout_ticks = dev->ticks_per_ms * 2000;  // 2 s per wait
   a.B = B;
   a.k = k;

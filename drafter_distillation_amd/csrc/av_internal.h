@@ -18,13 +18,17 @@ constexpr int kMaxChunks = 64;   // chunks per row of the standalone backward
 //   rowres   [R][2]   per-row target argmax and loss (tagged)
 //   reqres   [B][2]   per-request loss sum, float64 halves (tagged)
 //   arrive   [B]      per-request count of completed verified rows (tagged)
+//   halfres  [R][2][2] per half of an unverified row: max of zp, its index (tagged)
+//   harrive  [R]      per-row count of completed halves (tagged)
 constexpr size_t kCtlBytes = 256;
 
 inline size_t ws_rowres_off() { return kCtlBytes; }
 inline size_t ws_reqres_off(int R) { return ws_rowres_off() + (size_t)R * 16; }
 inline size_t ws_arrive_off(int B, int R) { return ws_reqres_off(R) + (size_t)B * 16; }
+inline size_t ws_halfres_off(int B, int R) { return ws_arrive_off(B, R) + (size_t)B * 8; }
+inline size_t ws_harrive_off(int B, int R) { return ws_halfres_off(B, R) + (size_t)R * 32; }
 inline size_t ws_total(int B, int R) {
-  size_t n = ws_arrive_off(B, R) + (size_t)B * 8;
+  size_t n = ws_harrive_off(B, R) + (size_t)R * 8;
   return (n + 255) & ~(size_t)255;
 }
 
@@ -71,12 +75,14 @@ struct FwdArgs {
   uint64_t* rowres;
   uint64_t* reqres;
   uint64_t* arrive;
+  uint64_t* halfres;
+  uint64_t* harrive;
   long long timeout_ticks;
   int B, k, V, R;
   int nvec;      // vectors per row (V / vec)
   int nr, nl;    // vectors per thread held in registers / in LDS
   int ragged;
-  int lpt;       // dense layout, rows handed out longest first
+  int lpt;       // dense layout, rows handed out longest first (unverified rows in halves)
   float lam, tau, gs;
 };
 

@@ -532,13 +532,15 @@ __device__ __forceinline__ uint32_t arrive(uint64_t* p, uint32_t tag) {
 // Work item: a row, its request, and whether it is verified.
 struct Item {
   int row, req, r0, bkb;  // r0: first row of the request; bkb: its verified rows
+  int half;               // unverified rows of the longest-first order: 0 or 1; else -1
   bool verified;
 };
 
 // Dense layout, longest first: verified rows position-major (position p holds
 // the cnt[p] requests with b_k > p, which lead `order`, sorted by b_k
 // descending), then unverified rows position-major (the requests with
-// b_k <= p, which trail `order`).
+// b_k <= p, which trail `order`), each as two halves, so that the last work
+// items of a launch are short.
 __device__ __forceinline__ Item map_item(const FwdArgs& a, const RowSmem& sm, const int* s_off,
                                          const uint16_t* order, const uint8_t* key, int idx) {
   Item m;
@@ -553,6 +555,7 @@ __device__ __forceinline__ Item map_item(const FwdArgs& a, const RowSmem& sm, co
     m.req = lo;
     m.r0 = s_off[lo];
     m.bkb = s_off[lo + 1] - m.r0;
+    m.half = -1;
     m.verified = true;
   } else if (a.lpt) {
     const int k = opaque_s(a.k), rv = sm.cum[k];
@@ -565,9 +568,11 @@ __device__ __forceinline__ Item map_item(const FwdArgs& a, const RowSmem& sm, co
       }
       p = lo;
       j = idx - sm.cum[p];
+      m.half = -1;
       m.verified = true;
     } else {
-      const int u = idx - rv;
+      const int u = (idx - rv) >> 1;
+      m.half = (idx - rv) & 1;
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (sm.cumu[mid] <= u) lo = mid;
@@ -587,6 +592,7 @@ __device__ __forceinline__ Item map_item(const FwdArgs& a, const RowSmem& sm, co
     m.req = idx / k;
     m.r0 = m.req * k;
     m.bkb = min(max(a.bk[m.req], 1), k);
+    m.half = -1;
     m.verified = idx - m.r0 < m.bkb;
   }
   return m;
@@ -744,32 +750,6 @@ struct RowIO {
   }
 };
 
-// Zero gradient of a row, 16-byte stores where the row allows them.
-template <int VAR>
-__device__ __forceinline__ void zero_row(const FwdArgs& a, long long rowv, int tid) {
-  constexpr int VEC = Tr<VAR>::VEC;
-  const int V = opaque_s(a.V);
-  const Rsrc g = row_rsrc(a.grad + rowv * VEC, (uint32_t)V * 4u);
-  if constexpr (VEC >= 4) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    const int n4 = V / 4, nfull = n4 / kRowBlock;  // 16-byte pieces per row, full slots
-    const uint32_t off = (uint32_t)tid * 16u;
-#pragma unroll 4
-    for (int s = 0; s < nfull; ++s)
-      bstore16<kStoreAux>(z, g, off, (uint32_t)s * (kRowBlock * 16u));
-    if (nfull * kRowBlock + tid < n4)
-      bstore16<kStoreAux>(z, g, off, (uint32_t)nfull * (kRowBlock * 16u));
-  } else {
-    const int nfull = V / kRowBlock;
-    const uint32_t off = (uint32_t)tid * 4u;
-#pragma unroll 4
-    for (int s = 0; s < nfull; ++s)
-      __builtin_amdgcn_raw_buffer_store_b32(0u, g, off, (uint32_t)s * (kRowBlock * 4u), kStoreAux);
-    if (nfull * kRowBlock + tid < V)
-      __builtin_amdgcn_raw_buffer_store_b32(0u, g, off, (uint32_t)nfull * (kRowBlock * 4u), kStoreAux);
-  }
-}
-
 // Folds one zp vector of consecutive entries into a running (max, first
 // index) pair; vectors come in increasing order, so a strict > keeps the first.
 template <int VAR>
@@ -789,10 +769,38 @@ __device__ __forceinline__ void argmax_vec(const typename Tr<VAR>::S& x, int vi,
   }
 }
 
-// Unverified row: target argmax only, zero gradient.
+// Zero gradient of slots [s0, s1) of a row (16-byte pieces where the row
+// allows them; a slot is kRowBlock pieces).
 template <int VAR>
-__device__ __forceinline__ void unverified_row(const FwdArgs& a, RowSmem& sm, int row, int par) {
+__device__ __forceinline__ void zero_slots(const FwdArgs& a, long long rowv, int tid, int s0, int s1) {
+  constexpr int VEC = Tr<VAR>::VEC;
+  const int V = opaque_s(a.V);
+  const Rsrc g = row_rsrc(a.grad + rowv * VEC, (uint32_t)V * 4u);
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  if constexpr (VEC >= 4) {
+    const int n4 = V / 4;  // 16-byte pieces per row
+    const uint32_t off = (uint32_t)tid * 16u;
+#pragma unroll 4
+    for (int s = s0; s < s1; ++s)
+      if (s * kRowBlock + tid < n4) bstore16<kStoreAux>(z, g, off, (uint32_t)s * (kRowBlock * 16u));
+  } else {
+    const uint32_t off = (uint32_t)tid * 4u;
+#pragma unroll 4
+    for (int s = s0; s < s1; ++s)
+      if (s * kRowBlock + tid < V)
+        __builtin_amdgcn_raw_buffer_store_b32(0u, g, off, (uint32_t)s * (kRowBlock * 4u), kStoreAux);
+  }
+}
+
+// Unverified row (half < 0) or half of one: target argmax only, zero
+// gradient.  Half h covers the first / second half of the row's vector slots
+// and of its gradient's 16-byte slots; the half that completes the row second
+// merges the two maxima (the lower index wins ties) and writes the results.
+template <int VAR>
+__device__ __forceinline__ void unverified_row(const FwdArgs& a, RowSmem& sm, int row, int par, int half,
+                                               uint32_t tag) {
   using T = Tr<VAR>;
+  constexpr int VEC = T::VEC;
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   const int lane = tid & 63, wid = tid >> 6;
@@ -802,14 +810,26 @@ __device__ __forceinline__ void unverified_row(const FwdArgs& a, RowSmem& sm, in
   const Rsrc rzp = row_rsrc(T::row(a.zp, rowv), (uint32_t)opaque_s(a.V) * (uint32_t)T::EB);
   constexpr uint32_t VB = T::VEC * T::EB, SIN = kRowBlock * VB;
   const uint32_t voff = (uint32_t)tid * VB;
-  const int nvec = opaque_s(a.nvec), nfull = nvec / kRowBlock;
+  const int nvec = opaque_s(a.nvec);
+  const int ns = (nvec + kRowBlock - 1) / kRowBlock;       // vector slots
+  const int gpieces = VEC >= 4 ? opaque_s(a.V) / 4 : opaque_s(a.V);
+  const int gs = (gpieces + kRowBlock - 1) / kRowBlock;    // gradient slots
+  int s0 = 0, s1 = ns, g0 = 0, g1 = gs;
+  if (half >= 0) {
+    s0 = half ? ns / 2 : 0;
+    s1 = half ? ns : ns / 2;
+    g0 = half ? gs / 2 : 0;
+    g1 = half ? gs : gs / 2;
+  }
+  const int full_end = min(s1, nvec / kRowBlock);  // slots in which every thread has a vector
   float m = -INFINITY;
   int bi = INT_MAX;
 #pragma unroll 4
-  for (int s = 0; s < nfull; ++s)
+  for (int s = s0; s < full_end; ++s)
     argmax_vec<VAR>(T::bload(rzp, voff, (uint32_t)s * SIN), s * kRowBlock + tid, m, bi);
-  if (nfull * kRowBlock + tid < nvec)
-    argmax_vec<VAR>(T::bload(rzp, voff, (uint32_t)nfull * SIN), nfull * kRowBlock + tid, m, bi);
+  for (int s = max(full_end, s0); s < s1; ++s)
+    if (s * kRowBlock + tid < nvec)
+      argmax_vec<VAR>(T::bload(rzp, voff, (uint32_t)s * SIN), s * kRowBlock + tid, m, bi);
   wargmax(m, bi);
   if (lane == 0) {
     sm.f[par][wid][0] = m;
@@ -825,14 +845,39 @@ __device__ __forceinline__ void unverified_row(const FwdArgs& a, RowSmem& sm, in
       I = sm.i[par][lane];
     }
     wargmax(M, I);
-    if (lane == 0) {
+    bool write = half < 0;
+    if (half >= 0) {  // publish this half; the second half to finish merges
+      const KArgs K = cold_args();
+      uint32_t n = 0;
+      if (lane == 0) {
+        uint64_t* hr = K->halfres + 4 * (long long)row + 2 * half;
+        tput(hr, tag, __float_as_uint(M));
+        tput(hr + 1, tag, (uint32_t)I);
+        n = arrive(K->harrive + row, tag);
+      }
+      n = __shfl(n, 0);
+      if (n == 2u) {
+        uint64_t* ho = K->halfres + 4 * (long long)row + 2 * (half ^ 1);
+        uint64_t w0 = 0, w1 = 0;
+        Waiter wt(a.ctl, K->timeout_ticks);
+        for (;;) {
+          w0 = tget(ho);
+          w1 = tget(ho + 1);
+          if (tag_ok(w0, tag) && tag_ok(w1, tag)) break;
+          if (!wt.keep_going()) break;
+        }
+        amax_merge(M, I, lo_f(w0), (int)(uint32_t)w1);
+        write = true;
+      }
+    }
+    if (write && lane == 0) {
       const KArgs K = cold_args();
       K->row_loss[row] = 0.0f;
       K->tgt[row] = I;
       if (K->stats) store16(K->stats + 4 * (long long)row, (f32x4){0.0f, 0.0f, 0.0f, 0.0f});
     }
   }
-  if (a.grad) zero_row<VAR>(a, rowv, tid);
+  if (a.grad) zero_slots<VAR>(a, rowv, tid, g0, g1);
 }
 
 // Gradient of one vector (entries at lo.., lo+H..; the label entry Arg gets
@@ -1333,12 +1378,15 @@ __global__ __launch_bounds__(kRowBlock) void fused_kernel(FwdArgs a) {
   }
   __syncthreads();
   const uint32_t tag = sm.tag;
+  // Work items: rows, with the unverified rows of the longest-first order
+  // counted twice (two halves each).
+  const uint32_t nitems = (uint32_t)a.R + (a.lpt ? (uint32_t)(a.R - sm.cum[a.k]) : 0u);
   for (int iter = 0;; ++iter) {
     const int par = iter & 1;
     const uint64_t w = sm.item[par];
     const uint32_t idx = __builtin_amdgcn_readfirstlane((uint32_t)w);
     const uint32_t stat = __builtin_amdgcn_readfirstlane((uint32_t)(w >> 32));
-    if (idx >= (uint32_t)a.R) break;
+    if (idx >= nitems) break;
     if (bad || stat != 0u) {  // failed launch: drain without work
       if (tid == 0) sm.item[par ^ 1] = claim(a);
       __syncthreads();
@@ -1346,7 +1394,7 @@ __global__ __launch_bounds__(kRowBlock) void fused_kernel(FwdArgs a) {
     }
     const Item it = map_item(a, sm, s_off, order, key, (int)idx);
     if (it.verified) verified_row<VAR, FULL>(a, sm, lp, lq, it, par, tag);
-    else unverified_row<VAR>(a, sm, it.row, par);
+    else unverified_row<VAR>(a, sm, it.row, par, it.half, tag);
   }
   // The workgroup that leaves last sums the request losses, reports the
   // status, resets the dispenser and the done count, and advances the epoch.
