@@ -203,15 +203,17 @@ struct Tr<kBf16x8> {  // 8 bfloat16 per 16-byte load
   using S = u32x4;
   __device__ static const void* row(const void* base, long long r) { return (const u32x4*)base + r; }
   __device__ static S load(const void* row, unsigned vi) { return ((const u32x4*)row)[vi]; }
+  template <int AUX = 0>
   __device__ static S bload(Rsrc r, uint32_t voff, uint32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX);
   }
   // Entries 0..3 at byte voff + soff, entries 4..7 hoff bytes further (hoff
   // goes into the per-lane offset: a scalar offset the compiler cannot prove
   // uniform would make it loop over lanes).
+  template <int AUX = 0>
   __device__ static S bload2(Rsrc r, uint32_t voff, uint32_t soff, uint32_t hoff) {
-    const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
-    const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(r, voff + hoff, soff, 0);
+    const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, AUX);
+    const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(r, voff + hoff, soff, AUX);
     return S{a.x, a.y, b.x, b.y};
   }
   __device__ static float at(const S& s, int e) {
@@ -229,8 +231,9 @@ struct Tr<kBf16x1> {  // one bfloat16 per access (rows not 16-byte aligned)
   using S = uint32_t;
   __device__ static const void* row(const void* base, long long r) { return (const uint16_t*)base + r; }
   __device__ static S load(const void* row, unsigned vi) { return ((const uint16_t*)row)[vi]; }
+  template <int AUX = 0>
   __device__ static S bload(Rsrc r, uint32_t voff, uint32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, AUX);
   }
   __device__ static float at(const S& s, int) { return __uint_as_float(s << 16); }
   __device__ static float elem(const void* base, long long j) {
@@ -244,8 +247,9 @@ struct Tr<kF32x4> {  // 4 float32 per 16-byte load
   using S = f32x4;
   __device__ static const void* row(const void* base, long long r) { return (const f32x4*)base + r; }
   __device__ static S load(const void* row, unsigned vi) { return ((const f32x4*)row)[vi]; }
+  template <int AUX = 0>
   __device__ static S bload(Rsrc r, uint32_t voff, uint32_t soff) {
-    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX);
     return __builtin_bit_cast(f32x4, w);
   }
   __device__ static float at(const S& s, int e) { return s[e]; }
@@ -258,8 +262,9 @@ struct Tr<kF32x1> {
   using S = float;
   __device__ static const void* row(const void* base, long long r) { return (const float*)base + r; }
   __device__ static S load(const void* row, unsigned vi) { return ((const float*)row)[vi]; }
+  template <int AUX = 0>
   __device__ static S bload(Rsrc r, uint32_t voff, uint32_t soff) {
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, AUX));
   }
   __device__ static float at(const S& s, int) { return s; }
   __device__ static float elem(const void* base, long long j) { return ((const float*)base)[j]; }
@@ -283,6 +288,21 @@ __device__ __forceinline__ void store_vec(float* g, unsigned vi, const float* v)
 }
 
 // Same through a row's buffer resource: VEC entries at byte offset voff + soff.
+// Cache policy (buffer instruction aux bits) of the logit loads.  Data read
+// once (held on chip, or only scanned for the argmax) and the second read of
+// the streamed part of a verified row are nontemporal; the first read of the
+// streamed part is not, so that its second read can hit in cache.
+#ifndef AV_AUX_RES
+#define AV_AUX_RES 2
+#endif
+#ifndef AV_AUX_STR
+#define AV_AUX_STR 0
+#endif
+#ifndef AV_AUX_RE
+#define AV_AUX_RE 2
+#endif
+constexpr int kAuxOnce = AV_AUX_RES, kAuxFirst = AV_AUX_STR, kAuxAgain = AV_AUX_RE;
+
 // Cache policy of the gradient stores (buffer instruction aux bits).
 #ifndef AV_STORE_AUX
 #define AV_STORE_AUX 2  // nontemporal: the gradient is not read again by this pass
@@ -722,9 +742,11 @@ struct RowIO {
   __device__ __forceinline__ bool has(int nbv) const { return lane < nbv; }
   __device__ __forceinline__ int lo(int s) const { return lo0 + s * SE; }
   __device__ __forceinline__ int H(int nbv) const { return kHalves ? 4 * nbv : 4; }
+  template <int AUX = 0>
   __device__ __forceinline__ S load(Rsrc r, int s, int nbv) const {
-    if constexpr (kHalves) return T::bload2(r, voff, (uint32_t)s * SIN, (uint32_t)(nbv * 4 * T::EB));
-    else return T::bload(r, voff, (uint32_t)s * SIN);
+    if constexpr (kHalves)
+      return T::template bload2<AUX>(r, voff, (uint32_t)s * SIN, (uint32_t)(nbv * 4 * T::EB));
+    else return T::template bload<AUX>(r, voff, (uint32_t)s * SIN);
   }
   // The thread's vector from an LDS slot filled by direct loads (lane l's
   // 16 bytes at 16 l of the wave's part: the block's entries in order).
@@ -824,12 +846,15 @@ __device__ __forceinline__ void unverified_row(const FwdArgs& a, RowSmem& sm, in
   const int full_end = min(s1, nvec / kRowBlock);  // slots in which every thread has a vector
   float m = -INFINITY;
   int bi = INT_MAX;
-#pragma unroll 4
+#ifndef AV_UU
+#define AV_UU 4
+#endif
+#pragma unroll AV_UU
   for (int s = s0; s < full_end; ++s)
-    argmax_vec<VAR>(T::bload(rzp, voff, (uint32_t)s * SIN), s * kRowBlock + tid, m, bi);
+    argmax_vec<VAR>(T::template bload<kAuxOnce>(rzp, voff, (uint32_t)s * SIN), s * kRowBlock + tid, m, bi);
   for (int s = max(full_end, s0); s < s1; ++s)
     if (s * kRowBlock + tid < nvec)
-      argmax_vec<VAR>(T::bload(rzp, voff, (uint32_t)s * SIN), s * kRowBlock + tid, m, bi);
+      argmax_vec<VAR>(T::template bload<kAuxOnce>(rzp, voff, (uint32_t)s * SIN), s * kRowBlock + tid, m, bi);
   wargmax(m, bi);
   if (lane == 0) {
     sm.f[par][wid][0] = m;
@@ -943,7 +968,7 @@ __device__ __forceinline__ void wait_vmem_but() {  // all but the N most recent
 __device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Direct loads of slot s of a row's zp and zq into LDS slot position l.
-template <int VAR>
+template <int VAR, int AUX>
 __device__ __forceinline__ void dma_slot(const RowIO<VAR>& io, Rsrc rzp, Rsrc rzq,
                                          typename Tr<VAR>::S (*lp)[kRowBlock],
                                          typename Tr<VAR>::S (*lq)[kRowBlock], int l, int s, int nvec,
@@ -951,9 +976,9 @@ __device__ __forceinline__ void dma_slot(const RowIO<VAR>& io, Rsrc rzp, Rsrc rz
   if (io.has(io.nb(s, nvec))) {
     const uint32_t so = (uint32_t)s * RowIO<VAR>::SIN;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rzp, (__attribute__((address_space(3))) void*)&lp[l][io.wid * 64], 16, (uint32_t)tid * 16u, so, 0, 0);
+        rzp, (__attribute__((address_space(3))) void*)&lp[l][io.wid * 64], 16, (uint32_t)tid * 16u, so, 0, AUX);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rzq, (__attribute__((address_space(3))) void*)&lq[l][io.wid * 64], 16, (uint32_t)tid * 16u, so, 0, 0);
+        rzq, (__attribute__((address_space(3))) void*)&lq[l][io.wid * 64], 16, (uint32_t)tid * 16u, so, 0, AUX);
   }
 }
 
@@ -997,7 +1022,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
     const IO io(tid);
 #pragma unroll
     for (int l = 0; l < NL; ++l)
-      if (l < nl) dma_slot<VAR>(io, rzp, rzq, lp, lq, l, nr + l, nvec, tid);
+      if (l < nl) dma_slot<VAR, kAuxOnce>(io, rzp, rzq, lp, lq, l, nr + l, nvec, tid);
   }
   // Defined in every lane (zero where unused), so the register copies never
   // carry values from one row to the next.
@@ -1010,8 +1035,8 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
       rq[v] = S{};
       const int nbv = io.nb(v, nvec);
       if (v < nr && io.has(nbv)) {
-        rp[v] = io.load(rzp, v, nbv);
-        rq[v] = io.load(rzq, v, nbv);
+        rp[v] = io.template load<kAuxOnce>(rzp, v, nbv);
+        rq[v] = io.template load<kAuxOnce>(rzq, v, nbv);
       }
     }
   }
@@ -1033,18 +1058,18 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
     };
     if (npair == 0) {
 #pragma unroll
-      for (int l = 0; l < NL; ++l) dma_slot<VAR>(io, rzp, rzq, lp, lq, l, nr + l, nvec, tid);
+      for (int l = 0; l < NL; ++l) dma_slot<VAR, kAuxOnce>(io, rzp, rzq, lp, lq, l, nr + l, nvec, tid);
     } else {
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        if (von + j < ns) dma_slot<VAR>(io, rzp, rzq, lp, lq, j, von + j, nvec, tid);
+        if (von + j < ns) dma_slot<VAR, kAuxFirst>(io, rzp, rzq, lp, lq, j, von + j, nvec, tid);
       if (npair >= 2) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          if (von + 2 + j < ns) dma_slot<VAR>(io, rzp, rzq, lp, lq, 2 + j, von + 2 + j, nvec, tid);
+          if (von + 2 + j < ns) dma_slot<VAR, kAuxFirst>(io, rzp, rzq, lp, lq, 2 + j, von + 2 + j, nvec, tid);
       } else {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) dma_slot<VAR>(io, rzp, rzq, lp, lq, 2 + j, nr + 2 + j, nvec, tid);
+        for (int j = 0; j < 2; ++j) dma_slot<VAR, kAuxOnce>(io, rzp, rzq, lp, lq, 2 + j, nr + 2 + j, nvec, tid);
       }
     }
     for (int q = 0; q < npair; ++q) {
@@ -1068,11 +1093,11 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int sl = von + 2 * (q + 2) + j;
-          if (sl < ns) dma_slot<VAR>(io, rzp, rzq, lp, lq, 2 * h + j, sl, nvec, tid);
+          if (sl < ns) dma_slot<VAR, kAuxFirst>(io, rzp, rzq, lp, lq, 2 * h + j, sl, nvec, tid);
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) dma_slot<VAR>(io, rzp, rzq, lp, lq, 2 * h + j, nr + 2 * h + j, nvec, tid);
+        for (int j = 0; j < 2; ++j) dma_slot<VAR, kAuxOnce>(io, rzp, rzq, lp, lq, 2 * h + j, nr + 2 * h + j, nvec, tid);
       }
     }
   } else {
@@ -1082,13 +1107,13 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
 #endif
 #pragma unroll AV_SU
     for (int s = von; s < nfull; ++s) {
-      const S xp = io.load(rzp, s, 64), xq = io.load(rzq, s, 64);
+      const S xp = io.template load<kAuxFirst>(rzp, s, 64), xq = io.template load<kAuxFirst>(rzq, s, 64);
       acc_vec<VAR>(xp, xq, io.lo(s), io.H(64), A, false);
     }
     if (tail) {
       const int nbv = io.nb(nfull, nvec);
       if (io.has(nbv)) {
-        const S xp = io.load(rzp, nfull, nbv), xq = io.load(rzq, nfull, nbv);
+        const S xp = io.template load<kAuxFirst>(rzp, nfull, nbv), xq = io.template load<kAuxFirst>(rzq, nfull, nbv);
         acc_vec<VAR>(xp, xq, io.lo(nfull), io.H(nbv), A, false);
       }
     }
@@ -1246,7 +1271,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
         wait_lds_reads();
 #pragma unroll
         for (int l = 0; l < NL; ++l)
-          if (s0 + l < ns) dma_slot<VAR>(io, rzp, rzq, lp, lq, l, s0 + l, nvec, tid);
+          if (s0 + l < ns) dma_slot<VAR, kAuxAgain>(io, rzp, rzq, lp, lq, l, s0 + l, nvec, tid);
         if (!regs_done) {  // the register slots' gradient overlaps the first loads
 #pragma unroll
           for (int v = 0; v < NR; ++v) grad_vec<VAR>(rp[v], rq[v], io, v, 64, rk, gk, Arg, rg);
@@ -1278,13 +1303,13 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
 #endif
 #pragma unroll AV_GU
         for (int s = von; s < nfull; ++s) {
-          const S xp = io.load(rzp, s, 64), xq = io.load(rzq, s, 64);
+          const S xp = io.template load<kAuxAgain>(rzp, s, 64), xq = io.template load<kAuxAgain>(rzq, s, 64);
           grad_vec<VAR>(xp, xq, io, s, 64, rk, gk, Arg, rg);
         }
         if (tail) {
           const int nbv = io.nb(nfull, nvec);
           if (io.has(nbv)) {
-            const S xp = io.load(rzp, nfull, nbv), xq = io.load(rzq, nfull, nbv);
+            const S xp = io.template load<kAuxAgain>(rzp, nfull, nbv), xq = io.template load<kAuxAgain>(rzq, nfull, nbv);
             grad_vec<VAR>(xp, xq, io, nfull, nbv, rk, gk, Arg, rg);
           }
         }
