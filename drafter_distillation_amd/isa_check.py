@@ -112,7 +112,8 @@ def compile_asm(src: str, extra=()) -> str:
 
     with tempfile.TemporaryDirectory() as td:
         out = os.path.join(td, "k.s")
-        subprocess.check_call([B._hipcc(), *B.HIPCC_FLAGS, *extra, "--cuda-device-only", "-S", src, "-o", out],
+        flags = [*B.HIPCC_FLAGS, *B.SOURCE_FLAGS.get(os.path.basename(src), []), *extra]
+        subprocess.check_call([B._hipcc(), *flags, "--cuda-device-only", "-S", src, "-o", out],
                               stderr=subprocess.DEVNULL)
         with open(out) as f:
             return f.read()
