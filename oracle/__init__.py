@@ -16,3 +16,9 @@ from .opd import (  # noqa: F401
     verify_opd,
     clip_margin,
 )
+from .head_update import (  # noqa: F401
+    ADAMW_DEFAULTS,
+    adamw_step,
+    head_loss_and_grads,
+    length_head_update,
+)
