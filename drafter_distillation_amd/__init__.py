@@ -18,7 +18,9 @@ from ._lib import (  # noqa: F401
     AV_ROUND_FLOOR,
     AVError,
     LIB_PATH,
+    av_head_update_workspace_bytes,
     av_length_head,
+    av_length_head_update,
     av_status_str,
     av_verify_opd_bwd,
     av_verify_opd_fwd,

@@ -36,9 +36,12 @@ class AVError(RuntimeError):
 _lib = None
 _lib_lock = threading.Lock()
 
-_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_vp, _i, _f, _d, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_double, ctypes.c_size_t
 _SIGS = {
     "av_length_head": (_i, [_vp, _vp, _f, _f, _i, _i, _i, _i, _vp, _vp, _vp]),
+    "av_head_update_workspace_bytes": (_sz, [_i]),
+    "av_length_head_update": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i,
+                                   _d, _d, _d, _d, _d, _vp, _vp, _vp, _vp, _sz, _vp]),
     "av_workspace_bytes": (_sz, [_i, _i, _i]),
     "av_workspace_init": (_i, [_vp, _sz, _vp]),
     "av_verify_opd_fwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _f, _f, _f,
@@ -137,6 +140,46 @@ def av_length_head(h: torch.Tensor, w: torch.Tensor, bias: float, gamma: float, 
                                   int(round_mode), _ptr(rate), _ptr(bk), _stream(dev))
     _check("av_length_head", rc)
     return rate, bk
+
+
+def av_head_update_workspace_bytes(B: int) -> int:
+    return int(lib().av_head_update_workspace_bytes(int(B)))
+
+
+def av_length_head_update(h: torch.Tensor, acc: torch.Tensor, bk: torch.Tensor, k: int, *,
+                          w: torch.Tensor, bias: torch.Tensor, m_w: torch.Tensor, v_w: torch.Tensor,
+                          m_b: torch.Tensor, v_b: torch.Tensor, step: int, lr: float = 2e-4,
+                          beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
+                          weight_decay: float = 0.01, want_rate: bool = True,
+                          want_grad_h: bool = False) -> dict:
+    """Online update of the length head (see include/av.h).  w, bias [1], m_w,
+    v_w, m_b [1], v_b [1] are float32 GPU tensors updated in place.  Returns
+    dict(loss [1], rate [B] or None, grad_h [B, H] or None)."""
+    _need_gpu("h", h, torch.float32)
+    _need_gpu("acc", acc, torch.int32)
+    _need_gpu("bk", bk, torch.int32)
+    for name, t in (("w", w), ("bias", bias), ("m_w", m_w), ("v_w", v_w), ("m_b", m_b), ("v_b", v_b)):
+        _need_gpu(name, t, torch.float32)
+    B, H = h.shape
+    if acc.shape != (B,) or bk.shape != (B,):
+        raise ValueError("acc and bk must have shape [B]")
+    if w.shape != (H,) or m_w.shape != (H,) or v_w.shape != (H,):
+        raise ValueError("w, m_w and v_w must have shape [H]")
+    if bias.numel() != 1 or m_b.numel() != 1 or v_b.numel() != 1:
+        raise ValueError("bias, m_b and v_b must have one element")
+    dev = h.device
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    rate = torch.empty(B, dtype=torch.float32, device=dev) if want_rate else None
+    grad_h = torch.empty((B, H), dtype=torch.float32, device=dev) if want_grad_h else None
+    with torch.cuda.device(dev):
+        ws = workspace(dev, av_head_update_workspace_bytes(B))
+        rc = lib().av_length_head_update(
+            _ptr(h), _ptr(acc), _ptr(bk), B, H, int(k), _ptr(w), _ptr(bias), _ptr(m_w), _ptr(v_w),
+            _ptr(m_b), _ptr(v_b), int(step), float(lr), float(beta1), float(beta2), float(eps),
+            float(weight_decay), _ptr(loss), _ptr(rate), _ptr(grad_h), _ptr(ws), ws.numel(),
+            _stream(dev))
+    _check("av_length_head_update", rc)
+    return dict(loss=loss, rate=rate, grad_h=grad_h)
 
 
 def _dtype_code(zp: torch.Tensor) -> int:

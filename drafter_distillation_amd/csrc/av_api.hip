@@ -146,6 +146,50 @@ int av_length_head(const float* h, const float* w, float bias, float gamma, int 
   return e == hipSuccess ? AV_OK : hip_fail(e);
 }
 
+size_t av_head_update_workspace_bytes(int B) {
+  if (B < 1) return 0;
+  return (size_t)B * 2 * sizeof(double);
+}
+
+int av_length_head_update(const float* h, const int32_t* acc, const int32_t* bk, int B, int H, int k,
+                          float* w, float* bias, float* m_w, float* v_w, float* m_b, float* v_b,
+                          int step, double lr, double beta1, double beta2, double eps,
+                          double weight_decay, float* loss_out, float* rate_out, float* grad_h_out,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!h || !acc || !bk || !w || !bias || !m_w || !v_w || !m_b || !v_b || !workspace) return AV_EINVAL;
+  if (B < 1 || H < 1 || k < 1 || k > AV_MAX_K || step < 1) return AV_EINVAL;
+  if (!(isfinite(lr) && lr >= 0.0) || !(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0))
+    return AV_EINVAL;
+  if (!(isfinite(eps) && eps > 0.0) || !(isfinite(weight_decay) && weight_decay >= 0.0)) return AV_EINVAL;
+  if (workspace_bytes < av_head_update_workspace_bytes(B) || ((uintptr_t)workspace & 7u) != 0) return AV_EINVAL;
+  avk::HeadUpdArgs a;
+  a.h = h;
+  a.acc = acc;
+  a.bk = bk;
+  a.w = w;
+  a.bias = bias;
+  a.m_w = m_w;
+  a.v_w = v_w;
+  a.m_b = m_b;
+  a.v_b = v_b;
+  a.loss = loss_out;
+  a.rate = rate_out;
+  a.grad_h = grad_h_out;
+  a.ws = (double*)workspace;
+  a.B = B;
+  a.H = H;
+  a.k = k;
+  a.lr = lr;
+  a.beta1 = beta1;
+  a.beta2 = beta2;
+  a.eps = eps;
+  a.wd = weight_decay;
+  a.bc1 = 1.0 - pow(beta1, (double)step);
+  a.sqrt_bc2 = sqrt(1.0 - pow(beta2, (double)step));
+  hipError_t e = avk::launch_head_update(a, (hipStream_t)stream);
+  return e == hipSuccess ? AV_OK : hip_fail(e);
+}
+
 int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_off,
                       const void* zp, const void* zq, const int32_t* draft, const int32_t* bk,
                       float lambda, float tau, float grad_scale, int32_t* tgt_argmax,

@@ -106,12 +106,32 @@ struct HeadArgs {
   int B, H, k, mode;
 };
 
+struct HeadUpdArgs {
+  const float* h;
+  const int32_t* acc;
+  const int32_t* bk;
+  float* w;
+  float* bias;
+  float* m_w;
+  float* v_w;
+  float* m_b;
+  float* v_b;
+  float* loss;
+  float* rate;
+  float* grad_h;
+  double* ws;  // [2B]: d loss / d z_b, then the squared errors
+  int B, H, k;
+  double lr, beta1, beta2, eps, wd;
+  double bc1, sqrt_bc2;  // 1 - beta1^t, sqrt(1 - beta2^t)
+};
+
 // full: every on-chip slot of a row is filled (nvec >= (regs + lds) * kRowBlock)
 // and the default on-chip split is used.
 hipError_t launch_fused(Variant v, bool full, const FwdArgs& a, int grid, size_t lds, hipStream_t s);
 hipError_t fused_blocks_per_cu(Variant v, bool full, size_t lds, int* out);
 hipError_t launch_bwd(Variant v, const BwdArgs& a, hipStream_t s);
 hipError_t launch_head(const HeadArgs& a, hipStream_t s);
+hipError_t launch_head_update(const HeadUpdArgs& a, hipStream_t s);
 hipError_t launch_zero(uint64_t* p, size_t words, hipStream_t s);
 
 }  // namespace avk

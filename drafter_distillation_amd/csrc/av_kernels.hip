@@ -1514,29 +1514,104 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(BwdArgs a) {
 // length head and workspace fill
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(kBlock) void head_kernel(HeadArgs a) {
-  __shared__ double s[kWaves];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const float* hb = a.h + (long long)b * a.H;
+// ---------------------------------------------------------------------------
+// length head: prediction, and its online update
+// ---------------------------------------------------------------------------
+
+// sigmoid(w . h_b + bias) in float64 for the workgroup's request: per-thread
+// partial dot products, wave butterflies, then the wave partials in a fixed
+// order (the same bits on every call).  Every thread gets the result.
+__device__ __forceinline__ double head_rate(const float* hb, const float* w, int H, double bias,
+                                            double* s) {
+  const int tid = threadIdx.x;
   double acc = 0.0;
-  for (int j = tid; j < a.H; j += kBlock) acc = fma((double)hb[j], (double)a.w[j], acc);
+  for (int j = tid; j < H; j += kBlock) acc = fma((double)hb[j], (double)w[j], acc);
   acc = wsumd(acc);
   if ((tid & 63) == 0) s[tid >> 6] = acc;
   __syncthreads();
+  const double z = ((s[0] + s[1]) + (s[2] + s[3])) + bias;
+  if (z >= 0.0) return 1.0 / (1.0 + exp(-z));
+  const double e = exp(z);
+  return e / (1.0 + e);
+}
+
+__global__ __launch_bounds__(kBlock) void head_kernel(HeadArgs a) {
+  __shared__ double s[kWaves];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const double sg = head_rate(a.h + (long long)b * a.H, a.w, a.H, (double)a.bias, s);
   if (tid == 0) {
-    const double z = ((s[0] + s[1]) + (s[2] + s[3])) + (double)a.bias;
-    double sg;
-    if (z >= 0.0) {
-      sg = 1.0 / (1.0 + exp(-z));
-    } else {
-      const double e = exp(z);
-      sg = e / (1.0 + e);
-    }
     const double x = (double)a.gamma * sg * (double)a.k;
     const double n = a.mode == 0 ? ceil(x) : floor(x);
     const int bk = n < 1.0 ? 1 : (n > (double)a.k ? a.k : (int)n);
     a.bk[b] = bk;
     if (a.rate) a.rate[b] = (float)sg;
+  }
+}
+
+// Online update, step 1 (one workgroup per request): the prediction, the
+// label acc_b / b_k, and d loss / d z_b = 2 (rate_b - label_b) rate_b (1 - rate_b) / B
+// with loss = mean_b (rate_b - label_b)^2.  ws[b] = d loss / d z_b,
+// ws[B + b] = (rate_b - label_b)^2.
+__global__ __launch_bounds__(kBlock) void head_grad_kernel(HeadUpdArgs a) {
+  __shared__ double s[kWaves];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const double sg = head_rate(a.h + (long long)b * a.H, a.w, a.H, (double)a.bias[0], s);
+  if (tid == 0) {
+    const int n = min(max(a.bk[b], 1), a.k);
+    const double e = sg - (double)a.acc[b] / (double)n;
+    a.ws[b] = 2.0 * e * sg * (1.0 - sg) / (double)a.B;
+    a.ws[a.B + b] = e * e;
+    if (a.rate) a.rate[b] = (float)sg;
+  }
+}
+
+// One AdamW step on one parameter held in float32 (arithmetic in float64):
+// decoupled weight decay, then bias-corrected moments.
+__device__ __forceinline__ void adamw(float* th, float* m, float* v, double g, const HeadUpdArgs& a) {
+  const double mm = a.beta1 * (double)*m + (1.0 - a.beta1) * g;
+  const double vv = a.beta2 * (double)*v + (1.0 - a.beta2) * g * g;
+  double t = (double)*th * (1.0 - a.lr * a.wd);
+  t -= (a.lr / a.bc1) * mm / (sqrt(vv) / a.sqrt_bc2 + a.eps);
+  *th = (float)t;
+  *m = (float)mm;
+  *v = (float)vv;
+}
+
+// Online update, step 2 (one thread per weight): g_w[j] = sum_b dz_b h[b, j]
+// in request order, d loss / d h[b, j] = dz_b w[j] (the weight before the
+// step), then the AdamW step on w[j]; thread 0 of workgroup 0 also sums
+// g_bias and the loss in request order and steps the bias.
+__global__ __launch_bounds__(kBlock) void head_step_kernel(HeadUpdArgs a) {
+  constexpr int kChunk = 1024;
+  __shared__ double sdz[kChunk];
+  const int tid = threadIdx.x;
+  const int j = blockIdx.x * kBlock + tid;
+  const bool in = j < a.H;
+  const double wj = in ? (double)a.w[j] : 0.0;
+  double g = 0.0;
+  for (int b0 = 0; b0 < a.B; b0 += kChunk) {
+    const int nb = min(kChunk, a.B - b0);
+    __syncthreads();
+    for (int i = tid; i < nb; i += kBlock) sdz[i] = a.ws[b0 + i];
+    __syncthreads();
+    if (in) {
+      const float* hj = a.h + (long long)b0 * a.H + j;
+      for (int i = 0; i < nb; ++i) {
+        const double d = sdz[i];
+        g = fma(d, (double)hj[(long long)i * a.H], g);
+        if (a.grad_h) a.grad_h[(long long)(b0 + i) * a.H + j] = (float)(d * wj);
+      }
+    }
+  }
+  if (in) adamw(a.w + j, a.m_w + j, a.v_w + j, g, a);
+  if (blockIdx.x == 0 && tid == 0) {
+    double gb = 0.0, sq = 0.0;
+    for (int b = 0; b < a.B; ++b) {
+      gb += a.ws[b];
+      sq += a.ws[a.B + b];
+    }
+    if (a.loss) a.loss[0] = (float)(sq / (double)a.B);
+    adamw(a.bias, a.m_b, a.v_b, gb, a);
   }
 }
 
@@ -1594,6 +1669,14 @@ hipError_t launch_bwd(Variant v, const BwdArgs& a, hipStream_t s) {
 
 hipError_t launch_head(const HeadArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(head_kernel, dim3(a.B), dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_head_update(const HeadUpdArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(head_grad_kernel, dim3(a.B), dim3(kBlock), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(head_step_kernel, dim3((a.H + kBlock - 1) / kBlock), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 

@@ -82,6 +82,50 @@ int av_length_head(const float* h, const float* w, float bias, float gamma,
                    float* rate_out, int32_t* bk_out, void* stream);
 
 /*
+ * av_length_head_update -- one online update of the length head from the
+ * outcome of a verification step (Pith review page, Referee Report major
+ * comment 1, paper Sec. 3.2 "Online Update of the Length Head": an MSE loss
+ * against the observed acceptance rate; "Axiom & Free-Parameter Ledger":
+ * length head learning rate 2e-4, AdamW).  For each request b:
+ *     rate_b  = sigmoid(w . h_b + bias)              (as av_length_head)
+ *     label_b = acc_b / clamp(bk_b, 1, k)            (accepted fraction of
+ *                                                     the verified block)
+ *     loss    = (1/B) sum_b (rate_b - label_b)^2
+ * then the gradients of loss with respect to w, bias and h, and one AdamW
+ * step on w and bias with step number t = `step`:
+ *     theta <- theta (1 - lr wd);  m <- beta1 m + (1 - beta1) g;
+ *     v <- beta2 v + (1 - beta2) g^2;
+ *     theta <- theta - lr / (1 - beta1^t) * m / (sqrt(v) / sqrt(1 - beta2^t) + eps)
+ * Sums run in float64 in request order; parameters and moments stay float32.
+ *
+ *   h            [B, H] float32 pooled drafter state (the same input as
+ *                av_length_head)
+ *   acc, bk      [B] int32: accepted lengths (av_verify_opd_fwd's acc_len)
+ *                and the verification lengths that step used
+ *   w [H], bias [1], m_w [H], v_w [H], m_b [1], v_b [1]
+ *                float32, updated in place (moments zero for a fresh head)
+ *   step         number of this update, >= 1 (the caller counts updates)
+ *   lr, beta1, beta2, eps, weight_decay
+ *                AdamW constants (the pages print lr; the common defaults
+ *                are 0.9, 0.999, 1e-8, 0.01)
+ *   loss_out [1], rate_out [B], grad_h_out [B, H]: float32 outputs or NULL;
+ *                grad_h_out uses w before the step
+ *   workspace    >= av_head_update_workspace_bytes(B) bytes, 8-byte aligned,
+ *                no initialisation needed
+ * All pointers are device pointers; the call is asynchronous on `stream` (two
+ * launches).  Errors (AV_EINVAL): NULL required pointer, B < 1, H < 1, k < 1
+ * or > AV_MAX_K, step < 1, lr or weight_decay negative or non-finite, beta1 or
+ * beta2 outside [0, 1), eps not positive and finite, workspace too small or
+ * misaligned.
+ */
+size_t av_head_update_workspace_bytes(int B);
+int av_length_head_update(const float* h, const int32_t* acc, const int32_t* bk, int B, int H, int k,
+                          float* w, float* bias, float* m_w, float* v_w, float* m_b, float* v_b,
+                          int step, double lr, double beta1, double beta2, double eps,
+                          double weight_decay, float* loss_out, float* rate_out, float* grad_h_out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * av_workspace_bytes -- size of the scratch area av_verify_opd_fwd needs for
  * B requests and R stored rows (R = B*k dense).  Independent of V and dtype.
  * Returns 0 for invalid sizes.

@@ -144,6 +144,46 @@ def test_bwd_rejects_bad_arguments_on_host(kw, code):
     assert rc == code
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(h=NULL), dd.AV_EINVAL),
+    (dict(acc=NULL), dd.AV_EINVAL),
+    (dict(bk=NULL), dd.AV_EINVAL),
+    (dict(w=NULL), dd.AV_EINVAL),
+    (dict(bias=NULL), dd.AV_EINVAL),
+    (dict(m_w=NULL), dd.AV_EINVAL),
+    (dict(v_b=NULL), dd.AV_EINVAL),
+    (dict(ws=NULL), dd.AV_EINVAL),
+    (dict(B=0), dd.AV_EINVAL),
+    (dict(H=0), dd.AV_EINVAL),
+    (dict(k=0), dd.AV_EINVAL),
+    (dict(k=65), dd.AV_EINVAL),
+    (dict(step=0), dd.AV_EINVAL),
+    (dict(lr=-1e-4), dd.AV_EINVAL),
+    (dict(lr=float("nan")), dd.AV_EINVAL),
+    (dict(beta1=1.0), dd.AV_EINVAL),
+    (dict(beta2=-0.1), dd.AV_EINVAL),
+    (dict(eps=0.0), dd.AV_EINVAL),
+    (dict(wd=float("inf")), dd.AV_EINVAL),
+    (dict(ws_bytes=8), dd.AV_EINVAL),                      # needs 16 bytes per request
+    (dict(ws=ctypes.c_void_p(0x10004)), dd.AV_EINVAL),     # not 8-byte aligned
+])
+def test_head_update_rejects_bad_arguments_on_host(kw, code):
+    a = dict(h=P, acc=P, bk=P, B=4, H=16, k=16, w=P, bias=P, m_w=P, v_w=P, m_b=P, v_b=P, step=1,
+             lr=2e-4, beta1=0.9, beta2=0.999, eps=1e-8, wd=0.01, loss=NULL, rate=NULL, gh=NULL,
+             ws=P, ws_bytes=1 << 20, stream=NULL)
+    a.update(kw)
+    rc = _lib.lib().av_length_head_update(
+        a["h"], a["acc"], a["bk"], a["B"], a["H"], a["k"], a["w"], a["bias"], a["m_w"], a["v_w"],
+        a["m_b"], a["v_b"], a["step"], a["lr"], a["beta1"], a["beta2"], a["eps"], a["wd"], a["loss"],
+        a["rate"], a["gh"], a["ws"], a["ws_bytes"], a["stream"])
+    assert rc == code
+
+
+def test_head_update_workspace_bytes():
+    assert dd.av_head_update_workspace_bytes(128) == 128 * 16
+    assert dd.av_head_update_workspace_bytes(0) == 0
+
+
 def test_workspace_init_rejects_bad_arguments():
     lib = _lib.lib()
     assert lib.av_workspace_init(NULL, 1 << 20, NULL) == dd.AV_EINVAL
