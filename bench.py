@@ -11,6 +11,11 @@ Inputs are generated on the host (seeded), copied to HBM before timing, and
 stay resident.  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+`--workload head_update` measures instead the online update of the length
+head (av_length_head_update) on the same workload's head: B=128 pooled
+states of H=4096, labels from one verification pass, gradients with respect
+to w, bias and h, one AdamW step per call.
 """
 
 from __future__ import annotations
@@ -158,6 +163,136 @@ def cpu_baseline(n_requests: int):
     }
 
 
+def head_update_bytes(B, H):
+    """Bytes the head update must move at least once: h, acc and b_k read;
+    w and its two moments read and written; the bias and its moments; the
+    gradient with respect to h, the rates and the loss written."""
+    return 4 * B * H + 8 * B + 3 * 2 * 4 * H + 3 * 2 * 4 + 4 * B * H + 4 * B + 4
+
+
+def cpu_baseline_head_update(h, w, bias, acc, bk, k, reps: int):
+    """The float64 oracle's update, single-threaded, `reps` consecutive steps."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        state, ww, bb = None, w, bias
+        for _ in range(reps):
+            r = oracle.length_head_update(h, ww, bb, acc, bk, k, state)
+            ww, bb, state = r["w"], r["bias"], r["state"]
+        dt = (time.perf_counter() - t0) / reps
+    return {
+        "value": round(dt * 1e6, 1),
+        "unit": "us per update",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{reps} consecutive updates of the same head (B={h.shape[0]}, H={h.shape[1]}), "
+                  f"float64 numpy, one thread",
+        "seconds": round(dt * reps, 3),
+    }
+
+
+def bench_head_update(args):
+    import numpy as np
+    import torch
+
+    import drafter_distillation_amd as dd
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dd.lib()
+    w = synth.make("concurrent", seed=args.seed)
+    B, k, V, H = w.B, w.k, w.V, w.H
+    h = torch.from_numpy(w.h).to(dev)
+    wt = torch.from_numpy(w.w).to(dev)
+    bk = torch.empty(B, dtype=torch.int32, device=dev)
+    dd.av_length_head(h, wt, w.bias, w.gamma, k, bk_out=bk)
+    # labels from one verification pass over the same workload
+    zp = torch.from_numpy(w.zp.view(np.int16)).view(torch.bfloat16).to(dev)
+    zq = torch.from_numpy(w.zq.view(np.int16)).view(torch.bfloat16).to(dev)
+    out = dd.av_verify_opd_fwd(zp, zq, torch.from_numpy(w.draft).to(dev), k=k, bk=bk, lam=w.lam,
+                               tau=w.tau, want_grad=False)
+    acc = out["acc_len"]
+    torch.cuda.synchronize()
+    del zp, zq, out
+    state = dict(w=wt.clone(), bias=torch.tensor([w.bias], dtype=torch.float32, device=dev),
+                 m_w=torch.zeros(H, dtype=torch.float32, device=dev),
+                 v_w=torch.zeros(H, dtype=torch.float32, device=dev),
+                 m_b=torch.zeros(1, dtype=torch.float32, device=dev),
+                 v_b=torch.zeros(1, dtype=torch.float32, device=dev))
+    # The host takes longer to issue an update than the GPU takes to run it,
+    # so the timed region replays a captured graph of `steps` consecutive
+    # updates (their step numbers are fixed at capture; the work is the same).
+    cap = torch.cuda.Stream(dev)
+    cap.wait_stream(torch.cuda.current_stream(dev))
+    n = 0
+
+    def update():
+        nonlocal n
+        n += 1
+        dd.av_length_head_update(h, acc, bk, k, step=n, want_grad_h=True, **state)
+
+    with torch.cuda.stream(cap):
+        for _ in range(args.warmup):
+            update()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        for _ in range(args.steps):
+            update()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(cap):
+        graph.replay()  # warm replay
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(cap)
+        graph.replay()
+        e1.record(cap)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    nbytes = head_update_bytes(B, H)
+    achieved = nbytes / (kern_us * 1e-6) / 1e9
+    line = {
+        "metric": "length-head online update (MSE vs acc/b_k, grads w.r.t. w, bias, h, AdamW step) "
+                  "us per update at B=128, H=4096",
+        "value": round(kern_us, 2),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {
+            "workload": "head update: the concurrent workload's length head (B=128, H=4096, k=16), "
+                        "labels from one verification pass, float32 parameters and moments",
+            "B": B, "H": H, "k": k, "seed": args.seed, "bytes_per_update": nbytes,
+            "launches_per_update": 2, "timing": "HIP events around one replay of a captured "
+                                                 "graph of `steps` consecutive updates",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_head_update(
+            w.h.astype(np.float64), w.w.astype(np.float64), float(w.bias),
+            acc.cpu().numpy(), bk.cpu().numpy(), k, reps=20)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,6 +301,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=128)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--workload", choices=["concurrent", "head_update"], default="concurrent",
+                    help="concurrent: the fused verify+OPD step (default); head_update: the "
+                         "length head's online update")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run a plain copy of this many MiB before warmup (counter calibration)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -186,6 +324,10 @@ def main():
               "(the multi-GPU split over requests is described in DESIGN.md); use --gpus 1",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "head_update":
+        bench_head_update(args)
+        return
 
     import numpy as np
     import torch

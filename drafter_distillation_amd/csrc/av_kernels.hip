@@ -1577,41 +1577,58 @@ __device__ __forceinline__ void adamw(float* th, float* m, float* v, double g, c
   *v = (float)vv;
 }
 
-// Online update, step 2 (one thread per weight): g_w[j] = sum_b dz_b h[b, j]
-// in request order, d loss / d h[b, j] = dz_b w[j] (the weight before the
-// step), then the AdamW step on w[j]; thread 0 of workgroup 0 also sums
-// g_bias and the loss in request order and steps the bias.
-__global__ __launch_bounds__(kBlock) void head_step_kernel(HeadUpdArgs a) {
-  constexpr int kChunk = 1024;
-  __shared__ double sdz[kChunk];
-  const int tid = threadIdx.x;
-  const int j = blockIdx.x * kBlock + tid;
+// Online update, step 2: workgroup g owns weights 64 g .. 64 g + 63 (lane =
+// weight) and its 8 waves split the requests (wave w takes b = w, w + 8, ...).
+// g_w[j] = sum_b dz_b h[b, j]: each wave sums its requests in order, then the
+// 8 wave sums are added in wave order; d loss / d h[b, j] = dz_b w[j] (the
+// weight before the step); then wave 0 takes the AdamW step on its weights.
+// Wave 0 of workgroup 0 also sums g_bias and the loss (per lane in request
+// order, then lanes by a fixed butterfly) and steps the bias.
+constexpr int kStepWaves = 8, kStepCols = 64, kStepChunk = 1024;
+__global__ __launch_bounds__(kStepWaves * 64) void head_step_kernel(HeadUpdArgs a) {
+  __shared__ double part[kStepWaves][kStepCols];
+  __shared__ double sdz[kStepChunk];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int j = blockIdx.x * kStepCols + lane;
   const bool in = j < a.H;
   const double wj = in ? (double)a.w[j] : 0.0;
   double g = 0.0;
-  for (int b0 = 0; b0 < a.B; b0 += kChunk) {
-    const int nb = min(kChunk, a.B - b0);
+  for (int b0 = 0; b0 < a.B; b0 += kStepChunk) {
+    const int nb = min(kStepChunk, a.B - b0);
     __syncthreads();
-    for (int i = tid; i < nb; i += kBlock) sdz[i] = a.ws[b0 + i];
+    for (int i = tid; i < nb; i += kStepWaves * 64) sdz[i] = a.ws[b0 + i];
     __syncthreads();
     if (in) {
       const float* hj = a.h + (long long)b0 * a.H + j;
-      for (int i = 0; i < nb; ++i) {
+      float* gh = a.grad_h ? a.grad_h + (long long)b0 * a.H + j : nullptr;
+#pragma unroll 4
+      for (int i = wid; i < nb; i += kStepWaves) {
         const double d = sdz[i];
         g = fma(d, (double)hj[(long long)i * a.H], g);
-        if (a.grad_h) a.grad_h[(long long)(b0 + i) * a.H + j] = (float)(d * wj);
+        if (gh) gh[(long long)i * a.H] = (float)(d * wj);
       }
     }
   }
-  if (in) adamw(a.w + j, a.m_w + j, a.v_w + j, g, a);
-  if (blockIdx.x == 0 && tid == 0) {
-    double gb = 0.0, sq = 0.0;
-    for (int b = 0; b < a.B; ++b) {
-      gb += a.ws[b];
-      sq += a.ws[a.B + b];
+  part[wid][lane] = g;
+  __syncthreads();
+  if (wid == 0) {
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < kStepWaves; ++w) t += part[w][lane];
+    if (in) adamw(a.w + j, a.m_w + j, a.v_w + j, t, a);
+    if (blockIdx.x == 0) {
+      double gb = 0.0, sq = 0.0;
+      for (int b = lane; b < a.B; b += 64) {
+        gb += a.ws[b];
+        sq += a.ws[a.B + b];
+      }
+      gb = wsumd(gb);
+      sq = wsumd(sq);
+      if (lane == 0) {
+        if (a.loss) a.loss[0] = (float)(sq / (double)a.B);
+        adamw(a.bias, a.m_b, a.v_b, gb, a);
+      }
     }
-    if (a.loss) a.loss[0] = (float)(sq / (double)a.B);
-    adamw(a.bias, a.m_b, a.v_b, gb, a);
   }
 }
 
@@ -1676,7 +1693,8 @@ hipError_t launch_head_update(const HeadUpdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(head_grad_kernel, dim3(a.B), dim3(kBlock), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(head_step_kernel, dim3((a.H + kBlock - 1) / kBlock), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL(head_step_kernel, dim3((a.H + kStepCols - 1) / kStepCols), dim3(kStepWaves * 64), 0, s,
+                     a);
   return hipGetLastError();
 }
 

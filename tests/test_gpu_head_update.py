@@ -127,3 +127,37 @@ def test_exact_prediction_only_decays(av):
     assert np.array_equal(g["w"].cpu().numpy(), ref)
     assert float(g["bias"].item()) == 0.0
     assert not g["m_w"].any().item() and not g["v_w"].any().item()
+
+
+def test_graph_replay_matches_eager(av):
+    """A captured update, replayed from the same starting state several times
+    (with eager work between replays), gives the eager update's bits."""
+    rng = np.random.default_rng(11)
+    B, H, k = 16, 200, 16
+    h = torch.tensor(rng.normal(0, 1, (B, H)).astype(np.float32), device="cuda")
+    acc = torch.tensor(rng.integers(0, 9, B), dtype=torch.int32, device="cuda")
+    bk = torch.full((B,), 8, dtype=torch.int32, device="cuda")
+    init = _gpu_state(rng.normal(0, 0.1, H), 0.2,
+                      dict(m_w=rng.normal(0, 1e-3, H), v_w=rng.uniform(0, 1e-6, H), m_b=1e-3, v_b=1e-7))
+    st = {n: t.clone() for n, t in init.items()}
+    ref = av.av_length_head_update(h, acc, bk, k, step=3, want_grad_h=True, **st)
+    torch.cuda.synchronize()
+    ref_state = {n: t.clone() for n, t in st.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # allocates this stream's workspace before capture
+        av.av_length_head_update(h, acc, bk, k, step=3, **{n: t.clone() for n, t in init.items()})
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        out = av.av_length_head_update(h, acc, bk, k, step=3, want_grad_h=True, **st)
+    for _ in range(3):
+        for n, t in st.items():
+            t.copy_(init[n])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n in st:
+            assert torch.equal(st[n], ref_state[n]), n
+        for key in ("loss", "rate", "grad_h"):
+            assert torch.equal(out[key], ref[key]), key
