@@ -22,3 +22,10 @@ from .head_update import (  # noqa: F401
     head_loss_and_grads,
     length_head_update,
 )
+from .spec_sample import (  # noqa: F401
+    accept_test,
+    philox4x32_10,
+    race_uniforms,
+    residual_keys,
+    spec_verify,
+)
