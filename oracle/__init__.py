@@ -24,7 +24,9 @@ from .head_update import (  # noqa: F401
 )
 from .spec_sample import (  # noqa: F401
     accept_test,
+    exponential_from_word,
     philox4x32_10,
+    race_exponentials,
     race_uniforms,
     residual_keys,
     spec_verify,

@@ -78,14 +78,34 @@ def philox4x32_10(c0, c1, c2, c3, k0: int, k1: int):
     return c0, c1, c2, c3
 
 
-def race_uniforms(row: int, V: int, seed: int) -> np.ndarray:
-    """The uniforms u_j, j < V, of the residual draw at stored row `row`."""
+def race_words(row: int, V: int, seed: int) -> np.ndarray:
+    """The generator words behind the residual draw at stored row `row`."""
     j = np.arange(V, dtype=np.uint64)
     words = philox4x32_10(j >> np.uint64(2), np.full(V, row, dtype=np.uint64), np.zeros(V), np.zeros(V),
                           seed & MASK32, (seed >> 32) & MASK32)
     sel = (j & np.uint64(3)).astype(np.int64)
-    w = np.choose(sel, words)
-    return (w.astype(np.float64) + 0.5) / 4294967296.0
+    return np.choose(sel, words).astype(np.int64)
+
+
+def race_uniforms(row: int, V: int, seed: int) -> np.ndarray:
+    """The uniforms u_j = (word_j + 1/2) / 2^32, j < V, of the residual draw."""
+    return (race_words(row, V, seed).astype(np.float64) + 0.5) / 4294967296.0
+
+
+def exponential_from_word(w: np.ndarray) -> np.ndarray:
+    """E = -ln(u) for u = (w + 1/2) / 2^32.  For u >= 1/2 it is formed as
+    -log1p(-(1 - u)) from 1 - u = (2^32 - 1 - w + 1/2) / 2^32, which keeps
+    full relative precision where u is close to 1 (the same value, computed
+    stably)."""
+    w = np.asarray(w, dtype=np.int64)
+    u = (w.astype(np.float64) + 0.5) / 4294967296.0
+    v = ((4294967295 - w).astype(np.float64) + 0.5) / 4294967296.0
+    return np.where(u < 0.5, -np.log(u), -np.log1p(-v))
+
+
+def race_exponentials(row: int, V: int, seed: int) -> np.ndarray:
+    """E_j = -ln(u_j), j < V, of the residual draw at stored row `row`."""
+    return exponential_from_word(race_words(row, V, seed))
 
 
 def residual_keys(zp_row: np.ndarray, zq_row: np.ndarray, row: int, seed: int):
@@ -97,7 +117,7 @@ def residual_keys(zp_row: np.ndarray, zq_row: np.ndarray, row: int, seed: int):
     r = np.maximum(0.0, p - q)
     if not np.any(r > 0.0):   # p = q: nothing to correct, draw from p
         r = p
-    e = -np.log(race_uniforms(row, len(zp), seed))
+    e = race_exponentials(row, len(zp), seed)
     return r, r / e, p, q
 
 

@@ -38,6 +38,21 @@ def _logits(p):
     return np.log(np.asarray(p, dtype=np.float64))
 
 
+def test_exponentials_match_the_series_at_the_extremes():
+    # -ln(u) = sum_n (1-u)^n / n, summed exactly in rationals, for words whose
+    # u lies within 2^-32 of 1, around 1/2, and at the bottom of the range
+    import fractions
+    words = [2 ** 32 - 1, 2 ** 32 - 2, 2 ** 32 - 1000, 2 ** 31, 2 ** 31 - 1, 3 * 2 ** 30, 12345, 0]
+    got = oracle.exponential_from_word(np.array(words))
+    for w, e in zip(words, got):
+        u = fractions.Fraction(2 * w + 1, 2 ** 33)
+        if 1 - u <= fractions.Fraction(1, 2):
+            ref = float(sum((1 - u) ** n / n for n in range(1, 80)))
+        else:
+            ref = -math.log(float(u))   # u <= 1/2: the library log is exact to an ulp here
+        assert math.isclose(e, ref, rel_tol=1e-14), (w, e, ref)
+
+
 def test_exponential_race_draws_the_residual_distribution():
     # p - q has residual mass on entries 0, 2, 3 (normalised: 0.2, 0.5, 0.3)
     p = np.array([0.3, 0.1, 0.5, 0.1])
@@ -122,6 +137,7 @@ def test_race_keys_follow_their_definition_on_a_tiny_row():
     for j in range(5):
         words = oracle.philox4x32_10([j // 4], [row], [0], [0], seed & 0xFFFFFFFF, seed >> 32)
         u = (int(words[j % 4][0]) + 0.5) / 2 ** 32
+        assert math.isclose(oracle.race_exponentials(row, 5, seed)[j], -math.log(u), rel_tol=1e-9)
         pj = math.exp(zp[j]) / sum(math.exp(x) for x in zp)
         qj = math.exp(zq[j]) / sum(math.exp(x) for x in zq)
         assert math.isclose(key[j], max(0.0, pj - qj) / -math.log(u), rel_tol=1e-12, abs_tol=0)
