@@ -21,6 +21,8 @@ from ._lib import (  # noqa: F401
     av_head_update_workspace_bytes,
     av_length_head,
     av_length_head_update,
+    av_spec_verify,
+    av_spec_workspace_bytes,
     av_status_str,
     av_verify_opd_bwd,
     av_verify_opd_fwd,

@@ -48,6 +48,9 @@ _SIGS = {
                                _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i, _vp]),
     "av_verify_opd_bwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _f, _f, _f,
                                _vp, _i, _vp]),
+    "av_spec_workspace_bytes": (_sz, [_i]),
+    "av_spec_verify": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_uint64, _vp, _vp,
+                            _vp, _vp, _vp, _sz, _vp]),
     "av_status_str": (ctypes.c_char_p, [_i]),
     "av_last_hip_error": (ctypes.c_char_p, []),
 }
@@ -98,7 +101,9 @@ def _need_gpu(name: str, t: torch.Tensor, dtype=None) -> None:
 
 
 # ---------------------------------------------------------------------------
-# workspace cache: one zero-initialised scratch buffer per (device, stream)
+# workspace cache: one scratch buffer per (entry point, device, stream).  The
+# fused pass's buffer holds state that persists between its calls (a launch
+# epoch and counters), so no other entry point may write into it.
 # ---------------------------------------------------------------------------
 
 _ws: dict = {}
@@ -108,13 +113,16 @@ def av_workspace_bytes(B: int, k: int, R: int) -> int:
     return int(lib().av_workspace_bytes(int(B), int(k), int(R)))
 
 
-def workspace(dev: torch.device, nbytes: int) -> torch.Tensor:
-    """A workspace of at least nbytes for calls on the current stream of dev."""
-    key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
+def workspace(dev: torch.device, nbytes: int, kind: str = "fwd") -> torch.Tensor:
+    """A workspace of at least nbytes for `kind` calls on the current stream of
+    dev ("fwd": zero-initialised once by av_workspace_init, as the fused pass
+    requires)."""
+    key = (kind, dev.index, torch.cuda.current_stream(dev).cuda_stream)
     buf = _ws.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
-        _check("av_workspace_init", lib().av_workspace_init(_ptr(buf), buf.numel(), _stream(dev)))
+        buf = torch.empty(max(nbytes, 1 << 16), dtype=torch.uint8, device=dev)
+        if kind == "fwd":
+            _check("av_workspace_init", lib().av_workspace_init(_ptr(buf), buf.numel(), _stream(dev)))
         _ws[key] = buf
     return buf
 
@@ -172,7 +180,7 @@ def av_length_head_update(h: torch.Tensor, acc: torch.Tensor, bk: torch.Tensor, 
     rate = torch.empty(B, dtype=torch.float32, device=dev) if want_rate else None
     grad_h = torch.empty((B, H), dtype=torch.float32, device=dev) if want_grad_h else None
     with torch.cuda.device(dev):
-        ws = workspace(dev, av_head_update_workspace_bytes(B))
+        ws = workspace(dev, av_head_update_workspace_bytes(B), kind="head_update")
         rc = lib().av_length_head_update(
             _ptr(h), _ptr(acc), _ptr(bk), B, H, int(k), _ptr(w), _ptr(bias), _ptr(m_w), _ptr(v_w),
             _ptr(m_b), _ptr(v_b), int(step), float(lr), float(beta1), float(beta2), float(eps),
@@ -180,6 +188,56 @@ def av_length_head_update(h: torch.Tensor, acc: torch.Tensor, bk: torch.Tensor, 
             _stream(dev))
     _check("av_length_head_update", rc)
     return dict(loss=loss, rate=rate, grad_h=grad_h)
+
+
+def av_spec_workspace_bytes(R: int) -> int:
+    return int(lib().av_spec_workspace_bytes(int(R)))
+
+
+def av_spec_verify(zp: torch.Tensor, zq: torch.Tensor, draft: torch.Tensor, u: torch.Tensor, *, k: int,
+                   seed: int, bk: Optional[torch.Tensor] = None, row_off: Optional[torch.Tensor] = None,
+                   want_stats: bool = False, out: Optional[dict] = None) -> dict:
+    """Sampling-based block verification (see include/av.h).  zp, zq [R, V]
+    bf16/f32; draft [R] int32; u [R] float32 uniforms; dense layout with bk
+    [B] or ragged with row_off [B+1].  Returns dict(acc_len [B], token [B],
+    row_stats [R, 2] or None, status [1])."""
+    _need_gpu("zp", zp)
+    _need_gpu("zq", zq, zp.dtype)
+    _need_gpu("draft", draft, torch.int32)
+    _need_gpu("u", u, torch.float32)
+    if zp.dim() != 2 or zq.shape != zp.shape or draft.shape != (zp.shape[0],) or u.shape != draft.shape:
+        raise ValueError("zp, zq must be [R, V], draft and u [R]")
+    R, V = zp.shape
+    dev = zp.device
+    if row_off is not None:
+        _need_gpu("row_off", row_off, torch.int32)
+        B = row_off.numel() - 1
+    else:
+        if bk is None:
+            raise ValueError("dense layout needs bk")
+        _need_gpu("bk", bk, torch.int32)
+        B = bk.numel()
+    o = dict(out or {})
+
+    def get(name, shape, dtype):
+        t = o.get(name)
+        if t is None:
+            t = torch.empty(shape, dtype=dtype, device=dev)
+            o[name] = t
+        return t
+
+    acc = get("acc_len", (B,), torch.int32)
+    token = get("token", (B,), torch.int32)
+    stats = get("row_stats", (R, 2), torch.float32) if want_stats else None
+    status = get("status", (1,), torch.int32)
+    with torch.cuda.device(dev):
+        ws = workspace(dev, av_spec_workspace_bytes(R), kind="spec")
+        rc = lib().av_spec_verify(
+            _dtype_code(zp), B, int(k), V, R, _ptr(row_off), _ptr(zp), _ptr(zq), _ptr(draft), _ptr(bk),
+            _ptr(u), ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF), _ptr(acc), _ptr(token), _ptr(stats),
+            _ptr(status), _ptr(ws), ws.numel(), _stream(dev))
+    _check("av_spec_verify", rc)
+    return o
 
 
 def _dtype_code(zp: torch.Tensor) -> int:

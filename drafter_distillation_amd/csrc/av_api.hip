@@ -190,6 +190,44 @@ int av_length_head_update(const float* h, const int32_t* acc, const int32_t* bk,
   return e == hipSuccess ? AV_OK : hip_fail(e);
 }
 
+size_t av_spec_workspace_bytes(int R) {
+  if (R < 1) return 0;
+  return (size_t)R * 16;
+}
+
+int av_spec_verify(int dtype, int B, int k, int V, int R, const int32_t* row_off, const void* zp,
+                   const void* zq, const int32_t* draft, const int32_t* bk, const float* u,
+                   uint64_t seed, int32_t* acc_len, int32_t* token, float* row_stats, int32_t* status,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (!zp || !zq || !draft || !u || !acc_len || !token || !workspace) return AV_EINVAL;
+  if (!row_off && !bk) return AV_EINVAL;
+  Plan p;
+  int rc = plan_rows(dtype, B, k, V, R, row_off, zp, zq, nullptr, &p);
+  if (rc != AV_OK) return rc;
+  if (workspace_bytes < av_spec_workspace_bytes(R) || !aligned16(workspace)) return AV_EINVAL;
+  avk::SpecArgs a;
+  a.zp = zp;
+  a.zq = zq;
+  a.draft = draft;
+  a.bk = bk;
+  a.row_off = row_off;
+  a.u = u;
+  a.acc = acc_len;
+  a.token = token;
+  a.stats = row_stats;
+  a.status = status;
+  a.ws = (uint32_t*)workspace;
+  a.seed = seed;
+  a.B = B;
+  a.k = k;
+  a.V = V;
+  a.R = R;
+  a.nvec = p.nvec;
+  a.ragged = p.ragged ? 1 : 0;
+  hipError_t e = avk::launch_spec(p.var, a, (hipStream_t)stream);
+  return e == hipSuccess ? AV_OK : hip_fail(e);
+}
+
 int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_off,
                       const void* zp, const void* zq, const int32_t* draft, const int32_t* bk,
                       float lambda, float tau, float grad_scale, int32_t* tgt_argmax,

@@ -125,6 +125,22 @@ struct HeadUpdArgs {
   double bc1, sqrt_bc2;  // 1 - beta1^t, sqrt(1 - beta2^t)
 };
 
+struct SpecArgs {
+  const void* zp;
+  const void* zq;
+  const int32_t* draft;
+  const int32_t* bk;
+  const int32_t* row_off;
+  const float* u;
+  int32_t* acc;
+  int32_t* token;
+  float* stats;     // [R, 2] lse_p, lse_q of verified rows, or NULL
+  int32_t* status;  // [1] or NULL
+  uint32_t* ws;     // [R][4]: accepted flag, lse_p bits, lse_q bits
+  uint64_t seed;
+  int B, k, V, R, nvec, ragged;
+};
+
 // full: every on-chip slot of a row is filled (nvec >= (regs + lds) * kRowBlock)
 // and the default on-chip split is used.
 hipError_t launch_fused(Variant v, bool full, const FwdArgs& a, int grid, size_t lds, hipStream_t s);
@@ -132,6 +148,7 @@ hipError_t fused_blocks_per_cu(Variant v, bool full, size_t lds, int* out);
 hipError_t launch_bwd(Variant v, const BwdArgs& a, hipStream_t s);
 hipError_t launch_head(const HeadArgs& a, hipStream_t s);
 hipError_t launch_head_update(const HeadUpdArgs& a, hipStream_t s);
+hipError_t launch_spec(Variant v, const SpecArgs& a, hipStream_t s);
 hipError_t launch_zero(uint64_t* p, size_t words, hipStream_t s);
 
 }  // namespace avk

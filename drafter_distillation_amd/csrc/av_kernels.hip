@@ -1632,6 +1632,272 @@ __global__ __launch_bounds__(kStepWaves * 64) void head_step_kernel(HeadUpdArgs 
   }
 }
 
+// ---------------------------------------------------------------------------
+// sampling-based verification
+//
+// Position i of a block is accepted with probability min(1, p_i(d_i) /
+// q_i(d_i)) up to the first rejection; the token that replaces the first
+// rejected draft is drawn from max(0, p - q) by an exponential race:
+// argmax_j r_j / E_j with E_j = -ln u_j, u_j from Philox4x32-10 keyed by the
+// caller's seed at counter (j / 4, row, 0, 0), word j % 4.
+// ---------------------------------------------------------------------------
+
+// Philox4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw, SC 2011): each round
+// multiplies words 0 and 2 by the round constants and mixes the high and low
+// halves of the products with words 1 and 3 and the key, which is bumped by
+// the Weyl constants between rounds.
+__device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3,
+                                              uint32_t k0, uint32_t k1) {
+  constexpr uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u, W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+#pragma unroll
+  for (int rnd = 0; rnd < 10; ++rnd) {
+    if (rnd > 0) {
+      k0 += W0;
+      k1 += W1;
+    }
+    const uint32_t lo0 = M0 * c0, hi0 = __umulhi(M0, c0);
+    const uint32_t lo1 = M1 * c2, hi1 = __umulhi(M1, c2);
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+}
+
+// E = -ln(u), u = (w + 1/2) / 2^32; from 1 - u through log1p where u >= 1/2,
+// where u itself would round to 1 in float32.
+__device__ __forceinline__ float race_exponential(uint32_t w) {
+  constexpr float k2m32 = 0x1p-32f;
+  if (w < 0x80000000u) return -logf(((float)w + 0.5f) * k2m32);
+  return -log1pf(-(((float)(0xFFFFFFFFu - w) + 0.5f) * k2m32));
+}
+
+// Per-thread online (max, sum exp) of zp and zq over a row.
+struct SpecAcc {
+  float mp, sp, mq, sq;
+};
+
+template <int VAR>
+__device__ __forceinline__ void spec_fold(const typename Tr<VAR>::S& xp, const typename Tr<VAR>::S& xq,
+                                          SpecAcc& A) {
+  using T = Tr<VAR>;
+  float vp = T::at(xp, 0), vq = T::at(xq, 0);
+#pragma unroll
+  for (int e = 1; e < T::VEC; ++e) {
+    vp = fmaxf(vp, T::at(xp, e));
+    vq = fmaxf(vq, T::at(xq, e));
+  }
+  const float np = fmaxf(A.mp, vp), nq = fmaxf(A.mq, vq);
+  A.sp *= __builtin_amdgcn_exp2f((A.mp - np) * kLog2e);
+  A.sq *= __builtin_amdgcn_exp2f((A.mq - nq) * kLog2e);
+  A.mp = np;
+  A.mq = nq;
+  const float npL = np * kLog2e, nqL = nq * kLog2e;
+#pragma unroll
+  for (int e = 0; e < T::VEC; ++e) {
+    A.sp += __builtin_amdgcn_exp2f(__builtin_fmaf(T::at(xp, e), kLog2e, -npL));
+    A.sq += __builtin_amdgcn_exp2f(__builtin_fmaf(T::at(xq, e), kLog2e, -nqL));
+  }
+}
+
+// Step 1, one 256-thread workgroup per stored row (unverified dense rows
+// exit): lse_p, lse_q and the acceptance decision u * q(d) < p(d) (a draft
+// outside [0, V) is rejected).
+template <int VAR>
+__global__ __launch_bounds__(kBlock) void spec_stats_kernel(SpecArgs a) {
+  using T = Tr<VAR>;
+  using S = typename T::S;
+  constexpr uint32_t VB = T::VEC * T::EB;
+  __shared__ float s[kWaves][4];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  if (r == 0 && tid == 0 && a.status) a.status[0] = 0;
+  if (!a.ragged) {
+    const int req = r / a.k, i = r - req * a.k;
+    if (i >= min(max(a.bk[req], 1), a.k)) return;
+  }
+  const long long rowv = (long long)r * a.nvec;
+  const Rsrc rzp = row_rsrc(T::row(a.zp, rowv), (uint32_t)a.V * T::EB);
+  const Rsrc rzq = row_rsrc(T::row(a.zq, rowv), (uint32_t)a.V * T::EB);
+  SpecAcc A = {-INFINITY, 0.0f, -INFINITY, 0.0f};
+  int v = tid;
+  for (; v + 3 * kBlock < a.nvec; v += 4 * kBlock) {
+    S xp[4], xq[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      xp[j] = T::template bload<kAuxOnce>(rzp, (uint32_t)(v + j * kBlock) * VB, 0);
+      xq[j] = T::template bload<kAuxOnce>(rzq, (uint32_t)(v + j * kBlock) * VB, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) spec_fold<VAR>(xp[j], xq[j], A);
+  }
+  for (; v < a.nvec; v += kBlock)
+    spec_fold<VAR>(T::template bload<kAuxOnce>(rzp, (uint32_t)v * VB, 0),
+                   T::template bload<kAuxOnce>(rzq, (uint32_t)v * VB, 0), A);
+  // combine: butterflies (empty threads have s = 0), then the 4 waves in order
+  float dummy = 0.0f;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float omp = __shfl_xor(A.mp, o), osp = __shfl_xor(A.sp, o);
+    const float omq = __shfl_xor(A.mq, o), osq = __shfl_xor(A.sq, o);
+    lse_merge(A.mp, A.sp, dummy, omp, osp, 0.0f);
+    lse_merge(A.mq, A.sq, dummy, omq, osq, 0.0f);
+  }
+  if (lane == 0) {
+    s[wid][0] = A.mp;
+    s[wid][1] = A.sp;
+    s[wid][2] = A.mq;
+    s[wid][3] = A.sq;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    SpecAcc G = {s[0][0], s[0][1], s[0][2], s[0][3]};
+    for (int w = 1; w < kWaves; ++w) {
+      lse_merge(G.mp, G.sp, dummy, s[w][0], s[w][1], 0.0f);
+      lse_merge(G.mq, G.sq, dummy, s[w][2], s[w][3], 0.0f);
+    }
+    const float lse_p = G.mp + kLn2 * __builtin_amdgcn_logf(G.sp);
+    const float lse_q = G.mq + kLn2 * __builtin_amdgcn_logf(G.sq);
+    const int d = a.draft[r];
+    uint32_t acc = 0u;
+    if ((unsigned)d < (unsigned)a.V) {
+      const float pd = __builtin_amdgcn_exp2f((T::elem(T::row(a.zp, rowv), d) - lse_p) * kLog2e);
+      const float qd = __builtin_amdgcn_exp2f((T::elem(T::row(a.zq, rowv), d) - lse_q) * kLog2e);
+      acc = (a.u[r] * qd < pd) ? 1u : 0u;
+    }
+    const u32x4 rec = {acc, __float_as_uint(lse_p), __float_as_uint(lse_q), 0u};
+    *(u32x4*)(a.ws + 4 * (long long)r) = rec;  // one 16-byte record per row
+    settle16(rec);
+    if (a.stats) {
+      a.stats[2 * (long long)r] = lse_p;
+      a.stats[2 * (long long)r + 1] = lse_q;
+    }
+  }
+}
+
+// One entry of the race: key max(0, p_j - q_j) / E_j (or p_j / E_j when the
+// residual is zero everywhere); keeps the largest key, lowest index on ties.
+__device__ __forceinline__ void race_entry(float zpj, float zqj, uint32_t w, int j, float lpL, float lqL,
+                                           bool from_p, float& best, int& bi, bool& anyr) {
+  const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(zpj, kLog2e, -lpL));
+  const float q = __builtin_amdgcn_exp2f(__builtin_fmaf(zqj, kLog2e, -lqL));
+  const float r = from_p ? p : fmaxf(p - q, 0.0f);
+  anyr = anyr || r > 0.0f;
+  const float key = r * __builtin_amdgcn_rcpf(race_exponential(w));
+  if (key > best || (key == best && j < bi)) {
+    best = key;
+    bi = j;
+  }
+}
+
+// Step 2, one 1024-thread workgroup per request: the accepted length (first
+// rejected verified position) and, at that position, the race over the row.
+template <int VAR>
+__global__ __launch_bounds__(kRowBlock) void spec_sample_kernel(SpecArgs a) {
+  using T = Tr<VAR>;
+  using S = typename T::S;
+  constexpr int VEC = T::VEC, NW = kRowBlock / 64;
+  constexpr uint32_t VB = VEC * T::EB;
+  __shared__ int s_first;
+  __shared__ float s_best[NW];
+  __shared__ int s_bi[NW], s_any[NW];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  int r0, n;
+  if (a.ragged) {
+    r0 = a.row_off[b];
+    n = a.row_off[b + 1] - r0;
+    if (n < 1 || n > a.k || r0 < 0 || r0 + n > a.R) {  // invalid offsets: nothing is verified
+      if (tid == 0) {
+        a.acc[b] = 0;
+        a.token[b] = -1;
+        if (a.status) atomicOr(a.status, (int32_t)AV_DEV_BAD_OFFSETS);
+      }
+      return;
+    }
+  } else {
+    r0 = b * a.k;
+    n = min(max(a.bk[b], 1), a.k);
+  }
+  if (wid == 0) {
+    const bool rej = lane < n && a.ws[4 * (long long)(r0 + lane)] == 0u;
+    const uint64_t m = __ballot(rej);
+    if (lane == 0) s_first = m ? (__ffsll((unsigned long long)m) - 1) : n;
+  }
+  __syncthreads();
+  const int first = s_first;
+  if (first >= n) {
+    if (tid == 0) {
+      a.acc[b] = n;
+      a.token[b] = -1;
+    }
+    return;
+  }
+  const int row = r0 + first;
+  const uint32_t* wsr = a.ws + 4 * (long long)row;
+  const float lpL = __uint_as_float(wsr[1]) * kLog2e, lqL = __uint_as_float(wsr[2]) * kLog2e;
+  const long long rowv = (long long)row * a.nvec;
+  const Rsrc rzp = row_rsrc(T::row(a.zp, rowv), (uint32_t)a.V * T::EB);
+  const Rsrc rzq = row_rsrc(T::row(a.zq, rowv), (uint32_t)a.V * T::EB);
+  const uint32_t k0 = (uint32_t)a.seed, k1 = (uint32_t)(a.seed >> 32);
+  float best = -1.0f;
+  int bi = INT_MAX;
+  for (int pass = 0; pass < 2; ++pass) {  // pass 1 only if the residual is zero everywhere
+    const bool from_p = pass == 1;
+    bool anyr = false;
+    for (int v = tid; v < a.nvec; v += kRowBlock) {
+      const S xp = T::template bload<kAuxOnce>(rzp, (uint32_t)v * VB, 0);
+      const S xq = T::template bload<kAuxOnce>(rzq, (uint32_t)v * VB, 0);
+      const int j0 = v * VEC;
+#pragma unroll
+      for (int g = 0; g < (VEC + 3) / 4; ++g) {  // one generator call per 4 entries
+        uint32_t c0 = (uint32_t)(j0 + 4 * g) >> 2, c1 = (uint32_t)row, c2 = 0u, c3 = 0u;
+        philox4x32_10(c0, c1, c2, c3, k0, k1);
+        const uint32_t wd[4] = {c0, c1, c2, c3};
+#pragma unroll
+        for (int e = 0; e < (VEC < 4 ? VEC : 4); ++e) {
+          const int ee = 4 * g + e, j = j0 + ee;
+          race_entry(T::at(xp, ee), T::at(xq, ee), wd[(j & 3)], j, lpL, lqL, from_p, best, bi, anyr);
+        }
+      }
+    }
+    // workgroup argmax (largest key, lowest index) and whether any residual is positive
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ob = __shfl_xor(best, o);
+      const int oi = __shfl_xor(bi, o);
+      if (ob > best || (ob == best && oi < bi)) {
+        best = ob;
+        bi = oi;
+      }
+    }
+    const bool wany = __any(anyr);
+    if (lane == 0) {
+      s_best[wid] = best;
+      s_bi[wid] = bi;
+      s_any[wid] = wany ? 1 : 0;
+    }
+    __syncthreads();
+    best = s_best[0];
+    bi = s_bi[0];
+    int any = s_any[0];
+    for (int w = 1; w < NW; ++w) {
+      if (s_best[w] > best || (s_best[w] == best && s_bi[w] < bi)) {
+        best = s_best[w];
+        bi = s_bi[w];
+      }
+      any |= s_any[w];
+    }
+    __syncthreads();
+    if (any || from_p) break;
+    best = -1.0f;
+    bi = INT_MAX;
+  }
+  if (tid == 0) {
+    a.acc[b] = first;
+    a.token[b] = bi;
+  }
+}
+
 __global__ __launch_bounds__(kBlock) void zero_kernel(uint64_t* p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += (size_t)gridDim.x * kBlock)
     p[i] = 0ull;
@@ -1687,6 +1953,24 @@ hipError_t launch_bwd(Variant v, const BwdArgs& a, hipStream_t s) {
 hipError_t launch_head(const HeadArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(head_kernel, dim3(a.B), dim3(kBlock), 0, s, a);
   return hipGetLastError();
+}
+
+template <int VAR>
+hipError_t launch_spec_t(const SpecArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(spec_stats_kernel<VAR>, dim3(a.R), dim3(kBlock), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(spec_sample_kernel<VAR>, dim3(a.B), dim3(kRowBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_spec(Variant v, const SpecArgs& a, hipStream_t s) {
+  switch (v) {
+    case kBf16x8: return launch_spec_t<kBf16x8>(a, s);
+    case kBf16x1: return launch_spec_t<kBf16x1>(a, s);
+    case kF32x4: return launch_spec_t<kF32x4>(a, s);
+    default: return launch_spec_t<kF32x1>(a, s);
+  }
 }
 
 hipError_t launch_head_update(const HeadUpdArgs& a, hipStream_t s) {

@@ -126,6 +126,52 @@ int av_length_head_update(const float* h, const int32_t* acc, const int32_t* bk,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * av_spec_verify -- sampling-based block verification (speculative sampling).
+ *
+ * The pages list the standard speculative-decoding acceptance formula as an
+ * axiom (Pith review page, "Axiom & Free-Parameter Ledger", after Leviathan
+ * et al. 2023) and cite Chen et al. 2023 on speculative sampling; this is
+ * that published method at temperature 1.  For request b (rows as in
+ * av_verify_opd_fwd; only verified positions i < b_k are tested), with
+ * p = softmax(zp[r,:]) and q = softmax(zq[r,:]) at row r = row(b, i):
+ *   position i is accepted iff u[r] * q(d) < p(d), d = draft[r] (a draft
+ *     outside [0, V) is rejected), i.e. with probability min(1, p(d)/q(d));
+ *   acc_len[b] = number of positions accepted before the first rejection;
+ *   token[b]   = at the first rejected position, a draw from the residual
+ *     max(0, p - q) / sum(max(0, p - q)) (p itself if that is zero
+ *     everywhere), by the exponential race argmax_j r_j / E_j (ties to the
+ *     lowest j), E_j = -ln(u_j), u_j = (w_j + 1/2) / 2^32 where w_j is word
+ *     j % 4 of Philox4x32-10 (Salmon et al., SC 2011) with key (seed low 32
+ *     bits, seed high 32 bits) and counter (j / 4, r, 0, 0); -1 when every
+ *     verified position is accepted (the caller draws the bonus token from
+ *     the target's next distribution).
+ * Every emitted token (accepted draft or replacement) is then distributed
+ * as a draw from the target.
+ *
+ * Arguments
+ *   dtype, B, k, V, R, row_off, zp, zq, draft, bk: as av_verify_opd_fwd
+ *   u            [R] float32 uniforms in [0, 1) for the acceptance tests
+ *                (the caller's generator)
+ *   seed         64-bit key of the replacement draw
+ *   acc_len, token  [B] int32 out
+ *   row_stats    [R, 2] float32 out or NULL: (lse_p, lse_q) of verified rows
+ *   status       [1] int32 out or NULL: 0, or AV_DEV_BAD_OFFSETS for a
+ *                ragged request whose offsets are invalid (it gets acc 0,
+ *                token -1)
+ *   workspace    >= av_spec_workspace_bytes(R) bytes, 16-byte aligned, no
+ *                initialisation needed
+ * All pointers are device pointers; asynchronous on `stream` (two launches).
+ * Errors: as av_verify_opd_fwd for the shared arguments; AV_EINVAL for NULL
+ * u/acc_len/token/workspace or a workspace that is too small or misaligned.
+ */
+size_t av_spec_workspace_bytes(int R);
+int av_spec_verify(int dtype, int B, int k, int V, int R, const int32_t* row_off,
+                   const void* zp, const void* zq, const int32_t* draft, const int32_t* bk,
+                   const float* u, uint64_t seed, int32_t* acc_len, int32_t* token,
+                   float* row_stats, int32_t* status, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/*
  * av_workspace_bytes -- size of the scratch area av_verify_opd_fwd needs for
  * B requests and R stored rows (R = B*k dense).  Independent of V and dtype.
  * Returns 0 for invalid sizes.

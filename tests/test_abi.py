@@ -179,6 +179,31 @@ def test_head_update_rejects_bad_arguments_on_host(kw, code):
     assert rc == code
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(zp=NULL), dd.AV_EINVAL),
+    (dict(draft=NULL), dd.AV_EINVAL),
+    (dict(u=NULL), dd.AV_EINVAL),
+    (dict(acc=NULL), dd.AV_EINVAL),
+    (dict(token=NULL), dd.AV_EINVAL),
+    (dict(ws=NULL), dd.AV_EINVAL),
+    (dict(bk=NULL), dd.AV_EINVAL),
+    (dict(B=0), dd.AV_EINVAL),
+    (dict(k=65), dd.AV_EINVAL),
+    (dict(R=7), dd.AV_EINVAL),
+    (dict(ws_bytes=16 * 8 - 1), dd.AV_EINVAL),
+    (dict(ws=ctypes.c_void_p(0x10008)), dd.AV_EINVAL),
+    (dict(dtype=5), dd.AV_EUNSUPPORTED),
+])
+def test_spec_rejects_bad_arguments_on_host(kw, code):
+    a = dict(dtype=1, B=2, k=4, V=64, R=8, row_off=NULL, zp=P, zq=P, draft=P, bk=P, u=P, seed=1,
+             acc=P, token=P, stats=NULL, status=NULL, ws=P, ws_bytes=1 << 20, stream=NULL)
+    a.update(kw)
+    rc = _lib.lib().av_spec_verify(a["dtype"], a["B"], a["k"], a["V"], a["R"], a["row_off"], a["zp"],
+                                   a["zq"], a["draft"], a["bk"], a["u"], a["seed"], a["acc"], a["token"],
+                                   a["stats"], a["status"], a["ws"], a["ws_bytes"], a["stream"])
+    assert rc == code
+
+
 def test_head_update_workspace_bytes():
     assert dd.av_head_update_workspace_bytes(128) == 128 * 16
     assert dd.av_head_update_workspace_bytes(0) == 0
