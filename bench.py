@@ -16,6 +16,10 @@ stay resident.  Prints one JSON line.
 head (av_length_head_update) on the same workload's head: B=128 pooled
 states of H=4096, labels from one verification pass, gradients with respect
 to w, bias and h, one AdamW step per call.
+
+`--workload spec` measures sampling-based verification (av_spec_verify) of
+the same workload: acceptance tests with the caller's uniforms on every
+verified row, and the residual draw at each request's first rejection.
 """
 
 from __future__ import annotations
@@ -293,6 +297,109 @@ def bench_head_update(args):
     print(json.dumps(line), flush=True)
 
 
+def spec_bytes(V, Rv, n_rej, elem=2):
+    """Bytes sampling verification must move at least once: zp and zq of every
+    verified row (its statistics), zp and zq of each request's rejected row
+    again for the residual draw (the statistics are needed first), the
+    uniforms, drafts and per-row records, and the per-request outputs."""
+    return 2 * elem * V * Rv + 2 * elem * V * n_rej + 12 * Rv + 8 * n_rej
+
+
+def bench_spec(args):
+    import numpy as np
+    import torch
+
+    import drafter_distillation_amd as dd
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dd.lib()
+    w = synth.make("concurrent", seed=args.seed)
+    B, k, V, H, R = w.B, w.k, w.V, w.H, w.R
+    zp = torch.from_numpy(w.zp.view(np.int16)).view(torch.bfloat16).to(dev)
+    zq = torch.from_numpy(w.zq.view(np.int16)).view(torch.bfloat16).to(dev)
+    draft = torch.from_numpy(w.draft).to(dev)
+    bk = torch.empty(B, dtype=torch.int32, device=dev)
+    dd.av_length_head(torch.from_numpy(w.h).to(dev), torch.from_numpy(w.w).to(dev), w.bias, w.gamma, k,
+                      bk_out=bk)
+    u = torch.from_numpy(np.random.default_rng(args.seed + 1).random(R).astype(np.float32)).to(dev)
+    seed = 0x5EED0000 + args.seed
+    out = None
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev0=None, ev1=None):
+        nonlocal out
+        if ev0 is not None:
+            ev0.record(stream)
+        out = dd.av_spec_verify(zp, zq, draft, u, k=k, seed=seed, bk=bk, out=out)
+        if ev1 is not None:
+            ev1.record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        step(e0, e1)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs)
+    bkh = torch.clamp(bk, 1, k).cpu().numpy()
+    acc = out["acc_len"].cpu().numpy()
+    Rv, n_rej = int(bkh.sum()), int((acc < bkh).sum())
+    nbytes = spec_bytes(V, Rv, n_rej)
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    line = {
+        "metric": "sampling-based block verification GB/s at B=128,k=16,V=151936 bf16",
+        "value": round(achieved, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "spec: the concurrent workload (B=128, k=16, V=151936, bf16 logits, greedy "
+                        "drafts of the drafter logits, b_k from the length head), uniforms seeded",
+            "B": B, "k": k, "V": V, "verified_rows": Rv, "rejecting_requests": n_rej,
+            "accepted_positions": int(acc.sum()), "bytes_per_step": nbytes,
+            "kernel_ms": round(kern_ms, 4), "launches_per_step": 2,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        from threadpoolctl import threadpool_limits
+        nb = 16
+        uh = u.cpu().numpy()
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            zpd = oracle.bf16_bits_to_f64(w.zp[:nb * k])
+            zqd = oracle.bf16_bits_to_f64(w.zq[:nb * k])
+            res = oracle.spec_verify(zpd, zqd, w.draft[:nb * k], uh[:nb * k], k=k, seed=seed, bk=bkh[:nb])
+            dt = time.perf_counter() - t0
+        sb = spec_bytes(V, int(bkh[:nb].sum()), int((res["acc"] < bkh[:nb]).sum()))
+        line["cpu_baseline"] = {
+            "value": round(sb / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {nb} of {B} requests of the same workload, float64 numpy, one thread, "
+                      f"{dt:.1f} s", "seconds": round(dt, 3)}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -301,9 +408,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=128)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--workload", choices=["concurrent", "head_update"], default="concurrent",
+    ap.add_argument("--workload", choices=["concurrent", "head_update", "spec"], default="concurrent",
                     help="concurrent: the fused verify+OPD step (default); head_update: the "
-                         "length head's online update")
+                         "length head's online update; spec: sampling-based verification")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run a plain copy of this many MiB before warmup (counter calibration)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -327,6 +434,9 @@ def main():
 
     if args.workload == "head_update":
         bench_head_update(args)
+        return
+    if args.workload == "spec":
+        bench_spec(args)
         return
 
     import numpy as np

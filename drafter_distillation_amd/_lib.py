@@ -48,7 +48,7 @@ _SIGS = {
                                _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i, _vp]),
     "av_verify_opd_bwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _f, _f, _f,
                                _vp, _i, _vp]),
-    "av_spec_workspace_bytes": (_sz, [_i]),
+    "av_spec_workspace_bytes": (_sz, [_i, _i]),
     "av_spec_verify": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_uint64, _vp, _vp,
                             _vp, _vp, _vp, _sz, _vp]),
     "av_status_str": (ctypes.c_char_p, [_i]),
@@ -190,8 +190,8 @@ def av_length_head_update(h: torch.Tensor, acc: torch.Tensor, bk: torch.Tensor, 
     return dict(loss=loss, rate=rate, grad_h=grad_h)
 
 
-def av_spec_workspace_bytes(R: int) -> int:
-    return int(lib().av_spec_workspace_bytes(int(R)))
+def av_spec_workspace_bytes(B: int, R: int) -> int:
+    return int(lib().av_spec_workspace_bytes(int(B), int(R)))
 
 
 def av_spec_verify(zp: torch.Tensor, zq: torch.Tensor, draft: torch.Tensor, u: torch.Tensor, *, k: int,
@@ -231,7 +231,7 @@ def av_spec_verify(zp: torch.Tensor, zq: torch.Tensor, draft: torch.Tensor, u: t
     stats = get("row_stats", (R, 2), torch.float32) if want_stats else None
     status = get("status", (1,), torch.int32)
     with torch.cuda.device(dev):
-        ws = workspace(dev, av_spec_workspace_bytes(R), kind="spec")
+        ws = workspace(dev, av_spec_workspace_bytes(B, R), kind="spec")
         rc = lib().av_spec_verify(
             _dtype_code(zp), B, int(k), V, R, _ptr(row_off), _ptr(zp), _ptr(zq), _ptr(draft), _ptr(bk),
             _ptr(u), ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF), _ptr(acc), _ptr(token), _ptr(stats),

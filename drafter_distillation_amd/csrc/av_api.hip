@@ -190,9 +190,9 @@ int av_length_head_update(const float* h, const int32_t* acc, const int32_t* bk,
   return e == hipSuccess ? AV_OK : hip_fail(e);
 }
 
-size_t av_spec_workspace_bytes(int R) {
-  if (R < 1) return 0;
-  return (size_t)R * 16;
+size_t av_spec_workspace_bytes(int B, int R) {
+  if (B < 1 || R < 1) return 0;
+  return (size_t)R * 16 + (size_t)B * avk::kSpecMaxChunks * 16;
 }
 
 int av_spec_verify(int dtype, int B, int k, int V, int R, const int32_t* row_off, const void* zp,
@@ -204,7 +204,12 @@ int av_spec_verify(int dtype, int B, int k, int V, int R, const int32_t* row_off
   Plan p;
   int rc = plan_rows(dtype, B, k, V, R, row_off, zp, zq, nullptr, &p);
   if (rc != AV_OK) return rc;
-  if (workspace_bytes < av_spec_workspace_bytes(R) || !aligned16(workspace)) return AV_EINVAL;
+  if (workspace_bytes < av_spec_workspace_bytes(B, R) || !aligned16(workspace)) return AV_EINVAL;
+  // chunks of the race: at least kSpecChunkVecs vectors, at most kSpecMaxChunks per row
+  int chunk = avk::kSpecChunkVecs;
+  if ((long long)chunk * avk::kSpecMaxChunks < p.nvec)
+    chunk = (p.nvec + avk::kSpecMaxChunks - 1) / avk::kSpecMaxChunks;
+  const int nchunk = (p.nvec + chunk - 1) / chunk;
   avk::SpecArgs a;
   a.zp = zp;
   a.zq = zq;
@@ -217,6 +222,9 @@ int av_spec_verify(int dtype, int B, int k, int V, int R, const int32_t* row_off
   a.stats = row_stats;
   a.status = status;
   a.ws = (uint32_t*)workspace;
+  a.chunks = (uint32_t*)((char*)workspace + (size_t)R * 16);
+  a.chunk = chunk;
+  a.nchunk = nchunk;
   a.seed = seed;
   a.B = B;
   a.k = k;

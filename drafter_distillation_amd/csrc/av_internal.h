@@ -137,9 +137,13 @@ struct SpecArgs {
   float* stats;     // [R, 2] lse_p, lse_q of verified rows, or NULL
   int32_t* status;  // [1] or NULL
   uint32_t* ws;     // [R][4]: accepted flag, lse_p bits, lse_q bits
+  uint32_t* chunks; // [B][nchunk][4]: best residual key and index, best p key and index
   uint64_t seed;
   int B, k, V, R, nvec, ragged;
+  int chunk, nchunk;  // vectors per chunk of the race, chunks per row (<= kSpecMaxChunks)
 };
+constexpr int kSpecMaxChunks = 64;
+constexpr int kSpecChunkVecs = 2048;  // fewest vectors per chunk
 
 // full: every on-chip slot of a row is filled (nvec >= (regs + lds) * kRowBlock)
 // and the default on-chip split is used.

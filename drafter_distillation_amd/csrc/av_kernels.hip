@@ -1665,12 +1665,25 @@ __device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32
   }
 }
 
-// E = -ln(u), u = (w + 1/2) / 2^32; from 1 - u through log1p where u >= 1/2,
-// where u itself would round to 1 in float32.
+// E = -ln(u), u = (w + 1/2) / 2^32, to about 1e-7 relative.  Where u is
+// within 1/16 of 1, u itself would lose the low bits of 1 - u in float32, so
+// E comes from v = 1 - u = (2^32 - 1 - w + 1/2) / 2^32 by the series
+// -ln(1 - v) = v (1 + v/2 + v^2/3 + ...) (7 terms: the tail is below
+// (1/16)^7); elsewhere from the hardware log2 of u.
 __device__ __forceinline__ float race_exponential(uint32_t w) {
   constexpr float k2m32 = 0x1p-32f;
-  if (w < 0x80000000u) return -logf(((float)w + 0.5f) * k2m32);
-  return -log1pf(-(((float)(0xFFFFFFFFu - w) + 0.5f) * k2m32));
+  const float v = ((float)(0xFFFFFFFFu - w) + 0.5f) * k2m32;
+  if (v < 0.0625f) {
+    float t = 1.0f / 7.0f;
+    t = __builtin_fmaf(t, v, 1.0f / 6.0f);
+    t = __builtin_fmaf(t, v, 0.2f);
+    t = __builtin_fmaf(t, v, 0.25f);
+    t = __builtin_fmaf(t, v, 1.0f / 3.0f);
+    t = __builtin_fmaf(t, v, 0.5f);
+    t = __builtin_fmaf(t, v, 1.0f);
+    return v * t;
+  }
+  return -kLn2 * __builtin_amdgcn_logf(((float)w + 0.5f) * k2m32);
 }
 
 // Per-thread online (max, sum exp) of zp and zq over a row.
@@ -1775,63 +1788,74 @@ __global__ __launch_bounds__(kBlock) void spec_stats_kernel(SpecArgs a) {
   }
 }
 
-// One entry of the race: key max(0, p_j - q_j) / E_j (or p_j / E_j when the
-// residual is zero everywhere); keeps the largest key, lowest index on ties.
-__device__ __forceinline__ void race_entry(float zpj, float zqj, uint32_t w, int j, float lpL, float lqL,
-                                           bool from_p, float& best, int& bi, bool& anyr) {
-  const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(zpj, kLog2e, -lpL));
-  const float q = __builtin_amdgcn_exp2f(__builtin_fmaf(zqj, kLog2e, -lqL));
-  const float r = from_p ? p : fmaxf(p - q, 0.0f);
-  anyr = anyr || r > 0.0f;
-  const float key = r * __builtin_amdgcn_rcpf(race_exponential(w));
+// Race keys of one entry: r_j / E_j with r_j = max(0, p_j - q_j), and p_j / E_j
+// (the draw from p, used when the residual is zero everywhere).  Keeps the
+// largest of each, lowest index on ties.
+struct RaceBest {
+  float rk, pk;
+  int ri, pi;
+};
+__device__ __forceinline__ void race_keep(float key, int j, float& best, int& bi) {
   if (key > best || (key == best && j < bi)) {
     best = key;
     bi = j;
   }
 }
+__device__ __forceinline__ void race_entry(float zpj, float zqj, uint32_t w, int j, float lpL, float lqL,
+                                           RaceBest& R) {
+  const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(zpj, kLog2e, -lpL));
+  const float q = __builtin_amdgcn_exp2f(__builtin_fmaf(zqj, kLog2e, -lqL));
+  const float ie = __builtin_amdgcn_rcpf(race_exponential(w));
+  race_keep(fmaxf(p - q, 0.0f) * ie, j, R.rk, R.ri);
+  race_keep(p * ie, j, R.pk, R.pi);
+}
+__device__ __forceinline__ void race_merge(RaceBest& R, const RaceBest& O) {
+  race_keep(O.rk, O.ri, R.rk, R.ri);
+  race_keep(O.pk, O.pi, R.pk, R.pi);
+}
 
-// Step 2, one 1024-thread workgroup per request: the accepted length (first
-// rejected verified position) and, at that position, the race over the row.
-template <int VAR>
-__global__ __launch_bounds__(kRowBlock) void spec_sample_kernel(SpecArgs a) {
-  using T = Tr<VAR>;
-  using S = typename T::S;
-  constexpr int VEC = T::VEC, NW = kRowBlock / 64;
-  constexpr uint32_t VB = VEC * T::EB;
-  __shared__ int s_first;
-  __shared__ float s_best[NW];
-  __shared__ int s_bi[NW], s_any[NW];
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  int r0, n;
+// The accepted length of request b: the first verified position whose test
+// failed (n if none).  Run by one wave; every lane gets the result.
+__device__ __forceinline__ int spec_first(const SpecArgs& a, int r0, int n) {
+  const int lane = threadIdx.x & 63;
+  const bool rej = lane < n && a.ws[4 * (long long)(r0 + lane)] == 0u;
+  const uint64_t m = __ballot(rej);
+  return m ? (__ffsll((unsigned long long)m) - 1) : n;
+}
+
+// Request b's rows (r0, n); false if its ragged offsets are invalid.
+__device__ __forceinline__ bool spec_span(const SpecArgs& a, int b, int& r0, int& n) {
   if (a.ragged) {
     r0 = a.row_off[b];
     n = a.row_off[b + 1] - r0;
-    if (n < 1 || n > a.k || r0 < 0 || r0 + n > a.R) {  // invalid offsets: nothing is verified
-      if (tid == 0) {
-        a.acc[b] = 0;
-        a.token[b] = -1;
-        if (a.status) atomicOr(a.status, (int32_t)AV_DEV_BAD_OFFSETS);
-      }
-      return;
-    }
-  } else {
-    r0 = b * a.k;
-    n = min(max(a.bk[b], 1), a.k);
+    return n >= 1 && n <= a.k && r0 >= 0 && r0 + n <= a.R;
   }
+  r0 = b * a.k;
+  n = min(max(a.bk[b], 1), a.k);
+  return true;
+}
+
+// Step 2, workgroup (c, b): chunk c of the row at request b's first
+// rejection (vectors [c C, (c+1) C), C = a.chunk): the chunk's best race keys
+// -> chunk record [b][c] = {residual key, its index, p key, its index}.
+template <int VAR>
+__global__ __launch_bounds__(kBlock) void spec_race_kernel(SpecArgs a) {
+  using T = Tr<VAR>;
+  using S = typename T::S;
+  constexpr int VEC = T::VEC;
+  constexpr uint32_t VB = VEC * T::EB;
+  __shared__ RaceBest s_r[kWaves];
+  const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  int r0, n;
+  if (!spec_span(a, b, r0, n)) return;
+  __shared__ int s_first;
   if (wid == 0) {
-    const bool rej = lane < n && a.ws[4 * (long long)(r0 + lane)] == 0u;
-    const uint64_t m = __ballot(rej);
-    if (lane == 0) s_first = m ? (__ffsll((unsigned long long)m) - 1) : n;
+    const int f = spec_first(a, r0, n);
+    if (lane == 0) s_first = f;
   }
   __syncthreads();
   const int first = s_first;
-  if (first >= n) {
-    if (tid == 0) {
-      a.acc[b] = n;
-      a.token[b] = -1;
-    }
-    return;
-  }
+  if (first >= n) return;
   const int row = r0 + first;
   const uint32_t* wsr = a.ws + 4 * (long long)row;
   const float lpL = __uint_as_float(wsr[1]) * kLog2e, lqL = __uint_as_float(wsr[2]) * kLog2e;
@@ -1839,62 +1863,82 @@ __global__ __launch_bounds__(kRowBlock) void spec_sample_kernel(SpecArgs a) {
   const Rsrc rzp = row_rsrc(T::row(a.zp, rowv), (uint32_t)a.V * T::EB);
   const Rsrc rzq = row_rsrc(T::row(a.zq, rowv), (uint32_t)a.V * T::EB);
   const uint32_t k0 = (uint32_t)a.seed, k1 = (uint32_t)(a.seed >> 32);
-  float best = -1.0f;
-  int bi = INT_MAX;
-  for (int pass = 0; pass < 2; ++pass) {  // pass 1 only if the residual is zero everywhere
-    const bool from_p = pass == 1;
-    bool anyr = false;
-    for (int v = tid; v < a.nvec; v += kRowBlock) {
-      const S xp = T::template bload<kAuxOnce>(rzp, (uint32_t)v * VB, 0);
-      const S xq = T::template bload<kAuxOnce>(rzq, (uint32_t)v * VB, 0);
-      const int j0 = v * VEC;
+  RaceBest R = {-1.0f, -1.0f, INT_MAX, INT_MAX};
+  const int v1 = min((c + 1) * a.chunk, a.nvec);
+  for (int v = c * a.chunk + tid; v < v1; v += kBlock) {
+    const S xp = T::template bload<kAuxOnce>(rzp, (uint32_t)v * VB, 0);
+    const S xq = T::template bload<kAuxOnce>(rzq, (uint32_t)v * VB, 0);
+    const int j0 = v * VEC;
 #pragma unroll
-      for (int g = 0; g < (VEC + 3) / 4; ++g) {  // one generator call per 4 entries
-        uint32_t c0 = (uint32_t)(j0 + 4 * g) >> 2, c1 = (uint32_t)row, c2 = 0u, c3 = 0u;
-        philox4x32_10(c0, c1, c2, c3, k0, k1);
-        const uint32_t wd[4] = {c0, c1, c2, c3};
+    for (int g = 0; g < (VEC + 3) / 4; ++g) {  // one generator call per 4 entries
+      uint32_t c0 = (uint32_t)(j0 + 4 * g) >> 2, c1 = (uint32_t)row, c2 = 0u, c3 = 0u;
+      philox4x32_10(c0, c1, c2, c3, k0, k1);
+      const uint32_t wd[4] = {c0, c1, c2, c3};
 #pragma unroll
-        for (int e = 0; e < (VEC < 4 ? VEC : 4); ++e) {
-          const int ee = 4 * g + e, j = j0 + ee;
-          race_entry(T::at(xp, ee), T::at(xq, ee), wd[(j & 3)], j, lpL, lqL, from_p, best, bi, anyr);
-        }
+      for (int e = 0; e < (VEC < 4 ? VEC : 4); ++e) {
+        const int ee = 4 * g + e, j = j0 + ee;
+        race_entry(T::at(xp, ee), T::at(xq, ee), wd[j & 3], j, lpL, lqL, R);
       }
     }
-    // workgroup argmax (largest key, lowest index) and whether any residual is positive
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    RaceBest O;
+    O.rk = __shfl_xor(R.rk, o);
+    O.ri = __shfl_xor(R.ri, o);
+    O.pk = __shfl_xor(R.pk, o);
+    O.pi = __shfl_xor(R.pi, o);
+    race_merge(R, O);
+  }
+  if (lane == 0) s_r[wid] = R;
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < kWaves; ++w) race_merge(R, s_r[w]);
+    const u32x4 rec = {__float_as_uint(R.rk), (uint32_t)R.ri, __float_as_uint(R.pk), (uint32_t)R.pi};
+    *(u32x4*)(a.chunks + 4 * ((long long)b * a.nchunk + c)) = rec;
+    settle16(rec);
+  }
+}
+
+// Step 3, one wave per request: the accepted length, and the token from the
+// chunk records (chunk order; the residual's draw unless every residual key
+// is zero, then p's).
+__global__ __launch_bounds__(64) void spec_finish_kernel(SpecArgs a) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  int r0, n;
+  if (!spec_span(a, b, r0, n)) {  // invalid ragged offsets: nothing is verified
+    if (lane == 0) {
+      a.acc[b] = 0;
+      a.token[b] = -1;
+      if (a.status) atomicOr(a.status, (int32_t)AV_DEV_BAD_OFFSETS);
+    }
+    return;
+  }
+  const int first = spec_first(a, r0, n);
+  int token = -1;
+  if (first < n) {
+    RaceBest R = {-1.0f, -1.0f, INT_MAX, INT_MAX};
+    if (lane < a.nchunk) {
+      const uint32_t* rec = a.chunks + 4 * ((long long)b * a.nchunk + lane);
+      R.rk = __uint_as_float(rec[0]);
+      R.ri = (int)rec[1];
+      R.pk = __uint_as_float(rec[2]);
+      R.pi = (int)rec[3];
+    }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
-      const float ob = __shfl_xor(best, o);
-      const int oi = __shfl_xor(bi, o);
-      if (ob > best || (ob == best && oi < bi)) {
-        best = ob;
-        bi = oi;
-      }
+      RaceBest O;
+      O.rk = __shfl_xor(R.rk, o);
+      O.ri = __shfl_xor(R.ri, o);
+      O.pk = __shfl_xor(R.pk, o);
+      O.pi = __shfl_xor(R.pi, o);
+      race_merge(R, O);
     }
-    const bool wany = __any(anyr);
-    if (lane == 0) {
-      s_best[wid] = best;
-      s_bi[wid] = bi;
-      s_any[wid] = wany ? 1 : 0;
-    }
-    __syncthreads();
-    best = s_best[0];
-    bi = s_bi[0];
-    int any = s_any[0];
-    for (int w = 1; w < NW; ++w) {
-      if (s_best[w] > best || (s_best[w] == best && s_bi[w] < bi)) {
-        best = s_best[w];
-        bi = s_bi[w];
-      }
-      any |= s_any[w];
-    }
-    __syncthreads();
-    if (any || from_p) break;
-    best = -1.0f;
-    bi = INT_MAX;
+    token = R.rk > 0.0f ? R.ri : R.pi;
   }
-  if (tid == 0) {
+  if (lane == 0) {
     a.acc[b] = first;
-    a.token[b] = bi;
+    a.token[b] = token;
   }
 }
 
@@ -1960,7 +2004,10 @@ hipError_t launch_spec_t(const SpecArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(spec_stats_kernel<VAR>, dim3(a.R), dim3(kBlock), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(spec_sample_kernel<VAR>, dim3(a.B), dim3(kRowBlock), 0, s, a);
+  hipLaunchKernelGGL(spec_race_kernel<VAR>, dim3(a.nchunk, a.B), dim3(kBlock), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(spec_finish_kernel, dim3(a.B), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -158,13 +158,13 @@ int av_length_head_update(const float* h, const int32_t* acc, const int32_t* bk,
  *   status       [1] int32 out or NULL: 0, or AV_DEV_BAD_OFFSETS for a
  *                ragged request whose offsets are invalid (it gets acc 0,
  *                token -1)
- *   workspace    >= av_spec_workspace_bytes(R) bytes, 16-byte aligned, no
+ *   workspace    >= av_spec_workspace_bytes(B, R) bytes, 16-byte aligned, no
  *                initialisation needed
- * All pointers are device pointers; asynchronous on `stream` (two launches).
+ * All pointers are device pointers; asynchronous on `stream` (three launches).
  * Errors: as av_verify_opd_fwd for the shared arguments; AV_EINVAL for NULL
  * u/acc_len/token/workspace or a workspace that is too small or misaligned.
  */
-size_t av_spec_workspace_bytes(int R);
+size_t av_spec_workspace_bytes(int B, int R);
 int av_spec_verify(int dtype, int B, int k, int V, int R, const int32_t* row_off,
                    const void* zp, const void* zq, const int32_t* draft, const int32_t* bk,
                    const float* u, uint64_t seed, int32_t* acc_len, int32_t* token,

@@ -190,7 +190,7 @@ def test_head_update_rejects_bad_arguments_on_host(kw, code):
     (dict(B=0), dd.AV_EINVAL),
     (dict(k=65), dd.AV_EINVAL),
     (dict(R=7), dd.AV_EINVAL),
-    (dict(ws_bytes=16 * 8 - 1), dd.AV_EINVAL),
+    (dict(ws_bytes=16 * 8 + 2 * 64 * 16 - 1), dd.AV_EINVAL),
     (dict(ws=ctypes.c_void_p(0x10008)), dd.AV_EINVAL),
     (dict(dtype=5), dd.AV_EUNSUPPORTED),
 ])
