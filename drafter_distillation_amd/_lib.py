@@ -45,9 +45,9 @@ _SIGS = {
     "av_workspace_bytes": (_sz, [_i, _i, _i]),
     "av_workspace_init": (_i, [_vp, _sz, _vp]),
     "av_verify_opd_fwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _f, _f, _f,
-                               _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _i, _vp]),
+                               _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _sz, _i, _vp]),
     "av_verify_opd_bwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _f, _f, _f,
-                               _vp, _i, _vp]),
+                               _vp, _i, _i, _vp]),
     "av_spec_workspace_bytes": (_sz, [_i, _i]),
     "av_spec_verify": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_uint64, _vp, _vp,
                             _vp, _vp, _vp, _sz, _vp]),
@@ -240,6 +240,14 @@ def av_spec_verify(zp: torch.Tensor, zq: torch.Tensor, draft: torch.Tensor, u: t
     return o
 
 
+def _grad_code(dtype: torch.dtype) -> int:
+    if dtype == torch.float32:
+        return AV_F32
+    if dtype == torch.bfloat16:
+        return AV_BF16
+    raise ValueError(f"gradient must be float32 or bfloat16, got {dtype}")
+
+
 def _dtype_code(zp: torch.Tensor) -> int:
     if zp.dtype == torch.bfloat16:
         return AV_BF16
@@ -252,6 +260,7 @@ def av_verify_opd_fwd(zp: torch.Tensor, zq: torch.Tensor, draft: torch.Tensor, *
                       bk: Optional[torch.Tensor] = None, row_off: Optional[torch.Tensor] = None,
                       lam: float, tau: float, grad_scale: float = 1.0, want_grad: bool = True,
                       want_stats: bool = True, onchip_limit: int = 0,
+                      grad_dtype: torch.dtype = torch.float32,
                       out: Optional[dict] = None) -> dict:
     """Fused verify + OPD pass (see include/av.h).
 
@@ -259,6 +268,8 @@ def av_verify_opd_fwd(zp: torch.Tensor, zq: torch.Tensor, draft: torch.Tensor, *
     or ragged layout with row_off [B+1] int32.  Returns a dict of output
     tensors (tgt_argmax, acc_len, row_loss, req_loss, total_loss, row_stats,
     grad, status); `out` may supply preallocated tensors under those names.
+    grad_dtype: torch.float32 (default) or torch.bfloat16 (each entry
+    rounded to nearest-even bfloat16).
     """
     _need_gpu("zp", zp)
     _need_gpu("zq", zq, zp.dtype)
@@ -290,7 +301,9 @@ def av_verify_opd_fwd(zp: torch.Tensor, zq: torch.Tensor, draft: torch.Tensor, *
     req_loss = get("req_loss", (B,), torch.float32)
     total = get("total_loss", (1,), torch.float32)
     stats = get("row_stats", (R, 4), torch.float32) if want_stats else None
-    grad = get("grad", (R, V), torch.float32) if want_grad else None
+    grad = get("grad", (R, V), grad_dtype) if want_grad else None
+    if grad is not None:
+        _need_gpu("grad", grad, grad_dtype)
     status = get("status", (1,), torch.int32)
     nbytes = av_workspace_bytes(B, k, R) if B >= 1 and R >= 1 else 0
     with torch.cuda.device(dev):
@@ -298,8 +311,8 @@ def av_verify_opd_fwd(zp: torch.Tensor, zq: torch.Tensor, draft: torch.Tensor, *
         rc = lib().av_verify_opd_fwd(
             _dtype_code(zp), B, int(k), V, R, _ptr(row_off), _ptr(zp), _ptr(zq), _ptr(draft),
             _ptr(bk), float(lam), float(tau), float(grad_scale), _ptr(tgt), _ptr(acc),
-            _ptr(row_loss), _ptr(req_loss), _ptr(total), _ptr(stats), _ptr(grad), _ptr(status),
-            _ptr(ws), ws.numel(), int(onchip_limit), _stream(dev))
+            _ptr(row_loss), _ptr(req_loss), _ptr(total), _ptr(stats), _ptr(grad),
+            _grad_code(grad_dtype), _ptr(status), _ptr(ws), ws.numel(), int(onchip_limit), _stream(dev))
     _check("av_verify_opd_fwd", rc)
     return o
 
@@ -308,7 +321,8 @@ def av_verify_opd_bwd(zp: torch.Tensor, zq: torch.Tensor, tgt_argmax: torch.Tens
                       row_stats: torch.Tensor, *, k: int, bk: Optional[torch.Tensor] = None,
                       row_off: Optional[torch.Tensor] = None, lam: float, tau: float,
                       grad_scale: float = 1.0, vecs_per_thread: int = 0,
-                      grad: Optional[torch.Tensor] = None) -> torch.Tensor:
+                      grad: Optional[torch.Tensor] = None,
+                      grad_dtype: torch.dtype = torch.float32) -> torch.Tensor:
     """Gradient alone from saved statistics (see include/av.h)."""
     _need_gpu("zp", zp)
     _need_gpu("zq", zq, zp.dtype)
@@ -323,11 +337,12 @@ def av_verify_opd_bwd(zp: torch.Tensor, zq: torch.Tensor, tgt_argmax: torch.Tens
         _need_gpu("bk", bk, torch.int32)
         B = bk.numel()
     if grad is None:
-        grad = torch.empty((R, V), dtype=torch.float32, device=dev)
+        grad = torch.empty((R, V), dtype=grad_dtype, device=dev)
+    _need_gpu("grad", grad, grad_dtype)
     with torch.cuda.device(dev):
         rc = lib().av_verify_opd_bwd(
             _dtype_code(zp), B, int(k), V, R, _ptr(row_off), _ptr(zp), _ptr(zq), _ptr(bk),
             _ptr(tgt_argmax), _ptr(row_stats), float(lam), float(tau), float(grad_scale),
-            _ptr(grad), int(vecs_per_thread), _stream(dev))
+            _ptr(grad), _grad_code(grad_dtype), int(vecs_per_thread), _stream(dev))
     _check("av_verify_opd_bwd", rc)
     return grad

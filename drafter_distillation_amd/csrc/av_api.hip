@@ -23,8 +23,8 @@ int hip_fail(hipError_t e) {
 struct DeviceInfo {
   int cus = 0;
   long long ticks_per_ms = 0;  // wall-clock counter rate
-  int occ[4][2] = {};          // fused-kernel workgroups per CU, per variant and full/general
-                               // form, with the most dynamic LDS a launch uses
+  int occ[4][2][2] = {};       // fused-kernel workgroups per CU, per variant, full/general
+                               // form and gradient type, with the most dynamic LDS a launch uses
 };
 // Most dynamic LDS of a fused launch: ragged offsets of 4095 requests, or the
 // longest-first schedule of avk::kMaxLptRequests requests.
@@ -47,7 +47,8 @@ hipError_t device_info(const DeviceInfo** out) {
     d.ticks_per_ms = khz > 0 ? (long long)khz : 100000;
     for (int v = 0; v < 4 && err == hipSuccess; ++v)
       for (int f = 0; f < 2 && err == hipSuccess; ++f)
-        err = avk::fused_blocks_per_cu((avk::Variant)v, f != 0, kMaxDynLds, &d.occ[v][f]);
+        for (int g = 0; g < 2 && err == hipSuccess; ++g)
+          err = avk::fused_blocks_per_cu((avk::Variant)v, f != 0, g != 0, kMaxDynLds, &d.occ[v][f][g]);
     g_dev_err[dev] = err;
   });
   if (g_dev_err[dev] != hipSuccess) return g_dev_err[dev];
@@ -65,7 +66,7 @@ struct Plan {
 };
 
 int plan_rows(int dtype, int B, int k, int V, int R, const int32_t* row_off, const void* zp,
-              const void* zq, const float* grad, Plan* p) {
+              const void* zq, const void* grad, Plan* p) {
   if (dtype != AV_F32 && dtype != AV_BF16) return AV_EUNSUPPORTED;
   if (B < 1 || k < 1 || k > AV_MAX_K || V < 1 || R < 1) return AV_EINVAL;
   p->ragged = row_off != nullptr;
@@ -240,8 +241,8 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_
                       const void* zp, const void* zq, const int32_t* draft, const int32_t* bk,
                       float lambda, float tau, float grad_scale, int32_t* tgt_argmax,
                       int32_t* acc_len, float* row_loss, float* req_loss, float* total_loss,
-                      float* row_stats, float* grad_zq, int32_t* status, void* workspace,
-                      size_t workspace_bytes, int onchip_limit, void* stream) {
+                      float* row_stats, void* grad_zq, int grad_dtype, int32_t* status,
+                      void* workspace, size_t workspace_bytes, int onchip_limit, void* stream) {
   if (!zp || !zq || !draft || !tgt_argmax || !acc_len || !row_loss || !workspace) return AV_EINVAL;
   if (!row_off && !bk) return AV_EINVAL;
   if (!(lambda >= 0.0f && lambda <= 1.0f)) return AV_EINVAL;
@@ -249,6 +250,7 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_
   if (!finite(grad_scale)) return AV_EINVAL;
   if (row_stats && !aligned16(row_stats)) return AV_EINVAL;
   if (!aligned16(workspace)) return AV_EINVAL;
+  if (grad_zq && grad_dtype != AV_F32 && grad_dtype != AV_BF16) return AV_EUNSUPPORTED;
   Plan p;
   int rc = plan_rows(dtype, B, k, V, R, row_off, zp, zq, grad_zq, &p);
   if (rc != AV_OK) return rc;
@@ -277,7 +279,8 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_
   const int nr_max = avk::variant_row_regs(p.var), nl_max = avk::variant_row_lds(p.var);
   const bool full = nr == nr_max && nl == nl_max &&
                     (long long)p.nvec >= (long long)(nr_max + nl_max) * avk::kRowBlock;
-  const int occ = dev->occ[p.var][full ? 1 : 0];
+  const bool gb = grad_zq && grad_dtype == AV_BF16;
+  const int occ = dev->occ[p.var][full ? 1 : 0][gb ? 1 : 0];
   if (occ < 1 || lds > kMaxDynLds) return AV_EUNSUPPORTED;
   long long grid = (long long)occ * dev->cus;
   if (grid > R) grid = R;
@@ -313,6 +316,7 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_
   a.nl = nl;
   a.ragged = p.ragged ? 1 : 0;
   a.lpt = lpt ? 1 : 0;
+  a.gbf16 = gb ? 1 : 0;
   a.lam = lambda;
   a.tau = tau;
   a.gs = grad_scale;
@@ -323,14 +327,15 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_
 int av_verify_opd_bwd(int dtype, int B, int k, int V, int R, const int32_t* row_off,
                       const void* zp, const void* zq, const int32_t* bk,
                       const int32_t* tgt_argmax, const float* row_stats, float lambda,
-                      float tau, float grad_scale, float* grad_zq, int vecs_per_thread,
-                      void* stream) {
+                      float tau, float grad_scale, void* grad_zq, int grad_dtype,
+                      int vecs_per_thread, void* stream) {
   if (!zp || !zq || !tgt_argmax || !row_stats || !grad_zq) return AV_EINVAL;
   if (!row_off && !bk) return AV_EINVAL;
   if (!(lambda >= 0.0f && lambda <= 1.0f)) return AV_EINVAL;
   if (!(tau > 0.0f)) return AV_EINVAL;
   if (!finite(grad_scale)) return AV_EINVAL;
   if (!aligned16(row_stats)) return AV_EINVAL;
+  if (grad_dtype != AV_F32 && grad_dtype != AV_BF16) return AV_EUNSUPPORTED;
   Plan p;
   int rc = plan_rows(dtype, B, k, V, R, row_off, zp, zq, grad_zq, &p);
   if (rc != AV_OK) return rc;
@@ -352,6 +357,7 @@ int av_verify_opd_bwd(int dtype, int B, int k, int V, int R, const int32_t* row_
   a.C = C;
   a.nvec = p.nvec;
   a.ragged = p.ragged ? 1 : 0;
+  a.gbf16 = grad_dtype == AV_BF16 ? 1 : 0;
   a.lam = lambda;
   a.tau = tau;
   a.gs = grad_scale;

@@ -69,7 +69,7 @@ struct FwdArgs {
   float* req_loss;
   float* total;
   float* stats;
-  float* grad;
+  void* grad;     // [R, V] float32, or bfloat16 when gbf16
   int32_t* status_out;
   uint64_t* ctl;
   uint64_t* rowres;
@@ -83,6 +83,7 @@ struct FwdArgs {
   int nr, nl;    // vectors per thread held in registers / in LDS
   int ragged;
   int lpt;       // dense layout, rows handed out longest first (unverified rows in halves)
+  int gbf16;     // gradient stored as bfloat16
   float lam, tau, gs;
 };
 
@@ -92,8 +93,8 @@ struct BwdArgs {
   const int32_t* bk;
   const int32_t* tgt;
   const float* stats;
-  float* grad;
-  int B, k, V, R, C, nvec, ragged;
+  void* grad;  // float32, or bfloat16 when gbf16
+  int B, k, V, R, C, nvec, ragged, gbf16;
   float lam, tau, gs;
 };
 
@@ -148,7 +149,7 @@ constexpr int kSpecChunkVecs = 2048;  // fewest vectors per chunk
 // full: every on-chip slot of a row is filled (nvec >= (regs + lds) * kRowBlock)
 // and the default on-chip split is used.
 hipError_t launch_fused(Variant v, bool full, const FwdArgs& a, int grid, size_t lds, hipStream_t s);
-hipError_t fused_blocks_per_cu(Variant v, bool full, size_t lds, int* out);
+hipError_t fused_blocks_per_cu(Variant v, bool full, bool gbf16, size_t lds, int* out);
 hipError_t launch_bwd(Variant v, const BwdArgs& a, hipStream_t s);
 hipError_t launch_head(const HeadArgs& a, hipStream_t s);
 hipError_t launch_head_update(const HeadUpdArgs& a, hipStream_t s);

@@ -194,6 +194,14 @@ __device__ __forceinline__ Rsrc row_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// The gradient row of vector-row offset rowv (VEC entries per vector):
+// float32, or bfloat16 (GB).
+template <bool GB, int VEC>
+__device__ __forceinline__ Rsrc grad_rsrc(void* grad, long long rowv, int V) {
+  if constexpr (GB) return row_rsrc((uint16_t*)grad + rowv * VEC, (uint32_t)V * 2u);
+  else return row_rsrc((float*)grad + rowv * VEC, (uint32_t)V * 4u);
+}
+
 template <int VAR>
 struct Tr;
 
@@ -284,6 +292,33 @@ __device__ __forceinline__ void store_vec(float* g, unsigned vi, const float* v)
     store16_nt(g + off, a);
   } else {
     __builtin_nontemporal_store(v[0], g + off);
+  }
+}
+
+// bfloat16 gradient output: each float32 entry rounded to nearest, ties to
+// even (the hardware's packed conversion in the default rounding mode), two
+// per 32-bit word, lower index in the low half.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+__device__ __forceinline__ uint32_t bf16_rne(float x) { return pack_bf16(x, 0.0f) & 0xFFFFu; }
+
+// Stores VEC bfloat16 gradient entries at element vi*VEC of a row.
+template <int VEC>
+__device__ __forceinline__ void store_vec_bf16(uint16_t* g, unsigned vi, const float* v) {
+  const unsigned off = vi * (unsigned)VEC;
+  if constexpr (VEC == 8) {
+    const u32x4 w = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]),
+                     pack_bf16(v[6], v[7])};
+    __builtin_nontemporal_store(w, (u32x4*)(g + off));
+    settle16(w);
+  } else if constexpr (VEC == 4) {
+    const u32x2 w = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+    __builtin_nontemporal_store(w, (u32x2*)(g + off));
+  } else {
+    __builtin_nontemporal_store((uint16_t)bf16_rne(v[0]), g + off);
   }
 }
 
@@ -759,8 +794,23 @@ struct RowIO {
       return slot[wid * 64 + lane];
     }
   }
+  // GB: bfloat16 gradient, at half the float32 byte offsets.
+  template <bool GB = false>
   __device__ __forceinline__ void store(Rsrc g, int s, int nbv, const float* v) const {
-    if constexpr (kHalves) {
+    if constexpr (GB) {
+      const uint32_t so = (uint32_t)s * (SOUT / 2), go = goff >> 1;
+      if constexpr (VEC == 8) {  // four entries from each half of the block: 8 bytes each
+        const u32x2 x = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+        const u32x2 y = {pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7])};
+        __builtin_amdgcn_raw_buffer_store_b64(x, g, go, so, kStoreAux);
+        __builtin_amdgcn_raw_buffer_store_b64(y, g, go + (uint32_t)nbv * 8u, so, kStoreAux);
+      } else if constexpr (VEC == 4) {
+        const u32x2 x = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+        __builtin_amdgcn_raw_buffer_store_b64(x, g, go, so, kStoreAux);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)bf16_rne(v[0]), g, go, so, kStoreAux);
+      }
+    } else if constexpr (kHalves) {
       const f32x4 x = {v[0], v[1], v[2], v[3]};
       const f32x4 y = {v[4], v[5], v[6], v[7]};
       const uint32_t so = (uint32_t)s * SOUT;
@@ -793,13 +843,29 @@ __device__ __forceinline__ void argmax_vec(const typename Tr<VAR>::S& x, int vi,
 
 // Zero gradient of slots [s0, s1) of a row (16-byte pieces where the row
 // allows them; a slot is kRowBlock pieces).
-template <int VAR>
+template <int VAR, bool GB>
 __device__ __forceinline__ void zero_slots(const FwdArgs& a, long long rowv, int tid, int s0, int s1) {
   constexpr int VEC = Tr<VAR>::VEC;
   const int V = opaque_s(a.V);
-  const Rsrc g = row_rsrc(a.grad + rowv * VEC, (uint32_t)V * 4u);
+  const Rsrc g = grad_rsrc<GB, VEC>(a.grad, rowv, V);
   const u32x4 z = {0u, 0u, 0u, 0u};
-  if constexpr (VEC >= 4) {
+  if constexpr (GB) {  // bfloat16 zeros: the same slots, in 8-byte pieces (4 entries)
+    const u32x2 z2 = {0u, 0u};
+    const int n4 = V / 4;
+    const uint32_t off = (uint32_t)tid * 8u;
+    if constexpr (VEC >= 4) {
+#pragma unroll 4
+      for (int s = s0; s < s1; ++s)
+        if (s * kRowBlock + tid < n4)
+          __builtin_amdgcn_raw_buffer_store_b64(z2, g, off, (uint32_t)s * (kRowBlock * 8u), kStoreAux);
+    } else {
+      const uint32_t off1 = (uint32_t)tid * 2u;
+#pragma unroll 4
+      for (int s = s0; s < s1; ++s)
+        if (s * kRowBlock + tid < V)
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0, g, off1, (uint32_t)s * (kRowBlock * 2u), kStoreAux);
+    }
+  } else if constexpr (VEC >= 4) {
     const int n4 = V / 4;  // 16-byte pieces per row
     const uint32_t off = (uint32_t)tid * 16u;
 #pragma unroll 4
@@ -818,7 +884,7 @@ __device__ __forceinline__ void zero_slots(const FwdArgs& a, long long rowv, int
 // gradient.  Half h covers the first / second half of the row's vector slots
 // and of its gradient's 16-byte slots; the half that completes the row second
 // merges the two maxima (the lower index wins ties) and writes the results.
-template <int VAR>
+template <int VAR, bool GB>
 __device__ __forceinline__ void unverified_row(const FwdArgs& a, RowSmem& sm, int row, int par, int half,
                                                uint32_t tag) {
   using T = Tr<VAR>;
@@ -902,12 +968,12 @@ __device__ __forceinline__ void unverified_row(const FwdArgs& a, RowSmem& sm, in
       if (K->stats) store16(K->stats + 4 * (long long)row, (f32x4){0.0f, 0.0f, 0.0f, 0.0f});
     }
   }
-  if (a.grad) zero_slots<VAR>(a, rowv, tid, g0, g1);
+  if (a.grad) zero_slots<VAR, GB>(a, rowv, tid, g0, g1);
 }
 
 // Gradient of one vector (entries at lo.., lo+H..; the label entry Arg gets
 // -gs*lam) -> store through io.
-template <int VAR>
+template <int VAR, bool GB>
 __device__ __forceinline__ void grad_vec(const typename Tr<VAR>::S& xp, const typename Tr<VAR>::S& xq,
                                          const RowIO<VAR>& io, int s, int nbv, const RowK& rk,
                                          const GradK& gk, int Arg, Rsrc g) {
@@ -932,7 +998,7 @@ __device__ __forceinline__ void grad_vec(const typename Tr<VAR>::S& xp, const ty
     for (int e = 0; e < VEC; ++e)
       if (e == el) out[e] = out[e] - gk.fix;
   }
-  io.store(g, s, nbv, out);
+  io.template store<GB>(g, s, nbv, out);
 }
 
 // Clip corrections of one vector: cs += (r + q) - g, ck += r - clip(r).
@@ -988,7 +1054,7 @@ __device__ __forceinline__ void dma_slot(const RowIO<VAR>& io, Rsrc rzp, Rsrc rz
 // rest are streamed (and read again for the gradient).  FULL: nr and nl are
 // the compile-time maxima and the row fills every on-chip slot (the common
 // case of a large vocabulary), so no on-chip access needs a guard.
-template <int VAR, bool FULL>
+template <int VAR, bool FULL, bool GB>
 __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
                                              typename Tr<VAR>::S (*lp)[kRowBlock],
                                              typename Tr<VAR>::S (*lq)[kRowBlock], const Item& it,
@@ -1257,7 +1323,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   // (fast form: through the LDS slots once their resident data is done) ----
   if (a.grad) {
     const GradK gk = grad_consts(opaque_s(a.lam), opaque_s(a.gs), S32);
-    const Rsrc rg = row_rsrc(a.grad + rowv * IO::VEC, (uint32_t)opaque_s(a.V) * 4u);
+    const Rsrc rg = grad_rsrc<GB, IO::VEC>(a.grad, rowv, opaque_s(a.V));
     if constexpr (RING) {
       // Stores of one full register slot's vector (all register slots are full).
       constexpr int kRegStores = NR * (IO::kHalves ? 2 : 1);
@@ -1265,7 +1331,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
       const IO io(opaque(tid));
 #pragma unroll
       for (int l = 0; l < NL; ++l)
-        grad_vec<VAR>(io.lds(lp[l], 64), io.lds(lq[l], 64), io, nr + l, 64, rk, gk, Arg, rg);
+        grad_vec<VAR, GB>(io.lds(lp[l], 64), io.lds(lq[l], 64), io, nr + l, 64, rk, gk, Arg, rg);
       bool regs_done = false;
       for (int s0 = von; s0 < ns; s0 += NL) {
         wait_lds_reads();
@@ -1274,7 +1340,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
           if (s0 + l < ns) dma_slot<VAR, kAuxAgain>(io, rzp, rzq, lp, lq, l, s0 + l, nvec, tid);
         if (!regs_done) {  // the register slots' gradient overlaps the first loads
 #pragma unroll
-          for (int v = 0; v < NR; ++v) grad_vec<VAR>(rp[v], rq[v], io, v, 64, rk, gk, Arg, rg);
+          for (int v = 0; v < NR; ++v) grad_vec<VAR, GB>(rp[v], rq[v], io, v, 64, rk, gk, Arg, rg);
           wait_vmem_but<kRegStores>();
           regs_done = true;
         } else {
@@ -1286,13 +1352,13 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
           if (sl < ns) {
             const int nbv = io.nb(sl, nvec);
             if (io.has(nbv))
-              grad_vec<VAR>(io.lds(lp[l], nbv), io.lds(lq[l], nbv), io, sl, nbv, rk, gk, Arg, rg);
+              grad_vec<VAR, GB>(io.lds(lp[l], nbv), io.lds(lq[l], nbv), io, sl, nbv, rk, gk, Arg, rg);
           }
         }
       }
       if (!regs_done) {
 #pragma unroll
-        for (int v = 0; v < NR; ++v) grad_vec<VAR>(rp[v], rq[v], io, v, 64, rk, gk, Arg, rg);
+        for (int v = 0; v < NR; ++v) grad_vec<VAR, GB>(rp[v], rq[v], io, v, 64, rk, gk, Arg, rg);
       }
       wait_lds_reads();  // the next row's direct loads may overwrite the LDS slots
     } else {
@@ -1304,13 +1370,13 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
 #pragma unroll AV_GU
         for (int s = von; s < nfull; ++s) {
           const S xp = io.template load<kAuxAgain>(rzp, s, 64), xq = io.template load<kAuxAgain>(rzq, s, 64);
-          grad_vec<VAR>(xp, xq, io, s, 64, rk, gk, Arg, rg);
+          grad_vec<VAR, GB>(xp, xq, io, s, 64, rk, gk, Arg, rg);
         }
         if (tail) {
           const int nbv = io.nb(nfull, nvec);
           if (io.has(nbv)) {
             const S xp = io.template load<kAuxAgain>(rzp, nfull, nbv), xq = io.template load<kAuxAgain>(rzq, nfull, nbv);
-            grad_vec<VAR>(xp, xq, io, nfull, nbv, rk, gk, Arg, rg);
+            grad_vec<VAR, GB>(xp, xq, io, nfull, nbv, rk, gk, Arg, rg);
           }
         }
       }
@@ -1320,7 +1386,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
         for (int v = 0; v < NR; ++v) {
           const int nbv = io.nb(v, nvec);
           if (v < nr && io.has(nbv))
-            grad_vec<VAR>(rp[v], rq[v], io, v, nbv, rk, gk, Arg, rg);
+            grad_vec<VAR, GB>(rp[v], rq[v], io, v, nbv, rk, gk, Arg, rg);
         }
       }
       if constexpr (NL > 0) {
@@ -1329,7 +1395,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
         for (int l = 0; l < NL; ++l) {
           const int sl = nr + l, nbv = io.nb(sl, nvec);
           if (l < nl && io.has(nbv))
-            grad_vec<VAR>(io.lds(lp[l], nbv), io.lds(lq[l], nbv), io, sl, nbv, rk, gk, Arg, rg);
+            grad_vec<VAR, GB>(io.lds(lp[l], nbv), io.lds(lq[l], nbv), io, sl, nbv, rk, gk, Arg, rg);
         }
       }
       wait_lds_reads();
@@ -1337,7 +1403,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   }
 }
 
-template <int VAR, bool FULL>
+template <int VAR, bool FULL, bool GB>
 __global__ __launch_bounds__(kRowBlock) void fused_kernel(FwdArgs a) {
   using S = typename Tr<VAR>::S;
   constexpr int NLA = RowCfg<VAR>::NL > 0 ? RowCfg<VAR>::NL : 1;
@@ -1418,8 +1484,8 @@ __global__ __launch_bounds__(kRowBlock) void fused_kernel(FwdArgs a) {
       continue;
     }
     const Item it = map_item(a, sm, s_off, order, key, (int)idx);
-    if (it.verified) verified_row<VAR, FULL>(a, sm, lp, lq, it, par, tag);
-    else unverified_row<VAR>(a, sm, it.row, par, it.half, tag);
+    if (it.verified) verified_row<VAR, FULL, GB>(a, sm, lp, lq, it, par, tag);
+    else unverified_row<VAR, GB>(a, sm, it.row, par, it.half, tag);
   }
   // The workgroup that leaves last sums the request losses, reports the
   // status, resets the dispenser and the done count, and advances the epoch.
@@ -1449,7 +1515,7 @@ __global__ __launch_bounds__(kRowBlock) void fused_kernel(FwdArgs a) {
 // standalone backward
 // ---------------------------------------------------------------------------
 
-template <int VAR>
+template <int VAR, bool GB>
 __global__ __launch_bounds__(kBlock) void bwd_kernel(BwdArgs a) {
   using T = Tr<VAR>;
   using S = typename T::S;
@@ -1468,7 +1534,8 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(BwdArgs a) {
   const int vhi = (int)((uint32_t)(chunk + 1) * (uint32_t)a.nvec / (uint32_t)a.C);
   const void* zp_r = T::row(a.zp, rowv);
   const void* zq_r = T::row(a.zq, rowv);
-  float* g_r = a.grad + rowv * VEC;
+  float* g_r = (float*)a.grad + rowv * VEC;
+  uint16_t* gb_r = (uint16_t*)a.grad + rowv * VEC;
   if (!verified) {
     float z[VEC];
 #pragma unroll
@@ -1476,7 +1543,10 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(BwdArgs a) {
 #pragma unroll
     for (int v = 0; v < NVMAX; ++v) {
       const int vi = vlo + v * kBlock + tid;
-      if (vi < vhi) store_vec<VEC>(g_r, (unsigned)vi, z);
+      if (vi < vhi) {
+        if constexpr (GB) store_vec_bf16<VEC>(gb_r, (unsigned)vi, z);
+        else store_vec<VEC>(g_r, (unsigned)vi, z);
+      }
     }
     return;
   }
@@ -1505,7 +1575,8 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(BwdArgs a) {
         out[e] = grad_entry(q, g, gk);
         if (vi * VEC + e == A) out[e] = out[e] - gk.fix;
       }
-      store_vec<VEC>(g_r, (unsigned)vi, out);
+      if constexpr (GB) store_vec_bf16<VEC>(gb_r, (unsigned)vi, out);
+      else store_vec<VEC>(g_r, (unsigned)vi, out);
     }
   }
 }
@@ -1947,21 +2018,30 @@ __global__ __launch_bounds__(kBlock) void zero_kernel(uint64_t* p, size_t n) {
     p[i] = 0ull;
 }
 
-template <int VAR>
-hipError_t launch_fused_t(bool full, const FwdArgs& a, int grid, size_t lds, hipStream_t s) {
-  if (full) hipLaunchKernelGGL((fused_kernel<VAR, true>), dim3(grid), dim3(kRowBlock), lds, s, a);
-  else hipLaunchKernelGGL((fused_kernel<VAR, false>), dim3(grid), dim3(kRowBlock), lds, s, a);
+template <int VAR, bool GB>
+hipError_t launch_fused_g(bool full, const FwdArgs& a, int grid, size_t lds, hipStream_t s) {
+  if (full) hipLaunchKernelGGL((fused_kernel<VAR, true, GB>), dim3(grid), dim3(kRowBlock), lds, s, a);
+  else hipLaunchKernelGGL((fused_kernel<VAR, false, GB>), dim3(grid), dim3(kRowBlock), lds, s, a);
   return hipGetLastError();
 }
 template <int VAR>
-hipError_t occ_t(bool full, size_t lds, int* out) {
-  if (full) return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, fused_kernel<VAR, true>, kRowBlock, lds);
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, fused_kernel<VAR, false>, kRowBlock, lds);
+hipError_t launch_fused_t(bool full, const FwdArgs& a, int grid, size_t lds, hipStream_t s) {
+  return a.gbf16 ? launch_fused_g<VAR, true>(full, a, grid, lds, s) : launch_fused_g<VAR, false>(full, a, grid, lds, s);
+}
+template <int VAR, bool GB>
+hipError_t occ_g(bool full, size_t lds, int* out) {
+  if (full) return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, fused_kernel<VAR, true, GB>, kRowBlock, lds);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, fused_kernel<VAR, false, GB>, kRowBlock, lds);
+}
+template <int VAR>
+hipError_t occ_t(bool full, bool gb, size_t lds, int* out) {
+  return gb ? occ_g<VAR, true>(full, lds, out) : occ_g<VAR, false>(full, lds, out);
 }
 template <int VAR>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   const unsigned grid = (unsigned)a.R * (unsigned)a.C;
-  hipLaunchKernelGGL(bwd_kernel<VAR>, dim3(grid), dim3(kBlock), 0, s, a);
+  if (a.gbf16) hipLaunchKernelGGL((bwd_kernel<VAR, true>), dim3(grid), dim3(kBlock), 0, s, a);
+  else hipLaunchKernelGGL((bwd_kernel<VAR, false>), dim3(grid), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1976,12 +2056,12 @@ hipError_t launch_fused(Variant v, bool full, const FwdArgs& a, int grid, size_t
   }
 }
 
-hipError_t fused_blocks_per_cu(Variant v, bool full, size_t lds, int* out) {
+hipError_t fused_blocks_per_cu(Variant v, bool full, bool gb, size_t lds, int* out) {
   switch (v) {
-    case kBf16x8: return occ_t<kBf16x8>(full, lds, out);
-    case kBf16x1: return occ_t<kBf16x1>(full, lds, out);
-    case kF32x4: return occ_t<kF32x4>(full, lds, out);
-    default: return occ_t<kF32x1>(full, lds, out);
+    case kBf16x8: return occ_t<kBf16x8>(full, gb, lds, out);
+    case kBf16x1: return occ_t<kBf16x1>(full, gb, lds, out);
+    case kF32x4: return occ_t<kF32x4>(full, gb, lds, out);
+    default: return occ_t<kF32x1>(full, gb, lds, out);
   }
 }
 

@@ -230,7 +230,12 @@ int av_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
  *   tgt_argmax   [R] int32 out;  acc_len [B] int32 out;  row_loss [R] float32 out
  *   req_loss     [B] float32 out or NULL;  total_loss [1] float32 out or NULL
  *   row_stats    [R, 4] float32 out or NULL
- *   grad_zq      [R, V] float32 out or NULL (NULL: forward only)
+ *   grad_zq      [R, V] out or NULL (NULL: forward only), of type grad_dtype
+ *   grad_dtype   AV_F32 (the default: float32 entries) or AV_BF16 (each
+ *                float32 entry rounded to nearest-even bfloat16, half the
+ *                bytes written; the pages do not fix the gradient's
+ *                precision, and bfloat16 rounding alone exceeds a 1e-3
+ *                relative tolerance, so float32 is the reference form)
  *   status       [1] int32 out or NULL: 0, or AV_DEV_* bits found on device
  *   workspace    >= av_workspace_bytes(B, k, R) bytes, zeroed once by
  *                av_workspace_init before first use
@@ -243,8 +248,8 @@ int av_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
  * V < 1, R inconsistent with the layout, lambda outside [0, 1] or NaN, tau
  * <= 0 or NaN, grad_scale non-finite, workspace too small, negative
  * onchip_limit, row_stats or workspace not 16-byte aligned.
- * AV_EUNSUPPORTED: dtype other than AV_F32/AV_BF16; ragged with B > 4095
- * (the offsets are cached on chip); R*V >= 2^46.
+ * AV_EUNSUPPORTED: dtype or grad_dtype other than AV_F32/AV_BF16; ragged
+ * with B > 4095 (the offsets are cached on chip); R*V >= 2^46.
  */
 int av_verify_opd_fwd(int dtype, int B, int k, int V, int R,
                       const int32_t* row_off, const void* zp, const void* zq,
@@ -252,7 +257,7 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R,
                       float lambda, float tau, float grad_scale,
                       int32_t* tgt_argmax, int32_t* acc_len, float* row_loss,
                       float* req_loss, float* total_loss, float* row_stats,
-                      float* grad_zq, int32_t* status,
+                      void* grad_zq, int grad_dtype, int32_t* status,
                       void* workspace, size_t workspace_bytes,
                       int onchip_limit, void* stream);
 
@@ -265,7 +270,8 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R,
  * the same float32 steps as the fused pass, so both write identical bits.
  *   row_off, zp, zq, bk, dtype, B, k, V, R: as for av_verify_opd_fwd
  *   tgt_argmax [R] int32, row_stats [R, 4] float32: from the forward call
- *   grad_zq    [R, V] float32 out (unverified dense rows are zeroed)
+ *   grad_zq    [R, V] out of type grad_dtype (AV_F32 or AV_BF16, as for
+ *              av_verify_opd_fwd; unverified dense rows are zeroed)
  *   vecs_per_thread  0 = automatic; otherwise the most 16-byte vectors one
  *              thread handles per work item (raised where needed so that a
  *              row has at most 64 items)
@@ -279,7 +285,7 @@ int av_verify_opd_bwd(int dtype, int B, int k, int V, int R,
                       const int32_t* row_off, const void* zp, const void* zq,
                       const int32_t* bk, const int32_t* tgt_argmax,
                       const float* row_stats, float lambda, float tau,
-                      float grad_scale, float* grad_zq,
+                      float grad_scale, void* grad_zq, int grad_dtype,
                       int vecs_per_thread, void* stream);
 
 /* Human-readable text for an av_status value (static storage). */

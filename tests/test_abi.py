@@ -55,12 +55,13 @@ def test_workspace_bytes():
 def fwd(**kw):
     a = dict(dtype=1, B=2, k=4, V=64, R=8, row_off=NULL, zp=P, zq=P, draft=P, bk=P, lam=0.5,
              tau=0.1, gs=1.0, tgt=P, acc=P, row_loss=P, req_loss=NULL, total=NULL, stats=P,
-             grad=P, status=NULL, ws=P, ws_bytes=1 << 30, vecs=0, stream=NULL)
+             grad=P, gdt=0, status=NULL, ws=P, ws_bytes=1 << 30, vecs=0, stream=NULL)
     a.update(kw)
     return _lib.lib().av_verify_opd_fwd(
         a["dtype"], a["B"], a["k"], a["V"], a["R"], a["row_off"], a["zp"], a["zq"], a["draft"],
         a["bk"], a["lam"], a["tau"], a["gs"], a["tgt"], a["acc"], a["row_loss"], a["req_loss"],
-        a["total"], a["stats"], a["grad"], a["status"], a["ws"], a["ws_bytes"], a["vecs"], a["stream"])
+        a["total"], a["stats"], a["grad"], a["gdt"], a["status"], a["ws"], a["ws_bytes"], a["vecs"],
+        a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -94,6 +95,7 @@ def fwd(**kw):
     (dict(dtype=2), dd.AV_EUNSUPPORTED),
     (dict(row_off=P, B=5000, R=5000), dd.AV_EUNSUPPORTED),  # ragged offsets cached on chip
     (dict(B=1 << 16, k=64, R=1 << 22, V=1 << 24), dd.AV_EUNSUPPORTED),  # R*V >= 2^46
+    (dict(gdt=3), dd.AV_EUNSUPPORTED),                      # gradient type
 ])
 def test_fwd_rejects_bad_arguments_on_host(kw, code):
     assert fwd(**kw) == code
@@ -133,14 +135,15 @@ def test_length_head_rejects_bad_arguments_on_host(kw, code):
     (dict(dtype=5), dd.AV_EUNSUPPORTED),
     (dict(V=64 * 256 * 64 + 8), dd.AV_EUNSUPPORTED),     # more than 64 items per row
     (dict(dtype=0, V=64 * 256 * 32 + 4), dd.AV_EUNSUPPORTED),
+    (dict(gdt=2), dd.AV_EUNSUPPORTED),
 ])
 def test_bwd_rejects_bad_arguments_on_host(kw, code):
     a = dict(dtype=1, B=2, k=4, V=64, R=8, row_off=NULL, zp=P, zq=P, bk=P, tgt=P, stats=P,
-             lam=0.5, tau=0.1, gs=1.0, grad=P, vecs=0, stream=NULL)
+             lam=0.5, tau=0.1, gs=1.0, grad=P, gdt=0, vecs=0, stream=NULL)
     a.update(kw)
     rc = _lib.lib().av_verify_opd_bwd(a["dtype"], a["B"], a["k"], a["V"], a["R"], a["row_off"],
                                       a["zp"], a["zq"], a["bk"], a["tgt"], a["stats"], a["lam"],
-                                      a["tau"], a["gs"], a["grad"], a["vecs"], a["stream"])
+                                      a["tau"], a["gs"], a["grad"], a["gdt"], a["vecs"], a["stream"])
     assert rc == code
 
 
