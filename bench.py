@@ -50,7 +50,7 @@ def kernel_sha() -> str:
     return hsh.hexdigest()[:16]
 
 
-def algorithmic_bytes(B, k, V, H, R, Rv, elem=2):
+def algorithmic_bytes(B, k, V, H, R, Rv, elem=2, gelem=4):
     """Bytes the pass must move at least once (per step).
 
     fused kernel: zp of every stored row (target argmax is defined for all),
@@ -58,7 +58,7 @@ def algorithmic_bytes(B, k, V, H, R, Rv, elem=2):
     unverified rows are part of the output), draft tokens, b_k, and the small
     per-row / per-request outputs.  length head: h, w, rate and b_k.
     """
-    fused = (elem * V * R + elem * V * Rv + 4 * V * R
+    fused = (elem * V * R + elem * V * Rv + gelem * V * R
              + 4 * R + 4 * B            # draft, bk
              + 4 * R + 4 * R + 16 * R   # argmax, row loss, row stats
              + 4 * B + 4 * B + 4)       # acc, req loss, total
@@ -408,6 +408,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-requests", type=int, default=128)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--grad", choices=["f32", "bf16"], default="f32",
+                    help="gradient output type of the fused pass (default float32)")
     ap.add_argument("--workload", choices=["concurrent", "head_update", "spec"], default="concurrent",
                     help="concurrent: the fused verify+OPD step (default); head_update: the "
                          "length head's online update; spec: sampling-based verification")
@@ -468,7 +470,8 @@ def main():
         "req_loss": torch.empty(B, dtype=torch.float32, device=dev),
         "total_loss": torch.empty(1, dtype=torch.float32, device=dev),
         "row_stats": torch.empty((R, 4), dtype=torch.float32, device=dev),
-        "grad": torch.empty((R, V), dtype=torch.float32, device=dev),
+        "grad": torch.empty((R, V), dtype=torch.bfloat16 if args.grad == "bf16" else torch.float32,
+                            device=dev),
         "status": torch.empty(1, dtype=torch.int32, device=dev),
     }
     stream = torch.cuda.current_stream(dev)
@@ -478,7 +481,7 @@ def main():
         if ev0 is not None:
             ev0.record(stream)
         dd.av_verify_opd_fwd(zp, zq, draft, k=k, bk=bk, lam=w.lam, tau=w.tau,
-                             grad_scale=1.0, out=out)
+                             grad_scale=1.0, out=out, grad_dtype=out["grad"].dtype)
         if ev1 is not None:
             ev1.record(stream)
 
@@ -500,16 +503,18 @@ def main():
     if int(out["status"].item()) != 0:
         raise RuntimeError(f"device status {int(out['status'].item())}")
 
-    fused_b, head_b = algorithmic_bytes(B, k, V, H, R, Rv)
+    gelem = 2 if args.grad == "bf16" else 4
+    fused_b, head_b = algorithmic_bytes(B, k, V, H, R, Rv, gelem=gelem)
     ms_step = elapsed / args.steps * 1e3
     value = (fused_b + head_b) * args.steps / elapsed / 1e9
     kern_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
     kern_avg_ms = sum(kern_ms) / len(kern_ms)
     achieved = fused_b / (kern_avg_ms * 1e-3) / 1e9
-    unverified_grad = 4 * V * (R - Rv)
+    unverified_grad = gelem * V * (R - Rv)
 
+    metric = METRIC if args.grad == "f32" else METRIC + ", bf16 gradient"
     line = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -522,10 +527,10 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": "concurrent: B=128 requests, k=16, V=151936, bf16 logits, fp32 gradient, "
+            "workload": f"concurrent: B=128 requests, k=16, V=151936, bf16 logits, {args.grad} gradient, "
                         "b_k from the length head (H=4096), lambda=0.5, tau=0.1",
             "B": B, "k": k, "V": V, "H": H, "rows": R, "verified_rows": Rv,
-            "logits": "bf16", "grad": "f32", "seed": args.seed,
+            "logits": "bf16", "grad": args.grad, "seed": args.seed,
             "rows_per_s": round(R / (ms_step * 1e-3), 1),
             "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
             "bytes_per_step": fused_b + head_b,
@@ -539,7 +544,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(),
+            "traffic": measured_traffic() if args.grad == "f32" else None,
         },
     }
     if not args.no_cpu_baseline:
