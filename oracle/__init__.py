@@ -31,3 +31,4 @@ from .spec_sample import (  # noqa: F401
     residual_keys,
     spec_verify,
 )
+from .lm_head import lm_head_backward  # noqa: F401
