@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     av_head_update_workspace_bytes,
     av_length_head,
     av_length_head_update,
+    av_lm_head_bwd,
     av_spec_verify,
     av_spec_workspace_bytes,
     av_status_str,

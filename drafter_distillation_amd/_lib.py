@@ -51,6 +51,9 @@ _SIGS = {
     "av_spec_workspace_bytes": (_sz, [_i, _i]),
     "av_spec_verify": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_uint64, _vp, _vp,
                             _vp, _vp, _vp, _sz, _vp]),
+    "av_lm_head_workspace_bytes": (_sz, []),
+    "av_lm_head_bwd": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "av_lm_head_last_error": (ctypes.c_char_p, []),
     "av_status_str": (ctypes.c_char_p, [_i]),
     "av_last_hip_error": (ctypes.c_char_p, []),
 }
@@ -238,6 +241,39 @@ def av_spec_verify(zp: torch.Tensor, zq: torch.Tensor, draft: torch.Tensor, u: t
             _ptr(status), _ptr(ws), ws.numel(), _stream(dev))
     _check("av_spec_verify", rc)
     return o
+
+
+def av_lm_head_bwd(dz: torch.Tensor, w: Optional[torch.Tensor], hid: Optional[torch.Tensor], *,
+                   want_d_hid: bool = True, want_d_w: bool = True) -> dict:
+    """Backward of the drafter's LM head (see include/av.h): dz [R, V], w
+    [V, H], hid [R, H] bfloat16 GPU tensors.  Returns dict(d_hid [R, H],
+    d_w [V, H]) float32 (None where not wanted)."""
+    _need_gpu("dz", dz, torch.bfloat16)
+    R, V = dz.shape
+    H = None
+    if want_d_hid:
+        _need_gpu("w", w, torch.bfloat16)
+        if w.shape[0] != V:
+            raise ValueError("w must be [V, H]")
+        H = w.shape[1]
+    if want_d_w:
+        _need_gpu("hid", hid, torch.bfloat16)
+        if hid.shape[0] != R or (H is not None and hid.shape[1] != H):
+            raise ValueError("hid must be [R, H]")
+        H = hid.shape[1]
+    dev = dz.device
+    d_hid = torch.empty((R, H), dtype=torch.float32, device=dev) if want_d_hid else None
+    d_w = torch.empty((V, H), dtype=torch.float32, device=dev) if want_d_w else None
+    with torch.cuda.device(dev):
+        nbytes = int(lib().av_lm_head_workspace_bytes())
+        ws = workspace(dev, nbytes, kind="lm_head")
+        rc = lib().av_lm_head_bwd(R, V, H, _ptr(dz), _ptr(w) if want_d_hid else None,
+                                  _ptr(hid) if want_d_w else None, _ptr(d_hid), _ptr(d_w), _ptr(ws),
+                                  ws.numel(), _stream(dev))
+    if rc == AV_EHIP:
+        raise AVError("av_lm_head_bwd", rc, lib().av_lm_head_last_error().decode())
+    _check("av_lm_head_bwd", rc)
+    return dict(d_hid=d_hid, d_w=d_w)
 
 
 def _grad_code(dtype: torch.dtype) -> int:

@@ -22,7 +22,11 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libav.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["av_kernels.hip", "av_api.hip"]
+SOURCES = ["av_kernels.hip", "av_api.hip", "av_lmhead.hip"]
+
+# Libraries the shared library links: hipBLASLt runs the LM-head backward's
+# plain GEMMs (csrc/av_lmhead.hip).
+LINK_FLAGS = ["-lhipblaslt"]
 
 # Per-source flags.  The kernels take no NaN input (the header puts
 # non-finite logits outside the contract), so float max needs no NaN-quieting
@@ -79,7 +83,7 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB + ".tmp"
-    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, *LINK_FLAGS, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

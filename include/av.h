@@ -288,6 +288,32 @@ int av_verify_opd_bwd(int dtype, int B, int k, int V, int R,
                       float grad_scale, void* grad_zq, int grad_dtype,
                       int vecs_per_thread, void* stream);
 
+/*
+ * av_lm_head_bwd -- backward of the drafter's LM head, the step after this
+ * pass in training (Pith review page, "Axiom & Free-Parameter Ledger":
+ * drafter updates with AdamW).  The head maps the hidden state of each
+ * position to its logits, zq[r, v] = sum_h hid[r, h] W[v, h] (no bias); with
+ * dz = d loss / d zq from av_verify_opd_fwd (grad_dtype AV_BF16):
+ *     d_hid[r, h] = sum_v dz[r, v] W[v, h]
+ *     d_w[v, h]   = sum_r dz[r, v] hid[r, h]
+ * Two bfloat16 GEMMs with float32 accumulation on the matrix cores
+ * (hipBLASLt).
+ *   dz     [R, V] bfloat16 row-major;  w [V, H] bfloat16;  hid [R, H] bfloat16
+ *   d_hid  [R, H] float32 out, or NULL (then w may be NULL)
+ *   d_w    [V, H] float32 out, or NULL (then hid may be NULL)
+ *   workspace, workspace_bytes: scratch for the GEMMs, may be NULL / 0;
+ *          av_lm_head_workspace_bytes() is the size the library asks for
+ * All pointers are device pointers; asynchronous on `stream`.  Errors:
+ * AV_EINVAL for R, V or H < 1, NULL dz, or an output without its operand;
+ * AV_EUNSUPPORTED if no GEMM kernel fits the shape and workspace; AV_EHIP
+ * for a runtime or hipBLASLt failure (text in av_lm_head_last_error()).
+ */
+size_t av_lm_head_workspace_bytes(void);
+int av_lm_head_bwd(int R, int V, int H, const void* dz, const void* w, const void* hid,
+                   float* d_hid, float* d_w, void* workspace, size_t workspace_bytes,
+                   void* stream);
+const char* av_lm_head_last_error(void);
+
 /* Human-readable text for an av_status value (static storage). */
 const char* av_status_str(int status);
 

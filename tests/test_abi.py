@@ -207,6 +207,23 @@ def test_spec_rejects_bad_arguments_on_host(kw, code):
     assert rc == code
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(dz=NULL), dd.AV_EINVAL),
+    (dict(R=0), dd.AV_EINVAL),
+    (dict(V=0), dd.AV_EINVAL),
+    (dict(H=0), dd.AV_EINVAL),
+    (dict(w=NULL), dd.AV_EINVAL),        # d_hid wanted without its operand
+    (dict(hid=NULL), dd.AV_EINVAL),      # d_w wanted without its operand
+    (dict(ws=NULL), dd.AV_EINVAL),       # workspace bytes without a workspace
+])
+def test_lm_head_rejects_bad_arguments_on_host(kw, code):
+    a = dict(R=4, V=64, H=16, dz=P, w=P, hid=P, d_hid=P, d_w=P, ws=P, ws_bytes=1 << 20, stream=NULL)
+    a.update(kw)
+    rc = _lib.lib().av_lm_head_bwd(a["R"], a["V"], a["H"], a["dz"], a["w"], a["hid"], a["d_hid"],
+                                   a["d_w"], a["ws"], a["ws_bytes"], a["stream"])
+    assert rc == code
+
+
 def test_head_update_workspace_bytes():
     assert dd.av_head_update_workspace_bytes(128) == 128 * 16
     assert dd.av_head_update_workspace_bytes(0) == 0

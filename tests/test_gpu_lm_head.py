@@ -1,0 +1,86 @@
+"""GPU parity of the drafter LM head's backward (through the C ABI) against
+the float64 oracle.  bfloat16 inputs are exact in both; the GPU accumulates
+in float32, so each entry must lie within 1e-3 of the sum of the absolute
+products that form it (the task's relative bar, applied to the scale of the
+sum rather than to a result that may cancel)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def av():
+    import drafter_distillation_amd as dd
+    dd.lib()
+    return dd
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def bf16_tensor(shape, seed, scale):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    return (torch.randn(shape, generator=g, device="cuda") * scale).to(torch.bfloat16)
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def check(got, ref, scale, what):
+    bad = np.abs(got - ref) > 1e-3 * scale + 1e-30
+    assert not bad.any(), f"{what}: {int(bad.sum())} entries off"
+
+
+@pytest.mark.parametrize("R,V,H", [(1, 1, 1), (5, 300, 64), (3, 1001, 17), (64, 151936, 256)])
+def test_shapes(av, R, V, H):
+    say(f"lm head bwd R={R} V={V} H={H}")
+    dz = bf16_tensor((R, V), 1, 1e-3)
+    w = bf16_tensor((V, H), 2, 0.02)
+    hid = bf16_tensor((R, H), 3, 1.0)
+    out = av.av_lm_head_bwd(dz, w, hid)
+    torch.cuda.synchronize()
+    dzh, wh, hh = host(dz), host(w), host(hid)
+    ref_h, ref_w = oracle.lm_head_backward(dzh, wh, hh)
+    check(host(out["d_hid"]), ref_h, np.abs(dzh) @ np.abs(wh), "d_hid")
+    check(host(out["d_w"]), ref_w, np.abs(dzh).T @ np.abs(hh), "d_w")
+
+
+def test_one_output_only(av):
+    dz = bf16_tensor((4, 500), 4, 1e-3)
+    w = bf16_tensor((500, 32), 5, 0.02)
+    hid = bf16_tensor((4, 32), 6, 1.0)
+    a = av.av_lm_head_bwd(dz, w, None, want_d_w=False)
+    b = av.av_lm_head_bwd(dz, None, hid, want_d_hid=False)
+    c = av.av_lm_head_bwd(dz, w, hid)
+    torch.cuda.synchronize()
+    assert a["d_w"] is None and b["d_hid"] is None
+    assert torch.equal(a["d_hid"], c["d_hid"]) and torch.equal(b["d_w"], c["d_w"])
+
+
+def test_full_size_sampled(av):
+    """The concurrent workload's shape: R=2048 rows, V=151936, H=4096."""
+    R, V, H = 2048, 151936, 4096
+    say("lm head bwd full size")
+    dz = bf16_tensor((R, V), 7, 1e-4)
+    w = bf16_tensor((V, H), 8, 0.02)
+    hid = bf16_tensor((R, H), 9, 1.0)
+    out = av.av_lm_head_bwd(dz, w, hid)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    wh = host(w)
+    for r in rng.choice(R, 3, replace=False):
+        dzr = host(dz[r])
+        ref = dzr @ wh
+        check(host(out["d_hid"][r]), ref, np.abs(dzr) @ np.abs(wh), f"d_hid row {r}")
+    hh = host(hid)
+    for v in rng.choice(V, 8, replace=False):
+        dzv = host(dz[:, v])
+        ref = dzv @ hh
+        check(host(out["d_w"][v]), ref, np.abs(dzv) @ np.abs(hh), f"d_w row {v}")
