@@ -20,6 +20,10 @@ to w, bias and h, one AdamW step per call.
 `--workload spec` measures sampling-based verification (av_spec_verify) of
 the same workload: acceptance tests with the caller's uniforms on every
 verified row, and the residual draw at each request's first rejection.
+
+`--workload lm_head` measures the backward of the drafter's LM head
+(av_lm_head_bwd) on the same workload's bfloat16 gradient: d hid = dz W and
+d W = dz^T hid with R=2048, V=151936, H=4096 (two bf16 GEMMs).
 """
 
 from __future__ import annotations
@@ -400,6 +404,98 @@ def bench_spec(args):
     print(json.dumps(line), flush=True)
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def bench_lm_head(args):
+    import numpy as np
+    import torch
+
+    import drafter_distillation_amd as dd
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dd.lib()
+    w = synth.make("concurrent", seed=args.seed)
+    B, k, V, R = w.B, w.k, w.V, w.R
+    H = 4096
+    zp = torch.from_numpy(w.zp.view(np.int16)).view(torch.bfloat16).to(dev)
+    zq = torch.from_numpy(w.zq.view(np.int16)).view(torch.bfloat16).to(dev)
+    bk = torch.empty(B, dtype=torch.int32, device=dev)
+    dd.av_length_head(torch.from_numpy(w.h).to(dev), torch.from_numpy(w.w).to(dev), w.bias, w.gamma, k,
+                      bk_out=bk)
+    dz = dd.av_verify_opd_fwd(zp, zq, torch.from_numpy(w.draft).to(dev), k=k, bk=bk, lam=w.lam, tau=w.tau,
+                              grad_scale=1.0 / float(torch.clamp(bk, 1, k).sum()),
+                              grad_dtype=torch.bfloat16)["grad"]
+    del zp, zq
+    g = torch.Generator(device=dev).manual_seed(args.seed)
+    wl = (torch.randn((V, H), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    hid = torch.randn((R, H), generator=g, device=dev).to(torch.bfloat16)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        dd.av_lm_head_bwd(dz, wl, hid)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        dd.av_lm_head_bwd(dz, wl, hid)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs)
+    flops = 2 * 2.0 * R * V * H
+    tflops = flops / (kern_ms * 1e-3) / 1e12
+    line = {
+        "metric": "drafter LM-head backward (d hid = dz W, d W = dz^T hid) TFLOP/s at R=2048, V=151936, "
+                  "H=4096 bf16",
+        "value": round(tflops, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "lm_head: dz = the concurrent workload's bf16 gradient (R=2048, V=151936), "
+                        "W [V, 4096] and hid [2048, 4096] random bf16, float32 accumulation and outputs",
+            "R": R, "V": V, "H": H, "flop_per_step": flops, "kernel_ms": round(kern_ms, 4),
+            "gemms": "hipBLASLt",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 1),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        from threadpoolctl import threadpool_limits
+        rows = 2
+        dzh = dz[:rows].float().cpu().numpy().astype(np.float64)
+        wh = wl.float().cpu().numpy().astype(np.float64)
+        hh = hid[:rows].float().cpu().numpy().astype(np.float64)
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            oracle.lm_head_backward(dzh, wh, hh)
+            dt = time.perf_counter() - t0
+        sflops = 2 * 2.0 * rows * V * H
+        line["cpu_baseline"] = {
+            "value": round(sflops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} of {R} rows (both products), float64 numpy, one thread, {dt:.1f} s",
+            "seconds": round(dt, 3)}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -410,7 +506,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--grad", choices=["f32", "bf16"], default="f32",
                     help="gradient output type of the fused pass (default float32)")
-    ap.add_argument("--workload", choices=["concurrent", "head_update", "spec"], default="concurrent",
+    ap.add_argument("--workload", choices=["concurrent", "head_update", "spec", "lm_head"],
+                    default="concurrent",
                     help="concurrent: the fused verify+OPD step (default); head_update: the "
                          "length head's online update; spec: sampling-based verification")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -439,6 +536,9 @@ def main():
         return
     if args.workload == "spec":
         bench_spec(args)
+        return
+    if args.workload == "lm_head":
+        bench_lm_head(args)
         return
 
     import numpy as np
