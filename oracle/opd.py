@@ -33,7 +33,11 @@ notes with its reason):
     paper) on request.  gamma scales the predicted rate before rounding.
   * clipping acts on each entry's value r_j = q_j (log q_j - log p_j); the
     interval [-tau, tau] is closed and a clipped entry passes no gradient.
-  * lam weights the cross-entropy term; temperature 1 (plain softmax).
+  * lam weights the cross-entropy term.
+  * the ledger's temperature belongs to the reverse-KL term: there p and q
+    are softmax(z / T) of both logit rows; the hard-label cross-entropy uses
+    the plain softmax of zq (T = 1 for it), and no T^2 factor is applied.
+    The default T = 1 is the ledger's value.
   * only verified positions (i < b_k) carry loss; the loss is a plain sum.
   * argmax ties go to the lowest index.
   * acc counts accepted draft tokens, so the pages' tau_accept = acc + 1.
@@ -130,17 +134,19 @@ def accepted_length(draft: Sequence[int], target: Sequence[int], b: int) -> int:
 @dataclasses.dataclass
 class RowTerms:
     argmax: int
-    lse_p: float
-    lse_q: float
+    lse_p: float          # log-sum-exp of zp / T
+    lse_q: float          # log-sum-exp of zq / T
     ce: float
     klc: float
     S: float
     loss: float
     grad: np.ndarray      # d loss / d zq, already multiplied by grad_scale
-    q: np.ndarray
+    q: np.ndarray         # softmax(zq / T)
     ell: np.ndarray       # log q - log p
     r: np.ndarray         # q * ell (entry-wise reverse-KL terms)
     c: np.ndarray         # bool: entry inside [-tau, tau]
+    lse_q1: float = 0.0   # log-sum-exp of zq (temperature 1, the CE term)
+    temperature: float = 1.0
 
 
 def _logsumexp(z: np.ndarray) -> float:
@@ -150,28 +156,35 @@ def _logsumexp(z: np.ndarray) -> float:
 
 def row_terms(zp_row: np.ndarray, zq_row: np.ndarray, lam: float, tau: float,
               grad_scale: float = 1.0,
-              clip_override: Optional[Dict[int, bool]] = None) -> RowTerms:
+              clip_override: Optional[Dict[int, bool]] = None,
+              temperature: float = 1.0) -> RowTerms:
     """Loss and gradient of one verified position.
 
-    p = softmax(zp), q = softmax(zq) at temperature 1; the hard label is the
-    target's greedy choice a.  With ell_j = log q_j - log p_j and
+    In the reverse-KL term p = softmax(zp / T) and q = softmax(zq / T); the
+    hard label is the target's greedy choice a, scored by the plain
+    softmax q1 = softmax(zq).  With ell_j = log q_j - log p_j and
     r_j = q_j * ell_j (taken as 0 where q_j underflows to 0):
-        loss = lam * (-log q_a) + (1 - lam) * sum_j clip(r_j, -tau, tau).
-    Differentiating with d log q_j / d zq_m = [j = m] - q_m:
-        d r_j / d zq_m = q_j ([j = m] - q_m) (ell_j + 1),
+        loss = lam * (-log q1_a) + (1 - lam) * sum_j clip(r_j, -tau, tau).
+    Differentiating with d log q_j / d zq_m = ([j = m] - q_m) / T:
+        d r_j / d zq_m = q_j ([j = m] - q_m) (ell_j + 1) / T,
     so with c_j = [-tau <= r_j <= tau] and S = sum_j c_j q_j (ell_j + 1):
-        d loss / d zq_m = lam (q_m - [m = a]) + (1 - lam) q_m (c_m (ell_m + 1) - S).
+        d loss / d zq_m = lam (q1_m - [m = a]) + (1 - lam) q_m (c_m (ell_m + 1) - S) / T.
+    At T = 1, q1 = q and this is the plain pass.
 
     clip_override forces c_j for chosen entries (used only to accept either
     branch for entries whose |r_j| sits on tau to within rounding).
     """
     zp = np.asarray(zp_row, dtype=np.float64)
     zq = np.asarray(zq_row, dtype=np.float64)
+    t = float(temperature)
+    if not t > 0.0:
+        raise ValueError("temperature must be positive")
     a = target_argmax(zp)
-    lse_p = _logsumexp(zp)
-    lse_q = _logsumexp(zq)
-    logp = zp - lse_p
-    logq = zq - lse_q
+    zpt, zqt = zp / t, zq / t
+    lse_p = _logsumexp(zpt)
+    lse_q = _logsumexp(zqt)
+    logp = zpt - lse_p
+    logq = zqt - lse_q
     q = np.exp(logq)
     ell = logq - logp
     r = np.where(q > 0.0, q * ell, 0.0)
@@ -180,16 +193,18 @@ def row_terms(zp_row: np.ndarray, zq_row: np.ndarray, lam: float, tau: float,
         c = c.copy()
         for j, v in clip_override.items():
             c[j] = bool(v)
-    ce = -float(logq[a])
+    lse_q1 = _logsumexp(zq)
+    q1 = np.exp(zq - lse_q1)
+    ce = lse_q1 - float(zq[a])
     clipped = np.where(c, r, np.clip(r, -tau, tau))
     klc = math.fsum(clipped.tolist())
     S = math.fsum(np.where(c, q * (ell + 1.0), 0.0).tolist())
     loss = lam * ce + (1.0 - lam) * klc
     onehot = np.zeros_like(q)
     onehot[a] = 1.0
-    grad = grad_scale * (lam * (q - onehot) + (1.0 - lam) * q * (np.where(c, ell + 1.0, 0.0) - S))
+    grad = grad_scale * (lam * (q1 - onehot) + (1.0 - lam) * q * (np.where(c, ell + 1.0, 0.0) - S) / t)
     return RowTerms(argmax=a, lse_p=lse_p, lse_q=lse_q, ce=ce, klc=klc, S=S, loss=loss,
-                    grad=grad, q=q, ell=ell, r=r, c=c)
+                    grad=grad, q=q, ell=ell, r=r, c=c, lse_q1=lse_q1, temperature=t)
 
 
 def clip_margin(r: np.ndarray, tau: float) -> np.ndarray:
@@ -204,7 +219,7 @@ def clip_margin(r: np.ndarray, tau: float) -> np.ndarray:
 def verify_opd(zp: np.ndarray, zq: np.ndarray, draft: np.ndarray, *, k: int,
                lam: float, tau: float, grad_scale: float = 1.0,
                bk: Optional[np.ndarray] = None, row_off: Optional[np.ndarray] = None,
-               want_grad: bool = True) -> dict:
+               want_grad: bool = True, temperature: float = 1.0) -> dict:
     """Reference results for B draft blocks.
 
     Dense layout (row_off is None): row b*k+i holds position i of request b;
@@ -214,7 +229,9 @@ def verify_opd(zp: np.ndarray, zq: np.ndarray, draft: np.ndarray, *, k: int,
 
     Unverified rows get the target argmax (the greedy choice is still
     defined) but no loss and a zero gradient; only verified positions enter
-    the OPD sum and the acceptance scan.
+    the OPD sum and the acceptance scan.  temperature applies to the
+    reverse-KL term (see row_terms); row_stats holds (lse of zp / T, lse of
+    zq / T, S, clipped KL) and lse_q1 the log-sum-exp of zq itself.
     """
     zp = np.asarray(zp, dtype=np.float64)
     zq = np.asarray(zq, dtype=np.float64)
@@ -232,6 +249,7 @@ def verify_opd(zp: np.ndarray, zq: np.ndarray, draft: np.ndarray, *, k: int,
     tgt = np.empty(R, dtype=np.int64)
     row_loss = np.zeros(R)
     row_stats = np.zeros((R, 4))
+    lse_q1 = np.zeros(R)
     verified = np.zeros(R, dtype=bool)
     grad = np.zeros((R, V)) if want_grad else None
     acc = np.empty(B, dtype=np.int64)
@@ -240,10 +258,11 @@ def verify_opd(zp: np.ndarray, zq: np.ndarray, draft: np.ndarray, *, k: int,
         for i in range(n):
             r = r0 + i
             if i < bkb:
-                t = row_terms(zp[r], zq[r], lam, tau, grad_scale)
+                t = row_terms(zp[r], zq[r], lam, tau, grad_scale, temperature=temperature)
                 tgt[r] = t.argmax
                 row_loss[r] = t.loss
                 row_stats[r] = (t.lse_p, t.lse_q, t.S, t.klc)
+                lse_q1[r] = t.lse_q1
                 verified[r] = True
                 if want_grad:
                     grad[r] = t.grad
@@ -253,4 +272,5 @@ def verify_opd(zp: np.ndarray, zq: np.ndarray, draft: np.ndarray, *, k: int,
         req_loss[b] = math.fsum(row_loss[r0:r0 + n].tolist())
     total = math.fsum(req_loss.tolist())
     return dict(tgt_argmax=tgt, acc_len=acc, row_loss=row_loss, req_loss=req_loss,
-                total_loss=total, row_stats=row_stats, grad=grad, verified=verified)
+                total_loss=total, row_stats=row_stats, grad=grad, verified=verified,
+                lse_q1=lse_q1)
