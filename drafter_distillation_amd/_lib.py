@@ -44,9 +44,9 @@ _SIGS = {
                                    _d, _d, _d, _d, _d, _vp, _vp, _vp, _vp, _sz, _vp]),
     "av_workspace_bytes": (_sz, [_i, _i, _i]),
     "av_workspace_init": (_i, [_vp, _sz, _vp]),
-    "av_verify_opd_fwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _f, _f, _f,
-                               _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _sz, _i, _vp]),
-    "av_verify_opd_bwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _f, _f, _f,
+    "av_verify_opd_fwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _f, _f, _f, _f,
+                               _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _sz, _i, _vp]),
+    "av_verify_opd_bwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f, _f, _f, _f,
                                _vp, _i, _i, _vp]),
     "av_spec_workspace_bytes": (_sz, [_i, _i]),
     "av_spec_verify": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_uint64, _vp, _vp,
@@ -296,16 +296,19 @@ def av_verify_opd_fwd(zp: torch.Tensor, zq: torch.Tensor, draft: torch.Tensor, *
                       bk: Optional[torch.Tensor] = None, row_off: Optional[torch.Tensor] = None,
                       lam: float, tau: float, grad_scale: float = 1.0, want_grad: bool = True,
                       want_stats: bool = True, onchip_limit: int = 0,
-                      grad_dtype: torch.dtype = torch.float32,
+                      grad_dtype: torch.dtype = torch.float32, temperature: float = 1.0,
+                      want_lse_q1: Optional[bool] = None,
                       out: Optional[dict] = None) -> dict:
     """Fused verify + OPD pass (see include/av.h).
 
     zp, zq: [R, V] bf16/f32; draft: [R] int32; dense layout with bk [B] int32,
     or ragged layout with row_off [B+1] int32.  Returns a dict of output
     tensors (tgt_argmax, acc_len, row_loss, req_loss, total_loss, row_stats,
-    grad, status); `out` may supply preallocated tensors under those names.
-    grad_dtype: torch.float32 (default) or torch.bfloat16 (each entry
-    rounded to nearest-even bfloat16).
+    grad, status, and lse_q1 when requested); `out` may supply preallocated
+    tensors under those names.  grad_dtype: torch.float32 (default) or
+    torch.bfloat16 (each entry rounded to nearest-even bfloat16).
+    temperature: of the reverse-KL term; want_lse_q1 defaults to
+    want_stats and temperature != 1 (the backward needs lse_q1 then).
     """
     _need_gpu("zp", zp)
     _need_gpu("zq", zq, zp.dtype)
@@ -337,6 +340,9 @@ def av_verify_opd_fwd(zp: torch.Tensor, zq: torch.Tensor, draft: torch.Tensor, *
     req_loss = get("req_loss", (B,), torch.float32)
     total = get("total_loss", (1,), torch.float32)
     stats = get("row_stats", (R, 4), torch.float32) if want_stats else None
+    if want_lse_q1 is None:
+        want_lse_q1 = want_stats and float(temperature) != 1.0
+    lse1 = get("lse_q1", (R,), torch.float32) if want_lse_q1 else None
     grad = get("grad", (R, V), grad_dtype) if want_grad else None
     if grad is not None:
         _need_gpu("grad", grad, grad_dtype)
@@ -346,8 +352,8 @@ def av_verify_opd_fwd(zp: torch.Tensor, zq: torch.Tensor, draft: torch.Tensor, *
         ws = workspace(dev, nbytes)
         rc = lib().av_verify_opd_fwd(
             _dtype_code(zp), B, int(k), V, R, _ptr(row_off), _ptr(zp), _ptr(zq), _ptr(draft),
-            _ptr(bk), float(lam), float(tau), float(grad_scale), _ptr(tgt), _ptr(acc),
-            _ptr(row_loss), _ptr(req_loss), _ptr(total), _ptr(stats), _ptr(grad),
+            _ptr(bk), float(lam), float(tau), float(grad_scale), float(temperature), _ptr(tgt), _ptr(acc),
+            _ptr(row_loss), _ptr(req_loss), _ptr(total), _ptr(stats), _ptr(lse1), _ptr(grad),
             _grad_code(grad_dtype), _ptr(status), _ptr(ws), ws.numel(), int(onchip_limit), _stream(dev))
     _check("av_verify_opd_fwd", rc)
     return o
@@ -358,12 +364,18 @@ def av_verify_opd_bwd(zp: torch.Tensor, zq: torch.Tensor, tgt_argmax: torch.Tens
                       row_off: Optional[torch.Tensor] = None, lam: float, tau: float,
                       grad_scale: float = 1.0, vecs_per_thread: int = 0,
                       grad: Optional[torch.Tensor] = None,
-                      grad_dtype: torch.dtype = torch.float32) -> torch.Tensor:
-    """Gradient alone from saved statistics (see include/av.h)."""
+                      grad_dtype: torch.dtype = torch.float32, temperature: float = 1.0,
+                      lse_q1: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Gradient alone from saved statistics (see include/av.h); lse_q1 from
+    the forward call is required when temperature != 1."""
     _need_gpu("zp", zp)
     _need_gpu("zq", zq, zp.dtype)
     _need_gpu("tgt_argmax", tgt_argmax, torch.int32)
     _need_gpu("row_stats", row_stats, torch.float32)
+    if lse_q1 is not None:
+        _need_gpu("lse_q1", lse_q1, torch.float32)
+        if lse_q1.shape != (zp.shape[0],):
+            raise ValueError("lse_q1 must be [R]")
     R, V = zp.shape
     dev = zp.device
     if row_off is not None:
@@ -378,7 +390,7 @@ def av_verify_opd_bwd(zp: torch.Tensor, zq: torch.Tensor, tgt_argmax: torch.Tens
     with torch.cuda.device(dev):
         rc = lib().av_verify_opd_bwd(
             _dtype_code(zp), B, int(k), V, R, _ptr(row_off), _ptr(zp), _ptr(zq), _ptr(bk),
-            _ptr(tgt_argmax), _ptr(row_stats), float(lam), float(tau), float(grad_scale),
-            _ptr(grad), _grad_code(grad_dtype), int(vecs_per_thread), _stream(dev))
+            _ptr(tgt_argmax), _ptr(row_stats), _ptr(lse_q1), float(lam), float(tau), float(grad_scale),
+            float(temperature), _ptr(grad), _grad_code(grad_dtype), int(vecs_per_thread), _stream(dev))
     _check("av_verify_opd_bwd", rc)
     return grad

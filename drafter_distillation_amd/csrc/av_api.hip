@@ -23,8 +23,9 @@ int hip_fail(hipError_t e) {
 struct DeviceInfo {
   int cus = 0;
   long long ticks_per_ms = 0;  // wall-clock counter rate
-  int occ[4][2][2] = {};       // fused-kernel workgroups per CU, per variant, full/general
-                               // form and gradient type, with the most dynamic LDS a launch uses
+  int occ[4][2][2][2] = {};    // fused-kernel workgroups per CU, per variant, full/general
+                               // form, gradient type and plain/tempered form, with the most
+                               // dynamic LDS a launch uses
 };
 // Most dynamic LDS of a fused launch: ragged offsets of 4095 requests, or the
 // longest-first schedule of avk::kMaxLptRequests requests.
@@ -48,7 +49,9 @@ hipError_t device_info(const DeviceInfo** out) {
     for (int v = 0; v < 4 && err == hipSuccess; ++v)
       for (int f = 0; f < 2 && err == hipSuccess; ++f)
         for (int g = 0; g < 2 && err == hipSuccess; ++g)
-          err = avk::fused_blocks_per_cu((avk::Variant)v, f != 0, g != 0, kMaxDynLds, &d.occ[v][f][g]);
+          for (int t = 0; t < 2 && err == hipSuccess; ++t)
+            err = avk::fused_blocks_per_cu((avk::Variant)v, f != 0, g != 0, t != 0, kMaxDynLds,
+                                           &d.occ[v][f][g][t]);
     g_dev_err[dev] = err;
   });
   if (g_dev_err[dev] != hipSuccess) return g_dev_err[dev];
@@ -98,6 +101,20 @@ int plan_chunks(const Plan& p, int vecs_per_thread, int* C) {
 }
 
 bool finite(float x) { return isfinite(x); }
+
+// Temperature constants of the kernels: 1 / T and log2(e) / T, each the
+// float32 rounding of the float64 value.
+struct Temp {
+  bool tm;
+  float inv_t, inv_tl;
+};
+bool temperature_ok(float t, Temp* out) {
+  if (!(t > 0.0f) || !finite(t)) return false;
+  out->tm = t != 1.0f;
+  out->inv_t = (float)(1.0 / (double)t);
+  out->inv_tl = (float)(1.4426950408889634074 / (double)t);
+  return true;
+}
 
 }  // namespace
 
@@ -239,15 +256,18 @@ int av_spec_verify(int dtype, int B, int k, int V, int R, const int32_t* row_off
 
 int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_off,
                       const void* zp, const void* zq, const int32_t* draft, const int32_t* bk,
-                      float lambda, float tau, float grad_scale, int32_t* tgt_argmax,
-                      int32_t* acc_len, float* row_loss, float* req_loss, float* total_loss,
-                      float* row_stats, void* grad_zq, int grad_dtype, int32_t* status,
-                      void* workspace, size_t workspace_bytes, int onchip_limit, void* stream) {
+                      float lambda, float tau, float grad_scale, float temperature,
+                      int32_t* tgt_argmax, int32_t* acc_len, float* row_loss, float* req_loss,
+                      float* total_loss, float* row_stats, float* lse_q1, void* grad_zq,
+                      int grad_dtype, int32_t* status, void* workspace, size_t workspace_bytes,
+                      int onchip_limit, void* stream) {
   if (!zp || !zq || !draft || !tgt_argmax || !acc_len || !row_loss || !workspace) return AV_EINVAL;
   if (!row_off && !bk) return AV_EINVAL;
   if (!(lambda >= 0.0f && lambda <= 1.0f)) return AV_EINVAL;
   if (!(tau > 0.0f)) return AV_EINVAL;
   if (!finite(grad_scale)) return AV_EINVAL;
+  Temp tp;
+  if (!temperature_ok(temperature, &tp)) return AV_EINVAL;
   if (row_stats && !aligned16(row_stats)) return AV_EINVAL;
   if (!aligned16(workspace)) return AV_EINVAL;
   if (grad_zq && grad_dtype != AV_F32 && grad_dtype != AV_BF16) return AV_EUNSUPPORTED;
@@ -280,7 +300,7 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_
   const bool full = nr == nr_max && nl == nl_max &&
                     (long long)p.nvec >= (long long)(nr_max + nl_max) * avk::kRowBlock;
   const bool gb = grad_zq && grad_dtype == AV_BF16;
-  const int occ = dev->occ[p.var][full ? 1 : 0][gb ? 1 : 0];
+  const int occ = dev->occ[p.var][full ? 1 : 0][gb ? 1 : 0][tp.tm ? 1 : 0];
   if (occ < 1 || lds > kMaxDynLds) return AV_EUNSUPPORTED;
   long long grid = (long long)occ * dev->cus;
   if (grid > R) grid = R;
@@ -298,6 +318,7 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_
   a.req_loss = req_loss;
   a.total = total_loss;
   a.stats = row_stats;
+  a.lse1 = lse_q1;
   a.grad = grad_zq;
   a.status_out = status;
   a.ctl = (uint64_t*)ws;
@@ -317,23 +338,29 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_
   a.ragged = p.ragged ? 1 : 0;
   a.lpt = lpt ? 1 : 0;
   a.gbf16 = gb ? 1 : 0;
+  a.tm = tp.tm ? 1 : 0;
   a.lam = lambda;
   a.tau = tau;
   a.gs = grad_scale;
+  a.inv_t = tp.inv_t;
+  a.inv_tl = tp.inv_tl;
   e = avk::launch_fused(p.var, full, a, (int)grid, lds, (hipStream_t)stream);
   return e == hipSuccess ? AV_OK : hip_fail(e);
 }
 
 int av_verify_opd_bwd(int dtype, int B, int k, int V, int R, const int32_t* row_off,
                       const void* zp, const void* zq, const int32_t* bk,
-                      const int32_t* tgt_argmax, const float* row_stats, float lambda,
-                      float tau, float grad_scale, void* grad_zq, int grad_dtype,
-                      int vecs_per_thread, void* stream) {
+                      const int32_t* tgt_argmax, const float* row_stats, const float* lse_q1,
+                      float lambda, float tau, float grad_scale, float temperature, void* grad_zq,
+                      int grad_dtype, int vecs_per_thread, void* stream) {
   if (!zp || !zq || !tgt_argmax || !row_stats || !grad_zq) return AV_EINVAL;
   if (!row_off && !bk) return AV_EINVAL;
   if (!(lambda >= 0.0f && lambda <= 1.0f)) return AV_EINVAL;
   if (!(tau > 0.0f)) return AV_EINVAL;
   if (!finite(grad_scale)) return AV_EINVAL;
+  Temp tp;
+  if (!temperature_ok(temperature, &tp)) return AV_EINVAL;
+  if (tp.tm && !lse_q1) return AV_EINVAL;
   if (!aligned16(row_stats)) return AV_EINVAL;
   if (grad_dtype != AV_F32 && grad_dtype != AV_BF16) return AV_EUNSUPPORTED;
   Plan p;
@@ -349,6 +376,7 @@ int av_verify_opd_bwd(int dtype, int B, int k, int V, int R, const int32_t* row_
   a.bk = bk;
   a.tgt = tgt_argmax;
   a.stats = row_stats;
+  a.lse1 = lse_q1;
   a.grad = grad_zq;
   a.B = B;
   a.k = k;
@@ -358,9 +386,12 @@ int av_verify_opd_bwd(int dtype, int B, int k, int V, int R, const int32_t* row_
   a.nvec = p.nvec;
   a.ragged = p.ragged ? 1 : 0;
   a.gbf16 = grad_dtype == AV_BF16 ? 1 : 0;
+  a.tm = tp.tm ? 1 : 0;
   a.lam = lambda;
   a.tau = tau;
   a.gs = grad_scale;
+  a.inv_t = tp.inv_t;
+  a.inv_tl = tp.inv_tl;
   hipError_t e = avk::launch_bwd(p.var, a, (hipStream_t)stream);
   return e == hipSuccess ? AV_OK : hip_fail(e);
 }

@@ -85,6 +85,10 @@ struct FwdArgs {
   int lpt;       // dense layout, rows handed out longest first (unverified rows in halves)
   int gbf16;     // gradient stored as bfloat16
   float lam, tau, gs;
+  // temperature of the reverse-KL term
+  float* lse1;          // [R] log-sum-exp of zq at temperature 1, or NULL
+  int tm;               // T differs from 1
+  float inv_t, inv_tl;  // 1 / T and log2(e) / T (float32 roundings of the float64 values)
 };
 
 struct BwdArgs {
@@ -93,9 +97,11 @@ struct BwdArgs {
   const int32_t* bk;
   const int32_t* tgt;
   const float* stats;
+  const float* lse1;  // [R] log-sum-exp of zq at temperature 1 (read when tm)
   void* grad;  // float32, or bfloat16 when gbf16
-  int B, k, V, R, C, nvec, ragged, gbf16;
+  int B, k, V, R, C, nvec, ragged, gbf16, tm;
   float lam, tau, gs;
+  float inv_t, inv_tl;
 };
 
 struct HeadArgs {
@@ -148,8 +154,9 @@ constexpr int kSpecChunkVecs = 2048;  // fewest vectors per chunk
 
 // full: every on-chip slot of a row is filled (nvec >= (regs + lds) * kRowBlock)
 // and the default on-chip split is used.
+// a.tm selects the tempered form of the kernels (fused and backward).
 hipError_t launch_fused(Variant v, bool full, const FwdArgs& a, int grid, size_t lds, hipStream_t s);
-hipError_t fused_blocks_per_cu(Variant v, bool full, bool gbf16, size_t lds, int* out);
+hipError_t fused_blocks_per_cu(Variant v, bool full, bool gbf16, bool tm, size_t lds, int* out);
 hipError_t launch_bwd(Variant v, const BwdArgs& a, hipStream_t s);
 hipError_t launch_head(const HeadArgs& a, hipStream_t s);
 hipError_t launch_head_update(const HeadUpdArgs& a, hipStream_t s);

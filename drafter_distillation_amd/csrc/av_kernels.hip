@@ -364,40 +364,65 @@ __device__ __forceinline__ void bstore_vec(Rsrc g, uint32_t voff, uint32_t soff,
 // per-entry math shared by the fused and the standalone backward pass
 // ---------------------------------------------------------------------------
 
+// Tempered form (TM): the reverse-KL term compares softmax(zp / T) with
+// softmax(zq / T); s = 1 / T and sL = log2(e) / T scale the logits there,
+// lse_p and lse_q are the log-sum-exps of the scaled rows, and the hard
+// cross-entropy keeps the plain softmax of zq (its log-sum-exp lse_q1).
 struct RowK {
-  float lseqL, delta, tau;
+  float lseqL, delta, tau, s, sL;
 };
-__device__ __forceinline__ RowK row_consts(float lse_p, float lse_q, float tau) {
+template <bool TM>
+__device__ __forceinline__ RowK row_consts(float lse_p, float lse_q, float tau, float s, float sL) {
   RowK k;
   k.lseqL = lse_q * kLog2e;
   k.delta = lse_q - lse_p;
   k.tau = tau;
+  k.s = TM ? s : 1.0f;
+  k.sL = TM ? sL : kLog2e;
   return k;
 }
-// q_j = exp(zq_j - lse_q); r_j = q_j (log q_j - log p_j), with the log-ratio
-// formed from the logits; g_j = c_j (r_j + q_j) = c_j q_j (ell_j + 1).
+// q_j = exp(s zq_j - lse_q); r_j = q_j (log q_j - log p_j), with the
+// log-ratio formed from the logits, s (zq_j - zp_j) - (lse_q - lse_p);
+// g_j = c_j (r_j + q_j) = c_j q_j (ell_j + 1).
+template <bool TM>
 __device__ __forceinline__ void opd_entry(float zp, float zq, const RowK& k, float& q, float& r,
                                           float& g) {
-  q = __builtin_amdgcn_exp2f(__builtin_fmaf(zq, kLog2e, -k.lseqL));
-  const float ell = (zq - zp) - k.delta;
+  q = __builtin_amdgcn_exp2f(__builtin_fmaf(zq, TM ? k.sL : kLog2e, -k.lseqL));
+  const float ell = TM ? __builtin_fmaf(k.s, zq - zp, -k.delta) : (zq - zp) - k.delta;
   r = q * ell;
   g = (__builtin_fabsf(r) <= k.tau) ? (r + q) : 0.0f;
 }
 
-// d loss / d zq_j = gs [lam (q_j - [j = a]) + (1 - lam)(g_j - S q_j)]
-//                 = A q_j + Bc g_j - [j = a] gs lam
+// d loss / d zq_j = gs [lam (q1_j - [j = a]) + (1 - lam) s (g_j - S q_j)]
+// (q1 = softmax(zq); at T = 1, q1 = q and s = 1):
+//   T = 1:  A q_j + Bc g_j - [j = a] gs lam,  A = gs (lam - (1 - lam) S)
+//   TM:     C1 q1_j + A q_j + Bc g_j - [j = a] gs lam,  A = -gs (1 - lam) s S
 struct GradK {
-  float a, b, fix;
+  float a, b, fix, c1, l1L;
 };
-__device__ __forceinline__ GradK grad_consts(float lam, float gs, float S) {
+template <bool TM>
+__device__ __forceinline__ GradK grad_consts(float lam, float gs, float S, float s, float lse1) {
   GradK g;
-  g.a = gs * (lam - (1.0f - lam) * S);
-  g.b = gs * (1.0f - lam);
+  if constexpr (TM) {
+    g.b = gs * (1.0f - lam) * s;
+    g.a = -g.b * S;
+    g.c1 = gs * lam;
+    g.l1L = lse1 * kLog2e;
+  } else {
+    g.a = gs * (lam - (1.0f - lam) * S);
+    g.b = gs * (1.0f - lam);
+    g.c1 = 0.0f;
+    g.l1L = 0.0f;
+  }
   g.fix = gs * lam;
   return g;
 }
-__device__ __forceinline__ float grad_entry(float q, float g, const GradK& c) {
-  return __builtin_fmaf(c.a, q, c.b * g);
+template <bool TM>
+__device__ __forceinline__ float grad_entry(float q, float g, float zq, const GradK& c) {
+  const float kl = __builtin_fmaf(c.a, q, c.b * g);
+  if constexpr (TM)
+    return __builtin_fmaf(c.c1, __builtin_amdgcn_exp2f(__builtin_fmaf(zq, kLog2e, -c.l1L)), kl);
+  return kl;
 }
 
 // ---------------------------------------------------------------------------
@@ -435,6 +460,7 @@ struct RowSmem {
   int cumu[AV_MAX_K + 1];     //   unverified rows at positions < p
   uint64_t exitw;
   uint32_t tag;
+  float f1[2][kRowWaves];     // tempered form: sq1
 };
 
 // Running statistics of one thread's part of a row.
@@ -444,6 +470,8 @@ struct RowAcc {
   float za;      // zq at that index
   float mq, sq;  // max of zq, sum exp(zq - mq)
   float kq;      // sum exp(zq - mq) (zq - zp): the reverse KL, once normalised
+  float sq1;     // tempered form: sum exp(zq - mq) at temperature 1 (the sums
+                 // above then scale exponents by 1 / T; kq's difference does not)
   float mq_on, mq_st;  // per region (on chip / streamed): max zq
   float pm_on, pm_st;  // per region: max exp(zq - mq) |zq - zp| (mq: running max)
 };
@@ -456,6 +484,7 @@ __device__ __forceinline__ void acc_init(RowAcc& A) {
   A.mq = -INFINITY;
   A.sq = 0.0f;
   A.kq = 0.0f;
+  A.sq1 = 0.0f;
   A.mq_on = -INFINITY;
   A.mq_st = -INFINITY;
   A.pm_on = 0.0f;
@@ -470,12 +499,17 @@ __device__ __forceinline__ int entry_index(int lo, int H, int e) {
 
 // Folds one vector (entries at lo.., lo+H..) into the running statistics
 // (online normaliser: sums are rescaled when a larger maximum appears).
-// `onchip` selects the clip-bound region of the vector.
-template <int VAR>
+// `onchip` selects the clip-bound region of the vector.  TM: exponents are
+// scaled by sL = log2(e) / T, and sq1 sums the unscaled ones; they are formed
+// as (z - max) sL, whose only rounding is that of a product that vanishes at
+// the maximum (z sL - max sL would round max sL, which grows like 1 / T, and
+// scale every term of the thread by that error).
+template <int VAR, bool TM>
 __device__ __forceinline__ void acc_vec(const typename Tr<VAR>::S& xp, const typename Tr<VAR>::S& xq,
-                                        int lo, int H, RowAcc& A, bool onchip) {
+                                        int lo, int H, RowAcc& A, bool onchip, float sL) {
   using T = Tr<VAR>;
   constexpr int VEC = T::VEC;
+  const float L = TM ? sL : kLog2e;
   float vp = T::at(xp, 0), vq = T::at(xq, 0);
 #pragma unroll
   for (int e = 1; e < VEC; ++e) {
@@ -498,26 +532,36 @@ __device__ __forceinline__ void acc_vec(const typename Tr<VAR>::S& xp, const typ
     }
   }
   const float np = fmaxf(A.mp, vp);
-  A.sp *= __builtin_amdgcn_exp2f((A.mp - np) * kLog2e);
+  A.sp *= __builtin_amdgcn_exp2f((A.mp - np) * L);
   A.mp = np;
-  const float npL = np * kLog2e;
+  const float npL = np * L;
 #pragma unroll
-  for (int e = 0; e < VEC; ++e)
-    A.sp += __builtin_amdgcn_exp2f(__builtin_fmaf(T::at(xp, e), kLog2e, -npL));
+  for (int e = 0; e < VEC; ++e) {
+    if constexpr (TM) A.sp += __builtin_amdgcn_exp2f((T::at(xp, e) - np) * L);
+    else A.sp += __builtin_amdgcn_exp2f(__builtin_fmaf(T::at(xp, e), L, -npL));
+  }
   const float nq = fmaxf(A.mq, vq);
-  const float sc = __builtin_amdgcn_exp2f((A.mq - nq) * kLog2e);
+  const float sc = __builtin_amdgcn_exp2f((A.mq - nq) * L);
   A.sq *= sc;
   A.kq *= sc;
+  if constexpr (TM) A.sq1 *= __builtin_amdgcn_exp2f((A.mq - nq) * kLog2e);
   const float scb = fmaxf(sc, kRescaleFloor);
   A.pm_on *= scb;
   A.pm_st *= scb;
   A.mq = nq;
-  const float nqL = nq * kLog2e;
+  const float nqL = nq * L;
   float pm = 0.0f;
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
     const float q = T::at(xq, e), p = T::at(xp, e);
-    const float eq = __builtin_amdgcn_exp2f(__builtin_fmaf(q, kLog2e, -nqL));
+    float eq;
+    if constexpr (TM) {
+      const float dq = q - nq;
+      eq = __builtin_amdgcn_exp2f(dq * L);
+      A.sq1 += __builtin_amdgcn_exp2f(dq * kLog2e);
+    } else {
+      eq = __builtin_amdgcn_exp2f(__builtin_fmaf(q, kLog2e, -nqL));
+    }
     const float d = q - p;
     A.sq += eq;
     A.kq = __builtin_fmaf(eq, d, A.kq);
@@ -534,18 +578,21 @@ __device__ __forceinline__ void acc_vec(const typename Tr<VAR>::S& xp, const typ
 
 // (m, s) <- log-sum-exp merge; commutative, so xor butterflies leave the same
 // bits in every lane.  Empty parts (s == 0) contribute nothing.
+// L scales the exponents (log2(e), or log2(e) / T for tempered sums).
 __device__ __forceinline__ void lse_merge(float& m, float& s, float& k, float om, float os,
-                                          float ok) {
+                                          float ok, float L = kLog2e) {
   const float M = fmaxf(m, om);
-  const float fa = (s == 0.0f) ? 0.0f : __builtin_amdgcn_exp2f((m - M) * kLog2e);
-  const float fb = (os == 0.0f) ? 0.0f : __builtin_amdgcn_exp2f((om - M) * kLog2e);
+  const float fa = (s == 0.0f) ? 0.0f : __builtin_amdgcn_exp2f((m - M) * L);
+  const float fb = (os == 0.0f) ? 0.0f : __builtin_amdgcn_exp2f((om - M) * L);
   m = M;
   s = s * fa + os * fb;
   k = k * fa + ok * fb;
 }
 
 // One butterfly step over the row statistics (not the per-thread bounds).
-__device__ __forceinline__ void merge_step(RowAcc& A, int o) {
+template <bool TM>
+__device__ __forceinline__ void merge_step(RowAcc& A, int o, float sL) {
+  const float L = TM ? sL : kLog2e;
   const float omp = __shfl_xor(A.mp, o), osp = __shfl_xor(A.sp, o);
   const int obi = __shfl_xor(A.bi, o);
   const float oza = __shfl_xor(A.za, o);
@@ -554,9 +601,14 @@ __device__ __forceinline__ void merge_step(RowAcc& A, int o) {
     A.bi = obi;
     A.za = oza;
   }
+  if constexpr (TM) {  // before mq moves: same maxima, unscaled exponents
+    const float osq1 = __shfl_xor(A.sq1, o);
+    float m1 = A.mq, dummy = 0.0f;
+    lse_merge(m1, A.sq1, dummy, omq, osq1, 0.0f);
+  }
   float dummy = 0.0f;
-  lse_merge(A.mp, A.sp, dummy, omp, osp, 0.0f);
-  lse_merge(A.mq, A.sq, A.kq, omq, osq, okq);
+  lse_merge(A.mp, A.sp, dummy, omp, osp, 0.0f, L);
+  lse_merge(A.mq, A.sq, A.kq, omq, osq, okq, L);
 }
 
 // Sum of the first 16 lanes, in a fixed order, broadcast from lane 0.
@@ -966,6 +1018,7 @@ __device__ __forceinline__ void unverified_row(const FwdArgs& a, RowSmem& sm, in
       K->row_loss[row] = 0.0f;
       K->tgt[row] = I;
       if (K->stats) store16(K->stats + 4 * (long long)row, (f32x4){0.0f, 0.0f, 0.0f, 0.0f});
+      if (K->lse1) K->lse1[row] = 0.0f;
     }
   }
   if (a.grad) zero_slots<VAR, GB>(a, rowv, tid, g0, g1);
@@ -973,7 +1026,7 @@ __device__ __forceinline__ void unverified_row(const FwdArgs& a, RowSmem& sm, in
 
 // Gradient of one vector (entries at lo.., lo+H..; the label entry Arg gets
 // -gs*lam) -> store through io.
-template <int VAR, bool GB>
+template <int VAR, bool GB, bool TM>
 __device__ __forceinline__ void grad_vec(const typename Tr<VAR>::S& xp, const typename Tr<VAR>::S& xq,
                                          const RowIO<VAR>& io, int s, int nbv, const RowK& rk,
                                          const GradK& gk, int Arg, Rsrc g) {
@@ -983,8 +1036,8 @@ __device__ __forceinline__ void grad_vec(const typename Tr<VAR>::S& xp, const ty
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
     float q, r, gg;
-    opd_entry(T::at(xp, e), T::at(xq, e), rk, q, r, gg);
-    out[e] = grad_entry(q, gg, gk);
+    opd_entry<TM>(T::at(xp, e), T::at(xq, e), rk, q, r, gg);
+    out[e] = grad_entry<TM>(q, gg, T::at(xq, e), gk);
   }
   const int lo = io.lo(s);
   int el = -1;  // entry that holds the label, if any
@@ -1001,17 +1054,31 @@ __device__ __forceinline__ void grad_vec(const typename Tr<VAR>::S& xp, const ty
   io.template store<GB>(g, s, nbv, out);
 }
 
-// Clip corrections of one vector: cs += (r + q) - g, ck += r - clip(r).
-template <int VAR>
+// Row maximum of zq and log2 of its normaliser sum exp(s (zq - m)): the
+// correction pass forms q_j from them.
+struct FineK {
+  float mq, l2s;
+};
+
+// Clip corrections of one vector: cs += (r + q) - g, ck += r - clip(r).  The
+// indicator c_j is the gradient pass's (same float32 steps); the values use
+// q_j = exp2((zq_j - m) sL - log2 sum), exact to a few ulp also for a dominant
+// entry of a row with large logits, where the corrections nearly cancel the
+// row's unclipped sums (the gradient pass's form rounds lse to float32 first).
+template <int VAR, bool TM>
 __device__ __forceinline__ void clip_vec(const typename Tr<VAR>::S& xp, const typename Tr<VAR>::S& xq,
-                                         const RowK& rk, float& cs, float& ck) {
+                                         const RowK& rk, const FineK& fk, float& cs, float& ck) {
   using T = Tr<VAR>;
 #pragma unroll
   for (int e = 0; e < T::VEC; ++e) {
+    const float zp = T::at(xp, e), zq = T::at(xq, e);
     float q, r, g;
-    opd_entry(T::at(xp, e), T::at(xq, e), rk, q, r, g);
-    cs += (r + q) - g;
-    ck += r - __builtin_amdgcn_fmed3f(r, -rk.tau, rk.tau);
+    opd_entry<TM>(zp, zq, rk, q, r, g);
+    const float qf = __builtin_amdgcn_exp2f(__builtin_fmaf(zq - fk.mq, rk.sL, -fk.l2s));
+    const float ell = TM ? __builtin_fmaf(rk.s, zq - zp, -rk.delta) : (zq - zp) - rk.delta;
+    const float rf = qf * ell;
+    cs += (__builtin_fabsf(r) <= rk.tau) ? 0.0f : rf + qf;
+    ck += rf - __builtin_amdgcn_fmed3f(rf, -rk.tau, rk.tau);
   }
 }
 
@@ -1054,7 +1121,7 @@ __device__ __forceinline__ void dma_slot(const RowIO<VAR>& io, Rsrc rzp, Rsrc rz
 // rest are streamed (and read again for the gradient).  FULL: nr and nl are
 // the compile-time maxima and the row fills every on-chip slot (the common
 // case of a large vocabulary), so no on-chip access needs a guard.
-template <int VAR, bool FULL, bool GB>
+template <int VAR, bool FULL, bool GB, bool TM>
 __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
                                              typename Tr<VAR>::S (*lp)[kRowBlock],
                                              typename Tr<VAR>::S (*lq)[kRowBlock], const Item& it,
@@ -1077,6 +1144,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   const int nfull = nvec / kRowBlock;  // slots in which every thread has a vector
   const bool tail = nfull >= von;      // the partial slot nfull (if any) is streamed
   const float tau = opaque_s(a.tau);
+  const float sL = TM ? opaque_s(a.inv_tl) : kLog2e;
 
   // ---- sweep 1: read the row once; keep its on-chip slots, fold every
   // vector into the running statistics.  Fast form: the streamed slots pass
@@ -1150,8 +1218,8 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
         if (sl < ns) {
           const int nbv = io.nb(sl, nvec);
           if (io.has(nbv))
-            acc_vec<VAR>(io.lds(lp[2 * h + j], nbv), io.lds(lq[2 * h + j], nbv), io.lo(sl), io.H(nbv), A,
-                         false);
+            acc_vec<VAR, TM>(io.lds(lp[2 * h + j], nbv), io.lds(lq[2 * h + j], nbv), io.lo(sl), io.H(nbv), A,
+                         false, sL);
         }
       }
       wait_lds_reads();  // this half is free again
@@ -1174,13 +1242,13 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
 #pragma unroll AV_SU
     for (int s = von; s < nfull; ++s) {
       const S xp = io.template load<kAuxFirst>(rzp, s, 64), xq = io.template load<kAuxFirst>(rzq, s, 64);
-      acc_vec<VAR>(xp, xq, io.lo(s), io.H(64), A, false);
+      acc_vec<VAR, TM>(xp, xq, io.lo(s), io.H(64), A, false, sL);
     }
     if (tail) {
       const int nbv = io.nb(nfull, nvec);
       if (io.has(nbv)) {
         const S xp = io.template load<kAuxFirst>(rzp, nfull, nbv), xq = io.template load<kAuxFirst>(rzq, nfull, nbv);
-        acc_vec<VAR>(xp, xq, io.lo(nfull), io.H(nbv), A, false);
+        acc_vec<VAR, TM>(xp, xq, io.lo(nfull), io.H(nbv), A, false, sL);
       }
     }
   }
@@ -1192,7 +1260,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
     for (int v = 0; v < NR; ++v) {
       const int nbv = io.nb(v, nvec);
       if (v < nr && io.has(nbv))
-        acc_vec<VAR>(rp[v], rq[v], io.lo(v), io.H(nbv), A, true);
+        acc_vec<VAR, TM>(rp[v], rq[v], io.lo(v), io.H(nbv), A, true, sL);
     }
   }
   if constexpr (NL > 0) {
@@ -1202,7 +1270,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
     for (int l = 0; l < NL; ++l) {
       const int sl = nr + l, nbv = io.nb(sl, nvec);
       if (l < nl && io.has(nbv))
-        acc_vec<VAR>(io.lds(lp[l], nbv), io.lds(lq[l], nbv), io.lo(sl), io.H(nbv), A, true);
+        acc_vec<VAR, TM>(io.lds(lp[l], nbv), io.lds(lq[l], nbv), io.lo(sl), io.H(nbv), A, true, sL);
     }
   }
 
@@ -1210,7 +1278,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   // every wave merges the 16 wave partials the same way ----
   RowAcc W = A;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) merge_step(W, o);
+  for (int o = 32; o >= 1; o >>= 1) merge_step<TM>(W, o, sL);
   if (lane == 0) {
     sm.f[par][wid][0] = W.mp;
     sm.f[par][wid][1] = W.sp;
@@ -1218,6 +1286,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
     sm.f[par][wid][3] = W.sq;
     sm.f[par][wid][4] = W.kq;
     sm.f[par][wid][5] = W.za;
+    if constexpr (TM) sm.f1[par][wid] = W.sq1;
     sm.i[par][wid] = W.bi;
   }
   if (tid == 0) sm.item[par ^ 1] = nxt;
@@ -1230,19 +1299,25 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
     W.sq = sm.f[par][lane][3];
     W.kq = sm.f[par][lane][4];
     W.za = sm.f[par][lane][5];
+    if constexpr (TM) W.sq1 = sm.f1[par][lane];
     W.bi = sm.i[par][lane];
   }
 #pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) merge_step(W, o);
+  for (int o = 8; o >= 1; o >>= 1) merge_step<TM>(W, o, sL);
   const float mp = __shfl(W.mp, 0), sp = __shfl(W.sp, 0);
   const float mq = __shfl(W.mq, 0), sq = __shfl(W.sq, 0), kq = __shfl(W.kq, 0);
   const float zqa = __shfl(W.za, 0);
   const int Arg = __shfl(W.bi, 0);
-  const float lse_p32 = mp + kLn2 * __builtin_amdgcn_logf(sp);
-  const float lse_q32 = mq + kLn2 * __builtin_amdgcn_logf(sq);
-  // sum_j q_j (log q_j - log p_j) = sum_j q_j (zq_j - zp_j) - (lse_q - lse_p)
-  const double KL = (double)kq / (double)sq - (double)(lse_q32 - lse_p32);
-  const RowK rk = row_consts(lse_p32, lse_q32, tau);
+  const float st = TM ? opaque_s(a.inv_t) : 1.0f;
+  const float lse_p32 = TM ? __builtin_fmaf(mp, st, kLn2 * __builtin_amdgcn_logf(sp))
+                           : mp + kLn2 * __builtin_amdgcn_logf(sp);
+  const float lse_q32 = TM ? __builtin_fmaf(mq, st, kLn2 * __builtin_amdgcn_logf(sq))
+                           : mq + kLn2 * __builtin_amdgcn_logf(sq);
+  const float lse_q1 = TM ? mq + kLn2 * __builtin_amdgcn_logf(__shfl(W.sq1, 0)) : lse_q32;
+  // sum_j q_j (log q_j - log p_j) = s sum_j q_j (zq_j - zp_j) - (lse_q - lse_p)
+  const double KL = (double)st * ((double)kq / (double)sq) - (double)(lse_q32 - lse_p32);
+  const RowK rk = row_consts<TM>(lse_p32, lse_q32, tau, st, sL);
+  const FineK fk{mq, __builtin_amdgcn_logf(sq)};
 
   // ---- clipping: an entry's |r_j| = q_j |ell_j| is at most
   //   exp(m_t - lse_q) exp(zq_j - m_t) |zq_j - zp_j| + exp(zq_j - lse_q) |lse_q - lse_p|
@@ -1250,37 +1325,49 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   // below tau / 2 lies inside the clip interval; only regions that fail it
   // are evaluated entry by entry, and S and the clipped KL follow from the
   // unclipped sums minus those corrections ----
+  // (tempered: exp(s m_t - lse_q) exp(s (zq_j - m_t)) s |zq_j - zp_j| + exp(s zq_j - lse_q) |delta|)
   const float adelta = __builtin_fabsf(rk.delta);
-  const float et = __builtin_amdgcn_exp2f((A.mq - lse_q32) * kLog2e);
-  const bool flag_on =
-      __builtin_fmaf(et, A.pm_on, adelta * __builtin_amdgcn_exp2f((A.mq_on - lse_q32) * kLog2e)) >
-      0.5f * tau;
-  const bool flag_st =
-      __builtin_fmaf(et, A.pm_st, adelta * __builtin_amdgcn_exp2f((A.mq_st - lse_q32) * kLog2e)) >
-      0.5f * tau;
+  bool flag_on, flag_st;
+  if constexpr (TM) {
+    const float ets = __builtin_amdgcn_exp2f(__builtin_fmaf(A.mq, sL, -rk.lseqL)) * st;
+    flag_on = __builtin_fmaf(ets, A.pm_on,
+                             adelta * __builtin_amdgcn_exp2f(__builtin_fmaf(A.mq_on, sL, -rk.lseqL))) >
+              0.5f * tau;
+    flag_st = __builtin_fmaf(ets, A.pm_st,
+                             adelta * __builtin_amdgcn_exp2f(__builtin_fmaf(A.mq_st, sL, -rk.lseqL))) >
+              0.5f * tau;
+  } else {
+    const float et = __builtin_amdgcn_exp2f((A.mq - lse_q32) * kLog2e);
+    flag_on =
+        __builtin_fmaf(et, A.pm_on, adelta * __builtin_amdgcn_exp2f((A.mq_on - lse_q32) * kLog2e)) >
+        0.5f * tau;
+    flag_st =
+        __builtin_fmaf(et, A.pm_st, adelta * __builtin_amdgcn_exp2f((A.mq_st - lse_q32) * kLog2e)) >
+        0.5f * tau;
+  }
   float cs = 0.0f, ck = 0.0f;
   if (flag_on) {
     const IO io(opaque(tid));
 #pragma unroll
     for (int v = 0; v < NR; ++v) {
       if (v < nr && io.has(io.nb(v, nvec)))
-        clip_vec<VAR>(rp[v], rq[v], rk, cs, ck);
+        clip_vec<VAR, TM>(rp[v], rq[v], rk, fk, cs, ck);
     }
     if constexpr (NL > 0) {
 #pragma unroll
       for (int l = 0; l < NL; ++l) {
         const int nbv = io.nb(nr + l, nvec);
         if (l < nl && io.has(nbv))
-          clip_vec<VAR>(io.lds(lp[l], nbv), io.lds(lq[l], nbv), rk, cs, ck);
+          clip_vec<VAR, TM>(io.lds(lp[l], nbv), io.lds(lq[l], nbv), rk, fk, cs, ck);
       }
     }
   }
   if (flag_st) {
     const IO io(opaque(tid));
-    for (int s = von; s < nfull; ++s) clip_vec<VAR>(io.load(rzp, s, 64), io.load(rzq, s, 64), rk, cs, ck);
+    for (int s = von; s < nfull; ++s) clip_vec<VAR, TM>(io.load(rzp, s, 64), io.load(rzq, s, 64), rk, fk, cs, ck);
     if (tail) {
       const int nbv = io.nb(nfull, nvec);
-      if (io.has(nbv)) clip_vec<VAR>(io.load(rzp, nfull, nbv), io.load(rzq, nfull, nbv), rk, cs, ck);
+      if (io.has(nbv)) clip_vec<VAR, TM>(io.load(rzp, nfull, nbv), io.load(rzq, nfull, nbv), rk, fk, cs, ck);
     }
   }
   double dcs = 0.0, dck = 0.0;
@@ -1304,13 +1391,14 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
     uint32_t n = 0;
     if (lane == 0) {
       const KArgs K = cold_args();
-      const double ce = (double)lse_q32 - (double)zqa;
+      const double ce = (double)lse_q1 - (double)zqa;
       const double lam = (double)opaque_s(a.lam);
       const float loss = (float)(lam * ce + (1.0 - lam) * KLc64);
       K->row_loss[row] = loss;
       K->tgt[row] = Arg;
       if (K->stats)
         store16(K->stats + 4 * (long long)row, (f32x4){lse_p32, lse_q32, S32, (float)KLc64});
+      if (K->lse1) K->lse1[row] = lse_q1;
       tput(K->rowres + 2 * (long long)row, tag, (uint32_t)Arg);
       tput(K->rowres + 2 * (long long)row + 1, tag, __float_as_uint(loss));
       n = arrive(K->arrive + it.req, tag);
@@ -1322,7 +1410,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   // ---- sweep 2: the gradient; streamed vectors are read a second time
   // (fast form: through the LDS slots once their resident data is done) ----
   if (a.grad) {
-    const GradK gk = grad_consts(opaque_s(a.lam), opaque_s(a.gs), S32);
+    const GradK gk = grad_consts<TM>(opaque_s(a.lam), opaque_s(a.gs), S32, st, lse_q1);
     const Rsrc rg = grad_rsrc<GB, IO::VEC>(a.grad, rowv, opaque_s(a.V));
     if constexpr (RING) {
       // Stores of one full register slot's vector (all register slots are full).
@@ -1331,7 +1419,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
       const IO io(opaque(tid));
 #pragma unroll
       for (int l = 0; l < NL; ++l)
-        grad_vec<VAR, GB>(io.lds(lp[l], 64), io.lds(lq[l], 64), io, nr + l, 64, rk, gk, Arg, rg);
+        grad_vec<VAR, GB, TM>(io.lds(lp[l], 64), io.lds(lq[l], 64), io, nr + l, 64, rk, gk, Arg, rg);
       bool regs_done = false;
       for (int s0 = von; s0 < ns; s0 += NL) {
         wait_lds_reads();
@@ -1340,7 +1428,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
           if (s0 + l < ns) dma_slot<VAR, kAuxAgain>(io, rzp, rzq, lp, lq, l, s0 + l, nvec, tid);
         if (!regs_done) {  // the register slots' gradient overlaps the first loads
 #pragma unroll
-          for (int v = 0; v < NR; ++v) grad_vec<VAR, GB>(rp[v], rq[v], io, v, 64, rk, gk, Arg, rg);
+          for (int v = 0; v < NR; ++v) grad_vec<VAR, GB, TM>(rp[v], rq[v], io, v, 64, rk, gk, Arg, rg);
           wait_vmem_but<kRegStores>();
           regs_done = true;
         } else {
@@ -1352,13 +1440,13 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
           if (sl < ns) {
             const int nbv = io.nb(sl, nvec);
             if (io.has(nbv))
-              grad_vec<VAR, GB>(io.lds(lp[l], nbv), io.lds(lq[l], nbv), io, sl, nbv, rk, gk, Arg, rg);
+              grad_vec<VAR, GB, TM>(io.lds(lp[l], nbv), io.lds(lq[l], nbv), io, sl, nbv, rk, gk, Arg, rg);
           }
         }
       }
       if (!regs_done) {
 #pragma unroll
-        for (int v = 0; v < NR; ++v) grad_vec<VAR, GB>(rp[v], rq[v], io, v, 64, rk, gk, Arg, rg);
+        for (int v = 0; v < NR; ++v) grad_vec<VAR, GB, TM>(rp[v], rq[v], io, v, 64, rk, gk, Arg, rg);
       }
       wait_lds_reads();  // the next row's direct loads may overwrite the LDS slots
     } else {
@@ -1370,13 +1458,13 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
 #pragma unroll AV_GU
         for (int s = von; s < nfull; ++s) {
           const S xp = io.template load<kAuxAgain>(rzp, s, 64), xq = io.template load<kAuxAgain>(rzq, s, 64);
-          grad_vec<VAR, GB>(xp, xq, io, s, 64, rk, gk, Arg, rg);
+          grad_vec<VAR, GB, TM>(xp, xq, io, s, 64, rk, gk, Arg, rg);
         }
         if (tail) {
           const int nbv = io.nb(nfull, nvec);
           if (io.has(nbv)) {
             const S xp = io.template load<kAuxAgain>(rzp, nfull, nbv), xq = io.template load<kAuxAgain>(rzq, nfull, nbv);
-            grad_vec<VAR, GB>(xp, xq, io, nfull, nbv, rk, gk, Arg, rg);
+            grad_vec<VAR, GB, TM>(xp, xq, io, nfull, nbv, rk, gk, Arg, rg);
           }
         }
       }
@@ -1386,7 +1474,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
         for (int v = 0; v < NR; ++v) {
           const int nbv = io.nb(v, nvec);
           if (v < nr && io.has(nbv))
-            grad_vec<VAR, GB>(rp[v], rq[v], io, v, nbv, rk, gk, Arg, rg);
+            grad_vec<VAR, GB, TM>(rp[v], rq[v], io, v, nbv, rk, gk, Arg, rg);
         }
       }
       if constexpr (NL > 0) {
@@ -1395,7 +1483,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
         for (int l = 0; l < NL; ++l) {
           const int sl = nr + l, nbv = io.nb(sl, nvec);
           if (l < nl && io.has(nbv))
-            grad_vec<VAR, GB>(io.lds(lp[l], nbv), io.lds(lq[l], nbv), io, sl, nbv, rk, gk, Arg, rg);
+            grad_vec<VAR, GB, TM>(io.lds(lp[l], nbv), io.lds(lq[l], nbv), io, sl, nbv, rk, gk, Arg, rg);
         }
       }
       wait_lds_reads();
@@ -1403,7 +1491,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   }
 }
 
-template <int VAR, bool FULL, bool GB>
+template <int VAR, bool FULL, bool GB, bool TM>
 __global__ __launch_bounds__(kRowBlock) void fused_kernel(FwdArgs a) {
   using S = typename Tr<VAR>::S;
   constexpr int NLA = RowCfg<VAR>::NL > 0 ? RowCfg<VAR>::NL : 1;
@@ -1484,7 +1572,7 @@ __global__ __launch_bounds__(kRowBlock) void fused_kernel(FwdArgs a) {
       continue;
     }
     const Item it = map_item(a, sm, s_off, order, key, (int)idx);
-    if (it.verified) verified_row<VAR, FULL, GB>(a, sm, lp, lq, it, par, tag);
+    if (it.verified) verified_row<VAR, FULL, GB, TM>(a, sm, lp, lq, it, par, tag);
     else unverified_row<VAR, GB>(a, sm, it.row, par, it.half, tag);
   }
   // The workgroup that leaves last sums the request losses, reports the
@@ -1515,7 +1603,7 @@ __global__ __launch_bounds__(kRowBlock) void fused_kernel(FwdArgs a) {
 // standalone backward
 // ---------------------------------------------------------------------------
 
-template <int VAR, bool GB>
+template <int VAR, bool GB, bool TM>
 __global__ __launch_bounds__(kBlock) void bwd_kernel(BwdArgs a) {
   using T = Tr<VAR>;
   using S = typename T::S;
@@ -1552,8 +1640,8 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(BwdArgs a) {
   }
   const f32x4 st = *(const f32x4*)(a.stats + 4 * (long long)row);
   const int A = a.tgt[row];
-  const RowK rk = row_consts(st[0], st[1], a.tau);
-  const GradK gk = grad_consts(a.lam, a.gs, st[2]);
+  const RowK rk = row_consts<TM>(st[0], st[1], a.tau, a.inv_t, a.inv_tl);
+  const GradK gk = grad_consts<TM>(a.lam, a.gs, st[2], a.inv_t, TM ? a.lse1[row] : 0.0f);
   S xp[NVMAX], xq[NVMAX];
 #pragma unroll
   for (int v = 0; v < NVMAX; ++v) {
@@ -1571,8 +1659,8 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         float q, r, g;
-        opd_entry(T::at(xp[v], e), T::at(xq[v], e), rk, q, r, g);
-        out[e] = grad_entry(q, g, gk);
+        opd_entry<TM>(T::at(xp[v], e), T::at(xq[v], e), rk, q, r, g);
+        out[e] = grad_entry<TM>(q, g, T::at(xq[v], e), gk);
         if (vi * VEC + e == A) out[e] = out[e] - gk.fix;
       }
       if constexpr (GB) store_vec_bf16<VEC>(gb_r, (unsigned)vi, out);
@@ -2018,31 +2106,41 @@ __global__ __launch_bounds__(kBlock) void zero_kernel(uint64_t* p, size_t n) {
     p[i] = 0ull;
 }
 
-template <int VAR, bool GB>
+template <int VAR, bool GB, bool TM>
 hipError_t launch_fused_g(bool full, const FwdArgs& a, int grid, size_t lds, hipStream_t s) {
-  if (full) hipLaunchKernelGGL((fused_kernel<VAR, true, GB>), dim3(grid), dim3(kRowBlock), lds, s, a);
-  else hipLaunchKernelGGL((fused_kernel<VAR, false, GB>), dim3(grid), dim3(kRowBlock), lds, s, a);
+  if (full) hipLaunchKernelGGL((fused_kernel<VAR, true, GB, TM>), dim3(grid), dim3(kRowBlock), lds, s, a);
+  else hipLaunchKernelGGL((fused_kernel<VAR, false, GB, TM>), dim3(grid), dim3(kRowBlock), lds, s, a);
   return hipGetLastError();
 }
 template <int VAR>
 hipError_t launch_fused_t(bool full, const FwdArgs& a, int grid, size_t lds, hipStream_t s) {
-  return a.gbf16 ? launch_fused_g<VAR, true>(full, a, grid, lds, s) : launch_fused_g<VAR, false>(full, a, grid, lds, s);
+  if (a.tm)
+    return a.gbf16 ? launch_fused_g<VAR, true, true>(full, a, grid, lds, s)
+                   : launch_fused_g<VAR, false, true>(full, a, grid, lds, s);
+  return a.gbf16 ? launch_fused_g<VAR, true, false>(full, a, grid, lds, s)
+                 : launch_fused_g<VAR, false, false>(full, a, grid, lds, s);
 }
-template <int VAR, bool GB>
+template <int VAR, bool GB, bool TM>
 hipError_t occ_g(bool full, size_t lds, int* out) {
-  if (full) return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, fused_kernel<VAR, true, GB>, kRowBlock, lds);
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, fused_kernel<VAR, false, GB>, kRowBlock, lds);
+  if (full)
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, fused_kernel<VAR, true, GB, TM>, kRowBlock, lds);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, fused_kernel<VAR, false, GB, TM>, kRowBlock, lds);
 }
 template <int VAR>
-hipError_t occ_t(bool full, bool gb, size_t lds, int* out) {
-  return gb ? occ_g<VAR, true>(full, lds, out) : occ_g<VAR, false>(full, lds, out);
+hipError_t occ_t(bool full, bool gb, bool tm, size_t lds, int* out) {
+  if (tm) return gb ? occ_g<VAR, true, true>(full, lds, out) : occ_g<VAR, false, true>(full, lds, out);
+  return gb ? occ_g<VAR, true, false>(full, lds, out) : occ_g<VAR, false, false>(full, lds, out);
+}
+template <int VAR, bool TM>
+hipError_t launch_bwd_g(const BwdArgs& a, hipStream_t s) {
+  const unsigned grid = (unsigned)a.R * (unsigned)a.C;
+  if (a.gbf16) hipLaunchKernelGGL((bwd_kernel<VAR, true, TM>), dim3(grid), dim3(kBlock), 0, s, a);
+  else hipLaunchKernelGGL((bwd_kernel<VAR, false, TM>), dim3(grid), dim3(kBlock), 0, s, a);
+  return hipGetLastError();
 }
 template <int VAR>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
-  const unsigned grid = (unsigned)a.R * (unsigned)a.C;
-  if (a.gbf16) hipLaunchKernelGGL((bwd_kernel<VAR, true>), dim3(grid), dim3(kBlock), 0, s, a);
-  else hipLaunchKernelGGL((bwd_kernel<VAR, false>), dim3(grid), dim3(kBlock), 0, s, a);
-  return hipGetLastError();
+  return a.tm ? launch_bwd_g<VAR, true>(a, s) : launch_bwd_g<VAR, false>(a, s);
 }
 
 }  // namespace
@@ -2056,12 +2154,12 @@ hipError_t launch_fused(Variant v, bool full, const FwdArgs& a, int grid, size_t
   }
 }
 
-hipError_t fused_blocks_per_cu(Variant v, bool full, bool gb, size_t lds, int* out) {
+hipError_t fused_blocks_per_cu(Variant v, bool full, bool gb, bool tm, size_t lds, int* out) {
   switch (v) {
-    case kBf16x8: return occ_t<kBf16x8>(full, gb, lds, out);
-    case kBf16x1: return occ_t<kBf16x1>(full, gb, lds, out);
-    case kF32x4: return occ_t<kF32x4>(full, gb, lds, out);
-    default: return occ_t<kF32x1>(full, gb, lds, out);
+    case kBf16x8: return occ_t<kBf16x8>(full, gb, tm, lds, out);
+    case kBf16x1: return occ_t<kBf16x1>(full, gb, tm, lds, out);
+    case kF32x4: return occ_t<kF32x4>(full, gb, tm, lds, out);
+    default: return occ_t<kF32x1>(full, gb, tm, lds, out);
   }
 }
 

@@ -215,6 +215,20 @@ int av_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
  *   row_stats[r] = {lse_p, lse_q, S_r, clipped-KL sum} (float32), the state
  *                  av_verify_opd_bwd needs.
  *
+ * Temperature (Pith review page, "Axiom & Free-Parameter Ledger": a
+ * reverse-KL temperature of 1.0, not defined further).  With temperature
+ * T != 1 the reverse-KL term uses p = softmax(zp / T) and q = softmax(zq / T)
+ * in every formula above (ell, r, c, S, the clipped sum, lse_p and lse_q,
+ * which become the log-sum-exps of zp / T and zq / T), while the
+ * cross-entropy keeps q1 = softmax(zq):
+ *     row_loss[r]  = lambda * (-log q1[a_r]) + (1 - lambda) * sum_j clip(r_j, -tau, tau)
+ *     grad_zq[r,j] = grad_scale * ( lambda (q1_j - [j = a_r])
+ *                     + (1 - lambda) q_j (c_j (ell_j + 1) - S_r) / T )
+ * (no T^2 factor).  T = 1 is the pass above, bit for bit.
+ *   lse_q1[r]    = log-sum-exp of zq[r,:] (temperature 1) of verified rows,
+ *                  0 for unverified dense rows; the backward needs it when
+ *                  T != 1.
+ *
  * Arguments
  *   dtype        AV_F32 or AV_BF16 (element type of zp and zq)
  *   B, k, V      requests, draft block length (1..AV_MAX_K), vocabulary
@@ -227,9 +241,11 @@ int av_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
  *                ignored (may be NULL) when ragged
  *   lambda       in [0, 1];  tau > 0 (may be +inf: no clipping);
  *   grad_scale   finite multiplier of the gradient (e.g. 1 / sum b_k)
+ *   temperature  T > 0, finite (1: the plain pass)
  *   tgt_argmax   [R] int32 out;  acc_len [B] int32 out;  row_loss [R] float32 out
  *   req_loss     [B] float32 out or NULL;  total_loss [1] float32 out or NULL
  *   row_stats    [R, 4] float32 out or NULL
+ *   lse_q1       [R] float32 out or NULL
  *   grad_zq      [R, V] out or NULL (NULL: forward only), of type grad_dtype
  *   grad_dtype   AV_F32 (the default: float32 entries) or AV_BF16 (each
  *                float32 entry rounded to nearest-even bfloat16, half the
@@ -246,18 +262,19 @@ int av_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
  *                time for the gradient.  A tuning and test knob.
  * Errors (AV_EINVAL): NULL required pointer, B < 1, k < 1 or > AV_MAX_K,
  * V < 1, R inconsistent with the layout, lambda outside [0, 1] or NaN, tau
- * <= 0 or NaN, grad_scale non-finite, workspace too small, negative
- * onchip_limit, row_stats or workspace not 16-byte aligned.
+ * <= 0 or NaN, grad_scale non-finite, temperature not positive and finite,
+ * workspace too small, negative onchip_limit, row_stats or workspace not
+ * 16-byte aligned.
  * AV_EUNSUPPORTED: dtype or grad_dtype other than AV_F32/AV_BF16; ragged
  * with B > 4095 (the offsets are cached on chip); R*V >= 2^46.
  */
 int av_verify_opd_fwd(int dtype, int B, int k, int V, int R,
                       const int32_t* row_off, const void* zp, const void* zq,
                       const int32_t* draft, const int32_t* bk,
-                      float lambda, float tau, float grad_scale,
+                      float lambda, float tau, float grad_scale, float temperature,
                       int32_t* tgt_argmax, int32_t* acc_len, float* row_loss,
                       float* req_loss, float* total_loss, float* row_stats,
-                      void* grad_zq, int grad_dtype, int32_t* status,
+                      float* lse_q1, void* grad_zq, int grad_dtype, int32_t* status,
                       void* workspace, size_t workspace_bytes,
                       int onchip_limit, void* stream);
 
@@ -266,17 +283,20 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R,
  *
  * Recomputes grad_zq exactly as av_verify_opd_fwd defines it, in one
  * streaming pass, from tgt_argmax and row_stats of an earlier forward call
- * with the same inputs and the same lambda/tau/grad_scale: every entry uses
- * the same float32 steps as the fused pass, so both write identical bits.
+ * with the same inputs and the same lambda/tau/grad_scale/temperature: every
+ * entry uses the same float32 steps as the fused pass, so both write
+ * identical bits.
  *   row_off, zp, zq, bk, dtype, B, k, V, R: as for av_verify_opd_fwd
  *   tgt_argmax [R] int32, row_stats [R, 4] float32: from the forward call
+ *   lse_q1     [R] float32 from the forward call; required when
+ *              temperature != 1, else ignored (may be NULL)
  *   grad_zq    [R, V] out of type grad_dtype (AV_F32 or AV_BF16, as for
  *              av_verify_opd_fwd; unverified dense rows are zeroed)
  *   vecs_per_thread  0 = automatic; otherwise the most 16-byte vectors one
  *              thread handles per work item (raised where needed so that a
  *              row has at most 64 items)
  * Errors as for av_verify_opd_fwd (AV_EINVAL also for a negative
- * vecs_per_thread).  AV_EUNSUPPORTED also for rows longer than 64 items:
+ * vecs_per_thread, and for a NULL lse_q1 when temperature != 1).  AV_EUNSUPPORTED also for rows longer than 64 items:
  * V > 1048576 (bf16, V % 8 == 0, 16-byte aligned rows), V > 524288 (f32,
  * V % 4 == 0, aligned), V > 262144 otherwise.  Needs no workspace; row_off
  * only selects the ragged layout (every stored row verified).
@@ -284,9 +304,9 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R,
 int av_verify_opd_bwd(int dtype, int B, int k, int V, int R,
                       const int32_t* row_off, const void* zp, const void* zq,
                       const int32_t* bk, const int32_t* tgt_argmax,
-                      const float* row_stats, float lambda, float tau,
-                      float grad_scale, void* grad_zq, int grad_dtype,
-                      int vecs_per_thread, void* stream);
+                      const float* row_stats, const float* lse_q1, float lambda,
+                      float tau, float grad_scale, float temperature, void* grad_zq,
+                      int grad_dtype, int vecs_per_thread, void* stream);
 
 /*
  * av_lm_head_bwd -- backward of the drafter's LM head, the step after this

@@ -147,6 +147,7 @@ class RowTerms:
     c: np.ndarray         # bool: entry inside [-tau, tau]
     lse_q1: float = 0.0   # log-sum-exp of zq (temperature 1, the CE term)
     temperature: float = 1.0
+    q1: Optional[np.ndarray] = None   # softmax(zq), the CE term's distribution
 
 
 def _logsumexp(z: np.ndarray) -> float:
@@ -204,7 +205,7 @@ def row_terms(zp_row: np.ndarray, zq_row: np.ndarray, lam: float, tau: float,
     onehot[a] = 1.0
     grad = grad_scale * (lam * (q1 - onehot) + (1.0 - lam) * q * (np.where(c, ell + 1.0, 0.0) - S) / t)
     return RowTerms(argmax=a, lse_p=lse_p, lse_q=lse_q, ce=ce, klc=klc, S=S, loss=loss,
-                    grad=grad, q=q, ell=ell, r=r, c=c, lse_q1=lse_q1, temperature=t)
+                    grad=grad, q=q, ell=ell, r=r, c=c, lse_q1=lse_q1, temperature=t, q1=q1)
 
 
 def clip_margin(r: np.ndarray, tau: float) -> np.ndarray:

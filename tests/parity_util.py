@@ -8,7 +8,10 @@ Acceptance rule (the arithmetic behind it is written out in the design notes):
   * lse_p, lse_q: |gpu - ref| <= 2e-6 |ref| + 2e-6;
   * gradient, per entry: |gpu - ref| <= 1e-3 |ref| + 2e-5 gs q_j (1 + |ell_j| + |S|)
     -- the second term bounds float32 rounding of q_j, ell_j and S where the
-    reference itself cancels to near zero;
+    reference itself cancels to near zero; with a reverse-KL temperature
+    T != 1 that term is scaled by 1 / T (the KL part's factor) and
+    2e-5 gs q1_j is added for the cross-entropy part's own softmax q1;
+  * lse of zq at temperature 1 (lse_q1): as lse_p, lse_q;
   * an entry whose |r_j| lies within 1e-4 tau of tau may be classified either
     way by float32; rows with such entries are accepted if they match the
     oracle with any combination of those indicators flipped (at most 3).
@@ -54,8 +57,9 @@ def gpu_inputs(w: synth.Workload, dev="cuda") -> dict:
 
 
 def run_fwd(av, inp: dict, w: synth.Workload, *, bk: Optional[np.ndarray], lam: float, tau: float,
-            gs: float = 1.0, vecs: int = 0, want_grad: bool = True) -> dict:
-    kw = dict(k=w.k, lam=lam, tau=tau, grad_scale=gs, onchip_limit=vecs, want_grad=want_grad)
+            gs: float = 1.0, vecs: int = 0, want_grad: bool = True, temperature: float = 1.0) -> dict:
+    kw = dict(k=w.k, lam=lam, tau=tau, grad_scale=gs, onchip_limit=vecs, want_grad=want_grad,
+              temperature=temperature)
     if w.row_off is not None:
         kw["row_off"] = inp["row_off"]
     else:
@@ -78,18 +82,25 @@ def close(a, b, rtol, atol) -> bool:
 
 
 def grad_row_ok(g: np.ndarray, t: oracle.RowTerms, gs: float) -> np.ndarray:
-    tol = GRAD_RTOL * np.abs(t.grad) + GRAD_QTOL * abs(gs) * t.q * (1.0 + np.abs(t.ell) + abs(t.S))
+    scale = t.q * (1.0 + np.abs(t.ell) + abs(t.S))
+    if t.temperature != 1.0:
+        scale = scale / t.temperature + t.q1
+    tol = GRAD_RTOL * np.abs(t.grad) + GRAD_QTOL * abs(gs) * scale
     return np.abs(g.astype(np.float64) - t.grad) <= tol
 
 
-def check_row(r: int, out: dict, zp_row, zq_row, lam, tau, gs, verified: bool, errors: list):
+def check_row(r: int, out: dict, zp_row, zq_row, lam, tau, gs, verified: bool, errors: list,
+              temperature: float = 1.0):
     """Compare one row of GPU output with the oracle; append messages to errors."""
     a_ref = oracle.target_argmax(zp_row)
     if int(out["tgt_argmax"][r]) != a_ref:
         errors.append(f"row {r}: argmax {out['tgt_argmax'][r]} != {a_ref}")
     grad = out.get("grad")
     stats = out.get("row_stats")
+    lse1 = out.get("lse_q1")
     if not verified:
+        if lse1 is not None and lse1[r] != 0.0:
+            errors.append(f"row {r}: unverified row has lse_q1 {lse1[r]}")
         if out["row_loss"][r] != 0.0:
             errors.append(f"row {r}: unverified loss {out['row_loss'][r]}")
         if grad is not None and np.any(grad[r] != 0.0):
@@ -97,14 +108,15 @@ def check_row(r: int, out: dict, zp_row, zq_row, lam, tau, gs, verified: bool, e
         if stats is not None and np.any(stats[r] != 0.0):
             errors.append(f"row {r}: unverified row has nonzero stats")
         return
-    t = oracle.row_terms(zp_row, zq_row, lam, tau, gs)
+    t = oracle.row_terms(zp_row, zq_row, lam, tau, gs, temperature=temperature)
     variants = [t]
     amb = np.nonzero(oracle.clip_margin(t.r, tau) <= CLIP_AMBIG)[0] if math.isfinite(tau) else []
     if 0 < len(amb) <= 3:
         for flips in itertools.product([False, True], repeat=len(amb)):
             if any(flips):
                 ov = {int(j): (not bool(t.c[j])) if f else bool(t.c[j]) for j, f in zip(amb, flips)}
-                variants.append(oracle.row_terms(zp_row, zq_row, lam, tau, gs, clip_override=ov))
+                variants.append(oracle.row_terms(zp_row, zq_row, lam, tau, gs, clip_override=ov,
+                                                 temperature=temperature))
     msgs = None
     for v in variants:
         m = []
@@ -120,6 +132,8 @@ def check_row(r: int, out: dict, zp_row, zq_row, lam, tau, gs, verified: bool, e
                 m.append(f"S {s[2]} vs {v.S}")
             if not close(s[3], v.klc, LOSS_RTOL, LOSS_ATOL):
                 m.append(f"KLc {s[3]} vs {v.klc}")
+        if lse1 is not None and not close(lse1[r], v.lse_q1, LSE_RTOL, LSE_ATOL):
+            m.append(f"lse_q1 {lse1[r]} vs {v.lse_q1}")
         if grad is not None:
             ok = grad_row_ok(grad[r], v, gs)
             if not ok.all():
@@ -133,7 +147,8 @@ def check_row(r: int, out: dict, zp_row, zq_row, lam, tau, gs, verified: bool, e
 
 
 def check_workload(out: dict, w: synth.Workload, bk: Optional[np.ndarray], lam: float, tau: float,
-                   gs: float = 1.0, rows: Optional[Iterable[int]] = None, max_errors: int = 10):
+                   gs: float = 1.0, rows: Optional[Iterable[int]] = None, max_errors: int = 10,
+                   temperature: float = 1.0):
     """Full comparison (rows=None) or comparison on sampled rows; argmax and
     acceptance are always checked on every row and request."""
     errors: list = []
@@ -157,7 +172,7 @@ def check_workload(out: dict, w: synth.Workload, bk: Optional[np.ndarray], lam: 
     check = range(w.R) if rows is None else rows
     for r in check:
         check_row(r, out, decode_rows(w, "zp", r), decode_rows(w, "zq", r), lam, tau, gs,
-                  bool(verified[r]), errors)
+                  bool(verified[r]), errors, temperature=temperature)
         if len(errors) >= max_errors:
             break
     # reductions: per request from the (already checked) row losses, in float64
@@ -174,12 +189,12 @@ def check_workload(out: dict, w: synth.Workload, bk: Optional[np.ndarray], lam: 
     return errors
 
 
-def oracle_reductions(w: synth.Workload, bk, lam, tau, gs=1.0) -> dict:
+def oracle_reductions(w: synth.Workload, bk, lam, tau, gs=1.0, temperature=1.0) -> dict:
     """Whole-batch oracle (small workloads only)."""
     zp = decode_rows(w, "zp", slice(None))
     zq = decode_rows(w, "zq", slice(None))
     if w.row_off is not None:
         return oracle.verify_opd(zp, zq, w.draft, k=w.k, lam=lam, tau=tau, grad_scale=gs,
-                                 row_off=w.row_off, want_grad=False)
+                                 row_off=w.row_off, want_grad=False, temperature=temperature)
     return oracle.verify_opd(zp, zq, w.draft, k=w.k, lam=lam, tau=tau, grad_scale=gs, bk=bk,
-                             want_grad=False)
+                             want_grad=False, temperature=temperature)

@@ -54,14 +54,14 @@ def test_workspace_bytes():
 
 def fwd(**kw):
     a = dict(dtype=1, B=2, k=4, V=64, R=8, row_off=NULL, zp=P, zq=P, draft=P, bk=P, lam=0.5,
-             tau=0.1, gs=1.0, tgt=P, acc=P, row_loss=P, req_loss=NULL, total=NULL, stats=P,
-             grad=P, gdt=0, status=NULL, ws=P, ws_bytes=1 << 30, vecs=0, stream=NULL)
+             tau=0.1, gs=1.0, temp=1.0, tgt=P, acc=P, row_loss=P, req_loss=NULL, total=NULL, stats=P,
+             lse1=NULL, grad=P, gdt=0, status=NULL, ws=P, ws_bytes=1 << 30, vecs=0, stream=NULL)
     a.update(kw)
     return _lib.lib().av_verify_opd_fwd(
         a["dtype"], a["B"], a["k"], a["V"], a["R"], a["row_off"], a["zp"], a["zq"], a["draft"],
-        a["bk"], a["lam"], a["tau"], a["gs"], a["tgt"], a["acc"], a["row_loss"], a["req_loss"],
-        a["total"], a["stats"], a["grad"], a["gdt"], a["status"], a["ws"], a["ws_bytes"], a["vecs"],
-        a["stream"])
+        a["bk"], a["lam"], a["tau"], a["gs"], a["temp"], a["tgt"], a["acc"], a["row_loss"],
+        a["req_loss"], a["total"], a["stats"], a["lse1"], a["grad"], a["gdt"], a["status"], a["ws"],
+        a["ws_bytes"], a["vecs"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -88,6 +88,10 @@ def fwd(**kw):
     (dict(tau=float("nan")), dd.AV_EINVAL),
     (dict(gs=float("inf")), dd.AV_EINVAL),
     (dict(gs=float("nan")), dd.AV_EINVAL),
+    (dict(temp=0.0), dd.AV_EINVAL),
+    (dict(temp=-2.0), dd.AV_EINVAL),
+    (dict(temp=float("nan")), dd.AV_EINVAL),
+    (dict(temp=float("inf")), dd.AV_EINVAL),
     (dict(ws_bytes=256), dd.AV_EINVAL),                  # workspace too small
     (dict(vecs=-1), dd.AV_EINVAL),
     (dict(stats=ctypes.c_void_p(0x10004)), dd.AV_EINVAL),  # row_stats not 16-byte aligned
@@ -136,14 +140,19 @@ def test_length_head_rejects_bad_arguments_on_host(kw, code):
     (dict(V=64 * 256 * 64 + 8), dd.AV_EUNSUPPORTED),     # more than 64 items per row
     (dict(dtype=0, V=64 * 256 * 32 + 4), dd.AV_EUNSUPPORTED),
     (dict(gdt=2), dd.AV_EUNSUPPORTED),
+    (dict(temp=0.0), dd.AV_EINVAL),
+    (dict(temp=float("inf")), dd.AV_EINVAL),
+    (dict(temp=2.0), dd.AV_EINVAL),                      # tempered: lse_q1 required
+    (dict(temp=0.5, lam=0.0), dd.AV_EINVAL),
 ])
 def test_bwd_rejects_bad_arguments_on_host(kw, code):
     a = dict(dtype=1, B=2, k=4, V=64, R=8, row_off=NULL, zp=P, zq=P, bk=P, tgt=P, stats=P,
-             lam=0.5, tau=0.1, gs=1.0, grad=P, gdt=0, vecs=0, stream=NULL)
+             lse1=NULL, lam=0.5, tau=0.1, gs=1.0, temp=1.0, grad=P, gdt=0, vecs=0, stream=NULL)
     a.update(kw)
     rc = _lib.lib().av_verify_opd_bwd(a["dtype"], a["B"], a["k"], a["V"], a["R"], a["row_off"],
-                                      a["zp"], a["zq"], a["bk"], a["tgt"], a["stats"], a["lam"],
-                                      a["tau"], a["gs"], a["grad"], a["gdt"], a["vecs"], a["stream"])
+                                      a["zp"], a["zq"], a["bk"], a["tgt"], a["stats"], a["lse1"],
+                                      a["lam"], a["tau"], a["gs"], a["temp"], a["grad"], a["gdt"],
+                                      a["vecs"], a["stream"])
     assert rc == code
 
 
