@@ -54,17 +54,19 @@ def kernel_sha() -> str:
     return hsh.hexdigest()[:16]
 
 
-def algorithmic_bytes(B, k, V, H, R, Rv, elem=2, gelem=4):
+def algorithmic_bytes(B, k, V, H, R, Rv, elem=2, gelem=4, lse1=False):
     """Bytes the pass must move at least once (per step).
 
     fused kernel: zp of every stored row (target argmax is defined for all),
     zq of verified rows, the fp32 gradient of every stored row (zeros for
     unverified rows are part of the output), draft tokens, b_k, and the small
-    per-row / per-request outputs.  length head: h, w, rate and b_k.
+    per-row / per-request outputs (with a reverse-KL temperature also the
+    plain log-sum-exp of zq per row).  length head: h, w, rate and b_k.
     """
     fused = (elem * V * R + elem * V * Rv + gelem * V * R
              + 4 * R + 4 * B            # draft, bk
              + 4 * R + 4 * R + 16 * R   # argmax, row loss, row stats
+             + (4 * R if lse1 else 0)   # lse of zq at temperature 1
              + 4 * B + 4 * B + 4)       # acc, req loss, total
     head = 4 * B * H + 4 * H + 8 * B
     return fused, head
@@ -139,7 +141,7 @@ def copy_calibration(torch, dev, mib: int, reps: int = 3) -> None:
     del src, dst
 
 
-def cpu_baseline(n_requests: int):
+def cpu_baseline(n_requests: int, temperature: float = 1.0):
     """The float64 oracle, untuned, on the first n_requests of the same
     workload, single-threaded; reported in the same unit (algorithmic GB/s)."""
     import numpy as np
@@ -156,10 +158,11 @@ def cpu_baseline(n_requests: int):
         zp = oracle.bf16_bits_to_f64(w.zp)
         zq = oracle.bf16_bits_to_f64(w.zq)
         oracle.length_head(w.h, w.w, w.bias, w.gamma, w.k)
-        oracle.verify_opd(zp, zq, w.draft, k=w.k, lam=w.lam, tau=w.tau, grad_scale=1.0, bk=bk)
+        oracle.verify_opd(zp, zq, w.draft, k=w.k, lam=w.lam, tau=w.tau, grad_scale=1.0, bk=bk,
+                          temperature=temperature)
         dt = time.perf_counter() - t0
     Rv = int(np.clip(bk, 1, w.k).sum())
-    fused, head = algorithmic_bytes(w.B, w.k, w.V, w.H, w.R, Rv)
+    fused, head = algorithmic_bytes(w.B, w.k, w.V, w.H, w.R, Rv, lse1=temperature != 1.0)
     return {
         "value": round((fused + head) / dt / 1e9, 4),
         "unit": "GB/s",
@@ -506,6 +509,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--grad", choices=["f32", "bf16"], default="f32",
                     help="gradient output type of the fused pass (default float32)")
+    ap.add_argument("--temperature", type=float, default=1.0,
+                    help="reverse-KL temperature of the fused pass (default 1: the plain pass)")
     ap.add_argument("--workload", choices=["concurrent", "head_update", "spec", "lm_head"],
                     default="concurrent",
                     help="concurrent: the fused verify+OPD step (default); head_update: the "
@@ -574,6 +579,9 @@ def main():
                             device=dev),
         "status": torch.empty(1, dtype=torch.int32, device=dev),
     }
+    tempered = args.temperature != 1.0
+    if tempered:
+        out["lse_q1"] = torch.empty(R, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(ev0=None, ev1=None):
@@ -581,7 +589,8 @@ def main():
         if ev0 is not None:
             ev0.record(stream)
         dd.av_verify_opd_fwd(zp, zq, draft, k=k, bk=bk, lam=w.lam, tau=w.tau,
-                             grad_scale=1.0, out=out, grad_dtype=out["grad"].dtype)
+                             grad_scale=1.0, out=out, grad_dtype=out["grad"].dtype,
+                             temperature=args.temperature, want_lse_q1=tempered)
         if ev1 is not None:
             ev1.record(stream)
 
@@ -604,7 +613,7 @@ def main():
         raise RuntimeError(f"device status {int(out['status'].item())}")
 
     gelem = 2 if args.grad == "bf16" else 4
-    fused_b, head_b = algorithmic_bytes(B, k, V, H, R, Rv, gelem=gelem)
+    fused_b, head_b = algorithmic_bytes(B, k, V, H, R, Rv, gelem=gelem, lse1=tempered)
     ms_step = elapsed / args.steps * 1e3
     value = (fused_b + head_b) * args.steps / elapsed / 1e9
     kern_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
@@ -613,6 +622,8 @@ def main():
     unverified_grad = gelem * V * (R - Rv)
 
     metric = METRIC if args.grad == "f32" else METRIC + ", bf16 gradient"
+    if tempered:
+        metric += f", reverse-KL temperature {args.temperature:g}"
     line = {
         "metric": metric,
         "value": round(value, 2),
@@ -628,9 +639,10 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"concurrent: B=128 requests, k=16, V=151936, bf16 logits, {args.grad} gradient, "
-                        "b_k from the length head (H=4096), lambda=0.5, tau=0.1",
+                        "b_k from the length head (H=4096), lambda=0.5, tau=0.1"
+                        + (f", reverse-KL temperature {args.temperature:g}" if tempered else ""),
             "B": B, "k": k, "V": V, "H": H, "rows": R, "verified_rows": Rv,
-            "logits": "bf16", "grad": args.grad, "seed": args.seed,
+            "logits": "bf16", "grad": args.grad, "seed": args.seed, "temperature": args.temperature,
             "rows_per_s": round(R / (ms_step * 1e-3), 1),
             "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
             "bytes_per_step": fused_b + head_b,
@@ -644,11 +656,11 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic() if args.grad == "f32" else None,
+            "traffic": measured_traffic() if args.grad == "f32" and not tempered else None,
         },
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(args.cpu_requests)
+        line["cpu_baseline"] = cpu_baseline(args.cpu_requests, args.temperature)
     print(json.dumps(line), flush=True)
 
 
