@@ -1814,8 +1814,10 @@ __device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32
       k0 += W0;
       k1 += W1;
     }
-    const uint32_t lo0 = M0 * c0, hi0 = __umulhi(M0, c0);
-    const uint32_t lo1 = M1 * c2, hi1 = __umulhi(M1, c2);
+    // full 64-bit products: one multiply instruction gives both halves
+    const uint64_t p0 = (uint64_t)M0 * c0, p1 = (uint64_t)M1 * c2;
+    const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
+    const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
     const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
     c0 = n0;
     c1 = lo1;
