@@ -1147,9 +1147,10 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   const float sL = TM ? opaque_s(a.inv_tl) : kLog2e;
 
   // ---- sweep 1: read the row once; keep its on-chip slots, fold every
-  // vector into the running statistics.  Fast form: the streamed slots pass
-  // through the LDS slots NL at a time (direct loads, no registers held
-  // while in flight), then the LDS slots take their resident data. ----
+  // vector into the running statistics.  Fast form: the register slots and
+  // then the streamed slots pass through the LDS slots two at a time (direct
+  // loads, no registers held while in flight), then the LDS slots take their
+  // resident data. ----
   constexpr bool RING = FULL && NL > 0;
   const int ns = nfull + (nfull * kRowBlock < nvec ? 1 : 0);  // slots, the partial one included
   if constexpr (!RING && NL > 0) {
@@ -1168,7 +1169,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
       rp[v] = S{};
       rq[v] = S{};
       const int nbv = io.nb(v, nvec);
-      if (v < nr && io.has(nbv)) {
+      if (!RING && v < nr && io.has(nbv)) {
         rp[v] = io.template load<kAuxOnce>(rzp, v, nbv);
         rq[v] = io.template load<kAuxOnce>(rzq, v, nbv);
       }
@@ -1177,62 +1178,91 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   RowAcc A;
   acc_init(A);
   if constexpr (RING) {
-    // Streamed slots go in pairs through the two halves of the LDS slots,
-    // double-buffered: pair p+1 is in flight while pair p is folded in.
-    // Each half takes its resident slots after its last streamed pair.  A
-    // wait for pair p leaves outstanding only what was issued after it (the
-    // next pair, or a half's resident slots), counted for slots every wave
-    // loads (partial slots are not counted).
+    // Every slot of the row comes in through the two halves of the LDS
+    // slots, two slots at a time, double-buffered: the register slots first
+    // (each copied from the LDS into its registers, then folded in), then
+    // the streamed slots; each half then takes its resident slots.  Only
+    // loads into the LDS are in flight, so every wait is counted here and the
+    // first slots are folded in while the rest of the row is on its way.  A
+    // wait for pair q leaves outstanding only what was issued after it (pair
+    // q + 1, or a half's resident slots), counted for slots every wave loads.
     static_assert(NL == 4, "two halves of two LDS slots");
+    constexpr int QR = (NR + 1) / 2;  // pairs that hold register slots
     const IO io(opaque(tid));
-    const int npair = (ns - von + 1) >> 1;
-    auto full_ops = [&](int q) {  // loads of pair q that every wave issues
-      const int s0 = von + 2 * q;
-      return (s0 < nfull ? 2 : 0) + (s0 + 1 < nfull ? 2 : 0);
-    };
-    if (npair == 0) {
-#pragma unroll
-      for (int l = 0; l < NL; ++l) dma_slot<VAR, kAuxOnce>(io, rzp, rzq, lp, lq, l, nr + l, nvec, tid);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        if (von + j < ns) dma_slot<VAR, kAuxFirst>(io, rzp, rzq, lp, lq, j, von + j, nvec, tid);
-      if (npair >= 2) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          if (von + 2 + j < ns) dma_slot<VAR, kAuxFirst>(io, rzp, rzq, lp, lq, 2 + j, von + 2 + j, nvec, tid);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) dma_slot<VAR, kAuxOnce>(io, rzp, rzq, lp, lq, 2 + j, nr + 2 + j, nvec, tid);
-      }
-    }
-    for (int q = 0; q < npair; ++q) {
-      const int h = q & 1;
-      const int after = (q + 1 < npair) ? full_ops(q + 1) : 4;
-      if (after >= 4) wait_vmem_but<4>();
-      else if (after >= 2) wait_vmem_but<2>();
-      else wait_vmem_all();
+    const int nst = ns - von;              // streamed slots
+    const int npair = (NR + nst + 1) >> 1;  // >= QR
+    auto slot_of = [&](int e) { return e < NR ? e : von + (e - NR); };  // ring entry -> row slot
+    const int nfullv = opaque(64);  // vectors of a wave block in a register slot
+    auto ops_of = [&](int q) {  // loads of pair q that every wave issues (resident slots past the end)
+      if (q >= npair) return 4;
+      int n = 0;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int sl = von + 2 * q + j;
-        if (sl < ns) {
-          const int nbv = io.nb(sl, nvec);
-          if (io.has(nbv))
-            acc_vec<VAR, TM>(io.lds(lp[2 * h + j], nbv), io.lds(lq[2 * h + j], nbv), io.lo(sl), io.H(nbv), A,
-                         false, sL);
-        }
+        const int e = 2 * q + j;
+        if (e < NR) n += 2;
+        else if (e < NR + nst && von + (e - NR) < nfull) n += 2;
       }
-      wait_lds_reads();  // this half is free again
-      if (q + 2 < npair) {
+      return n;
+    };
+    auto issue = [&](int q, int h) {  // pair q into half h, or the half's resident slots
+      if (q < npair) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int sl = von + 2 * (q + 2) + j;
-          if (sl < ns) dma_slot<VAR, kAuxFirst>(io, rzp, rzq, lp, lq, 2 * h + j, sl, nvec, tid);
+          const int e = 2 * q + j;
+          if (e < NR) dma_slot<VAR, kAuxOnce>(io, rzp, rzq, lp, lq, 2 * h + j, e, nvec, tid);
+          else if (e < NR + nst) dma_slot<VAR, kAuxFirst>(io, rzp, rzq, lp, lq, 2 * h + j, slot_of(e), nvec, tid);
         }
       } else {
 #pragma unroll
         for (int j = 0; j < 2; ++j) dma_slot<VAR, kAuxOnce>(io, rzp, rzq, lp, lq, 2 * h + j, nr + 2 * h + j, nvec, tid);
       }
+    };
+    auto wait_pair = [&](int q) {
+      const int after = ops_of(q + 1);
+      if (after >= 4) wait_vmem_but<4>();
+      else if (after >= 2) wait_vmem_but<2>();
+      else wait_vmem_all();
+    };
+    issue(0, 0);
+    issue(1, 1);
+#pragma unroll
+    for (int q = 0; q < QR; ++q) {  // pairs with register slots (compile-time indices)
+      const int h = q & 1;
+      wait_pair(q);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int e = 2 * q + j;
+        if (e < NR) {
+          if (io.has(nfullv)) {  // always: keeps one branch per register slot, as in the other forms
+            rp[e] = io.lds(lp[2 * h + j], 64);
+            rq[e] = io.lds(lq[2 * h + j], 64);
+            acc_vec<VAR, TM>(rp[e], rq[e], io.lo(e), io.H(64), A, true, sL);
+          }
+        } else if (e < NR + nst) {
+          const int sl = slot_of(e), nbv = io.nb(sl, nvec);
+          if (io.has(nbv))
+            acc_vec<VAR, TM>(io.lds(lp[2 * h + j], nbv), io.lds(lq[2 * h + j], nbv), io.lo(sl), io.H(nbv), A,
+                             false, sL);
+        }
+      }
+      wait_lds_reads();  // this half is free again
+      issue(q + 2, h);
+    }
+    for (int q = QR; q < npair; ++q) {  // streamed pairs
+      const int h = q & 1;
+      wait_pair(q);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int e = 2 * q + j;
+        if (e < NR + nst) {
+          const int sl = slot_of(e), nbv = io.nb(sl, nvec);
+          if (io.has(nbv))
+            acc_vec<VAR, TM>(io.lds(lp[2 * h + j], nbv), io.lds(lq[2 * h + j], nbv), io.lo(sl), io.H(nbv), A,
+                             false, sL);
+        }
+      }
+      wait_lds_reads();
+      issue(q + 2, h);
     }
   } else {
     const IO io(opaque(tid));
@@ -1254,7 +1284,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   }
   uint64_t nxt = 0;
   if (tid == 0) nxt = claim(a);  // its reply returns behind this row's loads
-  {
+  if constexpr (!RING) {  // the fast form folded its register slots in the ring
     const IO io(opaque(tid));
 #pragma unroll
     for (int v = 0; v < NR; ++v) {
