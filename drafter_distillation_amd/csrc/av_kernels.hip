@@ -1099,6 +1099,16 @@ __device__ __forceinline__ void wait_vmem_but() {  // all but the N most recent
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 __device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// All but the n most recent (n wave-uniform; counts above N wait as for N).
+template <int N>
+__device__ __forceinline__ void wait_vmem_upto(int n) {
+  if constexpr (N == 0) {
+    wait_vmem_all();
+  } else {
+    if (n >= N) wait_vmem_but<N>();
+    else wait_vmem_upto<N - 1>(n);
+  }
+}
 
 // Direct loads of slot s of a row's zp and zq into LDS slot position l.
 template <int VAR, int AUX>
@@ -1443,40 +1453,55 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
     const GradK gk = grad_consts<TM>(opaque_s(a.lam), opaque_s(a.gs), S32, st, lse_q1);
     const Rsrc rg = grad_rsrc<GB, IO::VEC>(a.grad, rowv, opaque_s(a.V));
     if constexpr (RING) {
-      // Stores of one full register slot's vector (all register slots are full).
-      constexpr int kRegStores = NR * (IO::kHalves ? 2 : 1);
-      static_assert(kRegStores <= 63, "vmcnt range");
+      // The resident slots' gradient frees both LDS halves; the streamed
+      // slots then come in again two at a time, double-buffered, the first
+      // two pairs behind the register slots' gradient.  A wait for pair q
+      // leaves outstanding what was issued after it (the register slots'
+      // stores, pair q - 1's stores, pair q + 1's loads), counted where every
+      // wave issues them, so the stores in flight need not drain.
+      constexpr int SPS = IO::kHalves ? 2 : 1;  // stores of one vector's gradient
+      constexpr int kRegStores = NR * SPS;      // all register slots are full
+      static_assert(kRegStores + 4 * SPS + 4 <= 63, "vmcnt range");
       const IO io(opaque(tid));
 #pragma unroll
       for (int l = 0; l < NL; ++l)
         grad_vec<VAR, GB, TM>(io.lds(lp[l], 64), io.lds(lq[l], 64), io, nr + l, 64, rk, gk, Arg, rg);
-      bool regs_done = false;
-      for (int s0 = von; s0 < ns; s0 += NL) {
-        wait_lds_reads();
+      const int np2 = (ns - von + 1) >> 1;
+      auto full = [&](int q, int j) { return q < np2 && von + 2 * q + j < nfull; };
+      auto loads_of = [&](int q) { return (full(q, 0) ? 2 : 0) + (full(q, 1) ? 2 : 0); };
+      auto stores_of = [&](int q) { return (full(q, 0) ? SPS : 0) + (full(q, 1) ? SPS : 0); };
+      auto reread = [&](int q, int h) {
+        if (q < np2) {
 #pragma unroll
-        for (int l = 0; l < NL; ++l)
-          if (s0 + l < ns) dma_slot<VAR, kAuxAgain>(io, rzp, rzq, lp, lq, l, s0 + l, nvec, tid);
-        if (!regs_done) {  // the register slots' gradient overlaps the first loads
-#pragma unroll
-          for (int v = 0; v < NR; ++v) grad_vec<VAR, GB, TM>(rp[v], rq[v], io, v, 64, rk, gk, Arg, rg);
-          wait_vmem_but<kRegStores>();
-          regs_done = true;
-        } else {
-          wait_vmem_all();
+          for (int j = 0; j < 2; ++j) {
+            const int sl = von + 2 * q + j;
+            if (sl < ns) dma_slot<VAR, kAuxAgain>(io, rzp, rzq, lp, lq, 2 * h + j, sl, nvec, tid);
+          }
         }
+      };
+      wait_lds_reads();
+      reread(0, 0);
+      reread(1, 1);
 #pragma unroll
-        for (int l = 0; l < NL; ++l) {
-          const int sl = s0 + l;
+      for (int v = 0; v < NR; ++v) grad_vec<VAR, GB, TM>(rp[v], rq[v], io, v, 64, rk, gk, Arg, rg);
+      for (int q = 0; q < np2; ++q) {
+        const int h = q & 1;
+        const int after = q == 0   ? loads_of(1) + kRegStores
+                          : q == 1 ? kRegStores + stores_of(0) + loads_of(2)
+                                   : stores_of(q - 1) + loads_of(q + 1);
+        wait_vmem_upto<kRegStores + 4 * SPS + 4>(after);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int sl = von + 2 * q + j;
           if (sl < ns) {
             const int nbv = io.nb(sl, nvec);
             if (io.has(nbv))
-              grad_vec<VAR, GB, TM>(io.lds(lp[l], nbv), io.lds(lq[l], nbv), io, sl, nbv, rk, gk, Arg, rg);
+              grad_vec<VAR, GB, TM>(io.lds(lp[2 * h + j], nbv), io.lds(lq[2 * h + j], nbv), io, sl, nbv, rk, gk,
+                                    Arg, rg);
           }
         }
-      }
-      if (!regs_done) {
-#pragma unroll
-        for (int v = 0; v < NR; ++v) grad_vec<VAR, GB, TM>(rp[v], rq[v], io, v, 64, rk, gk, Arg, rg);
+        wait_lds_reads();  // this half is free again
+        reread(q + 2, h);
       }
       wait_lds_reads();  // the next row's direct loads may overwrite the LDS slots
     } else {
