@@ -499,6 +499,47 @@ def bench_lm_head(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_hbm_probe(args):
+    """What the memory system delivers for the fused pass's byte patterns
+    without its arithmetic (drafter_distillation_amd/probe/hbm_probe.hip, run
+    as a child process): the achievable rates that the fused kernel's
+    algorithmic bandwidth is compared with, next to the 8 TB/s peak."""
+    import subprocess
+
+    from drafter_distillation_amd.build import PROBE_BIN
+
+    if not os.path.exists(PROBE_BIN):
+        raise SystemExit(f"{PROBE_BIN} is missing: build it with `python -m drafter_distillation_amd.build`")
+    out = subprocess.run([PROBE_BIN], capture_output=True, text=True, check=True).stdout
+    runs = []
+    for line in out.splitlines():
+        pat, block, per_cu, us, gbs = line.split()
+        runs.append({"pattern": pat, "block": int(block), "workgroups_per_cu": int(per_cu),
+                     "us": float(us), "GBs": float(gbs)})
+    best = {}
+    for r in runs:
+        if r["pattern"] not in best or r["GBs"] > best[r["pattern"]]["GBs"]:
+            best[r["pattern"]] = r
+    rows1024 = max((r for r in runs if r["pattern"] == "rows" and r["block"] == 1024), key=lambda r: r["GBs"])
+    line = {
+        "metric": "HBM bandwidth of the fused pass's byte patterns without arithmetic (GB/s)",
+        "value": rows1024["GBs"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "higher_is_better": True,
+        "data": "synthetic",
+        "config": {
+            "workload": "2048 rows of V=151936 bf16 zp and zq (622 MB each), a 1245 MB float32 gradient; "
+                        "value: one 1024-thread workgroup per row reads the row, barrier, writes its "
+                        "gradient (a verified row's phases)",
+            "best_by_pattern_GBs": {k: v["GBs"] for k, v in best.items()},
+            "frac_of_8TBs_by_pattern": {k: round(v["GBs"] / HBM_PEAK_GBS, 4) for k, v in best.items()},
+            "runs": runs,
+        },
+    }
+    print(json.dumps(line))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -511,7 +552,7 @@ def main():
                     help="gradient output type of the fused pass (default float32)")
     ap.add_argument("--temperature", type=float, default=1.0,
                     help="reverse-KL temperature of the fused pass (default 1: the plain pass)")
-    ap.add_argument("--workload", choices=["concurrent", "head_update", "spec", "lm_head"],
+    ap.add_argument("--workload", choices=["concurrent", "head_update", "spec", "lm_head", "hbm_probe"],
                     default="concurrent",
                     help="concurrent: the fused verify+OPD step (default); head_update: the "
                          "length head's online update; spec: sampling-based verification")
@@ -544,6 +585,9 @@ def main():
         return
     if args.workload == "lm_head":
         bench_lm_head(args)
+        return
+    if args.workload == "hbm_probe":
+        bench_hbm_probe(args)
         return
 
     import numpy as np

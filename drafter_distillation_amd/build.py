@@ -1,4 +1,5 @@
-"""Build the gfx950 HIP library in-tree: drafter_distillation_amd/libav.so.
+"""Build the gfx950 HIP library in-tree: drafter_distillation_amd/libav.so
+(and the HBM probe executable drafter_distillation_amd/probe/hbm_probe).
 
     python -m drafter_distillation_amd.build
 
@@ -23,6 +24,11 @@ LIB = os.path.join(PKG, "libav.so")
 OBJDIR = os.path.join(PKG, "_build")
 
 SOURCES = ["av_kernels.hip", "av_api.hip", "av_lmhead.hip"]
+
+# Stand-alone HBM bandwidth probe (bench.py --workload hbm_probe): the access
+# patterns of the fused pass without its arithmetic.
+PROBE_SRC = os.path.join(PKG, "probe", "hbm_probe.hip")
+PROBE_BIN = os.path.join(PKG, "probe", "hbm_probe")
 
 # Libraries the shared library links: hipBLASLt runs the LM-head backward's
 # plain GEMMs (csrc/av_lmhead.hip).
@@ -80,6 +86,8 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         objs.append(obj)
         cmds.append([hipcc, *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), *extra_flags, "-c",
                      os.path.join(CSRC, src), "-o", obj])
+    cmds.append([hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+                 "-packed-fp32-ops", "-Wall", PROBE_SRC, "-o", PROBE_BIN])
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB + ".tmp"
