@@ -436,6 +436,11 @@ constexpr int kLastWave = kRowWaves - 1;  // publishes rows and finishes request
 // underflow (an entry that small relative to the max has q_j |ell_j| far
 // below any tau for finite logits).
 constexpr float kRescaleFloor = 0x1p-100f;
+// A region whose bound on q_j |ell_j| stays below this fraction of tau needs
+// no entry-by-entry clip check.  The bound and the gradient pass's r_j carry
+// float32 rounding of order 1e-5 relative; the 1% margin covers it many times
+// over, so no entry of a certified region can reach the interval's edge.
+constexpr float kClipCertify = 0.99f;
 
 template <int VAR>
 struct RowCfg {  // vectors per thread kept in registers (NR) and in LDS (NL)
@@ -1362,9 +1367,10 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   // ---- clipping: an entry's |r_j| = q_j |ell_j| is at most
   //   exp(m_t - lse_q) exp(zq_j - m_t) |zq_j - zp_j| + exp(zq_j - lse_q) |lse_q - lse_p|
   // (m_t: the thread's max zq).  Every entry of a region whose bound stays
-  // below tau / 2 lies inside the clip interval; only regions that fail it
-  // are evaluated entry by entry, and S and the clipped KL follow from the
-  // unclipped sums minus those corrections ----
+  // below kClipCertify * tau lies inside the clip interval; only regions that
+  // fail it are evaluated entry by entry, and S and the clipped KL follow from
+  // the unclipped sums minus those corrections (zero for every entry inside
+  // the interval, so a certified region would contribute nothing) ----
   // (tempered: exp(s m_t - lse_q) exp(s (zq_j - m_t)) s |zq_j - zp_j| + exp(s zq_j - lse_q) |delta|)
   const float adelta = __builtin_fabsf(rk.delta);
   bool flag_on, flag_st;
@@ -1372,18 +1378,18 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
     const float ets = __builtin_amdgcn_exp2f(__builtin_fmaf(A.mq, sL, -rk.lseqL)) * st;
     flag_on = __builtin_fmaf(ets, A.pm_on,
                              adelta * __builtin_amdgcn_exp2f(__builtin_fmaf(A.mq_on, sL, -rk.lseqL))) >
-              0.5f * tau;
+              kClipCertify * tau;
     flag_st = __builtin_fmaf(ets, A.pm_st,
                              adelta * __builtin_amdgcn_exp2f(__builtin_fmaf(A.mq_st, sL, -rk.lseqL))) >
-              0.5f * tau;
+              kClipCertify * tau;
   } else {
     const float et = __builtin_amdgcn_exp2f((A.mq - lse_q32) * kLog2e);
     flag_on =
         __builtin_fmaf(et, A.pm_on, adelta * __builtin_amdgcn_exp2f((A.mq_on - lse_q32) * kLog2e)) >
-        0.5f * tau;
+        kClipCertify * tau;
     flag_st =
         __builtin_fmaf(et, A.pm_st, adelta * __builtin_amdgcn_exp2f((A.mq_st - lse_q32) * kLog2e)) >
-        0.5f * tau;
+        kClipCertify * tau;
   }
   float cs = 0.0f, ck = 0.0f;
   if (flag_on) {
