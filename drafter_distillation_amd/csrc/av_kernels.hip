@@ -1459,19 +1459,18 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
     const GradK gk = grad_consts<TM>(opaque_s(a.lam), opaque_s(a.gs), S32, st, lse_q1);
     const Rsrc rg = grad_rsrc<GB, IO::VEC>(a.grad, rowv, opaque_s(a.V));
     if constexpr (RING) {
-      // The resident slots' gradient frees both LDS halves; the streamed
+      // Each LDS half's resident slots' gradient frees the half; the streamed
       // slots then come in again two at a time, double-buffered, the first
       // two pairs behind the register slots' gradient.  A wait for pair q
-      // leaves outstanding what was issued after it (the register slots'
-      // stores, pair q - 1's stores, pair q + 1's loads), counted where every
-      // wave issues them, so the stores in flight need not drain.
+      // leaves outstanding what was issued after it (half 1's resident and
+      // the register slots' stores, pair q - 1's stores, pair q + 1's loads),
+      // counted where every wave issues them, so the stores in flight need
+      // not drain.
       constexpr int SPS = IO::kHalves ? 2 : 1;  // stores of one vector's gradient
       constexpr int kRegStores = NR * SPS;      // all register slots are full
       static_assert(kRegStores + 4 * SPS + 4 <= 63, "vmcnt range");
+      static_assert(NL == 4, "two halves of two LDS slots");
       const IO io(opaque(tid));
-#pragma unroll
-      for (int l = 0; l < NL; ++l)
-        grad_vec<VAR, GB, TM>(io.lds(lp[l], 64), io.lds(lq[l], 64), io, nr + l, 64, rk, gk, Arg, rg);
       const int np2 = (ns - von + 1) >> 1;
       auto full = [&](int q, int j) { return q < np2 && von + 2 * q + j < nfull; };
       auto loads_of = [&](int q) { return (full(q, 0) ? 2 : 0) + (full(q, 1) ? 2 : 0); };
@@ -1485,14 +1484,21 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
           }
         }
       };
-      wait_lds_reads();
-      reread(0, 0);
-      reread(1, 1);
+      // Each half's resident slots, then its first streamed pair.
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          grad_vec<VAR, GB, TM>(io.lds(lp[2 * h + j], 64), io.lds(lq[2 * h + j], 64), io, nr + 2 * h + j, 64, rk,
+                                gk, Arg, rg);
+        wait_lds_reads();
+        reread(h, h);
+      }
 #pragma unroll
       for (int v = 0; v < NR; ++v) grad_vec<VAR, GB, TM>(rp[v], rq[v], io, v, 64, rk, gk, Arg, rg);
       for (int q = 0; q < np2; ++q) {
         const int h = q & 1;
-        const int after = q == 0   ? loads_of(1) + kRegStores
+        const int after = q == 0   ? 2 * SPS + loads_of(1) + kRegStores
                           : q == 1 ? kRegStores + stores_of(0) + loads_of(2)
                                    : stores_of(q - 1) + loads_of(q + 1);
         wait_vmem_upto<kRegStores + 4 * SPS + 4>(after);
