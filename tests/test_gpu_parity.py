@@ -112,6 +112,26 @@ def test_small_shapes(av, dtype, V, vecs):
     full_parity(av, w, bk, 0.5, 0.1, gs=0.25, vecs=vecs)
 
 
+# Rows wide enough for the fast form (every on-chip slot filled: 13 slots of
+# 1024 16-byte vectors), at the edges of its LDS ring: no streamed slot, one
+# partial streamed slot of a single vector, one full slot, and an odd count
+# that ends in a partial slot only some waves load.
+FAST_BF16 = [106496, 106496 + 8, 106496 + 8192, 106496 + 2 * 8192 + 512 * 8]
+FAST_F32 = [53248, 53248 + 4, 53248 + 2 * 4096 + 100 * 4]
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", v) for v in FAST_BF16] + [("f32", v) for v in FAST_F32])
+def test_fast_form_ring_edges(av, dtype, V):
+    w = synth.make("concurrent", B=3, V=V, dtype=dtype)
+    bk = np.array([1, 16, 7])
+    out = full_parity(av, w, bk, 0.5, 0.1, gs=0.25)
+    inp = gpu_inputs(w)
+    g = av.av_verify_opd_bwd(inp["zp"], inp["zq"], torch.from_numpy(out["tgt_argmax"]).cuda(),
+                             torch.from_numpy(out["row_stats"]).cuda(), k=w.k, lam=0.5, tau=0.1,
+                             grad_scale=0.25, bk=torch.from_numpy(bk.astype(np.int32)).cuda())
+    assert np.array_equal(g.cpu().numpy().view(np.uint32), out["grad"].view(np.uint32))
+
+
 @pytest.mark.parametrize("lam", [0.0, 0.5, 1.0])
 @pytest.mark.parametrize("tau", [0.01, 0.05, 0.1, 1e9, float("inf")])
 def test_lambda_tau_branches(av, lam, tau):
