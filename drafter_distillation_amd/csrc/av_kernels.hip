@@ -441,6 +441,11 @@ constexpr float kRescaleFloor = 0x1p-100f;
 // float32 rounding of order 1e-5 relative; the 1% margin covers it many times
 // over, so no entry of a certified region can reach the interval's edge.
 constexpr float kClipCertify = 0.99f;
+// Temperature-1 sums are rescaled only when a logit passes their reference by
+// more than this (natural-log units): every term exp(z - ref) stays below
+// e^11 < 2^16, so a thread's float32 sums cannot overflow, and the rounding
+// of exponents up to 16 (log2 units) is under 1e-6 relative per term.
+constexpr float kLazyGap = 11.0f;
 
 template <int VAR>
 struct RowCfg {  // vectors per thread kept in registers (NR) and in LDS (NL)
@@ -477,6 +482,7 @@ struct RowAcc {
   float kq;      // sum exp(zq - mq) (zq - zp): the reverse KL, once normalised
   float sq1;     // tempered form: sum exp(zq - mq) at temperature 1 (the sums
                  // above then scale exponents by 1 / T; kq's difference does not)
+  float rp;      // temperature 1: reference of sp (sp = sum exp(zp - rp)), see kLazyGap
   float mq_on, mq_st;  // per region (on chip / streamed): max zq
   float pm_on, pm_st;  // per region: max exp(zq - mq) |zq - zp| (mq: running max)
 };
@@ -484,6 +490,7 @@ struct RowAcc {
 __device__ __forceinline__ void acc_init(RowAcc& A) {
   A.mp = -INFINITY;
   A.sp = 0.0f;
+  A.rp = -INFINITY;
   A.bi = INT_MAX;
   A.za = 0.0f;
   A.mq = -INFINITY;
@@ -537,36 +544,64 @@ __device__ __forceinline__ void acc_vec(const typename Tr<VAR>::S& xp, const typ
     }
   }
   const float np = fmaxf(A.mp, vp);
+  if constexpr (!TM) {
+    // Temperature 1: the sums keep their references (rp for zp, mq for zq)
+    // until a value passes one by more than kLazyGap; only then (rarely, for
+    // the whole wave at once) are they rescaled, to the running maxima.
+    A.mp = np;
+    if (__builtin_expect(__any(vp > A.rp + kLazyGap || vq > A.mq + kLazyGap), 0)) {
+      A.sp *= __builtin_amdgcn_exp2f((A.rp - np) * kLog2e);
+      A.rp = np;
+      const float nq = fmaxf(A.mq, vq);
+      const float sc = __builtin_amdgcn_exp2f((A.mq - nq) * kLog2e);
+      A.sq *= sc;
+      A.kq *= sc;
+      const float scb = fmaxf(sc, kRescaleFloor);
+      A.pm_on *= scb;
+      A.pm_st *= scb;
+      A.mq = nq;
+    }
+    const float rpL = A.rp * kLog2e, rqL = A.mq * kLog2e;
+    float pm = 0.0f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const float q = T::at(xq, e), p = T::at(xp, e);
+      A.sp += __builtin_amdgcn_exp2f(__builtin_fmaf(p, kLog2e, -rpL));
+      const float eq = __builtin_amdgcn_exp2f(__builtin_fmaf(q, kLog2e, -rqL));
+      const float d = q - p;
+      A.sq += eq;
+      A.kq = __builtin_fmaf(eq, d, A.kq);
+      pm = fmaxf(pm, eq * __builtin_fabsf(d));
+    }
+    if (onchip) {
+      A.mq_on = fmaxf(A.mq_on, vq);
+      A.pm_on = fmaxf(A.pm_on, pm);
+    } else {
+      A.mq_st = fmaxf(A.mq_st, vq);
+      A.pm_st = fmaxf(A.pm_st, pm);
+    }
+    return;
+  }
   A.sp *= __builtin_amdgcn_exp2f((A.mp - np) * L);
   A.mp = np;
-  const float npL = np * L;
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) {
-    if constexpr (TM) A.sp += __builtin_amdgcn_exp2f((T::at(xp, e) - np) * L);
-    else A.sp += __builtin_amdgcn_exp2f(__builtin_fmaf(T::at(xp, e), L, -npL));
-  }
+  for (int e = 0; e < VEC; ++e) A.sp += __builtin_amdgcn_exp2f((T::at(xp, e) - np) * L);
   const float nq = fmaxf(A.mq, vq);
   const float sc = __builtin_amdgcn_exp2f((A.mq - nq) * L);
   A.sq *= sc;
   A.kq *= sc;
-  if constexpr (TM) A.sq1 *= __builtin_amdgcn_exp2f((A.mq - nq) * kLog2e);
+  A.sq1 *= __builtin_amdgcn_exp2f((A.mq - nq) * kLog2e);
   const float scb = fmaxf(sc, kRescaleFloor);
   A.pm_on *= scb;
   A.pm_st *= scb;
   A.mq = nq;
-  const float nqL = nq * L;
   float pm = 0.0f;
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
     const float q = T::at(xq, e), p = T::at(xp, e);
-    float eq;
-    if constexpr (TM) {
-      const float dq = q - nq;
-      eq = __builtin_amdgcn_exp2f(dq * L);
-      A.sq1 += __builtin_amdgcn_exp2f(dq * kLog2e);
-    } else {
-      eq = __builtin_amdgcn_exp2f(__builtin_fmaf(q, kLog2e, -nqL));
-    }
+    const float dq = q - nq;
+    const float eq = __builtin_amdgcn_exp2f(dq * L);
+    A.sq1 += __builtin_amdgcn_exp2f(dq * kLog2e);
     const float d = q - p;
     A.sq += eq;
     A.kq = __builtin_fmaf(eq, d, A.kq);
@@ -1322,6 +1357,10 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   // ---- combine the statistics of the 1024 threads: wave butterflies, then
   // every wave merges the 16 wave partials the same way ----
   RowAcc W = A;
+  if constexpr (!TM) {  // the merges take the zp sum relative to the running max
+    W.sp = (W.sp == 0.0f) ? 0.0f : W.sp * __builtin_amdgcn_exp2f((W.rp - W.mp) * kLog2e);
+    W.rp = W.mp;
+  }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) merge_step<TM>(W, o, sL);
   if (lane == 0) {
