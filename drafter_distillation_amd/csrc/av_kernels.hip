@@ -651,6 +651,38 @@ __device__ __forceinline__ void merge_step(RowAcc& A, int o, float sL) {
   lse_merge(A.mq, A.sq, A.kq, omq, osq, okq, L);
 }
 
+// Temperature 1: a wave's row statistics combined by one pass of maxima, one
+// rescale of each lane's sums and one pass of sums (instead of a log-sum-exp
+// merge at each butterfly level).  On entry sp is relative to mp; on exit
+// every lane holds the same bits: the wave's max of zp, its first index and
+// the zq there, the sums relative to the wave's maxima, and kq.  Lanes with
+// empty sums contribute nothing.
+__device__ __forceinline__ void wave_combine(RowAcc& W) {
+  const float M = wmax(W.mp);
+  int bi = (W.mp == M) ? W.bi : INT_MAX;
+  float za = W.za;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const int obi = __shfl_xor(bi, o);
+    const float oza = __shfl_xor(za, o);
+    if (obi < bi) {
+      bi = obi;
+      za = oza;
+    }
+  }
+  const float sp = (W.sp == 0.0f) ? 0.0f : W.sp * __builtin_amdgcn_exp2f((W.mp - M) * kLog2e);
+  const float Mq = wmax(W.mq);
+  const float f = (W.sq == 0.0f) ? 0.0f : __builtin_amdgcn_exp2f((W.mq - Mq) * kLog2e);
+  W.sp = wsum(sp);
+  W.sq = wsum(W.sq * f);
+  W.kq = wsum(W.kq * f);
+  W.mp = M;
+  W.rp = M;
+  W.bi = bi;
+  W.za = za;
+  W.mq = Mq;
+}
+
 // Sum of the first 16 lanes, in a fixed order, broadcast from lane 0.
 __device__ __forceinline__ double wsumd16(double v) {
 #pragma unroll
@@ -1360,9 +1392,11 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   if constexpr (!TM) {  // the merges take the zp sum relative to the running max
     W.sp = (W.sp == 0.0f) ? 0.0f : W.sp * __builtin_amdgcn_exp2f((W.rp - W.mp) * kLog2e);
     W.rp = W.mp;
-  }
+    wave_combine(W);
+  } else {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) merge_step<TM>(W, o, sL);
+    for (int o = 32; o >= 1; o >>= 1) merge_step<TM>(W, o, sL);
+  }
   if (lane == 0) {
     sm.f[par][wid][0] = W.mp;
     sm.f[par][wid][1] = W.sp;
@@ -1386,8 +1420,12 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
     if constexpr (TM) W.sq1 = sm.f1[par][lane];
     W.bi = sm.i[par][lane];
   }
+  if constexpr (TM) {
 #pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) merge_step<TM>(W, o, sL);
+    for (int o = 8; o >= 1; o >>= 1) merge_step<TM>(W, o, sL);
+  } else {
+    wave_combine(W);
+  }
   const float mp = __shfl(W.mp, 0), sp = __shfl(W.sp, 0);
   const float mq = __shfl(W.mq, 0), sq = __shfl(W.sq, 0), kq = __shfl(W.kq, 0);
   const float zqa = __shfl(W.za, 0);
