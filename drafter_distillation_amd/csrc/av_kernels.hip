@@ -2019,20 +2019,55 @@ __device__ __forceinline__ void spec_fold(const typename Tr<VAR>::S& xp, const t
   }
 }
 
-// Step 1, one 256-thread workgroup per stored row (unverified dense rows
-// exit): lse_p, lse_q and the acceptance decision u * q(d) < p(d) (a draft
-// outside [0, V) is rejected).
+// Dense layout: the w-th verified row in request-major order, or -1 when
+// there are fewer than w + 1 (one wave's prefix scan over the requests).
+__device__ __forceinline__ int nth_verified_row(const SpecArgs& a, int w) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int b = b0 + lane;
+    const int nb = b < a.B ? min(max(a.bk[b], 1), a.k) : 0;
+    int incl = nb;  // inclusive prefix sum over the lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    const int excl = base + incl - nb;
+    const uint64_t hit = __ballot(nb > 0 && w >= excl && w < excl + nb);
+    if (hit) {
+      const int src = __ffsll((unsigned long long)hit) - 1;
+      return __shfl((b0 + lane) * a.k + (w - excl), src);
+    }
+    base += __shfl(incl, 63);
+  }
+  return -1;
+}
+
+// Step 1, one 256-thread workgroup per verified row: lse_p, lse_q and the
+// acceptance decision u * q(d) < p(d) (a draft outside [0, V) is rejected).
+// In the dense layout workgroup w takes the w-th verified row (the launch has
+// one per stored row; the surplus exit), so consecutive workgroups, which the
+// dispatcher spreads over the CUs, hold rows at every position and the
+// verified rows spread evenly.
 template <int VAR>
 __global__ __launch_bounds__(kBlock) void spec_stats_kernel(SpecArgs a) {
   using T = Tr<VAR>;
   using S = typename T::S;
   constexpr uint32_t VB = T::VEC * T::EB;
   __shared__ float s[kWaves][4];
-  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  if (r == 0 && tid == 0 && a.status) a.status[0] = 0;
+  __shared__ int s_row;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  if (blockIdx.x == 0 && tid == 0 && a.status) a.status[0] = 0;
+  int r = blockIdx.x;
   if (!a.ragged) {
-    const int req = r / a.k, i = r - req * a.k;
-    if (i >= min(max(a.bk[req], 1), a.k)) return;
+    if (wid == 0) {
+      const int row = nth_verified_row(a, (int)blockIdx.x);
+      if (lane == 0) s_row = row;
+    }
+    __syncthreads();
+    r = s_row;
+    if (r < 0) return;
   }
   const long long rowv = (long long)r * a.nvec;
   const Rsrc rzp = row_rsrc(T::row(a.zp, rowv), (uint32_t)a.V * T::EB);
