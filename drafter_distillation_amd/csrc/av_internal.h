@@ -150,7 +150,10 @@ struct SpecArgs {
   int chunk, nchunk;  // vectors per chunk of the race, chunks per row (<= kSpecMaxChunks)
 };
 constexpr int kSpecMaxChunks = 64;
-constexpr int kSpecChunkVecs = 2048;  // fewest vectors per chunk
+// Fewest vectors per chunk of the race (512: 38 chunks of a 151936-wide bf16
+// row, enough workgroups to keep the generator's arithmetic busy; 2048 was
+// 3% slower, 256 slower again).
+constexpr int kSpecChunkVecs = 512;
 
 // full: every on-chip slot of a row is filled (nvec >= (regs + lds) * kRowBlock)
 // and the default on-chip split is used.
