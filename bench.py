@@ -499,6 +499,83 @@ def bench_lm_head(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_bwd(args):
+    """The standalone backward (av_verify_opd_bwd) on the concurrent workload:
+    the gradient from the statistics a forward call without gradient saved.
+    Bytes per call: zp and zq of the verified rows read once, the gradient of
+    every row written (zeros for unverified rows), the row statistics and
+    argmax of the verified rows read."""
+    import numpy as np
+    import torch
+
+    import drafter_distillation_amd as dd
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dd.lib()
+    w = synth.make("concurrent", seed=args.seed)
+    B, k, V, R = w.B, w.k, w.V, w.R
+    zp = torch.from_numpy(w.zp.view(np.int16)).view(torch.bfloat16).to(dev)
+    zq = torch.from_numpy(w.zq.view(np.int16)).view(torch.bfloat16).to(dev)
+    draft = torch.from_numpy(w.draft).to(dev)
+    bk = torch.empty(B, dtype=torch.int32, device=dev)
+    dd.av_length_head(torch.from_numpy(w.h).to(dev), torch.from_numpy(w.w).to(dev), w.bias, w.gamma, k,
+                      bk_out=bk)
+    fwd = dd.av_verify_opd_fwd(zp, zq, draft, k=k, bk=bk, lam=w.lam, tau=w.tau, want_grad=False)
+    gdt = torch.bfloat16 if args.grad == "bf16" else torch.float32
+    grad = torch.empty((R, V), dtype=gdt, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev0=None, ev1=None):
+        if ev0 is not None:
+            ev0.record(stream)
+        dd.av_verify_opd_bwd(zp, zq, fwd["tgt_argmax"], fwd["row_stats"], k=k, bk=bk, lam=w.lam,
+                             tau=w.tau, grad_scale=1.0, grad=grad, grad_dtype=gdt)
+        if ev1 is not None:
+            ev1.record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    Rv = int(torch.clamp(bk, 1, k).sum().item())
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        step(e0, e1)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    gelem = 2 if args.grad == "bf16" else 4
+    nbytes = 2 * 2 * V * Rv + gelem * V * R + (16 + 4) * Rv + 4 * B
+    kern_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs)
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    line = {
+        "metric": "standalone OPD backward GB/s at B=128,k=16,V=151936 bf16"
+                  + (", bf16 gradient" if args.grad == "bf16" else ""),
+        "value": round(achieved, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "bwd: the concurrent workload (B=128, k=16, V=151936, bf16 logits, b_k from the "
+                        "length head); gradient from the saved row statistics",
+            "B": B, "k": k, "V": V, "rows": R, "verified_rows": Rv, "grad": args.grad,
+            "bytes_per_call": nbytes, "kernel_ms": round(kern_ms, 4),
+        },
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    print(json.dumps(line))
+
+
 def bench_hbm_probe(args):
     """What the memory system delivers for the fused pass's byte patterns
     without its arithmetic (drafter_distillation_amd/probe/hbm_probe.hip, run
@@ -552,7 +629,7 @@ def main():
                     help="gradient output type of the fused pass (default float32)")
     ap.add_argument("--temperature", type=float, default=1.0,
                     help="reverse-KL temperature of the fused pass (default 1: the plain pass)")
-    ap.add_argument("--workload", choices=["concurrent", "head_update", "spec", "lm_head", "hbm_probe"],
+    ap.add_argument("--workload", choices=["concurrent", "head_update", "spec", "lm_head", "hbm_probe", "bwd"],
                     default="concurrent",
                     help="concurrent: the fused verify+OPD step (default); head_update: the "
                          "length head's online update; spec: sampling-based verification")
@@ -588,6 +665,9 @@ def main():
         return
     if args.workload == "hbm_probe":
         bench_hbm_probe(args)
+        return
+    if args.workload == "bwd":
+        bench_bwd(args)
         return
 
     import numpy as np

@@ -1768,16 +1768,43 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(BwdArgs a) {
   const void* zq_r = T::row(a.zq, rowv);
   float* g_r = (float*)a.grad + rowv * VEC;
   uint16_t* gb_r = (uint16_t*)a.grad + rowv * VEC;
+  // bfloat16 rows (8 entries per vector): each wave takes a block of 64
+  // vectors, and lane l the entries 4l..4l+3 of the block's first half and
+  // the same four of its second half (halves of 4 nbv entries), so every
+  // store instruction of a wave writes one contiguous stretch (with 8
+  // consecutive entries per lane each 16-byte store would fill only half of
+  // every 32 bytes, and the gradient's write traffic would nearly double).
+  constexpr bool kHalves = VAR == kBf16x8;
+  const int lane = tid & 63, wid = tid >> 6;
+  auto block_of = [&](int v, int& base, int& nbv) {
+    base = vlo + v * kBlock + wid * 64;
+    nbv = min(max(vhi - base, 0), 64);
+  };
   if (!verified) {
     float z[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) z[e] = 0.0f;
 #pragma unroll
     for (int v = 0; v < NVMAX; ++v) {
-      const int vi = vlo + v * kBlock + tid;
-      if (vi < vhi) {
-        if constexpr (GB) store_vec_bf16<VEC>(gb_r, (unsigned)vi, z);
-        else store_vec<VEC>(g_r, (unsigned)vi, z);
+      if constexpr (kHalves) {
+        int base, nbv;
+        block_of(v, base, nbv);
+        if (lane < nbv) {
+          const long long e0 = 8LL * base + 4 * lane, e1 = e0 + 4LL * nbv;
+          if constexpr (GB) {
+            __builtin_nontemporal_store((u32x2){0u, 0u}, (u32x2*)(gb_r + e0));
+            __builtin_nontemporal_store((u32x2){0u, 0u}, (u32x2*)(gb_r + e1));
+          } else {
+            store16_nt(g_r + e0, (f32x4){0.0f, 0.0f, 0.0f, 0.0f});
+            store16_nt(g_r + e1, (f32x4){0.0f, 0.0f, 0.0f, 0.0f});
+          }
+        }
+      } else {
+        const int vi = vlo + v * kBlock + tid;
+        if (vi < vhi) {
+          if constexpr (GB) store_vec_bf16<VEC>(gb_r, (unsigned)vi, z);
+          else store_vec<VEC>(g_r, (unsigned)vi, z);
+        }
       }
     }
     return;
@@ -1787,6 +1814,48 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(BwdArgs a) {
   const RowK rk = row_consts<TM>(st[0], st[1], a.tau, a.inv_t, a.inv_tl);
   const GradK gk = grad_consts<TM>(a.lam, a.gs, st[2], a.inv_t, TM ? a.lse1[row] : 0.0f);
   S xp[NVMAX], xq[NVMAX];
+  if constexpr (kHalves) {
+    const char* pb = (const char*)zp_r;
+    const char* qb = (const char*)zq_r;
+#pragma unroll
+    for (int v = 0; v < NVMAX; ++v) {
+      int base, nbv;
+      block_of(v, base, nbv);
+      if (lane < nbv) {
+        const long long o0 = 16LL * base + 8 * lane, o1 = o0 + 8LL * nbv;
+        const u32x2 p0 = *(const u32x2*)(pb + o0), p1 = *(const u32x2*)(pb + o1);
+        const u32x2 q0 = *(const u32x2*)(qb + o0), q1 = *(const u32x2*)(qb + o1);
+        xp[v] = S{p0.x, p0.y, p1.x, p1.y};
+        xq[v] = S{q0.x, q0.y, q1.x, q1.y};
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < NVMAX; ++v) {
+      int base, nbv;
+      block_of(v, base, nbv);
+      if (lane < nbv) {
+        const long long e0 = 8LL * base + 4 * lane, e1 = e0 + 4LL * nbv;
+        float out[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          float q, r, g;
+          opd_entry<TM>(T::at(xp[v], e), T::at(xq[v], e), rk, q, r, g);
+          out[e] = grad_entry<TM>(q, g, T::at(xq[v], e), gk);
+          if ((e < 4 ? e0 + e : e1 + (e - 4)) == (long long)A) out[e] = out[e] - gk.fix;
+        }
+        if constexpr (GB) {
+          __builtin_nontemporal_store((u32x2){pack_bf16(out[0], out[1]), pack_bf16(out[2], out[3])},
+                                      (u32x2*)(gb_r + e0));
+          __builtin_nontemporal_store((u32x2){pack_bf16(out[4], out[5]), pack_bf16(out[6], out[7])},
+                                      (u32x2*)(gb_r + e1));
+        } else {
+          store16_nt(g_r + e0, (f32x4){out[0], out[1], out[2], out[3]});
+          store16_nt(g_r + e1, (f32x4){out[4], out[5], out[6], out[7]});
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int v = 0; v < NVMAX; ++v) {
     const int vi = vlo + v * kBlock + tid;
