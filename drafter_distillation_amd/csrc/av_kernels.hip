@@ -1897,7 +1897,32 @@ __device__ __forceinline__ double head_rate(const float* hb, const float* w, int
                                             double* s) {
   const int tid = threadIdx.x;
   double acc = 0.0;
-  for (int j = tid; j < H; j += kBlock) acc = fma((double)hb[j], (double)w[j], acc);
+  if (H % 4 == 0 && ((uintptr_t)hb % 16u) == 0 && ((uintptr_t)w % 16u) == 0) {
+    // 16-byte loads, four per operand in flight before the fp64 FMAs
+    const f32x4* h4 = (const f32x4*)hb;
+    const f32x4* w4 = (const f32x4*)w;
+    const int n4 = H >> 2;
+    int j = tid;
+    for (; j + 3 * kBlock < n4; j += 4 * kBlock) {
+      f32x4 x[4], y[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        x[u] = h4[j + u * kBlock];
+        y[u] = w4[j + u * kBlock];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = fma((double)x[u][e], (double)y[u][e], acc);
+    }
+    for (; j < n4; j += kBlock) {
+      const f32x4 x = h4[j], y = w4[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = fma((double)x[e], (double)y[e], acc);
+    }
+  } else {
+    for (int j = tid; j < H; j += kBlock) acc = fma((double)hb[j], (double)w[j], acc);
+  }
   acc = wsumd(acc);
   if ((tid & 63) == 0) s[tid >> 6] = acc;
   __syncthreads();
