@@ -64,6 +64,27 @@ def test_length_head(av, name, mode):
         np.testing.assert_allclose(rate, ref_rate, rtol=1e-6, atol=1e-30)
 
 
+@pytest.mark.parametrize("H", [301, 4097, 4096])
+def test_length_head_odd_width_and_misaligned(av, H):
+    # the dot product reads 16-byte vectors only when H % 4 == 0 and both
+    # operands are 16-byte aligned; odd widths and an operand at a 4-byte
+    # offset take the scalar loop
+    rng = np.random.default_rng(H)
+    B = 37
+    h = (rng.standard_normal((B, H)) / np.sqrt(H)).astype(np.float32)
+    w = (rng.standard_normal(H) / np.sqrt(H) * 8.0).astype(np.float32)
+    buf = torch.empty(B * H + 1, dtype=torch.float32, device="cuda")
+    hd = buf[1:].view(B, H)
+    hd.copy_(torch.from_numpy(h))
+    for hh in (torch.from_numpy(h).cuda(), hd):
+        rate, bk = av.av_length_head(hh, torch.from_numpy(w).cuda(), 0.1, 1.0, 16)
+        ref_rate, ref_bk, margin = oracle.length_head(h, w, 0.1, 1.0, 16)
+        rate, bk = rate.cpu().numpy(), bk.cpu().numpy()
+        sure = margin > 1e-9
+        assert np.array_equal(bk[sure], ref_bk[sure])
+        np.testing.assert_allclose(rate, ref_rate, rtol=1e-6, atol=1e-30)
+
+
 def test_length_head_extremes(av):
     H = 300
     w = np.full(H, 1.0, np.float32)
