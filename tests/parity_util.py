@@ -11,6 +11,10 @@ Acceptance rule (the arithmetic behind it is written out in the design notes):
     reference itself cancels to near zero; with a reverse-KL temperature
     T != 1 that term is scaled by 1 / T (the KL part's factor) and
     2e-5 gs q1_j is added for the cross-entropy part's own softmax q1;
+    an entry other than the label whose q_j (and q1_j) lies below the
+    smallest normal float32, 2^-126 (a logit about 87 below the row's
+    log-sum-exp), may read anything between 0 and the reference: the float32
+    exponential flushes such q_j to zero;
   * lse of zq at temperature 1 (lse_q1): as lse_p, lse_q;
   * an entry whose |r_j| lies within 1e-4 tau of tau may be classified either
     way by float32; rows with such entries are accepted if they match the
@@ -32,6 +36,7 @@ import synth
 LOSS_RTOL, LOSS_ATOL = 1e-3, 1e-5
 LSE_RTOL, LSE_ATOL = 2e-6, 2e-6
 GRAD_RTOL, GRAD_QTOL = 1e-3, 2e-5
+FLT_MIN_NORMAL = 2.0 ** -126  # smallest normal float32
 CLIP_AMBIG = 1e-4
 
 
@@ -86,7 +91,13 @@ def grad_row_ok(g: np.ndarray, t: oracle.RowTerms, gs: float) -> np.ndarray:
     if t.temperature != 1.0:
         scale = scale / t.temperature + t.q1
     tol = GRAD_RTOL * np.abs(t.grad) + GRAD_QTOL * abs(gs) * scale
-    return np.abs(g.astype(np.float64) - t.grad) <= tol
+    flushed = t.q < FLT_MIN_NORMAL
+    if t.q1 is not None:
+        flushed &= t.q1 < FLT_MIN_NORMAL
+    flushed[t.argmax] = False
+    g64 = g.astype(np.float64)
+    between = (np.abs(g64) <= np.abs(t.grad)) & (g64 * t.grad >= 0.0)
+    return (np.abs(g64 - t.grad) <= tol) | (flushed & between)
 
 
 def check_row(r: int, out: dict, zp_row, zq_row, lam, tau, gs, verified: bool, errors: list,

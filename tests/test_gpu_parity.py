@@ -230,6 +230,27 @@ def test_negative_clip_branch(av):
     full_parity(av, w, np.array([4, 3]), 0.0, 0.05, vecs=1)
 
 
+def test_rising_and_falling_logit_ramps(av):
+    # Logits that climb by 120 along the row (and rows that fall) keep raising
+    # each thread's running maxima: the first sweep's sums are rescaled again
+    # and again, in the fast form (every on-chip slot filled) and in the
+    # streamed one.
+    rng = np.random.default_rng(11)
+    B, k, V = 2, 4, 60000
+    ramp = np.linspace(-60.0, 60.0, V)
+    zp = np.empty((B * k, V))
+    for r in range(B * k):
+        zp[r] = (ramp if r % 2 == 0 else ramp[::-1]) + rng.normal(0, 0.5, V)
+    zq = zp + rng.normal(0, 1.0, (B * k, V))
+    w = synth.make("concurrent", B=B, V=V, dtype="f32")
+    w.k = k
+    w.zp = zp.astype(np.float32)
+    w.zq = zq.astype(np.float32)
+    w.draft = np.argmax(w.zq, axis=1).astype(np.int32)
+    for lam, tau, vecs in [(0.5, 0.1, 0), (0.0, 1e9, 0), (0.5, 0.1, 1 | (1 << 8))]:
+        full_parity(av, w, np.array([4, 3]), lam, tau, vecs=vecs)
+
+
 # ---------------------------------------------------------------------------
 # standalone backward, determinism, device-side status
 # ---------------------------------------------------------------------------
