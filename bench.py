@@ -576,6 +576,89 @@ def bench_bwd(args):
     print(json.dumps(line))
 
 
+def bench_fused_other(args):
+    """The fused pass on the ragged workload (B=128, k=16, V=151936, only the
+    b_k verified rows of each request stored) or the long one (B=64, k=32,
+    V=262144, b_k from the length head, H=5120): same timing as the default
+    bench, kernel only."""
+    import numpy as np
+    import torch
+
+    import drafter_distillation_amd as dd
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dd.lib()
+    w = synth.make(args.workload, seed=args.seed)
+    B, k, V, R = w.B, w.k, w.V, w.R
+    zp = torch.from_numpy(w.zp.view(np.int16)).view(torch.bfloat16).to(dev)
+    zq = torch.from_numpy(w.zq.view(np.int16)).view(torch.bfloat16).to(dev)
+    draft = torch.from_numpy(w.draft).to(dev)
+    kw = {}
+    if w.row_off is not None:
+        kw["row_off"] = torch.from_numpy(w.row_off).to(dev)
+        Rv = R
+    else:
+        bk = torch.empty(B, dtype=torch.int32, device=dev)
+        dd.av_length_head(torch.from_numpy(w.h).to(dev), torch.from_numpy(w.w).to(dev), w.bias, w.gamma, k,
+                          bk_out=bk)
+        kw["bk"] = bk
+        Rv = int(torch.clamp(bk, 1, k).sum().item())
+    gdt = torch.bfloat16 if args.grad == "bf16" else torch.float32
+    out = None
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev0=None, ev1=None):
+        nonlocal out
+        if ev0 is not None:
+            ev0.record(stream)
+        out = dd.av_verify_opd_fwd(zp, zq, draft, k=k, lam=w.lam, tau=w.tau, grad_scale=1.0, out=out,
+                                   grad_dtype=gdt, **kw)
+        if ev1 is not None:
+            ev1.record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if int(out["status"].item()) != 0:
+        raise RuntimeError(f"device status {int(out['status'].item())}")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        step(e0, e1)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    gelem = 2 if args.grad == "bf16" else 4
+    fused_b, _ = algorithmic_bytes(B, k, V, 0, R, Rv, gelem=gelem)
+    kern_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs)
+    achieved = fused_b / (kern_ms * 1e-3) / 1e9
+    desc = {"ragged": f"ragged: B={B} requests, k={k}, V={V}, bf16 logits, only the {R} verified rows stored "
+                      "(b_k drawn with p proportional to 1/b)",
+            "long": f"long: B={B} requests, k={k}, V={V}, bf16 logits, b_k from the length head (H={w.H})"}
+    line = {
+        "metric": f"fused verify+OPD fwd/bwd GB/s, {args.workload} workload",
+        "value": round(achieved, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": desc[args.workload] + f", lambda={w.lam}, tau={w.tau}, {args.grad} gradient",
+                   "B": B, "k": k, "V": V, "rows": R, "verified_rows": Rv, "bytes_per_call": fused_b,
+                   "kernel_ms": round(kern_ms, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    print(json.dumps(line))
+
+
 def bench_hbm_probe(args):
     """What the memory system delivers for the fused pass's byte patterns
     without its arithmetic (drafter_distillation_amd/probe/hbm_probe.hip, run
@@ -629,7 +712,7 @@ def main():
                     help="gradient output type of the fused pass (default float32)")
     ap.add_argument("--temperature", type=float, default=1.0,
                     help="reverse-KL temperature of the fused pass (default 1: the plain pass)")
-    ap.add_argument("--workload", choices=["concurrent", "head_update", "spec", "lm_head", "hbm_probe", "bwd"],
+    ap.add_argument("--workload", choices=["concurrent", "ragged", "long", "head_update", "spec", "lm_head", "hbm_probe", "bwd"],
                     default="concurrent",
                     help="concurrent: the fused verify+OPD step (default); head_update: the "
                          "length head's online update; spec: sampling-based verification")
@@ -668,6 +751,9 @@ def main():
         return
     if args.workload == "bwd":
         bench_bwd(args)
+        return
+    if args.workload in ("ragged", "long"):
+        bench_fused_other(args)
         return
 
     import numpy as np
