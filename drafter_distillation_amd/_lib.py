@@ -45,7 +45,10 @@ _SIGS = {
     "av_workspace_bytes": (_sz, [_i, _i, _i]),
     "av_workspace_init": (_i, [_vp, _sz, _vp]),
     "av_verify_opd_fwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _f, _f, _f, _f,
-                               _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _sz, _i, _vp]),
+                               _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _sz, _vp]),
+    "av_test_verify_opd_fwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _f, _f, _f, _f,
+                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _sz, _i, _i,
+                                    _vp]),
     "av_verify_opd_bwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f, _f, _f, _f,
                                _vp, _i, _i, _vp]),
     "av_spec_workspace_bytes": (_sz, [_i, _i]),
@@ -295,7 +298,7 @@ def _dtype_code(zp: torch.Tensor) -> int:
 def av_verify_opd_fwd(zp: torch.Tensor, zq: torch.Tensor, draft: torch.Tensor, *, k: int,
                       bk: Optional[torch.Tensor] = None, row_off: Optional[torch.Tensor] = None,
                       lam: float, tau: float, grad_scale: float = 1.0, want_grad: bool = True,
-                      want_stats: bool = True, onchip_limit: int = 0,
+                      want_stats: bool = True, onchip_limit: int = 0, split_rows: int = 0,
                       grad_dtype: torch.dtype = torch.float32, temperature: float = 1.0,
                       want_lse_q1: Optional[bool] = None,
                       out: Optional[dict] = None) -> dict:
@@ -309,6 +312,9 @@ def av_verify_opd_fwd(zp: torch.Tensor, zq: torch.Tensor, draft: torch.Tensor, *
     torch.bfloat16 (each entry rounded to nearest-even bfloat16).
     temperature: of the reverse-KL term; want_lse_q1 defaults to
     want_stats and temperature != 1 (the backward needs lse_q1 then).
+
+    onchip_limit and split_rows are test knobs that force a launch form
+    (include/av_test.h); with both 0 the public entry point is called.
     """
     _need_gpu("zp", zp)
     _need_gpu("zq", zq, zp.dtype)
@@ -350,11 +356,14 @@ def av_verify_opd_fwd(zp: torch.Tensor, zq: torch.Tensor, draft: torch.Tensor, *
     nbytes = av_workspace_bytes(B, k, R) if B >= 1 and R >= 1 else 0
     with torch.cuda.device(dev):
         ws = workspace(dev, nbytes)
-        rc = lib().av_verify_opd_fwd(
-            _dtype_code(zp), B, int(k), V, R, _ptr(row_off), _ptr(zp), _ptr(zq), _ptr(draft),
-            _ptr(bk), float(lam), float(tau), float(grad_scale), float(temperature), _ptr(tgt), _ptr(acc),
-            _ptr(row_loss), _ptr(req_loss), _ptr(total), _ptr(stats), _ptr(lse1), _ptr(grad),
-            _grad_code(grad_dtype), _ptr(status), _ptr(ws), ws.numel(), int(onchip_limit), _stream(dev))
+        args = (_dtype_code(zp), B, int(k), V, R, _ptr(row_off), _ptr(zp), _ptr(zq), _ptr(draft),
+                _ptr(bk), float(lam), float(tau), float(grad_scale), float(temperature), _ptr(tgt),
+                _ptr(acc), _ptr(row_loss), _ptr(req_loss), _ptr(total), _ptr(stats), _ptr(lse1),
+                _ptr(grad), _grad_code(grad_dtype), _ptr(status), _ptr(ws), ws.numel())
+        if onchip_limit or split_rows:
+            rc = lib().av_test_verify_opd_fwd(*args, int(onchip_limit), int(split_rows), _stream(dev))
+        else:
+            rc = lib().av_verify_opd_fwd(*args, _stream(dev))
     _check("av_verify_opd_fwd", rc)
     return o
 

@@ -9,6 +9,7 @@
 
 #include "av.h"
 #include "av_internal.h"
+#include "av_test.h"
 
 namespace {
 
@@ -23,10 +24,22 @@ int hip_fail(hipError_t e) {
 struct DeviceInfo {
   int cus = 0;
   long long ticks_per_ms = 0;  // wall-clock counter rate
-  int occ[4][2][2][2] = {};    // fused-kernel workgroups per CU, per variant, full/general
-                               // form, gradient type and plain/tempered form, with the most
-                               // dynamic LDS a launch uses
+  int occ[4][5][2][2] = {};    // fused-kernel workgroups per CU, per variant, kernel form
+                               // (see kForms), gradient type and plain/tempered form, with
+                               // the most dynamic LDS a launch uses
 };
+// Kernel forms: {fast form, split rows, register slots of the build}.
+struct FormDesc {
+  bool full, split;
+  int nr;
+};
+constexpr FormDesc kForms[5] = {{false, false, 0}, {true, false, 0}, {false, true, avk::kRowRegs16},
+                                {true, true, avk::kRowRegs16}, {true, true, avk::kPairRegs}};
+int form_index(bool full, bool split, int nr) {
+  if (!split) return full ? 1 : 0;
+  if (!full) return 2;
+  return nr == avk::kPairRegs ? 4 : 3;
+}
 // Most dynamic LDS of a fused launch: ragged offsets of 4095 requests, or the
 // longest-first schedule of avk::kMaxLptRequests requests.
 constexpr size_t kMaxDynLds = 4096 * sizeof(int32_t);
@@ -47,11 +60,11 @@ hipError_t device_info(const DeviceInfo** out) {
     if (err == hipSuccess) err = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
     d.ticks_per_ms = khz > 0 ? (long long)khz : 100000;
     for (int v = 0; v < 4 && err == hipSuccess; ++v)
-      for (int f = 0; f < 2 && err == hipSuccess; ++f)
+      for (int f = 0; f < 5 && err == hipSuccess; ++f)
         for (int g = 0; g < 2 && err == hipSuccess; ++g)
           for (int t = 0; t < 2 && err == hipSuccess; ++t)
-            err = avk::fused_blocks_per_cu((avk::Variant)v, f != 0, g != 0, t != 0, kMaxDynLds,
-                                           &d.occ[v][f][g][t]);
+            err = avk::fused_blocks_per_cu((avk::Variant)v, kForms[f].full, kForms[f].split, kForms[f].nr,
+                                           g != 0, t != 0, kMaxDynLds, &d.occ[v][f][g][t]);
     g_dev_err[dev] = err;
   });
   if (g_dev_err[dev] != hipSuccess) return g_dev_err[dev];
@@ -254,13 +267,19 @@ int av_spec_verify(int dtype, int B, int k, int V, int R, const int32_t* row_off
   return e == hipSuccess ? AV_OK : hip_fail(e);
 }
 
-int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_off,
-                      const void* zp, const void* zq, const int32_t* draft, const int32_t* bk,
-                      float lambda, float tau, float grad_scale, float temperature,
-                      int32_t* tgt_argmax, int32_t* acc_len, float* row_loss, float* req_loss,
-                      float* total_loss, float* row_stats, float* lse_q1, void* grad_zq,
-                      int grad_dtype, int32_t* status, void* workspace, size_t workspace_bytes,
-                      int onchip_limit, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The fused pass with its launch form chosen by the caller: onchip_limit as
+// av_test_verify_opd_fwd, split 0 = automatic, 1 = whole rows, 2 = split rows.
+int verify_opd_fwd_impl(int dtype, int B, int k, int V, int R, const int32_t* row_off,
+                        const void* zp, const void* zq, const int32_t* draft, const int32_t* bk,
+                        float lambda, float tau, float grad_scale, float temperature,
+                        int32_t* tgt_argmax, int32_t* acc_len, float* row_loss, float* req_loss,
+                        float* total_loss, float* row_stats, float* lse_q1, void* grad_zq,
+                        int grad_dtype, int32_t* status, void* workspace, size_t workspace_bytes,
+                        int onchip_limit, int split_mode, void* stream) {
   if (!zp || !zq || !draft || !tgt_argmax || !acc_len || !row_loss || !workspace) return AV_EINVAL;
   if (!row_off && !bk) return AV_EINVAL;
   if (!(lambda >= 0.0f && lambda <= 1.0f)) return AV_EINVAL;
@@ -274,15 +293,34 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_
   Plan p;
   int rc = plan_rows(dtype, B, k, V, R, row_off, zp, zq, grad_zq, &p);
   if (rc != AV_OK) return rc;
-  if (onchip_limit < 0) return AV_EINVAL;
+  if (onchip_limit < 0 || split_mode < 0 || split_mode > 2) return AV_EINVAL;
   if (p.ragged && B + 1 > 4096) return AV_EUNSUPPORTED;  // offsets are cached in LDS
   if (workspace_bytes < avk::ws_total(B, R)) return AV_EINVAL;
-  int nr = avk::variant_row_regs(p.var), nl = avk::variant_row_lds(p.var);
+
+  // Split rows: each verified row's halves on two CUs (both halves on chip,
+  // no logit read twice where a whole row would not fit), taken only on
+  // request: the two statistics exchanges per row and the per-row fixed costs
+  // paid twice make it slower than whole rows on every workload measured
+  // (B=128 x 16 rows of 151936, ragged 605 rows of 151936, 64 x 32 rows of
+  // 262144).  The halves meet at a 64-vector boundary (1 KB of bfloat16
+  // logits) near the middle of the row.
+  const bool wide = p.var == avk::kBf16x8 || p.var == avk::kF32x4;
+  int pv0 = (((p.nvec + 1) / 2) + 63) & ~63;
+  if (pv0 >= p.nvec) pv0 = (p.nvec + 1) / 2;
+  const long long part = p.nvec - pv0;  // the smaller half
+  const long long slot = avk::kRowBlock;
+  const bool split = wide && p.nvec >= 2 && split_mode == 2;
+  const int nl_max = avk::variant_row_lds(p.var);
+  int nr_max = avk::variant_row_regs(p.var);
+  if (split && onchip_limit == 0 && part < (long long)(nr_max + nl_max) * slot &&
+      part >= (long long)(avk::kPairRegs + nl_max) * slot)
+    nr_max = avk::kPairRegs;  // fast form with fewer register slots
+  int nr = nr_max, nl = nl_max;
   if (onchip_limit > 0) {
     nr = onchip_limit & 0xff;
     nl = (onchip_limit >> 8) & 0xff;
-    if (nr > avk::variant_row_regs(p.var)) nr = avk::variant_row_regs(p.var);
-    if (nl > avk::variant_row_lds(p.var)) nl = avk::variant_row_lds(p.var);
+    if (nr > nr_max) nr = nr_max;
+    if (nl > nl_max) nl = nl_max;
   }
 
   const DeviceInfo* dev = nullptr;
@@ -295,15 +333,22 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_
   size_t lds = 0;
   if (p.ragged) lds = (size_t)(B + 1) * sizeof(int32_t);
   else if (lpt) lds = ((size_t)B * 3 + 3) & ~(size_t)3;
-  // The fast form needs every on-chip slot filled and the default split.
-  const int nr_max = avk::variant_row_regs(p.var), nl_max = avk::variant_row_lds(p.var);
-  const bool full = nr == nr_max && nl == nl_max &&
-                    (long long)p.nvec >= (long long)(nr_max + nl_max) * avk::kRowBlock;
+  // The fast form needs every on-chip slot filled (in each half, when split)
+  // and the default on-chip split.
+  const long long rowvecs = split ? part : p.nvec;
+  const bool full = onchip_limit == 0 && rowvecs >= (long long)(nr_max + nl_max) * slot;
   const bool gb = grad_zq && grad_dtype == AV_BF16;
-  const int occ = dev->occ[p.var][full ? 1 : 0][gb ? 1 : 0][tp.tm ? 1 : 0];
+  const int occ = dev->occ[p.var][form_index(full, split, nr_max)][gb ? 1 : 0][tp.tm ? 1 : 0];
   if (occ < 1 || lds > kMaxDynLds) return AV_EUNSUPPORTED;
   long long grid = (long long)occ * dev->cus;
-  if (grid > R) grid = R;
+  if (split) {
+    // pairs of co-resident workgroups; no more pairs than rows
+    if (grid > 2LL * R) grid = 2LL * R;
+    grid &= ~1LL;
+    if (grid < 2) return AV_EUNSUPPORTED;
+  } else if (grid > R) {
+    grid = R;
+  }
 
   char* ws = (char*)workspace;
   avk::FwdArgs a;
@@ -327,6 +372,7 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_
   a.arrive = (uint64_t*)(ws + avk::ws_arrive_off(B, R));
   a.halfres = (uint64_t*)(ws + avk::ws_halfres_off(B, R));
   a.harrive = (uint64_t*)(ws + avk::ws_harrive_off(B, R));
+  a.xres = (uint64_t*)(ws + avk::ws_xres_off(B, R));
   a.timeout_ticks = dev->ticks_per_ms * 2000;  // 2 s per wait
   a.B = B;
   a.k = k;
@@ -337,6 +383,8 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_
   a.nl = nl;
   a.ragged = p.ragged ? 1 : 0;
   a.lpt = lpt ? 1 : 0;
+  a.split = split ? 2 : 1;
+  a.pv0 = split ? pv0 : 0;
   a.gbf16 = gb ? 1 : 0;
   a.tm = tp.tm ? 1 : 0;
   a.lam = lambda;
@@ -344,8 +392,37 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_
   a.gs = grad_scale;
   a.inv_t = tp.inv_t;
   a.inv_tl = tp.inv_tl;
-  e = avk::launch_fused(p.var, full, a, (int)grid, lds, (hipStream_t)stream);
+  e = avk::launch_fused(p.var, full, nr_max, a, (int)grid, lds, (hipStream_t)stream);
   return e == hipSuccess ? AV_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_off,
+                      const void* zp, const void* zq, const int32_t* draft, const int32_t* bk,
+                      float lambda, float tau, float grad_scale, float temperature,
+                      int32_t* tgt_argmax, int32_t* acc_len, float* row_loss, float* req_loss,
+                      float* total_loss, float* row_stats, float* lse_q1, void* grad_zq,
+                      int grad_dtype, int32_t* status, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return verify_opd_fwd_impl(dtype, B, k, V, R, row_off, zp, zq, draft, bk, lambda, tau, grad_scale,
+                             temperature, tgt_argmax, acc_len, row_loss, req_loss, total_loss, row_stats,
+                             lse_q1, grad_zq, grad_dtype, status, workspace, workspace_bytes, 0, 0, stream);
+}
+
+int av_test_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_off,
+                           const void* zp, const void* zq, const int32_t* draft, const int32_t* bk,
+                           float lambda, float tau, float grad_scale, float temperature,
+                           int32_t* tgt_argmax, int32_t* acc_len, float* row_loss, float* req_loss,
+                           float* total_loss, float* row_stats, float* lse_q1, void* grad_zq,
+                           int grad_dtype, int32_t* status, void* workspace, size_t workspace_bytes,
+                           int onchip_limit, int split_rows, void* stream) {
+  return verify_opd_fwd_impl(dtype, B, k, V, R, row_off, zp, zq, draft, bk, lambda, tau, grad_scale,
+                             temperature, tgt_argmax, acc_len, row_loss, req_loss, total_loss, row_stats,
+                             lse_q1, grad_zq, grad_dtype, status, workspace, workspace_bytes, onchip_limit,
+                             split_rows, stream);
 }
 
 int av_verify_opd_bwd(int dtype, int B, int k, int V, int R, const int32_t* row_off,

@@ -20,15 +20,20 @@ constexpr int kMaxChunks = 64;   // chunks per row of the standalone backward
 //   arrive   [B]      per-request count of completed verified rows (tagged)
 //   halfres  [R][2][2] per half of an unverified row: max of zp, its index (tagged)
 //   harrive  [R]      per-row count of completed halves (tagged)
+//   xres     [R][2][12] split rows: what each half of a verified row hands its
+//                     partner (tagged): 8 words of first-sweep statistics, then
+//                     4 words of clip corrections
 constexpr size_t kCtlBytes = 256;
+constexpr int kXWords = 12;  // exchange words per half-row
 
 inline size_t ws_rowres_off() { return kCtlBytes; }
 inline size_t ws_reqres_off(int R) { return ws_rowres_off() + (size_t)R * 16; }
 inline size_t ws_arrive_off(int B, int R) { return ws_reqres_off(R) + (size_t)B * 16; }
 inline size_t ws_halfres_off(int B, int R) { return ws_arrive_off(B, R) + (size_t)B * 8; }
 inline size_t ws_harrive_off(int B, int R) { return ws_halfres_off(B, R) + (size_t)R * 32; }
+inline size_t ws_xres_off(int B, int R) { return ws_harrive_off(B, R) + (size_t)R * 8; }
 inline size_t ws_total(int B, int R) {
-  size_t n = ws_harrive_off(B, R) + (size_t)R * 8;
+  size_t n = ws_xres_off(B, R) + (size_t)R * 2 * kXWords * 8;
   return (n + 255) & ~(size_t)255;
 }
 
@@ -53,6 +58,13 @@ inline int variant_nvmax(Variant v) { return v == kBf16x8 ? 8 : v == kF32x4 ? 8 
 #define AV_NL 4
 #endif
 constexpr int kRowRegs16 = AV_NR, kRowLds16 = AV_NL;
+// Split rows (each verified row's halves on two CUs): register slots of a half
+// whose 9..12 full slots fit on chip with 5 in registers and 4 in LDS (a
+// 151936-wide bfloat16 row: 9.3 slots per half); halves of 13 slots and more
+// use the whole-row split above.
+constexpr int kPairRegs = 5;
+// Smallest half-row (full 1024-vector slots) that the split form takes.
+constexpr int kPairMinSlots = kPairRegs + AV_NL;
 constexpr int kRowRegs1 = 32, kRowLds1 = 0;  // scalar variants
 inline int variant_row_regs(Variant v) { return (v == kBf16x8 || v == kF32x4) ? kRowRegs16 : kRowRegs1; }
 inline int variant_row_lds(Variant v) { return (v == kBf16x8 || v == kF32x4) ? kRowLds16 : kRowLds1; }
@@ -77,12 +89,15 @@ struct FwdArgs {
   uint64_t* arrive;
   uint64_t* halfres;
   uint64_t* harrive;
+  uint64_t* xres;
   long long timeout_ticks;
   int B, k, V, R;
   int nvec;      // vectors per row (V / vec)
   int nr, nl;    // vectors per thread held in registers / in LDS
   int ragged;
   int lpt;       // dense layout, rows handed out longest first (unverified rows in halves)
+  int split;     // 2: rows in halves on workgroup pairs (2p, 2p+1), each half kept on chip
+  int pv0;       // split: first vector of the second half
   int gbf16;     // gradient stored as bfloat16
   float lam, tau, gs;
   // temperature of the reverse-KL term
@@ -158,8 +173,9 @@ constexpr int kSpecChunkVecs = 512;
 // full: every on-chip slot of a row is filled (nvec >= (regs + lds) * kRowBlock)
 // and the default on-chip split is used.
 // a.tm selects the tempered form of the kernels (fused and backward).
-hipError_t launch_fused(Variant v, bool full, const FwdArgs& a, int grid, size_t lds, hipStream_t s);
-hipError_t fused_blocks_per_cu(Variant v, bool full, bool gbf16, bool tm, size_t lds, int* out);
+// nr: register slots of the build (kRowRegs16, or kPairRegs for split rows).
+hipError_t launch_fused(Variant v, bool full, int nr, const FwdArgs& a, int grid, size_t lds, hipStream_t s);
+hipError_t fused_blocks_per_cu(Variant v, bool full, bool split, int nr, bool gbf16, bool tm, size_t lds, int* out);
 hipError_t launch_bwd(Variant v, const BwdArgs& a, hipStream_t s);
 hipError_t launch_head(const HeadArgs& a, hipStream_t s);
 hipError_t launch_head_update(const HeadUpdArgs& a, hipStream_t s);

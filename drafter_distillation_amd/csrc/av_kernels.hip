@@ -194,12 +194,12 @@ __device__ __forceinline__ Rsrc row_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// The gradient row of vector-row offset rowv (VEC entries per vector):
-// float32, or bfloat16 (GB).
+// The gradient of the n entries from vector offset rowv (VEC entries per
+// vector): float32, or bfloat16 (GB).
 template <bool GB, int VEC>
-__device__ __forceinline__ Rsrc grad_rsrc(void* grad, long long rowv, int V) {
-  if constexpr (GB) return row_rsrc((uint16_t*)grad + rowv * VEC, (uint32_t)V * 2u);
-  else return row_rsrc((float*)grad + rowv * VEC, (uint32_t)V * 4u);
+__device__ __forceinline__ Rsrc grad_rsrc(void* grad, long long rowv, int n) {
+  if constexpr (GB) return row_rsrc((uint16_t*)grad + rowv * VEC, (uint32_t)n * 2u);
+  else return row_rsrc((float*)grad + rowv * VEC, (uint32_t)n * 4u);
 }
 
 template <int VAR>
@@ -720,8 +720,11 @@ struct Item {
 // descending), then unverified rows position-major (the requests with
 // b_k <= p, which trail `order`), each as two halves, so that the last work
 // items of a launch are short.
+// whole: unverified rows are one item each (split rows: the pair's two
+// workgroups take their halves).
 __device__ __forceinline__ Item map_item(const FwdArgs& a, const RowSmem& sm, const int* s_off,
-                                         const uint16_t* order, const uint8_t* key, int idx) {
+                                         const uint16_t* order, const uint8_t* key, int idx,
+                                         bool whole) {
   Item m;
   if (a.ragged) {
     int lo = 0, hi = opaque_s(a.B) - 1;  // last request whose first row is <= idx
@@ -750,8 +753,8 @@ __device__ __forceinline__ Item map_item(const FwdArgs& a, const RowSmem& sm, co
       m.half = -1;
       m.verified = true;
     } else {
-      const int u = (idx - rv) >> 1;
-      m.half = (idx - rv) & 1;
+      const int u = whole ? idx - rv : (idx - rv) >> 1;
+      m.half = whole ? 0 : (idx - rv) & 1;
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (sm.cumu[mid] <= u) lo = mid;
@@ -771,7 +774,7 @@ __device__ __forceinline__ Item map_item(const FwdArgs& a, const RowSmem& sm, co
     m.req = idx / k;
     m.r0 = m.req * k;
     m.bkb = min(max(a.bk[m.req], 1), k);
-    m.half = -1;
+    m.half = whole ? 0 : -1;
     m.verified = idx - m.r0 < m.bkb;
   }
   return m;
@@ -877,19 +880,21 @@ struct RowIO {
   static constexpr int SE = kRowBlock * VEC;                // entries per slot
   int wid, lane;
   uint32_t voff, goff;  // byte offsets of the thread's first load / store in slot 0
-  int lo0;              // index of the thread's entry 0 in slot 0
+  int lo0;              // row index of the thread's entry 0 in slot 0
 
-  __device__ __forceinline__ explicit RowIO(int tid) {
+  // ebase: row index of the first entry (a split row's second half starts
+  // inside the row).
+  __device__ __forceinline__ explicit RowIO(int tid, int ebase = 0) {
     wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     lane = tid & 63;
     if constexpr (kHalves) {
       voff = (uint32_t)(wid * 64 * VEC * T::EB + lane * 4 * T::EB);
       goff = (uint32_t)(wid * 64 * VEC * 4 + lane * 16);
-      lo0 = wid * 64 * VEC + lane * 4;
+      lo0 = ebase + wid * 64 * VEC + lane * 4;
     } else {
       voff = (uint32_t)(tid * VEC * T::EB);
       goff = (uint32_t)(tid * VEC * 4);
-      lo0 = tid * VEC;
+      lo0 = ebase + tid * VEC;
     }
   }
   // Vectors of the wave's block in slot s (wave-uniform; 64 unless the block
@@ -1197,30 +1202,157 @@ __device__ __forceinline__ void dma_slot(const RowIO<VAR>& io, Rsrc rzp, Rsrc rz
   }
 }
 
+// ---------------------------------------------------------------------------
+// split rows: what the two halves of a verified row hand each other
+// ---------------------------------------------------------------------------
+
+// First-sweep statistics of a row or of one half (every lane holds the same
+// values): max of zp and sum exp(s (zp - mp)) relative to it, the same of zq
+// with K = sum exp(s (zq - mq)) (zq - zp), zq at the first index of mp, and
+// (tempered form) sum exp(zq - mq).
+struct XRec {
+  float mp, sp, mq, sq, kq, za, sq1;
+  int bi;
+};
+
+// Word i of a half's record, for lanes 0..n-1 (the others get 0): lane i
+// publishes or reads word i.
+__device__ __forceinline__ uint64_t* xrec(const FwdArgs& a, int row, int h) {
+  return cold_args()->xres + ((long long)row * 2 + h) * kXWords;
+}
+
+// Publishes n words (lane i: word i) of this half's record and returns, in
+// lane i, word i of the partner's, once it carries this launch's tag
+// (bounded wait; on expiry the launch reports AV_DEV_TIMEOUT).  Called by
+// every wave with the same values; the last wave publishes.
+__device__ __forceinline__ uint32_t xswap(const FwdArgs& a, uint64_t* mine, uint64_t* theirs, uint32_t v,
+                                          int n, uint32_t tag) {
+  const int lane = threadIdx.x & 63;
+  if ((threadIdx.x >> 6) == kLastWave && lane < n) tput(mine + lane, tag, v);
+  uint64_t w = 0;
+  Waiter wt(a.ctl, cold_args()->timeout_ticks);
+  for (;;) {
+    bool ok = true;
+    if (lane < n) {
+      w = tget(theirs + lane);
+      ok = tag_ok(w, tag);
+    }
+    if (__all(ok)) break;
+    if (!__all(wt.keep_going())) break;
+  }
+  return (uint32_t)w;
+}
+
+// The statistics of the whole row from those of its halves, merged in a
+// fixed order (first half, then second), so both partners get the same bits.
+// The first half holds the lower indices: it wins ties of the maximum.
+template <bool TM>
+__device__ __forceinline__ XRec xmerge(const XRec& A, const XRec& B, float sL) {
+  const float L = TM ? sL : kLog2e;
+  XRec o;
+  const bool second = B.mp > A.mp;
+  o.bi = second ? B.bi : A.bi;
+  o.za = second ? B.za : A.za;
+  o.mp = fmaxf(A.mp, B.mp);
+  const float fa = (A.sp == 0.0f) ? 0.0f : __builtin_amdgcn_exp2f((A.mp - o.mp) * L);
+  const float fb = (B.sp == 0.0f) ? 0.0f : __builtin_amdgcn_exp2f((B.mp - o.mp) * L);
+  o.sp = A.sp * fa + B.sp * fb;
+  o.mq = fmaxf(A.mq, B.mq);
+  const float ga = (A.sq == 0.0f) ? 0.0f : __builtin_amdgcn_exp2f((A.mq - o.mq) * L);
+  const float gb = (B.sq == 0.0f) ? 0.0f : __builtin_amdgcn_exp2f((B.mq - o.mq) * L);
+  o.sq = A.sq * ga + B.sq * gb;
+  o.kq = A.kq * ga + B.kq * gb;
+  o.sq1 = 0.0f;
+  if constexpr (TM) {
+    const float ha = (A.sq1 == 0.0f) ? 0.0f : __builtin_amdgcn_exp2f((A.mq - o.mq) * kLog2e);
+    const float hb = (B.sq1 == 0.0f) ? 0.0f : __builtin_amdgcn_exp2f((B.mq - o.mq) * kLog2e);
+    o.sq1 = A.sq1 * ha + B.sq1 * hb;
+  }
+  return o;
+}
+
+template <bool TM>
+__device__ __forceinline__ XRec xchange_stats(const FwdArgs& a, const XRec& mine, int row, int ph,
+                                              uint32_t tag, float sL) {
+  const int lane = threadIdx.x & 63;
+  uint32_t v = 0;
+  switch (lane) {
+    case 0: v = __float_as_uint(mine.mp); break;
+    case 1: v = __float_as_uint(mine.sp); break;
+    case 2: v = __float_as_uint(mine.mq); break;
+    case 3: v = __float_as_uint(mine.sq); break;
+    case 4: v = __float_as_uint(mine.kq); break;
+    case 5: v = __float_as_uint(mine.za); break;
+    case 6: v = __float_as_uint(mine.sq1); break;
+    case 7: v = (uint32_t)mine.bi; break;
+    default: break;
+  }
+  const uint32_t w = xswap(a, xrec(a, row, ph), xrec(a, row, ph ^ 1), v, 8, tag);
+  XRec o;
+  o.mp = __uint_as_float(__shfl(w, 0));
+  o.sp = __uint_as_float(__shfl(w, 1));
+  o.mq = __uint_as_float(__shfl(w, 2));
+  o.sq = __uint_as_float(__shfl(w, 3));
+  o.kq = __uint_as_float(__shfl(w, 4));
+  o.za = __uint_as_float(__shfl(w, 5));
+  o.sq1 = __uint_as_float(__shfl(w, 6));
+  o.bi = (int)__shfl(w, 7);
+  return ph == 0 ? xmerge<TM>(mine, o, sL) : xmerge<TM>(o, mine, sL);
+}
+
+// Clip corrections of the whole row: this half's plus its partner's (a sum
+// of two float64 values: the same bits in either order).
+__device__ __forceinline__ void xchange_clip(const FwdArgs& a, double& cs, double& ck, int row, int ph,
+                                             uint32_t tag) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t bs = (uint64_t)__double_as_longlong(cs), bk = (uint64_t)__double_as_longlong(ck);
+  uint32_t v = 0;
+  switch (lane) {
+    case 0: v = (uint32_t)(bs >> 32); break;
+    case 1: v = (uint32_t)bs; break;
+    case 2: v = (uint32_t)(bk >> 32); break;
+    case 3: v = (uint32_t)bk; break;
+    default: break;
+  }
+  const uint32_t w = xswap(a, xrec(a, row, ph) + 8, xrec(a, row, ph ^ 1) + 8, v, 4, tag);
+  const uint64_t os = ((uint64_t)__shfl(w, 0) << 32) | (uint64_t)__shfl(w, 1);
+  const uint64_t ok = ((uint64_t)__shfl(w, 2) << 32) | (uint64_t)__shfl(w, 3);
+  cs = cs + __longlong_as_double((long long)os);
+  ck = ck + __longlong_as_double((long long)ok);
+}
+
 // Verified row: statistics, loss, and (optionally) the gradient.
 //
 // Slots 0 .. nr-1 of the row stay in registers, nr .. nr+nl-1 in LDS, the
 // rest are streamed (and read again for the gradient).  FULL: nr and nl are
 // the compile-time maxima and the row fills every on-chip slot (the common
 // case of a large vocabulary), so no on-chip access needs a guard.
-template <int VAR, bool FULL, bool GB, bool TM>
+//
+// Split rows (SP = 2): the workgroup takes half ph of the row (vectors
+// [0, pv0) or [pv0, nvec)) and its partner the other half, each on its own
+// CU; the halves hand each other their first-sweep statistics and then their
+// clip corrections, so both continue with the statistics of the whole row.
+template <int VAR, bool FULL, bool GB, bool TM, int NRT, int SP>
 __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
                                              typename Tr<VAR>::S (*lp)[kRowBlock],
                                              typename Tr<VAR>::S (*lq)[kRowBlock], const Item& it,
-                                             int par, uint32_t tag) {
+                                             int par, uint32_t tag, int ph) {
   using T = Tr<VAR>;
   using S = typename T::S;
   using IO = RowIO<VAR>;
-  constexpr int NR = RowCfg<VAR>::NR, NL = RowCfg<VAR>::NL;
+  constexpr int NR = NRT, NL = RowCfg<VAR>::NL;
   constexpr uint32_t SIN = IO::SIN;
   int tid = opaque(threadIdx.x);
   const int lane = tid & 63, wid = tid >> 6;
   const int row = it.row;
-  const long long rowv = (long long)row * a.nvec;
-  const uint32_t rbytes = (uint32_t)opaque_s(a.V) * (uint32_t)T::EB;
+  const int pv0 = SP == 2 ? opaque_s(a.pv0) : 0;
+  const int vbase = (SP == 2 && ph) ? pv0 : 0;  // first vector of this part
+  const int nvec = SP == 2 ? (ph ? opaque_s(a.nvec) - pv0 : pv0) : opaque_s(a.nvec);
+  const int ebase = vbase * IO::VEC;              // row index of the part's first entry
+  const long long rowv = (long long)row * a.nvec + vbase;
+  const uint32_t rbytes = (uint32_t)nvec * (uint32_t)(IO::VEC * T::EB);
   const Rsrc rzp = row_rsrc(T::row(a.zp, rowv), rbytes);
   const Rsrc rzq = row_rsrc(T::row(a.zq, rowv), rbytes);
-  const int nvec = opaque_s(a.nvec);
   const int nr = FULL ? NR : opaque_s(a.nr), nl = FULL ? NL : opaque_s(a.nl);
   const int von = nr + nl;             // first streamed slot
   const int nfull = nvec / kRowBlock;  // slots in which every thread has a vector
@@ -1236,7 +1368,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   constexpr bool RING = FULL && NL > 0;
   const int ns = nfull + (nfull * kRowBlock < nvec ? 1 : 0);  // slots, the partial one included
   if constexpr (!RING && NL > 0) {
-    const IO io(tid);
+    const IO io(tid, ebase);
 #pragma unroll
     for (int l = 0; l < NL; ++l)
       if (l < nl) dma_slot<VAR, kAuxOnce>(io, rzp, rzq, lp, lq, l, nr + l, nvec, tid);
@@ -1245,7 +1377,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   // carry values from one row to the next.
   S rp[NR], rq[NR];
   {
-    const IO io(tid);
+    const IO io(tid, ebase);
 #pragma unroll
     for (int v = 0; v < NR; ++v) {
       rp[v] = S{};
@@ -1270,7 +1402,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
     // q + 1, or a half's resident slots), counted for slots every wave loads.
     static_assert(NL == 4, "two halves of two LDS slots");
     constexpr int QR = (NR + 1) / 2;  // pairs that hold register slots
-    const IO io(opaque(tid));
+    const IO io(opaque(tid), ebase);
     const int nst = ns - von;              // streamed slots
     const int npair = (NR + nst + 1) >> 1;  // >= QR
     auto slot_of = [&](int e) { return e < NR ? e : von + (e - NR); };  // ring entry -> row slot
@@ -1347,7 +1479,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
       issue(q + 2, h);
     }
   } else {
-    const IO io(opaque(tid));
+    const IO io(opaque(tid), ebase);
 #ifndef AV_SU
 #define AV_SU 1
 #endif
@@ -1367,7 +1499,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   uint64_t nxt = 0;
   if (tid == 0) nxt = claim(a);  // its reply returns behind this row's loads
   if constexpr (!RING) {  // the fast form folded its register slots in the ring
-    const IO io(opaque(tid));
+    const IO io(opaque(tid), ebase);
 #pragma unroll
     for (int v = 0; v < NR; ++v) {
       const int nbv = io.nb(v, nvec);
@@ -1377,7 +1509,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   }
   if constexpr (NL > 0) {
     wait_vmem_all();  // the LDS copies of this wave have landed
-    const IO io(opaque(tid));
+    const IO io(opaque(tid), ebase);
 #pragma unroll
     for (int l = 0; l < NL; ++l) {
       const int sl = nr + l, nbv = io.nb(sl, nvec);
@@ -1426,16 +1558,19 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   } else {
     wave_combine(W);
   }
-  const float mp = __shfl(W.mp, 0), sp = __shfl(W.sp, 0);
-  const float mq = __shfl(W.mq, 0), sq = __shfl(W.sq, 0), kq = __shfl(W.kq, 0);
-  const float zqa = __shfl(W.za, 0);
-  const int Arg = __shfl(W.bi, 0);
+  XRec xr{__shfl(W.mp, 0), __shfl(W.sp, 0), __shfl(W.mq, 0), __shfl(W.sq, 0), __shfl(W.kq, 0),
+           __shfl(W.za, 0), TM ? __shfl(W.sq1, 0) : 0.0f, __shfl(W.bi, 0)};
+  if constexpr (SP == 2) xr = xchange_stats<TM>(a, xr, row, ph, tag, sL);
+  const float mp = xr.mp, sp = xr.sp;
+  const float mq = xr.mq, sq = xr.sq, kq = xr.kq;
+  const float zqa = xr.za;
+  const int Arg = xr.bi;
   const float st = TM ? opaque_s(a.inv_t) : 1.0f;
   const float lse_p32 = TM ? __builtin_fmaf(mp, st, kLn2 * __builtin_amdgcn_logf(sp))
                            : mp + kLn2 * __builtin_amdgcn_logf(sp);
   const float lse_q32 = TM ? __builtin_fmaf(mq, st, kLn2 * __builtin_amdgcn_logf(sq))
                            : mq + kLn2 * __builtin_amdgcn_logf(sq);
-  const float lse_q1 = TM ? mq + kLn2 * __builtin_amdgcn_logf(__shfl(W.sq1, 0)) : lse_q32;
+  const float lse_q1 = TM ? mq + kLn2 * __builtin_amdgcn_logf(xr.sq1) : lse_q32;
   // sum_j q_j (log q_j - log p_j) = s sum_j q_j (zq_j - zp_j) - (lse_q - lse_p)
   const double KL = (double)st * ((double)kq / (double)sq) - (double)(lse_q32 - lse_p32);
   const RowK rk = row_consts<TM>(lse_p32, lse_q32, tau, st, sL);
@@ -1470,7 +1605,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   }
   float cs = 0.0f, ck = 0.0f;
   if (flag_on) {
-    const IO io(opaque(tid));
+    const IO io(opaque(tid), ebase);
 #pragma unroll
     for (int v = 0; v < NR; ++v) {
       if (v < nr && io.has(io.nb(v, nvec)))
@@ -1486,7 +1621,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
     }
   }
   if (flag_st) {
-    const IO io(opaque(tid));
+    const IO io(opaque(tid), ebase);
     for (int s = von; s < nfull; ++s) clip_vec<VAR, TM>(io.load(rzp, s, 64), io.load(rzq, s, 64), rk, fk, cs, ck);
     if (tail) {
       const int nbv = io.nb(nfull, nvec);
@@ -1503,14 +1638,18 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
     sm.d[par][wid][1] = dck;
   }
   __syncthreads();
-  const double tcs = wsumd16((lane < kRowWaves) ? sm.d[par][lane][0] : 0.0);
-  const double tck = wsumd16((lane < kRowWaves) ? sm.d[par][lane][1] : 0.0);
+  double tcs = wsumd16((lane < kRowWaves) ? sm.d[par][lane][0] : 0.0);
+  double tck = wsumd16((lane < kRowWaves) ? sm.d[par][lane][1] : 0.0);
+  if constexpr (SP == 2) {
+    if (tau < INFINITY) xchange_clip(a, tcs, tck, row, ph, tag);  // with tau = inf both are 0
+  }
   const double S64 = (KL + 1.0) - tcs, KLc64 = KL - tck;
   const float S32 = (float)S64;
 
-  // ---- the row is complete: one wave publishes it; if it is the request's
-  // last verified row to complete, that wave also finishes the request ----
-  if (wid == kLastWave) {
+  // ---- the row is complete: one wave publishes it (split rows: the first
+  // half's); if it is the request's last verified row to complete, that wave
+  // also finishes the request ----
+  if ((SP == 1 || ph == 0) && wid == kLastWave) {
     uint32_t n = 0;
     if (lane == 0) {
       const KArgs K = cold_args();
@@ -1534,7 +1673,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   // (fast form: through the LDS slots once their resident data is done) ----
   if (a.grad) {
     const GradK gk = grad_consts<TM>(opaque_s(a.lam), opaque_s(a.gs), S32, st, lse_q1);
-    const Rsrc rg = grad_rsrc<GB, IO::VEC>(a.grad, rowv, opaque_s(a.V));
+    const Rsrc rg = grad_rsrc<GB, IO::VEC>(a.grad, rowv, nvec * IO::VEC);
     if constexpr (RING) {
       // Each LDS half's resident slots' gradient frees the half; the streamed
       // slots then come in again two at a time, double-buffered, the first
@@ -1547,7 +1686,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
       constexpr int kRegStores = NR * SPS;      // all register slots are full
       static_assert(kRegStores + 4 * SPS + 4 <= 63, "vmcnt range");
       static_assert(NL == 4, "two halves of two LDS slots");
-      const IO io(opaque(tid));
+      const IO io(opaque(tid), ebase);
       const int np2 = (ns - von + 1) >> 1;
       auto full = [&](int q, int j) { return q < np2 && von + 2 * q + j < nfull; };
       auto loads_of = [&](int q) { return (full(q, 0) ? 2 : 0) + (full(q, 1) ? 2 : 0); };
@@ -1595,7 +1734,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
       wait_lds_reads();  // the next row's direct loads may overwrite the LDS slots
     } else {
       {
-        const IO io(opaque(tid));
+        const IO io(opaque(tid), ebase);
 #ifndef AV_GU
 #define AV_GU 2
 #endif
@@ -1613,7 +1752,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
         }
       }
       {
-        const IO io(opaque(tid));
+        const IO io(opaque(tid), ebase);
 #pragma unroll
         for (int v = 0; v < NR; ++v) {
           const int nbv = io.nb(v, nvec);
@@ -1622,7 +1761,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
         }
       }
       if constexpr (NL > 0) {
-        const IO io(opaque(tid));
+        const IO io(opaque(tid), ebase);
 #pragma unroll
         for (int l = 0; l < NL; ++l) {
           const int sl = nr + l, nbv = io.nb(sl, nvec);
@@ -1635,7 +1774,12 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   }
 }
 
-template <int VAR, bool FULL, bool GB, bool TM>
+// SP = 2: split rows.  Workgroups 2p and 2p+1 form pair p and take the
+// pair's rows in a fixed order (items p, p + pairs, ...): workgroup 2p + h
+// takes half h of each (unverified rows as the two halves of their argmax
+// scan).  Both halves of a verified row are therefore in progress together,
+// and a half only waits for its partner, which works through the same list.
+template <int VAR, bool FULL, bool GB, bool TM, int NRT, int SP>
 __global__ __launch_bounds__(kRowBlock) void fused_kernel(FwdArgs a) {
   using S = typename Tr<VAR>::S;
   constexpr int NLA = RowCfg<VAR>::NL > 0 ? RowCfg<VAR>::NL : 1;
@@ -1652,7 +1796,7 @@ __global__ __launch_bounds__(kRowBlock) void fused_kernel(FwdArgs a) {
     const uint32_t epoch =
         (uint32_t)__hip_atomic_load(a.ctl + 1, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
     sm.tag = epoch + 1u;  // epochs stay below 0xFFFFFFFF, so tags are never 0
-    sm.item[0] = claim(a);
+    sm.item[0] = claim(a);  // split rows: only its status bits are used
   }
   int bad = 0;
   if (a.ragged) {
@@ -1702,12 +1846,16 @@ __global__ __launch_bounds__(kRowBlock) void fused_kernel(FwdArgs a) {
   __syncthreads();
   const uint32_t tag = sm.tag;
   // Work items: rows, with the unverified rows of the longest-first order
-  // counted twice (two halves each).
-  const uint32_t nitems = (uint32_t)a.R + (a.lpt ? (uint32_t)(a.R - sm.cum[a.k]) : 0u);
+  // counted twice (two halves each) unless rows are split (a pair takes both
+  // halves of each of its rows).
+  const uint32_t nitems =
+      (uint32_t)a.R + (SP == 1 && a.lpt ? (uint32_t)(a.R - sm.cum[a.k]) : 0u);
+  const int ph = SP == 2 ? (int)(blockIdx.x & 1u) : 0;
+  const uint32_t pair = blockIdx.x >> 1, npairs = gridDim.x >> 1;
   for (int iter = 0;; ++iter) {
     const int par = iter & 1;
     const uint64_t w = sm.item[par];
-    const uint32_t idx = __builtin_amdgcn_readfirstlane((uint32_t)w);
+    const uint32_t idx = SP == 2 ? pair + (uint32_t)iter * npairs : __builtin_amdgcn_readfirstlane((uint32_t)w);
     const uint32_t stat = __builtin_amdgcn_readfirstlane((uint32_t)(w >> 32));
     if (idx >= nitems) break;
     if (bad || stat != 0u) {  // failed launch: drain without work
@@ -1715,8 +1863,9 @@ __global__ __launch_bounds__(kRowBlock) void fused_kernel(FwdArgs a) {
       __syncthreads();
       continue;
     }
-    const Item it = map_item(a, sm, s_off, order, key, (int)idx);
-    if (it.verified) verified_row<VAR, FULL, GB, TM>(a, sm, lp, lq, it, par, tag);
+    Item it = map_item(a, sm, s_off, order, key, (int)idx, SP == 2);
+    if (SP == 2 && !it.verified) it.half = ph;
+    if (it.verified) verified_row<VAR, FULL, GB, TM, NRT, SP>(a, sm, lp, lq, it, par, tag, ph);
     else unverified_row<VAR, GB>(a, sm, it.row, par, it.half, tag);
   }
   // The workgroup that leaves last sums the request losses, reports the
@@ -2381,30 +2530,45 @@ __global__ __launch_bounds__(kBlock) void zero_kernel(uint64_t* p, size_t n) {
     p[i] = 0ull;
 }
 
-template <int VAR, bool GB, bool TM>
-hipError_t launch_fused_g(bool full, const FwdArgs& a, int grid, size_t lds, hipStream_t s) {
-  if (full) hipLaunchKernelGGL((fused_kernel<VAR, true, GB, TM>), dim3(grid), dim3(kRowBlock), lds, s, a);
-  else hipLaunchKernelGGL((fused_kernel<VAR, false, GB, TM>), dim3(grid), dim3(kRowBlock), lds, s, a);
-  return hipGetLastError();
-}
-template <int VAR>
-hipError_t launch_fused_t(bool full, const FwdArgs& a, int grid, size_t lds, hipStream_t s) {
-  if (a.tm)
-    return a.gbf16 ? launch_fused_g<VAR, true, true>(full, a, grid, lds, s)
-                   : launch_fused_g<VAR, false, true>(full, a, grid, lds, s);
-  return a.gbf16 ? launch_fused_g<VAR, true, false>(full, a, grid, lds, s)
-                 : launch_fused_g<VAR, false, false>(full, a, grid, lds, s);
+// The kernel forms built: whole rows (every variant, general or fast form);
+// split rows for the 16-byte variants, in the general form or in the fast
+// form with kRowRegs16 or kPairRegs register slots.
+enum Form { kWholeGeneral, kWholeFast, kSplitGeneral, kSplitFast, kSplitFastPair };
+inline Form form_of(bool full, bool split, int nr) {
+  if (!split) return full ? kWholeFast : kWholeGeneral;
+  if (!full) return kSplitGeneral;
+  return nr == kPairRegs ? kSplitFastPair : kSplitFast;
 }
 template <int VAR, bool GB, bool TM>
-hipError_t occ_g(bool full, size_t lds, int* out) {
-  if (full)
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, fused_kernel<VAR, true, GB, TM>, kRowBlock, lds);
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, fused_kernel<VAR, false, GB, TM>, kRowBlock, lds);
+const void* kernel_of(Form f) {
+  constexpr bool kWideVar = VAR == kBf16x8 || VAR == kF32x4;
+  switch (f) {
+    case kWholeFast: return (const void*)fused_kernel<VAR, true, GB, TM, RowCfg<VAR>::NR, 1>;
+    case kWholeGeneral: return (const void*)fused_kernel<VAR, false, GB, TM, RowCfg<VAR>::NR, 1>;
+    default: break;
+  }
+  if constexpr (kWideVar) {
+    switch (f) {
+      case kSplitGeneral: return (const void*)fused_kernel<VAR, false, GB, TM, kRowRegs16, 2>;
+      case kSplitFast: return (const void*)fused_kernel<VAR, true, GB, TM, kRowRegs16, 2>;
+      case kSplitFastPair: return (const void*)fused_kernel<VAR, true, GB, TM, kPairRegs, 2>;
+      default: break;
+    }
+  }
+  return nullptr;
 }
 template <int VAR>
-hipError_t occ_t(bool full, bool gb, bool tm, size_t lds, int* out) {
-  if (tm) return gb ? occ_g<VAR, true, true>(full, lds, out) : occ_g<VAR, false, true>(full, lds, out);
-  return gb ? occ_g<VAR, true, false>(full, lds, out) : occ_g<VAR, false, false>(full, lds, out);
+const void* kernel_t(Form f, bool gb, bool tm) {
+  if (tm) return gb ? kernel_of<VAR, true, true>(f) : kernel_of<VAR, false, true>(f);
+  return gb ? kernel_of<VAR, true, false>(f) : kernel_of<VAR, false, false>(f);
+}
+const void* fused_kernel_ptr(Variant v, Form f, bool gb, bool tm) {
+  switch (v) {
+    case kBf16x8: return kernel_t<kBf16x8>(f, gb, tm);
+    case kBf16x1: return kernel_t<kBf16x1>(f, gb, tm);
+    case kF32x4: return kernel_t<kF32x4>(f, gb, tm);
+    default: return kernel_t<kF32x1>(f, gb, tm);
+  }
 }
 template <int VAR, bool TM>
 hipError_t launch_bwd_g(const BwdArgs& a, hipStream_t s) {
@@ -2420,22 +2584,21 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_fused(Variant v, bool full, const FwdArgs& a, int grid, size_t lds, hipStream_t s) {
-  switch (v) {
-    case kBf16x8: return launch_fused_t<kBf16x8>(full, a, grid, lds, s);
-    case kBf16x1: return launch_fused_t<kBf16x1>(full, a, grid, lds, s);
-    case kF32x4: return launch_fused_t<kF32x4>(full, a, grid, lds, s);
-    default: return launch_fused_t<kF32x1>(full, a, grid, lds, s);
-  }
+hipError_t launch_fused(Variant v, bool full, int nr, const FwdArgs& a, int grid, size_t lds, hipStream_t s) {
+  const void* k = fused_kernel_ptr(v, form_of(full, a.split == 2, nr), a.gbf16 != 0, a.tm != 0);
+  if (!k) return hipErrorInvalidDeviceFunction;
+  FwdArgs arg = a;
+  void* params[] = {&arg};
+  return hipLaunchKernel(k, dim3(grid), dim3(kRowBlock), params, lds, s);
 }
 
-hipError_t fused_blocks_per_cu(Variant v, bool full, bool gb, bool tm, size_t lds, int* out) {
-  switch (v) {
-    case kBf16x8: return occ_t<kBf16x8>(full, gb, tm, lds, out);
-    case kBf16x1: return occ_t<kBf16x1>(full, gb, tm, lds, out);
-    case kF32x4: return occ_t<kF32x4>(full, gb, tm, lds, out);
-    default: return occ_t<kF32x1>(full, gb, tm, lds, out);
+hipError_t fused_blocks_per_cu(Variant v, bool full, bool split, int nr, bool gb, bool tm, size_t lds, int* out) {
+  const void* k = fused_kernel_ptr(v, form_of(full, split, nr), gb, tm);
+  if (!k) {
+    *out = 0;
+    return hipSuccess;
   }
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, k, kRowBlock, lds);
 }
 
 hipError_t launch_bwd(Variant v, const BwdArgs& a, hipStream_t s) {

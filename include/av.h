@@ -255,16 +255,12 @@ int av_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
  *   status       [1] int32 out or NULL: 0, or AV_DEV_* bits found on device
  *   workspace    >= av_workspace_bytes(B, k, R) bytes, zeroed once by
  *                av_workspace_init before first use
- *   onchip_limit 0 = automatic.  Otherwise (regs | lds << 8): how many
- *                16-byte vectors per thread of each row the pass keeps in
- *                registers and in LDS (each clamped to what the build
- *                provides); the rest of the row is read from HBM a second
- *                time for the gradient.  A tuning and test knob.
+ * Launch: one persistent 1024-thread workgroup per CU, whole rows taken
+ * from a dispense counter in the workspace, longest first.
  * Errors (AV_EINVAL): NULL required pointer, B < 1, k < 1 or > AV_MAX_K,
  * V < 1, R inconsistent with the layout, lambda outside [0, 1] or NaN, tau
  * <= 0 or NaN, grad_scale non-finite, temperature not positive and finite,
- * workspace too small, negative onchip_limit, row_stats or workspace not
- * 16-byte aligned.
+ * workspace too small, row_stats or workspace not 16-byte aligned.
  * AV_EUNSUPPORTED: dtype or grad_dtype other than AV_F32/AV_BF16; ragged
  * with B > 4095 (the offsets are cached on chip); R*V >= 2^46.
  */
@@ -275,8 +271,7 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R,
                       int32_t* tgt_argmax, int32_t* acc_len, float* row_loss,
                       float* req_loss, float* total_loss, float* row_stats,
                       float* lse_q1, void* grad_zq, int grad_dtype, int32_t* status,
-                      void* workspace, size_t workspace_bytes,
-                      int onchip_limit, void* stream);
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * av_verify_opd_bwd -- gradient alone, from saved row statistics.

@@ -62,9 +62,10 @@ def gpu_inputs(w: synth.Workload, dev="cuda") -> dict:
 
 
 def run_fwd(av, inp: dict, w: synth.Workload, *, bk: Optional[np.ndarray], lam: float, tau: float,
-            gs: float = 1.0, vecs: int = 0, want_grad: bool = True, temperature: float = 1.0) -> dict:
+            gs: float = 1.0, vecs: int = 0, want_grad: bool = True, temperature: float = 1.0,
+            split: int = 0) -> dict:
     kw = dict(k=w.k, lam=lam, tau=tau, grad_scale=gs, onchip_limit=vecs, want_grad=want_grad,
-              temperature=temperature)
+              temperature=temperature, split_rows=split)
     if w.row_off is not None:
         kw["row_off"] = inp["row_off"]
     else:

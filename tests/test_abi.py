@@ -1,6 +1,7 @@
 """The C ABI on a host without a GPU: the library loads, exports every entry
-point include/av.h declares, and rejects bad arguments on the host before it
-touches the HIP runtime.  No compute call is made here."""
+point include/av.h and include/av_test.h declare, and rejects bad arguments
+on the host before it touches the HIP runtime.  No compute call is made
+here."""
 
 import ctypes
 import os
@@ -11,7 +12,8 @@ import pytest
 import drafter_distillation_amd as dd
 from drafter_distillation_amd import _lib
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "av.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADERS = [os.path.join(INCLUDE, n) for n in sorted(os.listdir(INCLUDE)) if n.endswith(".h")]
 
 # Fake device addresses: never dereferenced, because every call below fails
 # host-side validation first.  16-byte aligned so only the intended check fails.
@@ -20,15 +22,18 @@ NULL = None
 
 
 def header_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(av_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(av_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
     lib = dd.lib()
     names = header_functions()
-    assert {"av_length_head", "av_verify_opd_fwd", "av_verify_opd_bwd"} <= set(names)
+    assert {"av_length_head", "av_verify_opd_fwd", "av_verify_opd_bwd",
+            "av_test_verify_opd_fwd"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -55,13 +60,16 @@ def test_workspace_bytes():
 def fwd(**kw):
     a = dict(dtype=1, B=2, k=4, V=64, R=8, row_off=NULL, zp=P, zq=P, draft=P, bk=P, lam=0.5,
              tau=0.1, gs=1.0, temp=1.0, tgt=P, acc=P, row_loss=P, req_loss=NULL, total=NULL, stats=P,
-             lse1=NULL, grad=P, gdt=0, status=NULL, ws=P, ws_bytes=1 << 30, vecs=0, stream=NULL)
+             lse1=NULL, grad=P, gdt=0, status=NULL, ws=P, ws_bytes=1 << 30, vecs=None, split=0,
+             stream=NULL)
     a.update(kw)
-    return _lib.lib().av_verify_opd_fwd(
-        a["dtype"], a["B"], a["k"], a["V"], a["R"], a["row_off"], a["zp"], a["zq"], a["draft"],
-        a["bk"], a["lam"], a["tau"], a["gs"], a["temp"], a["tgt"], a["acc"], a["row_loss"],
-        a["req_loss"], a["total"], a["stats"], a["lse1"], a["grad"], a["gdt"], a["status"], a["ws"],
-        a["ws_bytes"], a["vecs"], a["stream"])
+    args = (a["dtype"], a["B"], a["k"], a["V"], a["R"], a["row_off"], a["zp"], a["zq"], a["draft"],
+            a["bk"], a["lam"], a["tau"], a["gs"], a["temp"], a["tgt"], a["acc"], a["row_loss"],
+            a["req_loss"], a["total"], a["stats"], a["lse1"], a["grad"], a["gdt"], a["status"], a["ws"],
+            a["ws_bytes"])
+    if a["vecs"] is None:  # the public entry point
+        return _lib.lib().av_verify_opd_fwd(*args, a["stream"])
+    return _lib.lib().av_test_verify_opd_fwd(*args, a["vecs"], a["split"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -93,7 +101,10 @@ def fwd(**kw):
     (dict(temp=float("nan")), dd.AV_EINVAL),
     (dict(temp=float("inf")), dd.AV_EINVAL),
     (dict(ws_bytes=256), dd.AV_EINVAL),                  # workspace too small
-    (dict(vecs=-1), dd.AV_EINVAL),
+    (dict(vecs=-1), dd.AV_EINVAL),                       # test hook: knob out of range
+    (dict(vecs=0, split=3), dd.AV_EINVAL),
+    (dict(vecs=0, split=-1), dd.AV_EINVAL),
+    (dict(vecs=0, split=2, zp=NULL), dd.AV_EINVAL),      # the hook validates as the entry point
     (dict(stats=ctypes.c_void_p(0x10004)), dd.AV_EINVAL),  # row_stats not 16-byte aligned
     (dict(ws=ctypes.c_void_p(0x10008)), dd.AV_EINVAL),
     (dict(dtype=2), dd.AV_EUNSUPPORTED),

@@ -101,11 +101,11 @@ def test_length_head_extremes(av):
 # whole-batch parity on small shapes (every row, every entry)
 # ---------------------------------------------------------------------------
 
-def full_parity(av, w, bk, lam, tau, gs=1.0, vecs=0):
+def full_parity(av, w, bk, lam, tau, gs=1.0, vecs=0, split=0):
     say(f"parity {w.name} B={w.B} k={w.k} V={w.V} {w.dtype} {w.layout} lam={lam} tau={tau} "
-        f"gs={gs} vecs={vecs}")
+        f"gs={gs} vecs={vecs} split={split}")
     inp = gpu_inputs(w)
-    out = run_fwd(av, inp, w, bk=bk, lam=lam, tau=tau, gs=gs, vecs=vecs)
+    out = run_fwd(av, inp, w, bk=bk, lam=lam, tau=tau, gs=gs, vecs=vecs, split=split)
     assert_no_errors(check_workload(out, w, bk, lam, tau, gs))
     ref = oracle_reductions(w, bk, lam, tau, gs)
     np.testing.assert_allclose(out["req_loss"], ref["req_loss"], rtol=1e-3, atol=1e-4)
@@ -153,12 +153,69 @@ def test_fast_form_ring_edges(av, dtype, V):
     assert np.array_equal(g.cpu().numpy().view(np.uint32), out["grad"].view(np.uint32))
 
 
+# Split rows (each verified row's halves on two workgroups that exchange
+# statistics, a launch form the test hook selects): at small widths (general
+# form, the halves partly streamed when the on-chip knob is small), then at
+# widths where the halves take the fast form with 5 register slots (halves of
+# 9..12 full slots: none, one partial, one full or almost four streamed) or
+# with 9 (halves of 13 slots or more).
+SPLIT_V = [16, 64, 1000, 10000, 10008, 65544]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V", SPLIT_V)
+@pytest.mark.parametrize("vecs", [0, 1 | (1 << 8)])
+def test_split_rows_small_shapes(av, dtype, V, vecs):
+    w = synth.make("concurrent", B=3, V=V, dtype=dtype)
+    bk = np.array([1, 16, 7])
+    full_parity(av, w, bk, 0.5, 0.1, gs=0.25, vecs=vecs, split=2)
+
+
+SPLIT_FAST_BF16 = [147456, 151936, 163840, 212992 - 8, 212992, 262144]
+SPLIT_FAST_F32 = [73728, 73728 + 4 * 100, 106496 + 4 * 4096]
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", v) for v in SPLIT_FAST_BF16] + [("f32", v) for v in SPLIT_FAST_F32])
+def test_split_rows_fast_forms(av, dtype, V):
+    w = synth.make("concurrent", B=2, V=V, dtype=dtype)
+    bk = np.array([16, 5])
+    out = full_parity(av, w, bk, 0.5, 0.1, gs=0.25, split=2)
+    inp = gpu_inputs(w)
+    g = av.av_verify_opd_bwd(inp["zp"], inp["zq"], torch.from_numpy(out["tgt_argmax"]).cuda(),
+                             torch.from_numpy(out["row_stats"]).cuda(), k=w.k, lam=0.5, tau=0.1,
+                             grad_scale=0.25, bk=torch.from_numpy(bk.astype(np.int32)).cuda())
+    assert np.array_equal(g.cpu().numpy().view(np.uint32), out["grad"].view(np.uint32))
+    # the same rows as whole rows give the same argmax, acceptance and the
+    # same losses to rounding
+    whole = run_fwd(av, inp, w, bk=bk, lam=0.5, tau=0.1, gs=0.25, split=1)
+    assert np.array_equal(whole["tgt_argmax"], out["tgt_argmax"])
+    assert np.array_equal(whole["acc_len"], out["acc_len"])
+    np.testing.assert_allclose(whole["row_loss"], out["row_loss"], rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("split", [1, 2])
+def test_split_rows_ragged_and_ties(av, split):
+    w = synth.make("ragged", B=10, V=9000)
+    full_parity(av, w, None, 0.5, 0.1, gs=1.0 / w.R, split=split)
+    # exact bf16 ties across the two halves: the first half's index wins
+    w = synth.make("concurrent", B=1, V=12000, dtype="bf16")
+    zp = w.zp.copy()
+    big = synth.to_bf16_bits(np.array([40.0]))[0]
+    cut = 768 * 8  # first entry of the second half (64-vector boundary past the middle)
+    for i, (j1, j2) in enumerate([(cut - 1, cut), (5, cut + 3), (cut, 11999), (0, 11999)]):
+        zp[i, j1] = big
+        zp[i, j2] = big
+    w.zp = zp
+    out = full_parity(av, w, np.array([16]), 0.5, 0.1, split=split)
+    assert list(out["tgt_argmax"][:4]) == [cut - 1, 5, cut, 0]
+
+
 @pytest.mark.parametrize("lam", [0.0, 0.5, 1.0])
 @pytest.mark.parametrize("tau", [0.01, 0.05, 0.1, 1e9, float("inf")])
 def test_lambda_tau_branches(av, lam, tau):
     w = synth.make("long", B=2, V=24000)
-    for vecs in (0, 1 | (1 << 8)):
-        full_parity(av, w, np.array([32, 17]), lam, tau, vecs=vecs)
+    for vecs, split in ((0, 0), (1 | (1 << 8), 0), (0, 2)):
+        full_parity(av, w, np.array([32, 17]), lam, tau, vecs=vecs, split=split)
 
 
 @pytest.mark.parametrize("vecs", ONCHIP)
@@ -216,7 +273,7 @@ def test_negative_clip_branch(av):
     zp = rng.normal(0, 1, (B * k, V))
     zq = zp + rng.normal(0, 0.5, (B * k, V))
     for r in range(B * k):
-        j = 17 * (r + 1)
+        j = 17 * (r + 1) + (2100 if r % 2 else 0)  # odd rows: in the second half when split
         zp[r, j] = 14.0                 # p_j ~ 0.97
         zq[r, j] = 10.5 + 0.3 * r       # q_j ~ 0.3-0.9
     w = synth.make("concurrent", B=B, V=V, dtype="f32")
@@ -228,6 +285,7 @@ def test_negative_clip_branch(av):
     assert t.r.min() < -0.1             # the negative branch is exercised
     full_parity(av, w, np.array([4, 3]), 0.5, 0.1)
     full_parity(av, w, np.array([4, 3]), 0.0, 0.05, vecs=1)
+    full_parity(av, w, np.array([4, 3]), 0.5, 0.1, split=2)
 
 
 def test_rising_and_falling_logit_ramps(av):
@@ -247,8 +305,9 @@ def test_rising_and_falling_logit_ramps(av):
     w.zp = zp.astype(np.float32)
     w.zq = zq.astype(np.float32)
     w.draft = np.argmax(w.zq, axis=1).astype(np.int32)
-    for lam, tau, vecs in [(0.5, 0.1, 0), (0.0, 1e9, 0), (0.5, 0.1, 1 | (1 << 8))]:
-        full_parity(av, w, np.array([4, 3]), lam, tau, vecs=vecs)
+    for lam, tau, vecs, split in [(0.5, 0.1, 0, 0), (0.0, 1e9, 0, 0), (0.5, 0.1, 1 | (1 << 8), 0),
+                                  (0.5, 0.1, 0, 2)]:
+        full_parity(av, w, np.array([4, 3]), lam, tau, vecs=vecs, split=split)
 
 
 # ---------------------------------------------------------------------------
