@@ -46,6 +46,10 @@ _SIGS = {
     "av_workspace_init": (_i, [_vp, _sz, _vp]),
     "av_verify_opd_fwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _f, _f, _f, _f,
                                _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _sz, _vp]),
+    "av_verify_opd_fwd_noalloc": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _f, _f, _f, _f,
+                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp]),
+    "av_noalloc_max_bytes": (_sz, []),
+    "av_init": (_i, []),
     "av_test_verify_opd_fwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _f, _f, _f, _f,
                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _sz, _i, _i,
                                     _vp]),
@@ -301,7 +305,7 @@ def av_verify_opd_fwd(zp: torch.Tensor, zq: torch.Tensor, draft: torch.Tensor, *
                       want_stats: bool = True, onchip_limit: int = 0, split_rows: int = 0,
                       grad_dtype: torch.dtype = torch.float32, temperature: float = 1.0,
                       want_lse_q1: Optional[bool] = None,
-                      out: Optional[dict] = None) -> dict:
+                      out: Optional[dict] = None, noalloc: bool = False) -> dict:
     """Fused verify + OPD pass (see include/av.h).
 
     zp, zq: [R, V] bf16/f32; draft: [R] int32; dense layout with bk [B] int32,
@@ -315,6 +319,8 @@ def av_verify_opd_fwd(zp: torch.Tensor, zq: torch.Tensor, draft: torch.Tensor, *
 
     onchip_limit and split_rows are test knobs that force a launch form
     (include/av_test.h); with both 0 the public entry point is called.
+    noalloc: call av_verify_opd_fwd_noalloc (library-owned workspace; with
+    every output supplied in `out`, nothing is allocated).
     """
     _need_gpu("zp", zp)
     _need_gpu("zq", zq, zp.dtype)
@@ -353,13 +359,21 @@ def av_verify_opd_fwd(zp: torch.Tensor, zq: torch.Tensor, draft: torch.Tensor, *
     if grad is not None:
         _need_gpu("grad", grad, grad_dtype)
     status = get("status", (1,), torch.int32)
+    args = (_dtype_code(zp), B, int(k), V, R, _ptr(row_off), _ptr(zp), _ptr(zq), _ptr(draft),
+            _ptr(bk), float(lam), float(tau), float(grad_scale), float(temperature), _ptr(tgt),
+            _ptr(acc), _ptr(row_loss), _ptr(req_loss), _ptr(total), _ptr(stats), _ptr(lse1),
+            _ptr(grad), _grad_code(grad_dtype), _ptr(status))
+    if noalloc:
+        if onchip_limit or split_rows:
+            raise ValueError("noalloc takes the automatic launch form")
+        with torch.cuda.device(dev):
+            rc = lib().av_verify_opd_fwd_noalloc(*args, _stream(dev))
+        _check("av_verify_opd_fwd_noalloc", rc)
+        return o
     nbytes = av_workspace_bytes(B, k, R) if B >= 1 and R >= 1 else 0
     with torch.cuda.device(dev):
         ws = workspace(dev, nbytes)
-        args = (_dtype_code(zp), B, int(k), V, R, _ptr(row_off), _ptr(zp), _ptr(zq), _ptr(draft),
-                _ptr(bk), float(lam), float(tau), float(grad_scale), float(temperature), _ptr(tgt),
-                _ptr(acc), _ptr(row_loss), _ptr(req_loss), _ptr(total), _ptr(stats), _ptr(lse1),
-                _ptr(grad), _grad_code(grad_dtype), _ptr(status), _ptr(ws), ws.numel())
+        args = args + (_ptr(ws), ws.numel())
         if onchip_limit or split_rows:
             rc = lib().av_test_verify_opd_fwd(*args, int(onchip_limit), int(split_rows), _stream(dev))
         else:

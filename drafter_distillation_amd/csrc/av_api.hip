@@ -74,6 +74,35 @@ hipError_t device_info(const DeviceInfo** out) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Workspace of av_verify_opd_fwd_noalloc: one array per GPU, resident from
+// the library's load to the end of the process.  Its host-side name is only a
+// handle: kernels get the device address that hipGetSymbolAddress returns for
+// the current device, looked up (and the array zeroed) once per device.
+static __device__ __align__(256) unsigned char scratch[AV_NOALLOC_SCRATCH_BYTES];
+void* g_scratch[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+hipError_t scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* p = nullptr;
+    hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    // zeroed once, synchronously: the pass's launch epoch and tagged words
+    // start from zero; every later call leaves the array ready for the next
+    if (err == hipSuccess) err = hipMemset(p, 0, AV_NOALLOC_SCRATCH_BYTES);
+    if (err == hipSuccess) err = hipDeviceSynchronize();
+    g_scratch[dev] = err == hipSuccess ? p : nullptr;
+    g_scratch_err[dev] = err;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
 // Shared validation of the verify entry points.  Fills the layout facts.
 struct Plan {
   avk::Variant var;
@@ -410,6 +439,33 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_
   return verify_opd_fwd_impl(dtype, B, k, V, R, row_off, zp, zq, draft, bk, lambda, tau, grad_scale,
                              temperature, tgt_argmax, acc_len, row_loss, req_loss, total_loss, row_stats,
                              lse_q1, grad_zq, grad_dtype, status, workspace, workspace_bytes, 0, 0, stream);
+}
+
+int av_init(void) {
+  void* p = nullptr;
+  hipError_t e = scratch_ptr(&p);
+  const DeviceInfo* d = nullptr;
+  if (e == hipSuccess) e = device_info(&d);
+  return e == hipSuccess ? AV_OK : hip_fail(e);
+}
+
+size_t av_noalloc_max_bytes(void) { return AV_NOALLOC_SCRATCH_BYTES; }
+
+int av_verify_opd_fwd_noalloc(int dtype, int B, int k, int V, int R, const int32_t* row_off,
+                              const void* zp, const void* zq, const int32_t* draft, const int32_t* bk,
+                              float lambda, float tau, float grad_scale, float temperature,
+                              int32_t* tgt_argmax, int32_t* acc_len, float* row_loss, float* req_loss,
+                              float* total_loss, float* row_stats, float* lse_q1, void* grad_zq,
+                              int grad_dtype, int32_t* status, void* stream) {
+  const size_t need = av_workspace_bytes(B, k, R);
+  if (need == 0) return AV_EINVAL;
+  if (need > AV_NOALLOC_SCRATCH_BYTES) return AV_EUNSUPPORTED;
+  void* ws = nullptr;
+  hipError_t e = scratch_ptr(&ws);
+  if (e != hipSuccess) return hip_fail(e);
+  return verify_opd_fwd_impl(dtype, B, k, V, R, row_off, zp, zq, draft, bk, lambda, tau, grad_scale,
+                             temperature, tgt_argmax, acc_len, row_loss, req_loss, total_loss, row_stats,
+                             lse_q1, grad_zq, grad_dtype, status, ws, AV_NOALLOC_SCRATCH_BYTES, 0, 0, stream);
 }
 
 int av_test_verify_opd_fwd(int dtype, int B, int k, int V, int R, const int32_t* row_off,

@@ -274,6 +274,37 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * av_verify_opd_fwd_noalloc -- av_verify_opd_fwd for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments, outputs and errors
+ * without workspace / workspace_bytes.  The workspace is a library-owned
+ * array of AV_NOALLOC_SCRATCH_BYTES bytes per GPU, resident until the process
+ * ends; the call allocates nothing.  Limits and behaviour:
+ *  - av_workspace_bytes(B, k, R) must not exceed AV_NOALLOC_SCRATCH_BYTES
+ *    (4 MiB: B = 128 requests of 16 rows need 0.5 MiB; about 16000 rows in
+ *    all), else AV_EUNSUPPORTED before anything is enqueued;
+ *  - the array is looked up and zeroed synchronously on the first call on a
+ *    device (or by av_init); make that first call, or av_init, outside graph
+ *    capture;
+ *  - every call on a GPU shares that GPU's array: calls that may overlap on
+ *    one GPU (different streams without ordering) race; serialise them.
+ */
+#define AV_NOALLOC_SCRATCH_BYTES (4u << 20)
+int av_verify_opd_fwd_noalloc(int dtype, int B, int k, int V, int R,
+                              const int32_t* row_off, const void* zp, const void* zq,
+                              const int32_t* draft, const int32_t* bk,
+                              float lambda, float tau, float grad_scale, float temperature,
+                              int32_t* tgt_argmax, int32_t* acc_len, float* row_loss,
+                              float* req_loss, float* total_loss, float* row_stats,
+                              float* lse_q1, void* grad_zq, int grad_dtype, int32_t* status,
+                              void* stream);
+/* Size of that array (AV_NOALLOC_SCRATCH_BYTES). */
+size_t av_noalloc_max_bytes(void);
+/* Per-device set-up of the current device (the no-allocation array, launch
+ * facts); optional, for callers that must not pay it on a first call. */
+int av_init(void);
+
+/*
  * av_verify_opd_bwd -- gradient alone, from saved row statistics.
  *
  * Recomputes grad_zq exactly as av_verify_opd_fwd defines it, in one
