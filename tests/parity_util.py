@@ -16,9 +16,12 @@ Acceptance rule (the arithmetic behind it is written out in the design notes):
     log-sum-exp), may read anything between 0 and the reference: the float32
     exponential flushes such q_j to zero;
   * lse of zq at temperature 1 (lse_q1): as lse_p, lse_q;
-  * an entry whose |r_j| lies within 1e-4 tau of tau may be classified either
-    way by float32; rows with such entries are accepted if they match the
+  * an entry whose |r_j| lies within w_j of tau may be classified either way
+    by float32, where w_j bounds |r32_j - r_j| from the GPU's own log-sum-exp
+    errors (measured on the row) and float32 rounding of the entry's steps
+    (clip_window); rows with such entries are accepted if they match the
     oracle with any combination of those indicators flipped (at most 3).
+    AMBIGUOUS counts the entries and rows this rule touched.
 """
 
 from __future__ import annotations
@@ -37,7 +40,28 @@ LOSS_RTOL, LOSS_ATOL = 1e-3, 1e-5
 LSE_RTOL, LSE_ATOL = 2e-6, 2e-6
 GRAD_RTOL, GRAD_QTOL = 1e-3, 2e-5
 FLT_MIN_NORMAL = 2.0 ** -126  # smallest normal float32
-CLIP_AMBIG = 1e-4
+U32 = 2.0 ** -24  # unit roundoff of float32
+AMBIGUOUS = {"rows": 0, "entries": 0}
+
+
+def clip_window(t: oracle.RowTerms, zp_row, zq_row, tau: float, d_lse_p: float, d_lse_q: float) -> np.ndarray:
+    """Width of the band around tau in which the GPU's float32 r_j may fall on
+    the other side of tau than the float64 r_j.
+
+    The GPU forms q_j = exp2(fma(s zq_j, L, -lse_q L)) and
+    ell_j = s (zq_j - zp_j) - (lse_q - lse_p) (s = 1 / T, L = log2 e / T in
+    float32) from its float32 log-sum-exps, then r_j = q_j ell_j.  To first
+    order, with dq, dp the log-sum-exp errors:
+      q32 / q - 1   within  eq = dq + 4 u (1 + |s zq_j| + |lse_q|)
+                            (the exponent's roundings; exp2 to 1 ulp)
+      ell32 - ell   within  el = dq + dp + 4 u (1 + |s (zq_j - zp_j)| + |lse_q - lse_p|)
+      r32 - r       within  q (|ell| (eq + u) + el)
+    plus |tau32 - tau| <= u tau for the threshold itself; the band is twice
+    that bound."""
+    s = 1.0 / t.temperature
+    eq = d_lse_q + 4 * U32 * (1.0 + np.abs(s * zq_row) + abs(t.lse_q))
+    el = d_lse_q + d_lse_p + 4 * U32 * (1.0 + np.abs(s * (zq_row - zp_row)) + abs(t.lse_q - t.lse_p))
+    return 2.0 * (t.q * (np.abs(t.ell) * (eq + U32) + el) + U32 * tau)
 
 
 def logits_tensor(a: np.ndarray, dtype: str, dev="cuda") -> torch.Tensor:
@@ -101,6 +125,31 @@ def grad_row_ok(g: np.ndarray, t: oracle.RowTerms, gs: float) -> np.ndarray:
     return (np.abs(g64 - t.grad) <= tol) | (flushed & between)
 
 
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bfloat16 numbers at |x| (8 significant bits; below the
+    smallest normal, the subnormal spacing 2^-133)."""
+    m, e = np.frexp(np.abs(x))
+    return np.where(np.abs(x) >= 2.0 ** -126, np.ldexp(1.0, e - 8), 2.0 ** -133)
+
+
+def grad_row_ok_bf16(g: np.ndarray, t: oracle.RowTerms, gs: float) -> np.ndarray:
+    """A bfloat16 gradient entry is the float32 entry rounded to nearest: it
+    may differ from the float64 reference by the float32 bar plus one
+    bfloat16 spacing (half of one for the rounding, half as margin)."""
+    scale = t.q * (1.0 + np.abs(t.ell) + abs(t.S))
+    if t.temperature != 1.0:
+        scale = scale / t.temperature + t.q1
+    g64 = g.astype(np.float64)
+    tol = GRAD_RTOL * np.abs(t.grad) + GRAD_QTOL * abs(gs) * scale
+    tol = tol + bf16_ulp(np.maximum(np.abs(t.grad), np.abs(g64)) + tol)
+    flushed = t.q < FLT_MIN_NORMAL
+    if t.q1 is not None:
+        flushed &= t.q1 < FLT_MIN_NORMAL
+    flushed[t.argmax] = False
+    between = (np.abs(g64) <= np.abs(t.grad)) & (g64 * t.grad >= 0.0)
+    return (np.abs(g64 - t.grad) <= tol) | (flushed & between)
+
+
 def check_row(r: int, out: dict, zp_row, zq_row, lam, tau, gs, verified: bool, errors: list,
               temperature: float = 1.0):
     """Compare one row of GPU output with the oracle; append messages to errors."""
@@ -122,7 +171,18 @@ def check_row(r: int, out: dict, zp_row, zq_row, lam, tau, gs, verified: bool, e
         return
     t = oracle.row_terms(zp_row, zq_row, lam, tau, gs, temperature=temperature)
     variants = [t]
-    amb = np.nonzero(oracle.clip_margin(t.r, tau) <= CLIP_AMBIG)[0] if math.isfinite(tau) else []
+    amb = []
+    if math.isfinite(tau):
+        if stats is not None:  # the GPU's own log-sum-exp errors on this row
+            d_p, d_q = abs(float(stats[r][0]) - t.lse_p), abs(float(stats[r][1]) - t.lse_q)
+        else:                  # the bound the lse check allows
+            d_p = LSE_RTOL * abs(t.lse_p) + LSE_ATOL
+            d_q = LSE_RTOL * abs(t.lse_q) + LSE_ATOL
+        w = clip_window(t, zp_row, zq_row, tau, d_p, d_q)
+        amb = np.nonzero(np.abs(np.abs(t.r) - tau) <= w)[0]
+        if len(amb):
+            AMBIGUOUS["rows"] += 1
+            AMBIGUOUS["entries"] += len(amb)
     if 0 < len(amb) <= 3:
         for flips in itertools.product([False, True], repeat=len(amb)):
             if any(flips):
@@ -158,11 +218,58 @@ def check_row(r: int, out: dict, zp_row, zq_row, lam, tau, gs, verified: bool, e
     errors.append(f"row {r}: " + "; ".join(msgs))
 
 
+# State the forked workers of check_workload read (set before the pool starts).
+_POOL: dict = {}
+
+
+def _check_chunk(rows):
+    """Worker: check_row over a list of rows; returns (errors, ambiguous counts)."""
+    c = _POOL
+    AMBIGUOUS["rows"] = AMBIGUOUS["entries"] = 0
+    errors: list = []
+    for r in rows:
+        check_row(r, c["out"], decode_rows(c["w"], "zp", r), decode_rows(c["w"], "zq", r), c["lam"], c["tau"],
+                  c["gs"], bool(c["verified"][r]), errors, temperature=c["temperature"])
+        if len(errors) >= c["max_errors"]:
+            break
+    return errors, dict(AMBIGUOUS)
+
+
+def _check_rows(out, w, verified, rows, lam, tau, gs, temperature, max_errors, workers):
+    """check_row over `rows`: in this process, or in `workers` forked
+    processes that read the workload and the GPU outputs from this process's
+    memory (they run only the float64 oracle; nothing there touches the GPU)."""
+    rows = list(rows)
+    if workers <= 1 or len(rows) < 2 * workers:
+        errors: list = []
+        for r in rows:
+            check_row(r, out, decode_rows(w, "zp", r), decode_rows(w, "zq", r), lam, tau, gs,
+                      bool(verified[r]), errors, temperature=temperature)
+            if len(errors) >= max_errors:
+                break
+        return errors
+    import multiprocessing as mp
+    _POOL.update(out=out, w=w, verified=verified, lam=lam, tau=tau, gs=gs, temperature=temperature,
+                 max_errors=max_errors)
+    chunks = [rows[i::4 * workers] for i in range(4 * workers)]
+    errors = []
+    try:
+        with mp.get_context("fork").Pool(workers) as pool:
+            for e, amb in pool.imap_unordered(_check_chunk, chunks):
+                errors.extend(e)
+                AMBIGUOUS["rows"] += amb["rows"]
+                AMBIGUOUS["entries"] += amb["entries"]
+    finally:
+        _POOL.clear()
+    return errors[:max_errors]
+
+
 def check_workload(out: dict, w: synth.Workload, bk: Optional[np.ndarray], lam: float, tau: float,
                    gs: float = 1.0, rows: Optional[Iterable[int]] = None, max_errors: int = 10,
-                   temperature: float = 1.0):
+                   temperature: float = 1.0, workers: int = 0):
     """Full comparison (rows=None) or comparison on sampled rows; argmax and
-    acceptance are always checked on every row and request."""
+    acceptance are always checked on every row and request.  workers > 1 runs
+    the per-row comparisons in that many forked processes."""
     errors: list = []
     sp = spans(w, bk)
     verified = np.zeros(w.R, dtype=bool)
@@ -182,11 +289,7 @@ def check_workload(out: dict, w: synth.Workload, bk: Optional[np.ndarray], lam: 
             errors.append(f"request {b}: acc {out['acc_len'][b]} vs {acc}")
     # per-row loss / stats / gradient
     check = range(w.R) if rows is None else rows
-    for r in check:
-        check_row(r, out, decode_rows(w, "zp", r), decode_rows(w, "zq", r), lam, tau, gs,
-                  bool(verified[r]), errors, temperature=temperature)
-        if len(errors) >= max_errors:
-            break
+    errors.extend(_check_rows(out, w, verified, check, lam, tau, gs, temperature, max_errors, workers))
     # reductions: per request from the (already checked) row losses, in float64
     rl = out["row_loss"].astype(np.float64)
     for b, (r0, n, bkb) in enumerate(sp):

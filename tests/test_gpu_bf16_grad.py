@@ -1,17 +1,18 @@
 """bfloat16 gradient output of the fused pass and of the standalone backward.
 
 The bfloat16 gradient is defined as the float32 gradient rounded to nearest
-(ties to even), so it is checked bit for bit against the float32 result of the
-same call rounded by torch (the float32 result is itself checked against the
-oracle in test_gpu_parity.py); every other output must be identical to the
-float32 call's."""
+(ties to even).  It is checked against the float64 oracle's gradient, entry
+by entry within the float32 bar plus one bfloat16 spacing; and, as a second
+check, bit for bit against the float32 result of the same call rounded by
+torch.  Every other output must be identical to the float32 call's."""
 
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import synth
-from parity_util import gpu_inputs
+from parity_util import decode_rows, gpu_inputs, grad_row_ok_bf16, spans
 
 pytestmark = pytest.mark.gpu
 
@@ -27,7 +28,7 @@ def bits(t):
     return t.contiguous().view(torch.int16)
 
 
-def compare(av, w, bk, vecs=0, lam=0.5, tau=0.1, gs=0.5):
+def compare(av, w, bk, vecs=0, lam=0.5, tau=0.1, gs=0.5, every=1):
     inp = gpu_inputs(w)
     kw = dict(k=w.k, lam=lam, tau=tau, grad_scale=gs, onchip_limit=vecs)
     if w.row_off is not None:
@@ -38,6 +39,17 @@ def compare(av, w, bk, vecs=0, lam=0.5, tau=0.1, gs=0.5):
     b = av.av_verify_opd_fwd(inp["zp"], inp["zq"], inp["draft"], grad_dtype=torch.bfloat16, **kw)
     torch.cuda.synchronize()
     assert b["grad"].dtype == torch.bfloat16
+    # against the oracle: every verified row, entry by entry
+    g = b["grad"].float().cpu().numpy()
+    for r0, n, bkb in spans(w, bk):
+        for r in range(r0, r0 + bkb):
+            if r % every:
+                continue
+            t = oracle.row_terms(decode_rows(w, "zp", r), decode_rows(w, "zq", r), lam, tau, gs)
+            ok = grad_row_ok_bf16(g[r], t, gs)
+            assert ok.all(), (r, int(np.argmin(ok)), g[r][np.argmin(ok)], t.grad[np.argmin(ok)])
+        assert not g[r0 + bkb:r0 + n].any()
+    # and against the float32 call rounded by torch, bit for bit
     assert torch.equal(bits(b["grad"]), bits(a["grad"].to(torch.bfloat16)))
     for key in ("tgt_argmax", "acc_len", "row_loss", "req_loss", "total_loss", "row_stats", "status"):
         assert torch.equal(a[key], b[key]), key
@@ -65,4 +77,4 @@ def test_full_concurrent(av):
     w = synth.make("concurrent")
     from oracle import length_head
     _, bk, _ = length_head(w.h, w.w, w.bias, w.gamma, w.k)
-    compare(av, w, bk, gs=1.0 / bk.sum())
+    compare(av, w, bk, gs=1.0 / bk.sum(), every=8)  # oracle on every 8th row

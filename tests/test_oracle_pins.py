@@ -353,3 +353,54 @@ def test_clip_interval_is_closed():
     x = torch.tensor([tau, -tau, tau * 1.5], dtype=torch.float64, requires_grad=True)
     torch.clamp(x, -tau, tau).sum().backward()
     assert list(x.grad.numpy()) == [1.0, 1.0, 0.0]
+
+
+# ---------------------------------------------------------------------------
+# the helpers that decide which GPU decisions must match bit for bit
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("k,gamma,x,want", [
+    (16, 1.0, 4.8, 0.2), (16, 1.0, 8.5, 0.5), (16, 1.0, 3.25, 0.25), (16, 1.0, 15.9, 0.1),
+    (16, 1.0, 0.3, 0.3), (32, 1.0, 20.75, 0.25), (16, 0.5, 5.6, 0.4), (16, 1.0, 12.0, 0.0),
+    (16, 1.0, 8.0, 0.0), (32, 1.0, 7.0, 0.0),
+])
+def test_length_head_margin_hand_computed(k, gamma, x, want):
+    """margin is the distance of gamma * rate * k to the nearest integer.
+    With one input of width 1, w = 1 and bias 0, the pre-activation z is the
+    input itself; z = log(s / (1 - s)) for s = x / (gamma k) makes
+    gamma * sigmoid(z) * k = x up to float64 rounding (about 1e-15)."""
+    s = x / (gamma * k)
+    z = math.log(s / (1.0 - s))
+    h = np.array([[z]], np.float64)
+    w = np.array([1.0], np.float64)
+    for mode in ("ceil", "floor"):
+        rate, bk, margin = oracle.length_head(h, w, 0.0, gamma, k, mode)
+        assert abs(rate[0] - s) < 1e-14
+        assert abs(margin[0] - want) < 1e-12
+        if want > 1e-9:  # away from an integer the rounding is unambiguous
+            n = math.ceil(x) if mode == "ceil" else math.floor(x)
+            assert bk[0] == min(max(n, 1), k)
+        else:            # on an integer the oracle flags the decision
+            assert margin[0] <= 1e-9
+
+
+def test_clip_margin_hand_computed():
+    """clip_margin is ||r_j| - tau| / tau: 0 on either edge of the interval,
+    growing with the distance from it, the same for r and -r."""
+    r = np.array([0.1, -0.1, 0.05, -0.2, 0.1001, 0.0, -0.0999, 0.3])
+    want = np.array([0.0, 0.0, 0.5, 1.0, 0.001, 1.0, 0.001, 2.0])
+    np.testing.assert_allclose(oracle.clip_margin(r, 0.1), want, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(oracle.clip_margin(r * 7.0, 0.7), want, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("name", ["tiny", "single", "concurrent", "long"])
+def test_seeded_workloads_have_no_ambiguous_verification_lengths(name):
+    """Every b_k of the seeded workloads, under each (gamma, bias) pair the GPU
+    tests use, lies more than 1e-9 from a rounding boundary, so the GPU tests
+    can require every b_k bit for bit."""
+    import synth
+    w = synth.make(name, V=64)
+    for gamma, bias in [(w.gamma, w.bias), (1.0, 0.0), (0.75, 0.3), (1.6, -2.0)]:
+        for mode in ("ceil", "floor"):
+            _, _, margin = oracle.length_head(w.h, w.w, bias, gamma, w.k, mode)
+            assert margin.min() > 1e-9, (name, gamma, bias, mode, margin.min())
