@@ -24,6 +24,15 @@ verified row, and the residual draw at each request's first rejection.
 `--workload lm_head` measures the backward of the drafter's LM head
 (av_lm_head_bwd) on the same workload's bfloat16 gradient: d hid = dz W and
 d W = dz^T hid with R=2048, V=151936, H=4096 (two bf16 GEMMs).
+
+`--workload tiny` and `--workload single` report the latency of one step
+(length head + fused pass) on one request: B=1, k=16, V=4096 float32 logits
+(H=256), and B=1, k=16, V=151936 bfloat16 logits (H=4096).
+
+`--workload ragged` and `--workload long` time the fused pass on the ragged
+workload (B=128, only the b_k verified rows of each request stored) and on
+the long one (B=64, k=32, V=262144); `--workload long_sweep` prints one line
+per (lambda, tau) in {0, 0.5, 1} x {0.05, 0.1, 1e9} on the long workload.
 """
 
 from __future__ import annotations
@@ -141,36 +150,78 @@ def copy_calibration(torch, dev, mib: int, reps: int = 3) -> None:
     del src, dst
 
 
-def cpu_baseline(n_requests: int, temperature: float = 1.0):
-    """The float64 oracle, untuned, on the first n_requests of the same
-    workload, single-threaded; reported in the same unit (algorithmic GB/s)."""
+# Host cores the oracle baseline may use: the affinity mask, at most 16 (one
+# GPU's share of a GPU host's CPUs).
+MAX_ORACLE_CORES = 16
+
+# The workload the forked oracle workers read (set before the pool starts).
+_ORACLE_JOB: dict = {}
+
+
+def _oracle_request(b: int) -> float:
+    """Worker: the float64 oracle on request b of _ORACLE_JOB's workload
+    (decode, length head of that request, the pass); returns its seconds."""
     import numpy as np
 
     import oracle
-    import synth
-
     from threadpoolctl import threadpool_limits
 
-    w = synth.make("concurrent", B=n_requests)
-    _, bk, _ = oracle.length_head(w.h, w.w, w.bias, w.gamma, w.k)
+    j = _ORACLE_JOB
+    w, k = j["w"], j["w"].k
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        zp = oracle.bf16_bits_to_f64(w.zp)
-        zq = oracle.bf16_bits_to_f64(w.zq)
-        oracle.length_head(w.h, w.w, w.bias, w.gamma, w.k)
-        oracle.verify_opd(zp, zq, w.draft, k=w.k, lam=w.lam, tau=w.tau, grad_scale=1.0, bk=bk,
-                          temperature=temperature)
+        rows = slice(b * k, (b + 1) * k)
+        zp = oracle.bf16_bits_to_f64(w.zp[rows])
+        zq = oracle.bf16_bits_to_f64(w.zq[rows])
+        oracle.length_head(w.h[b:b + 1], w.w, w.bias, w.gamma, k)
+        oracle.verify_opd(zp, zq, w.draft[rows], k=k, lam=w.lam, tau=w.tau, grad_scale=1.0,
+                          bk=j["bk"][b:b + 1], temperature=j["temperature"])
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(w, single_requests: int = 16, temperature: float = 1.0):
+    """The float64 oracle, untuned, on the same workload: all B requests
+    spread over the host's cores (a fork pool over requests, one numpy thread
+    each), and the first `single_requests` requests on one core.  Reported in
+    the same unit as the GPU line (algorithmic GB/s).  Run before the process
+    touches the GPU, so the forked workers start from a process without a
+    device context."""
+    import multiprocessing as mp
+
+    import numpy as np
+
+    import oracle
+
+    _, bk, _ = oracle.length_head(w.h, w.w, w.bias, w.gamma, w.k)
+    cores = max(1, min(MAX_ORACLE_CORES, len(os.sched_getaffinity(0))))
+    _ORACLE_JOB.update(w=w, bk=bk, temperature=temperature)
+    try:
+        t0 = time.perf_counter()
+        with mp.get_context("fork").Pool(cores) as pool:
+            busy = sum(pool.map(_oracle_request, range(w.B), chunksize=1))
         dt = time.perf_counter() - t0
+        t1 = time.perf_counter()
+        for b in range(single_requests):
+            _oracle_request(b)
+        dt1 = time.perf_counter() - t1
+    finally:
+        _ORACLE_JOB.clear()
     Rv = int(np.clip(bk, 1, w.k).sum())
     fused, head = algorithmic_bytes(w.B, w.k, w.V, w.H, w.R, Rv, lse1=temperature != 1.0)
+    bk1 = np.clip(bk[:single_requests], 1, w.k)
+    f1, h1 = algorithmic_bytes(single_requests, w.k, w.V, w.H, single_requests * w.k, int(bk1.sum()),
+                               lse1=temperature != 1.0)
     return {
         "value": round((fused + head) / dt / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
-        "sample": f"first {n_requests} of 128 requests of the same workload ({w.R} rows, "
-                  f"{Rv} verified), float64 numpy, one thread, {dt:.1f} s",
+        "sample": f"all {w.B} requests of the same workload ({w.R} rows, {Rv} verified), float64 numpy, "
+                  f"{cores} worker processes over requests (one numpy thread each), {dt:.1f} s wall, "
+                  f"{busy:.1f} s of CPU work; single core: first {single_requests} requests, {dt1:.1f} s",
         "seconds": round(dt, 3),
+        "cpu_seconds": round(busy, 3),
+        "single_core_value": round((f1 + h1) / dt1 / 1e9, 4),
     }
 
 
@@ -579,8 +630,9 @@ def bench_bwd(args):
 def bench_fused_other(args):
     """The fused pass on the ragged workload (B=128, k=16, V=151936, only the
     b_k verified rows of each request stored) or the long one (B=64, k=32,
-    V=262144, b_k from the length head, H=5120): same timing as the default
-    bench, kernel only."""
+    V=262144, b_k from the length head, H=5120), kernel only, timed as the
+    default bench; `long_sweep` prints one line per (lambda, tau) of the long
+    workload's grid on the same resident inputs."""
     import numpy as np
     import torch
 
@@ -590,7 +642,8 @@ def bench_fused_other(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     dd.lib()
-    w = synth.make(args.workload, seed=args.seed)
+    name = "long" if args.workload == "long_sweep" else args.workload
+    w = synth.make(name, seed=args.seed)
     B, k, V, R = w.B, w.k, w.V, w.R
     zp = torch.from_numpy(w.zp.view(np.int16)).view(torch.bfloat16).to(dev)
     zq = torch.from_numpy(w.zq.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -598,25 +651,125 @@ def bench_fused_other(args):
     kw = {}
     if w.row_off is not None:
         kw["row_off"] = torch.from_numpy(w.row_off).to(dev)
+        bkh = np.diff(w.row_off)
         Rv = R
     else:
         bk = torch.empty(B, dtype=torch.int32, device=dev)
         dd.av_length_head(torch.from_numpy(w.h).to(dev), torch.from_numpy(w.w).to(dev), w.bias, w.gamma, k,
                           bk_out=bk)
         kw["bk"] = bk
-        Rv = int(torch.clamp(bk, 1, k).sum().item())
+        bkh = np.clip(bk.cpu().numpy(), 1, k)
+        Rv = int(bkh.sum())
     gdt = torch.bfloat16 if args.grad == "bf16" else torch.float32
+    gelem = 2 if args.grad == "bf16" else 4
+    fused_b, _ = algorithmic_bytes(B, k, V, 0, R, Rv, gelem=gelem)
+    stream = torch.cuda.current_stream(dev)
+    pairs = [(lam, tau) for lam in (0.0, 0.5, 1.0) for tau in (0.05, 0.1, 1e9)] \
+        if args.workload == "long_sweep" else [(w.lam, w.tau)]
+    out = None
+    for lam, tau in pairs:
+        def step(ev0=None, ev1=None):
+            nonlocal out
+            if ev0 is not None:
+                ev0.record(stream)
+            out = dd.av_verify_opd_fwd(zp, zq, draft, k=k, lam=lam, tau=tau, grad_scale=1.0, out=out,
+                                       grad_dtype=gdt, **kw)
+            if ev1 is not None:
+                ev1.record(stream)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        if int(out["status"].item()) != 0:
+            raise RuntimeError(f"device status {int(out['status'].item())}")
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for e0, e1 in evs:
+            step(e0, e1)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        kern_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs)
+        achieved = fused_b / (kern_ms * 1e-3) / 1e9
+        acch = out["acc_len"].cpu().numpy()
+        desc = {"ragged": f"ragged: B={B} requests, k={k}, V={V}, bf16 logits, only the {R} verified rows stored "
+                          "(b_k drawn with p proportional to 1/b)",
+                "long": f"long: B={B} requests, k={k}, V={V}, bf16 logits, b_k from the length head (H={w.H})"}
+        line = {
+            "metric": f"fused verify+OPD fwd/bwd GB/s, {name} workload",
+            "value": round(achieved, 2),
+            "unit": "GB/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "f32",
+            "data": "synthetic",
+            "config": {"workload": desc[name] + f", lambda={lam}, tau={tau:g}, {args.grad} gradient",
+                       "B": B, "k": k, "V": V, "rows": R, "verified_rows": Rv, "lambda": lam, "tau": tau,
+                       "bytes_per_call": fused_b, "kernel_ms": round(kern_ms, 4),
+                       "rows_per_s": round(R / (kern_ms * 1e-3), 1),
+                       "bk_hist_1_to_k": np.bincount(bkh, minlength=k + 1)[1:].tolist(),
+                       "accepted_hist_0_to_k": np.bincount(acch, minlength=k + 1).tolist()},
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        }
+        print(json.dumps(line), flush=True)
+
+
+def bench_latency(args):
+    """One step (length head + fused pass with gradient) on one request: the
+    tiny workload (B=1, k=16, V=4096 float32 logits, H=256) or the single one
+    (B=1, k=16, V=151936 bfloat16, H=4096).  Both are latency-bound, so the
+    line reports microseconds per step (HIP events around each step), with the
+    float64 oracle's time for the same step on one core beside it."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    w = synth.make(args.workload, seed=args.seed)
+    B, k, V, H, R = w.B, w.k, w.V, w.H, w.R
+    _, bk_ref, _ = oracle.length_head(w.h, w.w, w.bias, w.gamma, k)
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        reps = 5
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            zpd = oracle.bf16_bits_to_f64(w.zp) if w.dtype == "bf16" else w.zp.astype(np.float64)
+            zqd = oracle.bf16_bits_to_f64(w.zq) if w.dtype == "bf16" else w.zq.astype(np.float64)
+            oracle.length_head(w.h, w.w, w.bias, w.gamma, k)
+            oracle.verify_opd(zpd, zqd, w.draft, k=k, lam=w.lam, tau=w.tau, grad_scale=1.0, bk=bk_ref)
+        cpu_us = (time.perf_counter() - t0) / reps * 1e6
+
+    import torch
+
+    import drafter_distillation_amd as dd
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dd.lib()
+    if w.dtype == "bf16":
+        zp = torch.from_numpy(w.zp.view(np.int16)).view(torch.bfloat16).to(dev)
+        zq = torch.from_numpy(w.zq.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        zp = torch.from_numpy(w.zp).to(dev)
+        zq = torch.from_numpy(w.zq).to(dev)
+    draft = torch.from_numpy(w.draft).to(dev)
+    h = torch.from_numpy(w.h).to(dev)
+    wt = torch.from_numpy(w.w).to(dev)
+    rate = torch.empty(B, dtype=torch.float32, device=dev)
+    bk = torch.empty(B, dtype=torch.int32, device=dev)
     out = None
     stream = torch.cuda.current_stream(dev)
 
-    def step(ev0=None, ev1=None):
+    def step():
         nonlocal out
-        if ev0 is not None:
-            ev0.record(stream)
-        out = dd.av_verify_opd_fwd(zp, zq, draft, k=k, lam=w.lam, tau=w.tau, grad_scale=1.0, out=out,
-                                   grad_dtype=gdt, **kw)
-        if ev1 is not None:
-            ev1.record(stream)
+        dd.av_length_head(h, wt, w.bias, w.gamma, k, rate_out=rate, bk_out=bk)
+        out = dd.av_verify_opd_fwd(zp, zq, draft, k=k, bk=bk, lam=w.lam, tau=w.tau, grad_scale=1.0, out=out)
 
     for _ in range(args.warmup):
         step()
@@ -627,36 +780,42 @@ def bench_fused_other(args):
            for _ in range(args.steps)]
     t0 = time.perf_counter()
     for e0, e1 in evs:
-        step(e0, e1)
+        e0.record(stream)
+        step()
+        e1.record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    gelem = 2 if args.grad == "bf16" else 4
-    fused_b, _ = algorithmic_bytes(B, k, V, 0, R, Rv, gelem=gelem)
-    kern_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs)
-    achieved = fused_b / (kern_ms * 1e-3) / 1e9
-    desc = {"ragged": f"ragged: B={B} requests, k={k}, V={V}, bf16 logits, only the {R} verified rows stored "
-                      "(b_k drawn with p proportional to 1/b)",
-            "long": f"long: B={B} requests, k={k}, V={V}, bf16 logits, b_k from the length head (H={w.H})"}
+    us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+    us_med = us[len(us) // 2]
+    Rv = int(np.clip(bk.cpu().numpy(), 1, k).sum())
+    elem = 2 if w.dtype == "bf16" else 4
+    fused_b, head_b = algorithmic_bytes(B, k, V, H, R, Rv, elem=elem)
     line = {
-        "metric": f"fused verify+OPD fwd/bwd GB/s, {args.workload} workload",
-        "value": round(achieved, 2),
-        "unit": "GB/s",
+        "metric": f"fused verify+OPD step latency (length head + fused pass) us at B=1,k={k},V={V} {w.dtype}",
+        "value": round(us_med, 2),
+        "unit": "us",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(elapsed / args.steps * 1e3, 4),
-        "higher_is_better": True,
+        "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": desc[args.workload] + f", lambda={w.lam}, tau={w.tau}, {args.grad} gradient",
-                   "B": B, "k": k, "V": V, "rows": R, "verified_rows": Rv, "bytes_per_call": fused_b,
-                   "kernel_ms": round(kern_ms, 4)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "config": {"workload": f"{args.workload}: B=1 request, k={k}, V={V}, {w.dtype} logits, b_k from the "
+                               f"length head (H={H}), lambda={w.lam}, tau={w.tau}",
+                   "B": B, "k": k, "V": V, "H": H, "verified_rows": Rv, "bytes_per_step": fused_b + head_b,
+                   "us_min": round(us[0], 2), "us_p90": round(us[int(0.9 * (len(us) - 1))], 2),
+                   "timing": "HIP events around each step (two launches), median"},
+        "roofline": {"bound": "hbm", "achieved": round((fused_b + head_b) / (us_med * 1e-6) / 1e9, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round((fused_b + head_b) / (us_med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "note": "latency-bound: a handful of rows for 256 CUs"},
+        "cpu_baseline": {"value": round(cpu_us, 1), "unit": "us", "cores": 1, "kind": "oracle",
+                         "sample": f"the same step, float64 numpy, one thread, mean of {reps}"},
     }
-    print(json.dumps(line))
+    print(json.dumps(line), flush=True)
 
 
 def bench_hbm_probe(args):
@@ -706,13 +865,13 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-requests", type=int, default=128)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--grad", choices=["f32", "bf16"], default="f32",
                     help="gradient output type of the fused pass (default float32)")
     ap.add_argument("--temperature", type=float, default=1.0,
                     help="reverse-KL temperature of the fused pass (default 1: the plain pass)")
-    ap.add_argument("--workload", choices=["concurrent", "ragged", "long", "head_update", "spec", "lm_head", "hbm_probe", "bwd"],
+    ap.add_argument("--workload", choices=["concurrent", "tiny", "single", "ragged", "long", "long_sweep",
+                                            "head_update", "spec", "lm_head", "hbm_probe", "bwd"],
                     default="concurrent",
                     help="concurrent: the fused verify+OPD step (default); head_update: the "
                          "length head's online update; spec: sampling-based verification")
@@ -752,15 +911,25 @@ def main():
     if args.workload == "bwd":
         bench_bwd(args)
         return
-    if args.workload in ("ragged", "long"):
+    if args.workload in ("ragged", "long", "long_sweep"):
         bench_fused_other(args)
+        return
+    if args.workload in ("tiny", "single"):
+        bench_latency(args)
         return
 
     import numpy as np
+
+    import synth
+
+    w = synth.make("concurrent", seed=args.seed)
+    # the oracle baseline runs first, in worker processes forked before this
+    # process touches the GPU
+    cpu_line = None if args.no_cpu_baseline else cpu_baseline(w, temperature=args.temperature)
+
     import torch
 
     import drafter_distillation_amd as dd
-    import synth
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -769,7 +938,6 @@ def main():
     if args.copy_calibration_mib > 0:
         copy_calibration(torch, dev, args.copy_calibration_mib)
 
-    w = synth.make("concurrent", seed=args.seed)
     zp = torch.from_numpy(w.zp.view(np.int16)).view(torch.bfloat16).to(dev)
     zq = torch.from_numpy(w.zq.view(np.int16)).view(torch.bfloat16).to(dev)
     draft = torch.from_numpy(w.draft).to(dev)
@@ -825,6 +993,8 @@ def main():
     gelem = 2 if args.grad == "bf16" else 4
     fused_b, head_b = algorithmic_bytes(B, k, V, H, R, Rv, gelem=gelem, lse1=tempered)
     ms_step = elapsed / args.steps * 1e3
+    bkh = np.clip(bk.cpu().numpy(), 1, k)
+    acch = out["acc_len"].cpu().numpy()
     value = (fused_b + head_b) * args.steps / elapsed / 1e9
     kern_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
     kern_avg_ms = sum(kern_ms) / len(kern_ms)
@@ -859,6 +1029,8 @@ def main():
             "value_without_zero_fill_GBs": round((fused_b + head_b - unverified_grad) * args.steps
                                                  / elapsed / 1e9, 2),
             "kernel_ms": round(kern_avg_ms, 4),
+            "bk_hist_1_to_k": np.bincount(bkh, minlength=k + 1)[1:].tolist(),
+            "accepted_hist_0_to_k": np.bincount(acch, minlength=k + 1).tolist(),
         },
         "roofline": {
             "bound": "hbm",
@@ -869,8 +1041,8 @@ def main():
             "traffic": measured_traffic() if args.grad == "f32" and not tempered else None,
         },
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(args.cpu_requests, args.temperature)
+    if cpu_line is not None:
+        line["cpu_baseline"] = cpu_line
     print(json.dumps(line), flush=True)
 
 
