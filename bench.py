@@ -355,11 +355,16 @@ def bench_head_update(args):
     print(json.dumps(line), flush=True)
 
 
-def spec_bytes(V, Rv, n_rej, elem=2):
+def spec_bytes(V, Rv, n_rej, elem=2, stats_given=False):
     """Bytes sampling verification must move at least once: zp and zq of every
     verified row (its statistics), zp and zq of each request's rejected row
     again for the residual draw (the statistics are needed first), the
-    uniforms, drafts and per-row records, and the per-request outputs."""
+    uniforms, drafts and per-row records, and the per-request outputs.  With
+    the row statistics given (the fused pass's first sweep computed them):
+    the two gathered logits, the two statistics, the draft and the uniform of
+    each verified row, and zp and zq of each rejected row once."""
+    if stats_given:
+        return (2 * elem + 8 + 8) * Rv + 2 * elem * V * n_rej + 8 * n_rej
     return 2 * elem * V * Rv + 2 * elem * V * n_rej + 12 * Rv + 8 * n_rej
 
 
@@ -385,12 +390,17 @@ def bench_spec(args):
     seed = 0x5EED0000 + args.seed
     out = None
     stream = torch.cuda.current_stream(dev)
+    stats_in = None
+    if args.spec_stats == "fused":  # the row statistics of a fused pass on the same inputs
+        stats_in = dd.av_verify_opd_fwd(zp, zq, draft, k=k, bk=bk, lam=w.lam, tau=w.tau,
+                                        want_grad=False)["row_stats"]
+        torch.cuda.synchronize()
 
     def step(ev0=None, ev1=None):
         nonlocal out
         if ev0 is not None:
             ev0.record(stream)
-        out = dd.av_spec_verify(zp, zq, draft, u, k=k, seed=seed, bk=bk, out=out)
+        out = dd.av_spec_verify(zp, zq, draft, u, k=k, seed=seed, bk=bk, out=out, stats_in=stats_in)
         if ev1 is not None:
             ev1.record(stream)
 
@@ -408,10 +418,11 @@ def bench_spec(args):
     bkh = torch.clamp(bk, 1, k).cpu().numpy()
     acc = out["acc_len"].cpu().numpy()
     Rv, n_rej = int(bkh.sum()), int((acc < bkh).sum())
-    nbytes = spec_bytes(V, Rv, n_rej)
+    nbytes = spec_bytes(V, Rv, n_rej, stats_given=stats_in is not None)
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
     line = {
-        "metric": "sampling-based block verification GB/s at B=128,k=16,V=151936 bf16",
+        "metric": "sampling-based block verification GB/s at B=128,k=16,V=151936 bf16"
+                  + (", row statistics from the fused pass" if stats_in is not None else ""),
         "value": round(achieved, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -428,7 +439,8 @@ def bench_spec(args):
                         "drafts of the drafter logits, b_k from the length head), uniforms seeded",
             "B": B, "k": k, "V": V, "verified_rows": Rv, "rejecting_requests": n_rej,
             "accepted_positions": int(acc.sum()), "bytes_per_step": nbytes,
-            "kernel_ms": round(kern_ms, 4), "launches_per_step": 2,
+            "kernel_ms": round(kern_ms, 4), "launches_per_step": 3,
+            "row_statistics": "given (fused pass)" if stats_in is not None else "computed",
         },
         "roofline": {
             "bound": "hbm",
@@ -868,6 +880,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--grad", choices=["f32", "bf16"], default="f32",
                     help="gradient output type of the fused pass (default float32)")
+    ap.add_argument("--spec-stats", choices=["own", "fused"], default="own",
+                    help="spec workload: compute the row statistics (own) or take the fused pass's")
     ap.add_argument("--temperature", type=float, default=1.0,
                     help="reverse-KL temperature of the fused pass (default 1: the plain pass)")
     ap.add_argument("--workload", choices=["concurrent", "tiny", "single", "ragged", "long", "long_sweep",

@@ -56,8 +56,8 @@ _SIGS = {
     "av_verify_opd_bwd": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f, _f, _f, _f,
                                _vp, _i, _i, _vp]),
     "av_spec_workspace_bytes": (_sz, [_i, _i]),
-    "av_spec_verify": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_uint64, _vp, _vp,
-                            _vp, _vp, _vp, _sz, _vp]),
+    "av_spec_verify": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_uint64, _vp, _i,
+                            _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "av_lm_head_workspace_bytes": (_sz, []),
     "av_lm_head_bwd": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "av_lm_head_last_error": (ctypes.c_char_p, []),
@@ -206,11 +206,14 @@ def av_spec_workspace_bytes(B: int, R: int) -> int:
 
 def av_spec_verify(zp: torch.Tensor, zq: torch.Tensor, draft: torch.Tensor, u: torch.Tensor, *, k: int,
                    seed: int, bk: Optional[torch.Tensor] = None, row_off: Optional[torch.Tensor] = None,
-                   want_stats: bool = False, out: Optional[dict] = None) -> dict:
+                   want_stats: bool = False, stats_in: Optional[torch.Tensor] = None,
+                   out: Optional[dict] = None) -> dict:
     """Sampling-based block verification (see include/av.h).  zp, zq [R, V]
     bf16/f32; draft [R] int32; u [R] float32 uniforms; dense layout with bk
-    [B] or ragged with row_off [B+1].  Returns dict(acc_len [B], token [B],
-    row_stats [R, 2] or None, status [1])."""
+    [B] or ragged with row_off [B+1].  stats_in: [R, 2] or [R, 4] float32
+    with lse_p, lse_q in its first two columns (e.g. av_verify_opd_fwd's
+    row_stats), or None.  Returns dict(acc_len [B], token [B], row_stats
+    [R, 2] or None, status [1])."""
     _need_gpu("zp", zp)
     _need_gpu("zq", zq, zp.dtype)
     _need_gpu("draft", draft, torch.int32)
@@ -236,6 +239,12 @@ def av_spec_verify(zp: torch.Tensor, zq: torch.Tensor, draft: torch.Tensor, u: t
             o[name] = t
         return t
 
+    stride = 0
+    if stats_in is not None:
+        _need_gpu("stats_in", stats_in, torch.float32)
+        if stats_in.dim() != 2 or stats_in.shape[0] != R or stats_in.shape[1] < 2:
+            raise ValueError("stats_in must be [R, >= 2]")
+        stride = stats_in.shape[1]
     acc = get("acc_len", (B,), torch.int32)
     token = get("token", (B,), torch.int32)
     stats = get("row_stats", (R, 2), torch.float32) if want_stats else None
@@ -244,7 +253,8 @@ def av_spec_verify(zp: torch.Tensor, zq: torch.Tensor, draft: torch.Tensor, u: t
         ws = workspace(dev, av_spec_workspace_bytes(B, R), kind="spec")
         rc = lib().av_spec_verify(
             _dtype_code(zp), B, int(k), V, R, _ptr(row_off), _ptr(zp), _ptr(zq), _ptr(draft), _ptr(bk),
-            _ptr(u), ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF), _ptr(acc), _ptr(token), _ptr(stats),
+            _ptr(u), ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF), _ptr(stats_in), stride, _ptr(acc),
+            _ptr(token), _ptr(stats),
             _ptr(status), _ptr(ws), ws.numel(), _stream(dev))
     _check("av_spec_verify", rc)
     return o

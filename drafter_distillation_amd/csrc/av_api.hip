@@ -257,10 +257,12 @@ size_t av_spec_workspace_bytes(int B, int R) {
 
 int av_spec_verify(int dtype, int B, int k, int V, int R, const int32_t* row_off, const void* zp,
                    const void* zq, const int32_t* draft, const int32_t* bk, const float* u,
-                   uint64_t seed, int32_t* acc_len, int32_t* token, float* row_stats, int32_t* status,
-                   void* workspace, size_t workspace_bytes, void* stream) {
+                   uint64_t seed, const float* row_stats_in, int stats_stride, int32_t* acc_len,
+                   int32_t* token, float* row_stats, int32_t* status, void* workspace,
+                   size_t workspace_bytes, void* stream) {
   if (!zp || !zq || !draft || !u || !acc_len || !token || !workspace) return AV_EINVAL;
   if (!row_off && !bk) return AV_EINVAL;
+  if (row_stats_in && stats_stride < 2) return AV_EINVAL;
   Plan p;
   int rc = plan_rows(dtype, B, k, V, R, row_off, zp, zq, nullptr, &p);
   if (rc != AV_OK) return rc;
@@ -280,6 +282,8 @@ int av_spec_verify(int dtype, int B, int k, int V, int R, const int32_t* row_off
   a.acc = acc_len;
   a.token = token;
   a.stats = row_stats;
+  a.stats_in = row_stats_in;
+  a.stats_stride = stats_stride;
   a.status = status;
   a.ws = (uint32_t*)workspace;
   a.chunks = (uint32_t*)((char*)workspace + (size_t)R * 16);

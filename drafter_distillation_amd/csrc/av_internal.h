@@ -157,6 +157,8 @@ struct SpecArgs {
   int32_t* acc;
   int32_t* token;
   float* stats;     // [R, 2] lse_p, lse_q of verified rows, or NULL
+  const float* stats_in;  // [R, stats_stride] lse_p, lse_q given by the caller, or NULL
+  int stats_stride;
   int32_t* status;  // [1] or NULL
   uint32_t* ws;     // [R][4]: accepted flag, lse_p bits, lse_q bits
   uint32_t* chunks; // [B][nchunk][4]: best residual key and index, best p key and index

@@ -2147,11 +2147,25 @@ __global__ __launch_bounds__(kStepWaves * 64) void head_step_kernel(HeadUpdArgs 
     if (in) {
       const float* hj = a.h + (long long)b0 * a.H + j;
       float* gh = a.grad_h ? a.grad_h + (long long)b0 * a.H + j : nullptr;
-#pragma unroll 4
-      for (int i = wid; i < nb; i += kStepWaves) {
-        const double d = sdz[i];
-        g = fma(d, (double)hj[(long long)i * a.H], g);
-        if (gh) gh[(long long)i * a.H] = (float)(d * wj);
+      // groups of 16 of the wave's requests: every load of a group goes out
+      // before its first product (same order of the sum as one at a time)
+      constexpr int kG = 16;
+      for (int i0 = wid; i0 < nb; i0 += kG * kStepWaves) {
+        float x[kG];
+#pragma unroll
+        for (int u = 0; u < kG; ++u) {
+          const int i = i0 + u * kStepWaves;
+          x[u] = i < nb ? hj[(long long)i * a.H] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kG; ++u) {
+          const int i = i0 + u * kStepWaves;
+          if (i < nb) {
+            const double d = sdz[i];
+            g = fma(d, (double)x[u], g);
+            if (gh) gh[(long long)i * a.H] = (float)(d * wj);
+          }
+        }
       }
     }
   }
@@ -2368,6 +2382,37 @@ __global__ __launch_bounds__(kBlock) void spec_stats_kernel(SpecArgs a) {
       a.stats[2 * (long long)r] = lse_p;
       a.stats[2 * (long long)r + 1] = lse_q;
     }
+  }
+}
+
+// Step 1 with the row statistics given (the fused pass computed lse_p and
+// lse_q of every verified row in its first sweep): one thread per stored row
+// gathers p(d) and q(d) and takes the acceptance test; no row is read whole.
+template <int VAR>
+__global__ __launch_bounds__(kBlock) void spec_gather_kernel(SpecArgs a) {
+  using T = Tr<VAR>;
+  const long long r = (long long)blockIdx.x * kBlock + threadIdx.x;
+  if (r == 0 && a.status) a.status[0] = 0;
+  if (r >= a.R) return;
+  if (!a.ragged) {
+    const int b = (int)(r / a.k), i = (int)(r - (long long)b * a.k);
+    if (i >= min(max(a.bk[b], 1), a.k)) return;  // not verified
+  }
+  const float lse_p = a.stats_in[r * a.stats_stride], lse_q = a.stats_in[r * a.stats_stride + 1];
+  const long long rowv = r * a.nvec;
+  const int d = a.draft[r];
+  uint32_t acc = 0u;
+  if ((unsigned)d < (unsigned)a.V) {
+    const float pd = __builtin_amdgcn_exp2f((T::elem(T::row(a.zp, rowv), d) - lse_p) * kLog2e);
+    const float qd = __builtin_amdgcn_exp2f((T::elem(T::row(a.zq, rowv), d) - lse_q) * kLog2e);
+    acc = (a.u[r] * qd < pd) ? 1u : 0u;
+  }
+  const u32x4 rec = {acc, __float_as_uint(lse_p), __float_as_uint(lse_q), 0u};
+  *(u32x4*)(a.ws + 4 * r) = rec;
+  settle16(rec);
+  if (a.stats) {
+    a.stats[2 * r] = lse_p;
+    a.stats[2 * r + 1] = lse_q;
   }
 }
 
@@ -2617,7 +2662,10 @@ hipError_t launch_head(const HeadArgs& a, hipStream_t s) {
 
 template <int VAR>
 hipError_t launch_spec_t(const SpecArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(spec_stats_kernel<VAR>, dim3(a.R), dim3(kBlock), 0, s, a);
+  if (a.stats_in)
+    hipLaunchKernelGGL(spec_gather_kernel<VAR>, dim3((unsigned)((a.R + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL(spec_stats_kernel<VAR>, dim3(a.R), dim3(kBlock), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(spec_race_kernel<VAR>, dim3(a.nchunk, a.B), dim3(kBlock), 0, s, a);

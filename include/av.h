@@ -153,6 +153,14 @@ int av_length_head_update(const float* h, const int32_t* acc, const int32_t* bk,
  *   u            [R] float32 uniforms in [0, 1) for the acceptance tests
  *                (the caller's generator)
  *   seed         64-bit key of the replacement draw
+ *   row_stats_in [R, stats_stride] float32 or NULL: lse_p (column 0) and
+ *                lse_q (column 1) of every verified row, e.g. the row_stats
+ *                of av_verify_opd_fwd on the same inputs (stride 4), whose
+ *                first sweep already computed them; then no row is read
+ *                whole for the acceptance tests (p(d) and q(d) are gathered)
+ *                and only each request's first rejected row is read, for the
+ *                replacement draw.  NULL: the call computes them.
+ *   stats_stride >= 2 when row_stats_in is given
  *   acc_len, token  [B] int32 out
  *   row_stats    [R, 2] float32 out or NULL: (lse_p, lse_q) of verified rows
  *   status       [1] int32 out or NULL: 0, or AV_DEV_BAD_OFFSETS for a
@@ -162,14 +170,15 @@ int av_length_head_update(const float* h, const int32_t* acc, const int32_t* bk,
  *                initialisation needed
  * All pointers are device pointers; asynchronous on `stream` (three launches).
  * Errors: as av_verify_opd_fwd for the shared arguments; AV_EINVAL for NULL
- * u/acc_len/token/workspace or a workspace that is too small or misaligned.
+ * u/acc_len/token/workspace, a workspace that is too small or misaligned, or
+ * stats_stride < 2 with row_stats_in given.
  */
 size_t av_spec_workspace_bytes(int B, int R);
 int av_spec_verify(int dtype, int B, int k, int V, int R, const int32_t* row_off,
                    const void* zp, const void* zq, const int32_t* draft, const int32_t* bk,
-                   const float* u, uint64_t seed, int32_t* acc_len, int32_t* token,
-                   float* row_stats, int32_t* status, void* workspace, size_t workspace_bytes,
-                   void* stream);
+                   const float* u, uint64_t seed, const float* row_stats_in, int stats_stride,
+                   int32_t* acc_len, int32_t* token, float* row_stats, int32_t* status,
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * av_workspace_bytes -- size of the scratch area av_verify_opd_fwd needs for

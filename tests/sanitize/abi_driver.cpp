@@ -98,10 +98,14 @@ int main() {
   EXPECT(av_length_head_update(F, I, I, INT_MAX, 16, 16, F, F, F, F, F, F, 1, 2e-4, 0.9, 0.999, 1e-8, 0.01,
                                nullptr, nullptr, nullptr, P, 8, nullptr),
          AV_EINVAL);
-  EXPECT(av_spec_verify(1, INT_MAX, 4, 64, 8, nullptr, P, P, I, I, F, 1, I, I, nullptr, nullptr, P, 1 << 20,
+  EXPECT(av_spec_verify(1, INT_MAX, 4, 64, 8, nullptr, P, P, I, I, F, 1, nullptr, 0, I, I, nullptr, nullptr, P,
+                        1 << 20, nullptr),
+         AV_EINVAL);
+  EXPECT(av_spec_verify(1, 2, 4, 64, 8, nullptr, P, P, I, I, F, 1, nullptr, 0, I, I, nullptr, nullptr, P, 7,
                         nullptr),
          AV_EINVAL);
-  EXPECT(av_spec_verify(1, 2, 4, 64, 8, nullptr, P, P, I, I, F, 1, I, I, nullptr, nullptr, P, 7, nullptr),
+  EXPECT(av_spec_verify(1, 2, 4, 64, 8, nullptr, P, P, I, I, F, 1, F, 1, I, I, nullptr, nullptr, P, 1 << 20,
+                        nullptr),
          AV_EINVAL);
   EXPECT(av_workspace_init(nullptr, 1 << 20, nullptr), AV_EINVAL);
   EXPECT(av_workspace_init(reinterpret_cast<char*>(P) + 8, 1 << 20, nullptr), AV_EINVAL);

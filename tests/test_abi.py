@@ -216,14 +216,16 @@ def test_head_update_rejects_bad_arguments_on_host(kw, code):
     (dict(ws_bytes=16 * 8 + 2 * 64 * 16 - 1), dd.AV_EINVAL),
     (dict(ws=ctypes.c_void_p(0x10008)), dd.AV_EINVAL),
     (dict(dtype=5), dd.AV_EUNSUPPORTED),
+    (dict(sin=P, sstride=1), dd.AV_EINVAL),              # statistics given with a short stride
 ])
 def test_spec_rejects_bad_arguments_on_host(kw, code):
     a = dict(dtype=1, B=2, k=4, V=64, R=8, row_off=NULL, zp=P, zq=P, draft=P, bk=P, u=P, seed=1,
-             acc=P, token=P, stats=NULL, status=NULL, ws=P, ws_bytes=1 << 20, stream=NULL)
+             sin=NULL, sstride=0, acc=P, token=P, stats=NULL, status=NULL, ws=P, ws_bytes=1 << 20, stream=NULL)
     a.update(kw)
     rc = _lib.lib().av_spec_verify(a["dtype"], a["B"], a["k"], a["V"], a["R"], a["row_off"], a["zp"],
-                                   a["zq"], a["draft"], a["bk"], a["u"], a["seed"], a["acc"], a["token"],
-                                   a["stats"], a["status"], a["ws"], a["ws_bytes"], a["stream"])
+                                   a["zq"], a["draft"], a["bk"], a["u"], a["seed"], a["sin"], a["sstride"],
+                                   a["acc"], a["token"], a["stats"], a["status"], a["ws"], a["ws_bytes"],
+                                   a["stream"])
     assert rc == code
 
 

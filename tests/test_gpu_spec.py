@@ -46,13 +46,20 @@ def spans(w, bk):
     return [(b * w.k, min(max(int(bk[b]), 1), w.k)) for b in range(w.B)]
 
 
-def run_gpu(av, w, bk, u, seed, inp=None):
+def run_gpu(av, w, bk, u, seed, inp=None, fused_stats=False):
+    """fused_stats: take lse_p, lse_q from a fused verify+OPD pass on the same
+    inputs (its row_stats, stride 4) instead of the call's own first sweep."""
     inp = inp or gpu_inputs(w)
     kw = dict(k=w.k, seed=seed, want_stats=True)
     if w.row_off is not None:
         kw["row_off"] = inp["row_off"]
     else:
         kw["bk"] = torch.from_numpy(np.asarray(bk, dtype=np.int32)).cuda()
+    if fused_stats:
+        lay = {key: kw[key] for key in ("row_off", "bk") if key in kw}
+        f = av.av_verify_opd_fwd(inp["zp"], inp["zq"], inp["draft"], k=w.k, lam=0.5, tau=0.1, want_grad=False,
+                                 **lay)
+        kw["stats_in"] = f["row_stats"]
     out = av.av_spec_verify(inp["zp"], inp["zq"], inp["draft"], torch.from_numpy(u).cuda(), **kw)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in out.items()}
@@ -121,16 +128,38 @@ def sampled_drafts(w, rng):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("V", [1, 7, 8, 37, 1000, 4100, 65544])
-def test_small_shapes(av, dtype, V):
+@pytest.mark.parametrize("fused_stats", [False, True])
+def test_small_shapes(av, dtype, V, fused_stats):
     w = synth.make("concurrent", B=5, V=V, dtype=dtype)
     rng = np.random.default_rng(V)
     w.draft = sampled_drafts(w, rng)
     bk = np.array([1, 16, 7, 0, 40])
     u = rng.random(w.R).astype(np.float32)
-    say(f"spec small {dtype} V={V}")
+    say(f"spec small {dtype} V={V} fused_stats={fused_stats}")
     for seed in (0, 0xFEDCBA9876543210):
-        out = run_gpu(av, w, bk, u, seed)
+        out = run_gpu(av, w, bk, u, seed, fused_stats=fused_stats)
         check_all(w, bk, out, u, seed)
+
+
+def test_statistics_input_matches_own_sweep(av):
+    """With the fused pass's row statistics given, the call gathers p(d) and
+    q(d) instead of sweeping the rows; where both forms get the same lse
+    values (the call's own, fed back with stride 2), every output is the
+    same bit for bit."""
+    w = synth.make("concurrent", B=8, V=20000)
+    rng = np.random.default_rng(12)
+    w.draft = sampled_drafts(w, rng)
+    bk = np.array([16, 1, 5, 9, 16, 2, 7, 12])
+    u = rng.random(w.R).astype(np.float32)
+    inp = gpu_inputs(w)
+    bkt = torch.from_numpy(bk.astype(np.int32)).cuda()
+    own = av.av_spec_verify(inp["zp"], inp["zq"], inp["draft"], torch.from_numpy(u).cuda(), k=w.k, seed=4,
+                            bk=bkt, want_stats=True)
+    fed = av.av_spec_verify(inp["zp"], inp["zq"], inp["draft"], torch.from_numpy(u).cuda(), k=w.k, seed=4,
+                            bk=bkt, want_stats=True, stats_in=own["row_stats"].clone())
+    torch.cuda.synchronize()
+    for key in ("acc_len", "token", "status"):
+        assert torch.equal(own[key], fed[key]), key
 
 
 def test_ragged_and_edge_decisions(av):
@@ -143,8 +172,9 @@ def test_ragged_and_edge_decisions(av):
     w.draft[3] = -1         # out of range: rejected
     w.draft[8] = w.V
     say("spec ragged")
-    out = run_gpu(av, w, None, u, 11)
-    check_all(w, None, out, u, 11)
+    for fused_stats in (False, True):
+        out = run_gpu(av, w, None, u, 11, fused_stats=fused_stats)
+        check_all(w, None, out, u, 11)
 
 
 def test_equal_distributions_accept_everything(av):
@@ -238,5 +268,7 @@ def test_full_concurrent(av):
     _, bk, _ = oracle.length_head(w.h, w.w, w.bias, w.gamma, w.k)
     rng = np.random.default_rng(10)
     u = rng.random(w.R).astype(np.float32)
-    out = run_gpu(av, w, bk, u, 0x5EED)
-    check_all(w, bk, out, u, 0x5EED)
+    inp = gpu_inputs(w)
+    for fused_stats in (False, True):
+        out = run_gpu(av, w, bk, u, 0x5EED, inp=inp, fused_stats=fused_stats)
+        check_all(w, bk, out, u, 0x5EED)
