@@ -499,21 +499,38 @@ def bench_lm_head(args):
     wl = (torch.randn((V, H), generator=g, device=dev) * 0.02).to(torch.bfloat16)
     hid = torch.randn((R, H), generator=g, device=dev).to(torch.bfloat16)
     stream = torch.cuda.current_stream(dev)
-    for _ in range(args.warmup):
-        dd.av_lm_head_bwd(dz, wl, hid)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for e0, e1 in evs:
-        e0.record(stream)
-        dd.av_lm_head_bwd(dz, wl, hid)
-        e1.record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    kern_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs)
-    flops = 2 * 2.0 * R * V * H
+
+    def timed(fn, steps):
+        """Average of per-call HIP event pairs on the launching stream (ms),
+        and the wall time of the loop (s)."""
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        t0 = time.perf_counter()
+        for e0, e1 in evs:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return sum(e0.elapsed_time(e1) for e0, e1 in evs) / steps, time.perf_counter() - t0
+
+    kern_ms, elapsed = timed(lambda: dd.av_lm_head_bwd(dz, wl, hid), args.steps)
+    hid_ms, _ = timed(lambda: dd.av_lm_head_bwd(dz, wl, None, want_d_w=False), args.steps)
+    w_ms, _ = timed(lambda: dd.av_lm_head_bwd(dz, None, hid, want_d_hid=False), args.steps)
+    # the same two products through torch.mm (bfloat16 outputs, rocBLAS /
+    # hipBLASLt), for context; the transposed dz is made before timing
+    dzt = dz.t().contiguous()
+    torch_hid_ms, _ = timed(lambda: torch.mm(dz, wl), args.steps)
+    torch_w_ms, _ = timed(lambda: torch.mm(dzt, hid), args.steps)
+    del dzt
+    flops1 = 2.0 * R * V * H
+    flops = 2 * flops1
     tflops = flops / (kern_ms * 1e-3) / 1e12
+
+    def tf(ms):
+        return round(flops1 / (ms * 1e-3) / 1e12, 1)
+
     line = {
         "metric": "drafter LM-head backward (d hid = dz W, d W = dz^T hid) TFLOP/s at R=2048, V=151936, "
                   "H=4096 bf16",
@@ -532,7 +549,11 @@ def bench_lm_head(args):
             "workload": "lm_head: dz = the concurrent workload's bf16 gradient (R=2048, V=151936), "
                         "W [V, 4096] and hid [2048, 4096] random bf16, float32 accumulation and outputs",
             "R": R, "V": V, "H": H, "flop_per_step": flops, "kernel_ms": round(kern_ms, 4),
-            "gemms": "hipBLASLt",
+            "gemms": "gemm_kernel (own v_mfma_f32_32x32x16_bf16 tiles)",
+            "d_hid_ms": round(hid_ms, 4), "d_hid_tflops": tf(hid_ms),
+            "d_w_ms": round(w_ms, 4), "d_w_tflops": tf(w_ms),
+            "torch_mm_bf16_out": {"d_hid_ms": round(torch_hid_ms, 4), "d_hid_tflops": tf(torch_hid_ms),
+                                  "d_w_ms": round(torch_w_ms, 4), "d_w_tflops": tf(torch_w_ms)},
         },
         "roofline": {
             "bound": "mfma",

@@ -58,7 +58,7 @@ _SIGS = {
     "av_spec_workspace_bytes": (_sz, [_i, _i]),
     "av_spec_verify": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_uint64, _vp, _i,
                             _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
-    "av_lm_head_workspace_bytes": (_sz, []),
+    "av_lm_head_workspace_bytes": (_sz, [_i, _i, _i]),
     "av_lm_head_bwd": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "av_lm_head_last_error": (ctypes.c_char_p, []),
     "av_status_str": (ctypes.c_char_p, [_i]),
@@ -282,7 +282,7 @@ def av_lm_head_bwd(dz: torch.Tensor, w: Optional[torch.Tensor], hid: Optional[to
     d_hid = torch.empty((R, H), dtype=torch.float32, device=dev) if want_d_hid else None
     d_w = torch.empty((V, H), dtype=torch.float32, device=dev) if want_d_w else None
     with torch.cuda.device(dev):
-        nbytes = int(lib().av_lm_head_workspace_bytes())
+        nbytes = int(lib().av_lm_head_workspace_bytes(R, V, H))
         ws = workspace(dev, nbytes, kind="lm_head")
         rc = lib().av_lm_head_bwd(R, V, H, _ptr(dz), _ptr(w) if want_d_hid else None,
                                   _ptr(hid) if want_d_w else None, _ptr(d_hid), _ptr(d_w), _ptr(ws),

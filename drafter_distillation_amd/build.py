@@ -30,9 +30,8 @@ SOURCES = ["av_kernels.hip", "av_api.hip", "av_lmhead.hip"]
 PROBE_SRC = os.path.join(PKG, "probe", "hbm_probe.hip")
 PROBE_BIN = os.path.join(PKG, "probe", "hbm_probe")
 
-# Libraries the shared library links: hipBLASLt runs the LM-head backward's
-# plain GEMMs (csrc/av_lmhead.hip).
-LINK_FLAGS = ["-lhipblaslt"]
+# Libraries the shared library links beyond the HIP runtime (none).
+LINK_FLAGS: list = []
 
 # Per-source flags.  The kernels take no NaN input (the header puts
 # non-finite logits outside the contract), so float max needs no NaN-quieting

@@ -1,127 +1,472 @@
 // Backward of the drafter's LM head (the step after the verify + OPD pass):
 //   d_hid[r, h] = sum_v dz[r, v] W[v, h]        d_W[v, h] = sum_r dz[r, v] hid[r, h]
-// Two plain bfloat16 GEMMs with float32 accumulation and output, run by
-// hipBLASLt on the matrix cores.  Row-major operands are passed as their
-// column-major transposes: d_hid^T = W^T dz^T and d_W^T = hid^T dz.
-// Semantics are documented in include/av.h.
+// Two bfloat16 GEMMs with float32 accumulation and output on the matrix
+// cores of gfx950 (v_mfma_f32_32x32x16_bf16).  Semantics are documented in
+// include/av.h.
+//
+// gemm_kernel: C[M, N] = A[M, K] B[K, N], C row-major float32.
+//   A is K-contiguous (element (m, k) at A[m lda + k]) or M-contiguous (at
+//   A[k lda + m]); B is K-contiguous (B[n ldb + k]) or N-contiguous
+//   (B[k ldb + n]).  d_hid: A = dz (K-contiguous), B = W (N-contiguous);
+//   d_W: A = dz read as dz^T (M-contiguous), B = hid (N-contiguous).
+//   A workgroup of 256 threads (4 waves, 2 x 2) owns a 256 x 256 tile of C;
+//   each wave a 128 x 128 quarter: 4 x 4 blocks of 32 x 32, 256 float32
+//   accumulators per lane.  K advances 64 at a time through two LDS buffers
+//   that hold both operands as [row][k] (k contiguous, rows padded to 72
+//   values so that the lanes of a 16-byte fragment read fall on distinct
+//   banks): while one buffer feeds the matrix cores, the next K-step's
+//   operands are in flight from global memory into registers and then
+//   written to the other buffer.  An operand that is not K-contiguous is
+//   loaded as 8 x 8 blocks (eight 16-byte rows along M or N) and transposed
+//   in registers with byte permutes on its way to LDS.
+//   Long K (d_hid: K = V) is split over workgroups; the partial tiles go to
+//   the workspace and reduce_kernel adds them in split order.
+//   Tiles map to workgroup ids so that the workgroups of one XCD (ids equal
+//   mod 8) share operands in that XCD's L2: for d_hid each XCD takes 1/8 of
+//   the N tiles (reading 1/8 of W); for d_W each XCD takes every 8th M tile
+//   and runs its 16 N tiles back to back (one 1 MB slice of dz per M tile).
 
-#include <hipblaslt/hipblaslt.h>
+#include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
-
-#include <map>
-#include <mutex>
-#include <tuple>
 
 #include "av.h"
 
 namespace {
 
-constexpr int kMaxDevices = 64;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kLdk = kBK + 8;  // LDS row length (bfloat16 values)
+constexpr int kThreads = 256;
+constexpr int kMaxSplits = 8;
+constexpr int kMaxDim = 1 << 30;  // largest R (tile offsets stay in int)
+constexpr int kMaxLd = 1 << 22;   // largest V, H (per-thread buffer offsets stay in 31 bits)
+
 thread_local char g_err[256] = "";
 
-struct Blas {
-  hipblasLtHandle_t h = nullptr;
-  hipblasStatus_t st = HIPBLAS_STATUS_SUCCESS;
-};
-Blas g_blas[kMaxDevices];
-std::once_flag g_blas_once[kMaxDevices];
-
-// Chosen algorithm per (device, m, n, k, transB, workspace bytes).
-using AlgoKey = std::tuple<int, int, int, int, int, size_t>;
-std::mutex g_algo_mu;
-std::map<AlgoKey, hipblasLtMatmulAlgo_t> g_algo;
-
-int blas_fail(const char* what, int code) {
-  snprintf(g_err, sizeof(g_err), "hipBLASLt %s: status %d", what, code);
+int hip_fail(hipError_t e) {
+  snprintf(g_err, sizeof(g_err), "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
   return AV_EHIP;
 }
 
-struct Desc {  // matmul and matrix descriptors of one call, destroyed on exit
-  hipblasLtMatmulDesc_t md = nullptr;
-  hipblasLtMatrixLayout_t a = nullptr, b = nullptr, c = nullptr;
-  hipblasLtMatmulPreference_t pref = nullptr;
-  ~Desc() {
-    if (pref) hipblasLtMatmulPreferenceDestroy(pref);
-    if (c) hipblasLtMatrixLayoutDestroy(c);
-    if (b) hipblasLtMatrixLayoutDestroy(b);
-    if (a) hipblasLtMatrixLayoutDestroy(a);
-    if (md) hipblasLtMatmulDescDestroy(md);
+struct GemmArgs {
+  const uint16_t* A;
+  const uint16_t* B;
+  float* C;       // [M, N], or the splits' partial tiles [splits][M][N] when splits > 1
+  long long lda, ldb;
+  long long a_total, b_total;  // elements of A and B
+  int M, N, K;
+  int tiles_m, tiles_n, splits, kchunk;  // kchunk: K values per split (a multiple of kBK)
+  int group;      // N tiles per group of the tile order (see tile_of)
+  int per_xcd;    // tiles per XCD: ceil(tiles_m tiles_n splits / 8)
+  int vec;        // rows 16-byte aligned and M, N, K multiples of 8 (kFast / kEdge loads)
+};
+
+// Workgroup id -> (tile_m, tile_n, split); false for ids past the last tile.
+// Tiles are ordered split-major, then in groups of `group` N tiles, each group
+// covering every M tile with its N tiles adjacent; XCD x (the workgroups with
+// id % 8 == x) takes the x-th contiguous run of per_xcd tiles in that order,
+// so the workgroups running together on one XCD share operand slices in its L2.
+__device__ __forceinline__ bool tile_of(const GemmArgs& g, int id, int& tm, int& tn, int& sp) {
+  const int v = (id & 7) * g.per_xcd + (id >> 3);
+  const int tt = g.tiles_m * g.tiles_n;
+  sp = v / tt;
+  if (sp >= g.splits) return false;
+  const int rem = v - sp * tt;
+  const int grp = rem / (g.tiles_m * g.group);
+  const int w = rem - grp * g.tiles_m * g.group;
+  const int gs = min(g.group, g.tiles_n - grp * g.group);
+  tn = grp * g.group + w % gs;
+  tm = w / gs;
+  return true;
+}
+
+// Load modes: kFast, a tile inside M, N and K on 16-byte aligned rows (no
+// checks); kEdge, aligned rows with M, N and K multiples of 8, so that each
+// 16-byte piece lies wholly inside or wholly outside (outside: zeros);
+// kScalar, element by element, zeros outside.
+enum Mode { kFast = 0, kEdge = 1, kScalar = 2 };
+
+// 16-byte staging of one K-step: eight 16-byte pieces per thread per operand.
+struct Stage {
+  u32x4 v[8];
+};
+
+// Operands are read through buffer resources based at the K-step's corner of
+// the tile: a thread's pieces then differ by wave-uniform offsets, and no
+// 64-bit address is kept per piece.  The resource's extent is what is left
+// of the operand, so no load reaches past its end.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc rsrc_at(const uint16_t* P, long long total, long long off) {
+  const long long bytes = (total - off) * 2;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(P + off), (short)0,
+                                           bytes > 0x7fffffffLL ? 0x7fffffff : (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint32_t ld16(Rsrc r, uint32_t vo, uint32_t so) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, vo, so, 0);
+}
+
+// Where an operand lies: element (row, k) at P[row ld + k] (K-contiguous) or
+// P[k ld + row] (row-contiguous); `total` elements; `rows` rows (M or N).
+struct Opnd {
+  const uint16_t* P;
+  long long ld, total;
+  int rows;
+};
+
+// K-contiguous operand, rows r0 .. r0+255, k0 .. k0+63: piece q of thread t is
+// row t / 8 + 32 q, values 8 (t % 8) .. + 7 (eight threads cover one 128-byte
+// row segment).
+template <int MODE>
+__device__ __forceinline__ void load_k(const Opnd& o, int r0, int k0, int kend, Stage& st) {
+  const int tid = threadIdx.x, rr = tid >> 3, c = (tid & 7) * 8;
+  const Rsrc r = rsrc_at(o.P, o.total, (long long)r0 * o.ld + k0);
+  const uint32_t vo = (uint32_t)((rr * o.ld + c) * 2), step = (uint32_t)(32 * o.ld * 2);
+  const int gk = k0 + c;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int gr = r0 + rr + 32 * q;
+    if (MODE == kFast || (MODE == kEdge && gr < o.rows && gk < kend)) {
+      st.v[q] = __builtin_amdgcn_raw_buffer_load_b128(r, vo, q * step, 0);
+    } else if (MODE == kEdge) {
+      st.v[q] = u32x4{0u, 0u, 0u, 0u};
+    } else {
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
+      if (gr < o.rows)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (gk + e < kend) w[e >> 1] |= ld16(r, vo + 2 * e, q * step) << (16 * (e & 1));
+      st.v[q] = u32x4{w[0], w[1], w[2], w[3]};
+    }
+  }
+}
+__device__ __forceinline__ void store_k(const Stage& st, uint16_t* lds) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) *(u32x4*)(lds + ((tid >> 3) + 32 * q) * kLdk + (tid & 7) * 8) = st.v[q];
+}
+
+// Row-contiguous operand, rows r0 .. r0+255, k0 .. k0+63: thread t loads the
+// 8 x 8 block of rows 8 (t / 8) .. + 7 and k values 8 (t % 8) .. + 7 as eight
+// 16-byte pieces along the rows, one per k.
+template <int MODE>
+__device__ __forceinline__ void load_r(const Opnd& o, int r0, int k0, int kend, Stage& st) {
+  const int tid = threadIdx.x, cb = (tid >> 3) * 8, kk = (tid & 7) * 8;
+  const Rsrc r = rsrc_at(o.P, o.total, (long long)k0 * o.ld + r0);
+  const uint32_t vo = (uint32_t)((kk * o.ld + cb) * 2), step = (uint32_t)(o.ld * 2);
+  const int gr = r0 + cb;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int gk = k0 + kk + i;
+    if (MODE == kFast || (MODE == kEdge && gk < kend && gr < o.rows)) {
+      st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, vo, i * step, 0);
+    } else if (MODE == kEdge) {
+      st.v[i] = u32x4{0u, 0u, 0u, 0u};
+    } else {
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
+      if (gk < kend)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (gr + e < o.rows) w[e >> 1] |= ld16(r, vo + 2 * e, i * step) << (16 * (e & 1));
+      st.v[i] = u32x4{w[0], w[1], w[2], w[3]};
+    }
+  }
+}
+// Transposes the thread's block (piece i = the 8 rows' values at k = i) into
+// 8 rows of 8 k values and writes them to LDS rows 8 (t / 8) + c, columns
+// 8 (t % 8) .. + 7.  Output word i of row c pairs k = 2i and 2i + 1: the low
+// (c even) or high (c odd) halves of word c / 2 of pieces 2i and 2i + 1.
+__device__ __forceinline__ void store_r(const Stage& st, uint16_t* lds) {
+  const int tid = threadIdx.x;
+  uint16_t* base = lds + ((tid >> 3) * 8) * kLdk + (tid & 7) * 8;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = __builtin_amdgcn_perm(st.v[2 * i + 1][c >> 1], st.v[2 * i][c >> 1], sel);
+    *(u32x4*)(base + c * kLdk) = o;
+  }
+}
+
+// One K-step's products from LDS buffer `buf`: each wave's 128 x 128 quarter,
+// four 16-wide k steps of 4 x 4 matrix-core products.
+__device__ __forceinline__ void products(const uint16_t (*buf)[kBM * kLdk], f32x16 (&acc)[4][4]) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  // lane l reads row l % 32 of a 32-row block, k values 8 (l / 32) .. + 7 of a
+  // 16-wide k step
+  const int frow = lane & 31, fk = (lane >> 5) * 8;
+  const uint16_t* As = buf[0] + ((wid >> 1) * 128 + frow) * kLdk + fk;
+  const uint16_t* Bs = buf[1] + ((wid & 1) * 128 + frow) * kLdk + fk;
+  // fragments of 16-wide k step s + 1 are read while step s's products run:
+  // the scheduler is told to alternate one product and one read
+  bf16x8 a[2][4], b[2][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[0][i] = *(const bf16x8*)(As + i * 32 * kLdk);
+    b[0][i] = *(const bf16x8*)(Bs + i * 32 * kLdk);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+  for (int s = 0; s < kBK / 16; ++s) {
+    const int c = s & 1;
+    if (s + 1 < kBK / 16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[c ^ 1][i] = *(const bf16x8*)(As + i * 32 * kLdk + 16 * (s + 1));
+        b[c ^ 1][i] = *(const bf16x8*)(Bs + i * 32 * kLdk + 16 * (s + 1));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
+    if (s + 1 < kBK / 16) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    } else {
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    }
+  }
+}
+
+template <bool AK, bool BK, int MODE>
+struct Loader {
+  const Opnd& a;
+  const Opnd& b;
+  int m0, n0, kbeg, kend;
+  __device__ __forceinline__ void load(int t, Stage& sa, Stage& sb) const {
+    const int k0 = kbeg + t * kBK;
+    if constexpr (AK) load_k<MODE>(a, m0, k0, kend, sa);
+    else load_r<MODE>(a, m0, k0, kend, sa);
+    if constexpr (BK) load_k<MODE>(b, n0, k0, kend, sb);
+    else load_r<MODE>(b, n0, k0, kend, sb);
+  }
+  __device__ __forceinline__ static void store(uint16_t (*buf)[kBM * kLdk], const Stage& sa, const Stage& sb) {
+    if constexpr (AK) store_k(sa, buf[0]);
+    else store_r(sa, buf[0]);
+    if constexpr (BK) store_k(sb, buf[1]);
+    else store_r(sb, buf[1]);
   }
 };
 
-#define AV_BLAS(call)                                                     \
-  do {                                                                    \
-    const hipblasStatus_t s_ = (call);                                    \
-    if (s_ != HIPBLAS_STATUS_SUCCESS) return blas_fail(#call, (int)s_);   \
-  } while (0)
+// The K loop of one tile: acc += A[m0 .., kbeg .. kend) B[kbeg .. kend), n0 ..],
+// through the two LDS buffers.  Global loads run two K-steps ahead of the
+// products: step t + 2 is requested while step t's products run, and step
+// t + 1 (requested one step earlier) is written to LDS after them.
+template <bool AK, bool BK, int MODE>
+__device__ __forceinline__ void k_loop2(const Loader<AK, BK, MODE>& L, uint16_t (*lds)[2][kBM * kLdk],
+                                        f32x16 (&acc)[4][4]) {
+  const int nk = (L.kend - L.kbeg + kBK - 1) / kBK;
+  if (nk <= 0) return;
+  // Branch-free trips: past the last step, loads repeat the last step (in
+  // bounds, unused) and stores go to a buffer that is not read again.
+  const int last = nk - 1;
+  Stage s0a, s0b, s1a, s1b;
+  L.load(0, s0a, s0b);
+  L.store(lds[0], s0a, s0b);
+  L.load(min(1, last), s1a, s1b);
+  __syncthreads();
+  // two steps per trip, so that each register stage is a fixed set of registers;
+  // at the top of a trip LDS buffer 0 holds step t and stage 1 step t + 1
+  int t = 0;
+  for (; t + 1 < nk; t += 2) {
+    L.load(min(t + 2, last), s0a, s0b);
+    products(lds[0], acc);
+    L.store(lds[1], s1a, s1b);
+    __syncthreads();
+    L.load(min(t + 3, last), s1a, s1b);
+    products(lds[1], acc);
+    L.store(lds[0], s0a, s0b);
+    __syncthreads();
+  }
+  if (t < nk) products(lds[0], acc);  // odd step count: the last step
+}
 
-// Column-major C[m, n] = A[m, k] op(B)[k, n], A not transposed (lda = m),
-// B stored [k, n] (ldb = k) or, transposed, [n, k] (ldb = n); bf16 inputs,
-// float32 accumulation and output (ldc = m).
-int gemm(int dev, hipblasLtHandle_t h, int m, int n, int k, bool transb, const void* A, const void* B, float* C,
-         void* ws, size_t wsb, hipStream_t stream) {
-  Desc d;
-  const hipblasOperation_t opn = HIPBLAS_OP_N, opb = transb ? HIPBLAS_OP_T : HIPBLAS_OP_N;
-  AV_BLAS(hipblasLtMatmulDescCreate(&d.md, HIPBLAS_COMPUTE_32F, HIP_R_32F));
-  AV_BLAS(hipblasLtMatmulDescSetAttribute(d.md, HIPBLASLT_MATMUL_DESC_TRANSA, &opn, sizeof(opn)));
-  AV_BLAS(hipblasLtMatmulDescSetAttribute(d.md, HIPBLASLT_MATMUL_DESC_TRANSB, &opb, sizeof(opb)));
-  AV_BLAS(hipblasLtMatrixLayoutCreate(&d.a, HIP_R_16BF, m, k, m));
-  AV_BLAS(hipblasLtMatrixLayoutCreate(&d.b, HIP_R_16BF, transb ? n : k, transb ? k : n, transb ? n : k));
-  AV_BLAS(hipblasLtMatrixLayoutCreate(&d.c, HIP_R_32F, m, n, m));
-  hipblasLtMatmulAlgo_t algo;
-  const AlgoKey key{dev, m, n, k, transb ? 1 : 0, wsb};
-  bool have = false;
-  {
-    std::lock_guard<std::mutex> g(g_algo_mu);
-    auto it = g_algo.find(key);
-    if (it != g_algo.end()) {
-      algo = it->second;
-      have = true;
+// The same with loads one K-step ahead (element-wise loads: fewer registers).
+template <bool AK, bool BK, int MODE>
+__device__ __forceinline__ void k_loop1(const Loader<AK, BK, MODE>& L, uint16_t (*lds)[2][kBM * kLdk],
+                                        f32x16 (&acc)[4][4]) {
+  const int nk = (L.kend - L.kbeg + kBK - 1) / kBK;
+  if (nk <= 0) return;
+  Stage sa, sb;
+  L.load(0, sa, sb);
+  L.store(lds[0], sa, sb);
+  __syncthreads();
+  for (int t = 0; t < nk; ++t) {
+    if (t + 1 < nk) L.load(t + 1, sa, sb);
+    products(lds[t & 1], acc);
+    if (t + 1 < nk) L.store(lds[(t + 1) & 1], sa, sb);
+    __syncthreads();
+  }
+}
+
+template <bool AK, bool BK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kBM * kLdk];  // [buffer][A, B]
+  int tm, tn, sp;
+  if (!tile_of(g, blockIdx.x, tm, tn, sp)) return;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  const int m0 = tm * kBM, n0 = tn * kBN;
+  const int kbeg = sp * g.kchunk, kend = min(g.K, kbeg + g.kchunk);
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  const Opnd oa{g.A, g.lda, g.a_total, g.M}, ob{g.B, g.ldb, g.b_total, g.N};
+  if (!g.vec) {
+    k_loop1(Loader<AK, BK, kScalar>{oa, ob, m0, n0, kbeg, kend}, lds, acc);
+  } else if (m0 + kBM <= g.M && n0 + kBN <= g.N) {
+    // whole K-steps unchecked, then the partial last one (if any) checked
+    const int kfull = kend > kbeg ? kbeg + (kend - kbeg) / kBK * kBK : kbeg;
+    k_loop2(Loader<AK, BK, kFast>{oa, ob, m0, n0, kbeg, kfull}, lds, acc);
+    if (kfull < kend) k_loop1(Loader<AK, BK, kEdge>{oa, ob, m0, n0, kfull, kend}, lds, acc);
+  } else {
+    k_loop2(Loader<AK, BK, kEdge>{oa, ob, m0, n0, kbeg, kend}, lds, acc);
+  }
+
+  // register r of block (i, j): row 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32
+  float* C = g.C + (g.splits > 1 ? (long long)sp * g.M * g.N : 0);
+  const int col0 = n0 + wn * 128 + (lane & 31);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (row < g.M) {
+        float* crow = C + (long long)row * g.N;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = col0 + j * 32;
+          if (col < g.N) __builtin_nontemporal_store(acc[i][j][r], crow + col);
+        }
+      }
     }
+}
+
+// C = sum over splits of the partial tiles, in split order.
+__global__ __launch_bounds__(256) void reduce_kernel(const float* part, float* C, long long n, int splits) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
+    float s = part[i];
+    for (int q = 1; q < splits; ++q) s += part[(long long)q * n + i];
+    C[i] = s;
   }
-  if (!have) {
-    AV_BLAS(hipblasLtMatmulPreferenceCreate(&d.pref));
-    AV_BLAS(hipblasLtMatmulPreferenceSetAttribute(d.pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsb,
-                                                  sizeof(wsb)));
-    hipblasLtMatmulHeuristicResult_t res;
-    int nres = 0;
-    AV_BLAS(hipblasLtMatmulAlgoGetHeuristic(h, d.md, d.a, d.b, d.c, d.c, d.pref, 1, &res, &nres));
-    if (nres < 1) return AV_EUNSUPPORTED;
-    algo = res.algo;
-    std::lock_guard<std::mutex> g(g_algo_mu);
-    g_algo[key] = algo;
-  }
-  const float alpha = 1.0f, beta = 0.0f;
-  AV_BLAS(hipblasLtMatmul(h, d.md, &alpha, A, d.a, B, d.b, &beta, C, d.c, C, d.c, &algo, ws, wsb, stream));
-  return AV_OK;
+}
+
+template <bool AK, bool BK>
+hipError_t launch_gemm(GemmArgs& g, bool vec, hipStream_t s) {
+  const long long tiles = (long long)g.tiles_m * g.tiles_n * g.splits;
+  if (tiles > 0x7ffffff0LL) return hipErrorInvalidValue;
+  g.per_xcd = (int)((tiles + 7) / 8);
+  const dim3 grid((unsigned)(8LL * g.per_xcd));
+  g.vec = vec;
+  hipLaunchKernelGGL((gemm_kernel<AK, BK>), grid, dim3(kThreads), 0, s, g);
+  return hipGetLastError();
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Splits of d_hid's long K: enough workgroups for the device (about one per
+// CU), a K range per split that is a multiple of kBK.
+int hid_splits(int R, int V, int H, int cus) {
+  const long long tiles = ((long long)R + kBM - 1) / kBM * (((long long)H + kBN - 1) / kBN);
+  int s = 1;
+  while (s < kMaxSplits && tiles * s * 2 <= cus && (long long)V / (2 * s) >= 8 * kBK) s *= 2;
+  if (tiles * s < cus && s < kMaxSplits && (long long)V / (2 * s) >= 8 * kBK) s *= 2;
+  return s;
+}
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) return 256;
+  return cus;
 }
 
 }  // namespace
 
 extern "C" {
 
-size_t av_lm_head_workspace_bytes(void) { return (size_t)64 << 20; }
-
-const char* av_lm_head_last_error(void) { return g_err; }
+size_t av_lm_head_workspace_bytes(int R, int V, int H) {
+  if (R < 1 || V < 1 || H < 1 || R > kMaxDim || V > kMaxLd || H > kMaxLd) return 0;
+  const int s = hid_splits(R, V, H, device_cus());
+  return s > 1 ? (size_t)s * R * H * sizeof(float) : 0;
+}
 
 int av_lm_head_bwd(int R, int V, int H, const void* dz, const void* w, const void* hid, float* d_hid,
                    float* d_w, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!dz || R < 1 || V < 1 || H < 1) return AV_EINVAL;
+  if (R < 1 || V < 1 || H < 1 || !dz) return AV_EINVAL;
+  if (R > kMaxDim || V > kMaxLd || H > kMaxLd) return AV_EUNSUPPORTED;
   if ((d_hid && !w) || (d_w && !hid)) return AV_EINVAL;
   if (workspace_bytes > 0 && !workspace) return AV_EINVAL;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return AV_EHIP;
-  std::call_once(g_blas_once[dev], [dev]() { g_blas[dev].st = hipblasLtCreate(&g_blas[dev].h); });
-  if (g_blas[dev].st != HIPBLAS_STATUS_SUCCESS) return blas_fail("hipblasLtCreate", (int)g_blas[dev].st);
-  const hipblasLtHandle_t h = g_blas[dev].h;
   const hipStream_t s = (hipStream_t)stream;
-  int rc = AV_OK;
-  // d_hid^T [H, R] = W^T [H, V] dz^T [V, R]
-  if (d_hid) rc = gemm(dev, h, H, R, V, false, w, dz, d_hid, workspace, workspace_bytes, s);
-  // d_W^T [H, V] = hid^T [H, R] dz [R, V]  (dz^T stored [V, R], transposed)
-  if (rc == AV_OK && d_w) rc = gemm(dev, h, H, V, R, true, hid, dz, d_w, workspace, workspace_bytes, s);
-  return rc;
+  // 16-byte loads need every row start, and every edge of M, N and K, on an
+  // 8-value bound
+  const bool vec = R % 8 == 0 && V % 8 == 0 && H % 8 == 0 && aligned16(dz) && (!w || aligned16(w)) &&
+                   (!hid || aligned16(hid));
+  if (d_hid) {
+    GemmArgs g{};
+    g.A = (const uint16_t*)dz;
+    g.lda = V;
+    g.a_total = (long long)R * V;
+    g.B = (const uint16_t*)w;
+    g.ldb = H;
+    g.b_total = (long long)V * H;
+    g.M = R;
+    g.N = H;
+    g.K = V;
+    g.tiles_m = (R + kBM - 1) / kBM;
+    g.tiles_n = (H + kBN - 1) / kBN;
+    int splits = hid_splits(R, V, H, device_cus());
+    if ((size_t)splits * R * H * sizeof(float) > workspace_bytes || !aligned16(workspace)) splits = 1;
+    g.splits = splits;
+    g.kchunk = (int)((((long long)V + splits - 1) / splits + kBK - 1) / kBK * kBK);
+    g.group = g.tiles_n < 4 ? g.tiles_n : 4;
+    g.C = splits > 1 ? (float*)workspace : d_hid;
+    hipError_t e = launch_gemm<true, false>(g, vec, s);
+    if (e == hipSuccess && splits > 1) {
+      const long long n = (long long)R * H;
+      const long long blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+      hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const float*)workspace, d_hid,
+                         n, splits);
+      e = hipGetLastError();
+    }
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  if (d_w) {
+    GemmArgs g{};
+    g.A = (const uint16_t*)dz;  // dz^T: element (v, r) at dz[r V + v]
+    g.lda = V;
+    g.a_total = (long long)R * V;
+    g.B = (const uint16_t*)hid;
+    g.ldb = H;
+    g.b_total = (long long)R * H;
+    g.M = V;
+    g.N = H;
+    g.K = R;
+    g.tiles_m = (V + kBM - 1) / kBM;
+    g.tiles_n = (H + kBN - 1) / kBN;
+    g.splits = 1;
+    g.kchunk = (R + kBK - 1) / kBK * kBK;
+    g.group = g.tiles_n;
+    g.C = d_w;
+    const hipError_t e = launch_gemm<false, false>(g, vec, s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return AV_OK;
 }
+
+const char* av_lm_head_last_error(void) { return g_err; }
 
 }  // extern "C"

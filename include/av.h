@@ -351,19 +351,27 @@ int av_verify_opd_bwd(int dtype, int B, int k, int V, int R,
  * dz = d loss / d zq from av_verify_opd_fwd (grad_dtype AV_BF16):
  *     d_hid[r, h] = sum_v dz[r, v] W[v, h]
  *     d_w[v, h]   = sum_r dz[r, v] hid[r, h]
- * Two bfloat16 GEMMs with float32 accumulation on the matrix cores
- * (hipBLASLt).
+ * Two bfloat16 GEMMs with float32 accumulation on the matrix cores (the
+ * library's own v_mfma_f32_32x32x16_bf16 kernels; the long sum over V of
+ * d_hid may be split over workgroups, the partial sums then added in a fixed
+ * order, so results are deterministic for a given device).
  *   dz     [R, V] bfloat16 row-major;  w [V, H] bfloat16;  hid [R, H] bfloat16
  *   d_hid  [R, H] float32 out, or NULL (then w may be NULL)
  *   d_w    [V, H] float32 out, or NULL (then hid may be NULL)
- *   workspace, workspace_bytes: scratch for the GEMMs, may be NULL / 0;
- *          av_lm_head_workspace_bytes() is the size the library asks for
- * All pointers are device pointers; asynchronous on `stream`.  Errors:
- * AV_EINVAL for R, V or H < 1, NULL dz, or an output without its operand;
- * AV_EUNSUPPORTED if no GEMM kernel fits the shape and workspace; AV_EHIP
- * for a runtime or hipBLASLt failure (text in av_lm_head_last_error()).
+ *   workspace, workspace_bytes: device scratch for the split sum of d_hid,
+ *          16-byte aligned, may be NULL / 0 (then d_hid is one sum per
+ *          entry, which takes longer on small R H); av_lm_head_workspace_bytes
+ *          (R, V, H) is the size the library uses on the current device, 0
+ *          when it does not split.  Not read before it is written; nothing
+ *          to initialise, and it may be reused across calls on one stream.
+ * All pointers are device pointers; rows of 16-byte aligned operands with V
+ * and H multiples of 8 take the 16-byte load path, any other shape an
+ * element-wise one.  Asynchronous on `stream`.  Errors: AV_EINVAL for R, V or
+ * H < 1, NULL dz, an output without its operand, or workspace_bytes > 0 with
+ * a NULL workspace; AV_EUNSUPPORTED for R above 2^30 or V, H above 2^22; AV_EHIP for a
+ * launch failure (text in av_lm_head_last_error(), per thread).
  */
-size_t av_lm_head_workspace_bytes(void);
+size_t av_lm_head_workspace_bytes(int R, int V, int H);
 int av_lm_head_bwd(int R, int V, int H, const void* dz, const void* w, const void* hid,
                    float* d_hid, float* d_w, void* workspace, size_t workspace_bytes,
                    void* stream);

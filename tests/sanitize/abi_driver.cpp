@@ -38,7 +38,10 @@ int main() {
   (void)av_head_update_workspace_bytes(INT_MIN);
   EXPECT(av_workspace_bytes(0, 16, 10) == 0, 1);
   (void)av_noalloc_max_bytes();
-  (void)av_lm_head_workspace_bytes();
+  for (int R : {INT_MIN, -1, 0, 1, 2048, INT_MAX})
+    for (int V : {INT_MIN, 0, 1, 151936, INT_MAX})
+      for (int H : {INT_MIN, 0, 1, 4096, INT_MAX}) (void)av_lm_head_workspace_bytes(R, V, H);
+  EXPECT(av_lm_head_workspace_bytes(0, 64, 16) == 0, 1);
   for (int s : {-4, -3, -2, -1, 0, 1, INT_MAX, INT_MIN}) (void)av_status_str(s);
   (void)av_last_hip_error();
 

@@ -38,7 +38,13 @@ def check(got, ref, scale, what):
     assert not bad.any(), f"{what}: {int(bad.sum())} entries off"
 
 
-@pytest.mark.parametrize("R,V,H", [(1, 1, 1), (5, 300, 64), (3, 1001, 17), (64, 151936, 256)])
+# (1, 1, 1), (3, 1001, 17), (257, 777, 263): element-wise loads (a dimension
+# not a multiple of 8), several tiles with ragged edges; (264, 4104, 520):
+# 16-byte loads with checked edge tiles in M and N and a partial last K step;
+# (512, 8192, 512): unchecked interior tiles only; (64, 151936, 256): one
+# tile of d_hid with the sum over V split over 8 workgroups.
+@pytest.mark.parametrize("R,V,H", [(1, 1, 1), (5, 300, 64), (3, 1001, 17), (257, 777, 263), (264, 4104, 520),
+                                   (512, 8192, 512), (64, 151936, 256)])
 def test_shapes(av, R, V, H):
     say(f"lm head bwd R={R} V={V} H={H}")
     dz = bf16_tensor((R, V), 1, 1e-3)
@@ -50,6 +56,42 @@ def test_shapes(av, R, V, H):
     ref_h, ref_w = oracle.lm_head_backward(dzh, wh, hh)
     check(host(out["d_hid"]), ref_h, np.abs(dzh) @ np.abs(wh), "d_hid")
     check(host(out["d_w"]), ref_w, np.abs(dzh).T @ np.abs(hh), "d_w")
+
+
+def raw_call(av, dz, w, hid, d_hid, d_w, ws):
+    from drafter_distillation_amd import _lib
+    R, V = dz.shape
+    H = (w if w is not None else hid).shape[1]
+    rc = _lib.lib().av_lm_head_bwd(R, V, H, _lib._ptr(dz), _lib._ptr(w), _lib._ptr(hid), _lib._ptr(d_hid),
+                                   _lib._ptr(d_w), _lib._ptr(ws), 0 if ws is None else ws.numel(),
+                                   _lib._stream(dz.device))
+    assert rc == 0, rc
+
+
+@pytest.mark.parametrize("R,V,H", [(64, 151936, 256), (40, 20000, 300)])
+def test_split_sum_and_workspace(av, R, V, H):
+    """d_hid with the sum over V split (the workspace the library asks for)
+    and in one piece (no workspace): both within the bar of the oracle, and
+    repeated calls bit-identical."""
+    from drafter_distillation_amd import _lib
+    say(f"lm head bwd split sum R={R} V={V} H={H}")
+    nbytes = int(_lib.lib().av_lm_head_workspace_bytes(R, V, H))
+    assert nbytes > 0
+    dz = bf16_tensor((R, V), 11, 1e-3)
+    w = bf16_tensor((V, H), 12, 0.02)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    outs = []
+    for wsp in (ws, ws, None):
+        d_hid = torch.full((R, H), float("nan"), device="cuda")
+        raw_call(av, dz, w, None, d_hid, None, wsp)
+        outs.append(d_hid)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    dzh, wh = host(dz), host(w)
+    ref = dzh @ wh
+    scale = np.abs(dzh) @ np.abs(wh)
+    check(host(outs[0]), ref, scale, "d_hid split")
+    check(host(outs[2]), ref, scale, "d_hid whole")
 
 
 def test_one_output_only(av):
