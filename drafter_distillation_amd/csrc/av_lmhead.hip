@@ -4,27 +4,31 @@
 // cores of gfx950 (v_mfma_f32_32x32x16_bf16).  Semantics are documented in
 // include/av.h.
 //
-// gemm_kernel: C[M, N] = A[M, K] B[K, N], C row-major float32.
-//   A is K-contiguous (element (m, k) at A[m lda + k]) or M-contiguous (at
-//   A[k lda + m]); B is K-contiguous (B[n ldb + k]) or N-contiguous
-//   (B[k ldb + n]).  d_hid: A = dz (K-contiguous), B = W (N-contiguous);
-//   d_W: A = dz read as dz^T (M-contiguous), B = hid (N-contiguous).
-//   A workgroup of 256 threads (4 waves, 2 x 2) owns a 256 x 256 tile of C;
-//   each wave a 128 x 128 quarter: 4 x 4 blocks of 32 x 32, 256 float32
-//   accumulators per lane.  K advances 64 at a time through two LDS buffers
-//   that hold both operands as [row][k] (k contiguous, rows padded to 72
-//   values so that the lanes of a 16-byte fragment read fall on distinct
-//   banks): while one buffer feeds the matrix cores, the next K-step's
-//   operands are in flight from global memory into registers and then
-//   written to the other buffer.  An operand that is not K-contiguous is
-//   loaded as 8 x 8 blocks (eight 16-byte rows along M or N) and transposed
-//   in registers with byte permutes on its way to LDS.
-//   Long K (d_hid: K = V) is split over workgroups; the partial tiles go to
-//   the workspace and reduce_kernel adds them in split order.
-//   Tiles map to workgroup ids so that the workgroups of one XCD (ids equal
-//   mod 8) share operands in that XCD's L2: for d_hid each XCD takes 1/8 of
-//   the N tiles (reading 1/8 of W); for d_W each XCD takes every 8th M tile
-//   and runs its 16 N tiles back to back (one 1 MB slice of dz per M tile).
+// Both compute C[M, N] = A[M, K] B[K, N], C row-major float32.  A is
+// K-contiguous (element (m, k) at A[m lda + k]) or M-contiguous (at
+// A[k lda + m]); B is K-contiguous (B[n ldb + k]) or N-contiguous
+// (B[k ldb + n]).  d_hid: A = dz (K-contiguous), B = W (N-contiguous);
+// d_W: A = dz read as dz^T (M-contiguous), B = hid (N-contiguous).
+// A workgroup of 256 threads (4 waves, 2 x 2) owns a 256 x 256 tile of C;
+// each wave a 128 x 128 quarter: 4 x 4 blocks of 32 x 32, 256 float32
+// accumulators per lane.  K advances 64 at a time through two LDS buffers.
+//
+// gemm_kernel (register-staged; d_hid, and any shape without 16-byte rows):
+//   both operands are held in LDS as [row][k] (k contiguous, rows padded to
+//   72 values so that the lanes of a 16-byte fragment read fall on distinct
+//   banks); global loads run two K-steps ahead into registers and are
+//   written to the free buffer after each step's products.  An operand that
+//   is not K-contiguous is loaded as 8 x 8 blocks (eight 16-byte rows along
+//   M or N) and transposed in registers with byte permutes.
+// gemm_dma_kernel (d_W): operands go from global memory straight into LDS
+//   and M- or N-contiguous operands are read back transposed (see the
+//   section below).
+//
+// Long K (d_hid: K = V) is split over workgroups; the partial tiles go to
+// the workspace and reduce_kernel adds them in split order.  Tiles map to
+// workgroup ids so that the 32 workgroups that run together on one XCD (ids
+// equal mod 8) form an 8 x 4 block of tiles, which share operand slices in
+// that XCD's L2 (see tile_of).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -42,6 +46,7 @@ constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kLdk = kBK + 8;  // LDS row length (bfloat16 values)
 constexpr int kThreads = 256;
 constexpr int kMaxSplits = 8;
+constexpr int kDmaKs = 64, kDmaStages = 2;  // K per LDS stage and stages of the DMA kernel
 constexpr int kMaxDim = 1 << 30;  // largest R (tile offsets stay in int)
 constexpr int kMaxLd = 1 << 22;   // largest V, H (per-thread buffer offsets stay in 31 bits)
 
@@ -309,6 +314,30 @@ __device__ __forceinline__ void k_loop1(const Loader<AK, BK, MODE>& L, uint16_t 
   }
 }
 
+// Writes a workgroup's accumulators: register r of block (i, j) of wave
+// (wm, wn) is row 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32 of that
+// block.  Partial tiles of a split sum go to the split's slice of the workspace.
+__device__ __forceinline__ void store_tile(const GemmArgs& g, const f32x16 (&acc)[4][4], int m0, int n0, int sp) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  float* C = g.C + (g.splits > 1 ? (long long)sp * g.M * g.N : 0);
+  const int col0 = n0 + wn * 128 + (lane & 31);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (row < g.M) {
+        float* crow = C + (long long)row * g.N;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = col0 + j * 32;
+          if (col < g.N) __builtin_nontemporal_store(acc[i][j][r], crow + col);
+        }
+      }
+    }
+}
+
 template <bool AK, bool BK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kBM * kLdk];  // [buffer][A, B]
@@ -336,23 +365,205 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     k_loop2(Loader<AK, BK, kEdge>{oa, ob, m0, n0, kbeg, kend}, lds, acc);
   }
 
-  // register r of block (i, j): row 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32
-  float* C = g.C + (g.splits > 1 ? (long long)sp * g.M * g.N : 0);
-  const int col0 = n0 + wn * 128 + (lane & 31);
+  store_tile(g, acc, m0, n0, sp);
+}
+
+// ---------------------------------------------------------------------------
+// The main kernel: operands go from global memory straight into LDS
+// ---------------------------------------------------------------------------
+//
+// Each K-step of KS values is written to LDS by 16-byte buffer loads with the
+// LDS destination (lane l of a wave writes bytes 16 l .. 16 l + 15 of a 1 KB
+// block), so nothing passes through registers and no LDS store instruction
+// runs; ST buffers let the loads for step t + ST - 1 run while step t's
+// products do.  Within a 1 KB block the layout is fixed by the lane order, so
+// bank conflicts are avoided by choosing which global 16-byte chunk each lane
+// fetches (an XOR swizzle), and the fragment reads undo it:
+//  - K-contiguous operand, LDS [256 rows][KS k]: row r's chunk c (8 k values)
+//    sits at chunk position c ^ swk(r), which spreads the 16 rows that one
+//    16-byte fragment read serves at a time over all 64 banks;
+//  - row-contiguous operand, LDS [KS k][256 rows]: k-row k's chunk c (8 rows
+//    of the tile) sits at position c ^ 4 (k % 4); the fragments are read with
+//    ds_read_b64_tr_b16, which hands each lane of a 16-lane group one value
+//    from each of four lanes' 8-byte reads (lane i gets value i % 4 of the
+//    reads of lanes i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4), so four lanes
+//    reading 4 consecutive rows at 4 consecutive k give each lane 4
+//    consecutive k of its own row: half of a matrix-core operand fragment.
+// Loads that fall outside M, N or K take an offset past the buffer
+// resource's extent, which makes them write zeros.
+
+__device__ __forceinline__ void dma16(Rsrc r, const uint16_t* lds_block, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_block, 16, voff, 0, 0, 0);
+}
+
+constexpr uint32_t kOutside = 0x80000000u;  // an offset past every resource's extent
+
+template <int KS>
+struct KsGeom {
+  static constexpr int kCpr = KS / 8;            // 16-byte chunks per row of a K-contiguous tile
+  static constexpr int kRpb = 1024 / (2 * KS);   // its rows per 1 KB block
+  static constexpr int kRp256 = 128 / KS;        // its rows per 256 bytes (one pass over the banks)
+  static constexpr int kBlocks = KS / 2;         // 1 KB blocks per operand per step (either layout)
+  static constexpr int kBlocksPerWave = KS / 8;
+  __device__ static int swk(int r) { return (r / kRp256) % kCpr; }
+};
+
+// Per-lane offsets of one operand's DMA pieces for a step, relative to the
+// step's corner of the tile (the resource's base).  EDGE: pieces outside the
+// operand get kOutside.
+template <bool KC, int KS, bool EDGE>
+__device__ __forceinline__ void dma_offsets(const Opnd& o, int r0, int k0, int kend, uint32_t (&vo)[KS / 8]) {
+  using G = KsGeom<KS>;
+  const int L = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int q = 0; q < G::kBlocksPerWave; ++q) {
+    const int u = w * G::kBlocksPerWave + q;
+    if constexpr (KC) {
+      const int r = u * G::kRpb + L / G::kCpr, c = (L % G::kCpr) ^ G::swk(r);
+      vo[q] = (uint32_t)((r * o.ld + 8 * c) * 2);
+      if (EDGE && (r0 + r >= o.rows || k0 + 8 * c >= kend)) vo[q] = kOutside;
+    } else {
+      const int k = 2 * u + (L >> 5), c = (L & 31) ^ (4 * (k & 3));
+      vo[q] = (uint32_t)((k * o.ld + 8 * c) * 2);
+      if (EDGE && (k0 + k >= kend || r0 + 8 * c >= o.rows)) vo[q] = kOutside;
+    }
+  }
+}
+
+template <bool KC, int KS, bool EDGE>
+__device__ __forceinline__ void dma_step(const Opnd& o, int r0, int k0, int kend, const uint16_t* lds) {
+  using G = KsGeom<KS>;
+  uint32_t vo[KS / 8];
+  dma_offsets<KC, KS, EDGE>(o, r0, k0, kend, vo);
+  const Rsrc r = rsrc_at(o.P, o.total, KC ? (long long)r0 * o.ld + k0 : (long long)k0 * o.ld + r0);
+  const int w = threadIdx.x >> 6;
+#pragma unroll
+  for (int q = 0; q < G::kBlocksPerWave; ++q) dma16(r, lds + (w * G::kBlocksPerWave + q) * 512, vo[q]);
+}
+
+// Fragment of rows rb .. rb + 31, 16-wide k step s (lane l: row rb + l % 32,
+// k values 8 (l / 32) .. + 7).
+template <int KS>
+__device__ __forceinline__ bf16x8 frag_k(const uint16_t* lds, int rb, int s) {
+  const int l = threadIdx.x & 63, r = rb + (l & 31), kc = 2 * s + (l >> 5);
+  return *(const bf16x8*)(lds + r * KS + 8 * (kc ^ KsGeom<KS>::swk(r)));
+}
+template <int KS>
+__device__ __forceinline__ bf16x8 frag_t(const uint16_t* lds, int rb, int s) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const int l = threadIdx.x & 63, g = l >> 4, i = l & 15;
+  const int n = rb + 16 * (g & 1) + 4 * (i & 3);
+  s16x4 v[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int k = 16 * s + 8 * (g >> 1) + 4 * h + (i >> 2);
+    const uint16_t* p = lds + k * 256 + 8 * ((n >> 3) ^ (4 * (k & 3))) + (n & 7);
+    v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+  }
+  // k values 0..3 of the lane's 8, then 4..7
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <bool AKC, bool BKC, int KS>
+__device__ __forceinline__ void dma_products(const uint16_t* As, const uint16_t* Bs, f32x16 (&acc)[4][4]) {
+  const int wid = threadIdx.x >> 6, am = (wid >> 1) * 128, bn = (wid & 1) * 128;
+#pragma unroll
+  for (int s = 0; s < KS / 16; ++s) {
+    bf16x8 a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = AKC ? frag_k<KS>(As, am + 32 * i, s) : frag_t<KS>(As, am + 32 * i, s);
+      b[i] = BKC ? frag_k<KS>(Bs, bn + 32 * i, s) : frag_t<KS>(Bs, bn + 32 * i, s);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// s_waitcnt with only the vector-memory count set (the others at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// LDS of the main kernel: one array per stage, so that the compiler can tell
+// a stage being loaded from the one being read (it then does not make the
+// reads wait for the loads).
+template <int KS>
+struct DmaLds {
+  uint16_t* a[4];  // A operand of each stage
+  uint16_t* b[4];  // B operand of each stage
+};
+
+template <bool AKC, bool BKC, int KS, int ST, bool EDGE>
+__device__ __forceinline__ void dma_loop(const GemmArgs& g, const DmaLds<KS>& L, int m0, int n0, int kbeg,
+                                         int kend, f32x16 (&acc)[4][4]) {
+  constexpr int kD = 2 * KsGeom<KS>::kBlocksPerWave;  // DMA instructions per wave per step
+  const Opnd oa{g.A, g.lda, g.a_total, g.M}, ob{g.B, g.ldb, g.b_total, g.N};
+  const int nk = (kend - kbeg + KS - 1) / KS;
+  auto issue = [&](int t, int stage) {
+    const int k0 = kbeg + t * KS;
+    dma_step<AKC, KS, EDGE>(oa, m0, k0, kend, L.a[stage]);
+    dma_step<BKC, KS, EDGE>(ob, n0, k0, kend, L.b[stage]);
+  };
+#pragma unroll
+  for (int p = 0; p < ST - 1; ++p)
+    if (p < nk) issue(p, p);
+  // ST steps per trip, so that each step's stage is known at compile time
+  for (int t0 = 0; t0 < nk; t0 += ST) {
+#pragma unroll
+    for (int p = 0; p < ST; ++p) {
+      const int t = t0 + p;
+      if (t < nk) {
+        // step t's loads (this wave's) have landed when at most the later
+        // steps' loads are still in flight
+        const int later = min(ST - 2, nk - 1 - t);
+        if constexpr (ST >= 4) {
+          if (later >= 2) wait_vm<2 * kD>();
+          else if (later == 1) wait_vm<kD>();
+          else wait_vm<0>();
+        } else if constexpr (ST == 3) {
+          if (later >= 1) wait_vm<kD>();
+          else wait_vm<0>();
+        } else {
+          wait_vm<0>();
+        }
+        // every wave's loads of step t are in LDS, and every wave is done
+        // with the stage that step t + ST - 1 overwrites
+        __syncthreads();
+        if (t + ST - 1 < nk) issue(t + ST - 1, (p + ST - 1) % ST);
+        dma_products<AKC, BKC, KS>(L.a[p], L.b[p], acc);
+      }
+    }
+  }
+}
+
+template <bool AKC, bool BKC, int KS, int ST>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_dma_kernel(GemmArgs g) {
+  static_assert(ST >= 2 && ST <= 4, "stages");
+  constexpr int kOp = 256 * KS;  // bf16 values per operand per stage
+  __shared__ __attribute__((aligned(1024))) uint16_t a0[kOp], b0[kOp], a1[kOp], b1[kOp];
+  __shared__ __attribute__((aligned(1024))) uint16_t a2[ST > 2 ? kOp : 8], b2[ST > 2 ? kOp : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t a3[ST > 3 ? kOp : 8], b3[ST > 3 ? kOp : 8];
+  const DmaLds<KS> L{{a0, a1, a2, a3}, {b0, b1, b2, b3}};
+  int tm, tn, sp;
+  if (!tile_of(g, blockIdx.x, tm, tn, sp)) return;
+  const int m0 = tm * kBM, n0 = tn * kBN;
+  const int kbeg = sp * g.kchunk, kend = min(g.K, kbeg + g.kchunk);
+  f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (row < g.M) {
-        float* crow = C + (long long)row * g.N;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = col0 + j * 32;
-          if (col < g.N) __builtin_nontemporal_store(acc[i][j][r], crow + col);
-        }
-      }
-    }
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  if (m0 + kBM <= g.M && n0 + kBN <= g.N && (kend - kbeg) % KS == 0)
+    dma_loop<AKC, BKC, KS, ST, false>(g, L, m0, n0, kbeg, kend, acc);
+  else
+    dma_loop<AKC, BKC, KS, ST, true>(g, L, m0, n0, kbeg, kend, acc);
+  wait_vm<0>();
+  store_tile(g, acc, m0, n0, sp);
 }
 
 // C = sum over splits of the partial tiles, in split order.
@@ -371,7 +582,13 @@ hipError_t launch_gemm(GemmArgs& g, bool vec, hipStream_t s) {
   g.per_xcd = (int)((tiles + 7) / 8);
   const dim3 grid((unsigned)(8LL * g.per_xcd));
   g.vec = vec;
-  hipLaunchKernelGGL((gemm_kernel<AK, BK>), grid, dim3(kThreads), 0, s, g);
+  // Measured on MI355X at R=2048, V=151936, H=4096: with a row-contiguous A
+  // (d_W) the DMA kernel's transposing reads beat the register transposes
+  // (940 against 700 TFLOP/s); with a K-contiguous A and the long K of d_hid
+  // the register-staged kernel, whose loads run two steps ahead, beats the
+  // two-stage DMA pipeline, which drains at every step (1050 against 880).
+  if (vec && !AK) hipLaunchKernelGGL((gemm_dma_kernel<AK, BK, kDmaKs, kDmaStages>), grid, dim3(kThreads), 0, s, g);
+  else hipLaunchKernelGGL((gemm_kernel<AK, BK>), grid, dim3(kThreads), 0, s, g);
   return hipGetLastError();
 }
 
@@ -459,7 +676,7 @@ int av_lm_head_bwd(int R, int V, int H, const void* dz, const void* w, const voi
     g.tiles_n = (H + kBN - 1) / kBN;
     g.splits = 1;
     g.kchunk = (R + kBK - 1) / kBK * kBK;
-    g.group = g.tiles_n;
+    g.group = g.tiles_n < 4 ? g.tiles_n : 4;
     g.C = d_w;
     const hipError_t e = launch_gemm<false, false>(g, vec, s);
     if (e != hipSuccess) return hip_fail(e);

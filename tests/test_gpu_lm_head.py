@@ -94,6 +94,23 @@ def test_split_sum_and_workspace(av, R, V, H):
     check(host(outs[2]), ref, scale, "d_hid whole")
 
 
+@pytest.mark.parametrize("n,H", [(264, 520), (512, 256)])
+def test_identity_routes_every_entry(av, n, H):
+    """dz = I (n x n) makes d_hid = W and d_W = hid exactly (one nonzero
+    product per entry, small integers exact in bfloat16): any misrouted
+    load, swizzle or transposed read shows as a wrong entry."""
+    say(f"lm head bwd identity n={n} H={H}")
+    dz = torch.eye(n, device="cuda").to(torch.bfloat16)
+    v = torch.arange(n, device="cuda", dtype=torch.float32)[:, None]
+    h = torch.arange(H, device="cuda", dtype=torch.float32)[None, :]
+    w = ((3 * v + h) % 61 - 30).to(torch.bfloat16)
+    hid = ((5 * v + 7 * h) % 53 - 26).to(torch.bfloat16)
+    out = av.av_lm_head_bwd(dz, w, hid)
+    torch.cuda.synchronize()
+    assert torch.equal(out["d_hid"], w.float())
+    assert torch.equal(out["d_w"], hid.float())
+
+
 def test_one_output_only(av):
     dz = bf16_tensor((4, 500), 4, 1e-3)
     w = bf16_tensor((500, 32), 5, 0.02)
