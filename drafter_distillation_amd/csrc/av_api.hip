@@ -24,19 +24,23 @@ int hip_fail(hipError_t e) {
 struct DeviceInfo {
   int cus = 0;
   long long ticks_per_ms = 0;  // wall-clock counter rate
-  int occ[4][5][2][2] = {};    // fused-kernel workgroups per CU, per variant, kernel form
+  int occ[4][7][2][2] = {};    // fused-kernel workgroups per CU, per variant, kernel form
                                // (see kForms), gradient type and plain/tempered form, with
                                // the most dynamic LDS a launch uses
 };
-// Kernel forms: {fast form, split rows, register slots of the build}.
+// Kernel forms: {fast form, split (1 whole rows, 2 split rows, 3 split
+// tail), register slots of the build}.
 struct FormDesc {
-  bool full, split;
-  int nr;
+  bool full;
+  int split, nr;
 };
-constexpr FormDesc kForms[5] = {{false, false, 0}, {true, false, 0}, {false, true, avk::kRowRegs16},
-                                {true, true, avk::kRowRegs16}, {true, true, avk::kPairRegs}};
-int form_index(bool full, bool split, int nr) {
-  if (!split) return full ? 1 : 0;
+constexpr int kNumForms = 7;
+constexpr FormDesc kForms[kNumForms] = {{false, 1, 0}, {true, 1, 0}, {false, 2, avk::kRowRegs16},
+                                        {true, 2, avk::kRowRegs16}, {true, 2, avk::kPairRegs},
+                                        {false, 3, avk::kRowRegs16}, {true, 3, avk::kRowRegs16}};
+int form_index(bool full, int split, int nr) {
+  if (split == 3) return full ? 6 : 5;
+  if (split != 2) return full ? 1 : 0;
   if (!full) return 2;
   return nr == avk::kPairRegs ? 4 : 3;
 }
@@ -60,7 +64,7 @@ hipError_t device_info(const DeviceInfo** out) {
     if (err == hipSuccess) err = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
     d.ticks_per_ms = khz > 0 ? (long long)khz : 100000;
     for (int v = 0; v < 4 && err == hipSuccess; ++v)
-      for (int f = 0; f < 5 && err == hipSuccess; ++f)
+      for (int f = 0; f < kNumForms && err == hipSuccess; ++f)
         for (int g = 0; g < 2 && err == hipSuccess; ++g)
           for (int t = 0; t < 2 && err == hipSuccess; ++t)
             err = avk::fused_blocks_per_cu((avk::Variant)v, kForms[f].full, kForms[f].split, kForms[f].nr,
@@ -305,7 +309,8 @@ int av_spec_verify(int dtype, int B, int k, int V, int R, const int32_t* row_off
 namespace {
 
 // The fused pass with its launch form chosen by the caller: onchip_limit as
-// av_test_verify_opd_fwd, split 0 = automatic, 1 = whole rows, 2 = split rows.
+// av_test_verify_opd_fwd, split 0 = automatic, 1 = whole rows, 2 = split rows,
+// 3 = split tail (ragged only; half the rows whole, the rest in halves).
 int verify_opd_fwd_impl(int dtype, int B, int k, int V, int R, const int32_t* row_off,
                         const void* zp, const void* zq, const int32_t* draft, const int32_t* bk,
                         float lambda, float tau, float grad_scale, float temperature,
@@ -326,35 +331,28 @@ int verify_opd_fwd_impl(int dtype, int B, int k, int V, int R, const int32_t* ro
   Plan p;
   int rc = plan_rows(dtype, B, k, V, R, row_off, zp, zq, grad_zq, &p);
   if (rc != AV_OK) return rc;
-  if (onchip_limit < 0 || split_mode < 0 || split_mode > 2) return AV_EINVAL;
+  if (onchip_limit < 0 || split_mode < 0 || split_mode > 3) return AV_EINVAL;
   if (p.ragged && B + 1 > 4096) return AV_EUNSUPPORTED;  // offsets are cached in LDS
   if (workspace_bytes < avk::ws_total(B, R)) return AV_EINVAL;
 
   // Split rows: each verified row's halves on two CUs (both halves on chip,
-  // no logit read twice where a whole row would not fit), taken only on
-  // request: the two statistics exchanges per row and the per-row fixed costs
-  // paid twice make it slower than whole rows on every workload measured
-  // (B=128 x 16 rows of 151936, ragged 605 rows of 151936, 64 x 32 rows of
-  // 262144).  The halves meet at a 64-vector boundary (1 KB of bfloat16
-  // logits) near the middle of the row.
+  // no logit read twice where a whole row would not fit).  As the only form
+  // of a launch (split_mode 2, on request only) it is slower than whole rows
+  // on every workload measured (B=128 x 16 rows of 151936, ragged 605 rows of
+  // 151936, 64 x 32 rows of 262144): the two statistics exchanges per row and
+  // the per-row fixed costs are paid twice.  It pays where whole rows would
+  // leave CUs idle: a ragged launch whose rows end in a partial round runs
+  // the full rounds as whole rows and the rest as halves (split 3, chosen
+  // automatically).  The halves meet at a 64-vector boundary (1 KB of
+  // bfloat16 logits) near the middle of the row.
   const bool wide = p.var == avk::kBf16x8 || p.var == avk::kF32x4;
   int pv0 = (((p.nvec + 1) / 2) + 63) & ~63;
   if (pv0 >= p.nvec) pv0 = (p.nvec + 1) / 2;
   const long long part = p.nvec - pv0;  // the smaller half
   const long long slot = avk::kRowBlock;
-  const bool split = wide && p.nvec >= 2 && split_mode == 2;
   const int nl_max = avk::variant_row_lds(p.var);
-  int nr_max = avk::variant_row_regs(p.var);
-  if (split && onchip_limit == 0 && part < (long long)(nr_max + nl_max) * slot &&
-      part >= (long long)(avk::kPairRegs + nl_max) * slot)
-    nr_max = avk::kPairRegs;  // fast form with fewer register slots
-  int nr = nr_max, nl = nl_max;
-  if (onchip_limit > 0) {
-    nr = onchip_limit & 0xff;
-    nl = (onchip_limit >> 8) & 0xff;
-    if (nr > nr_max) nr = nr_max;
-    if (nl > nl_max) nl = nl_max;
-  }
+  const int nr_row = avk::variant_row_regs(p.var);
+  int nr_max = nr_row;
 
   const DeviceInfo* dev = nullptr;
   hipError_t e = device_info(&dev);
@@ -366,21 +364,62 @@ int verify_opd_fwd_impl(int dtype, int B, int k, int V, int R, const int32_t* ro
   size_t lds = 0;
   if (p.ragged) lds = (size_t)(B + 1) * sizeof(int32_t);
   else if (lpt) lds = ((size_t)B * 3 + 3) & ~(size_t)3;
+  if (lds > kMaxDynLds) return AV_EUNSUPPORTED;
+  const bool gb = grad_zq && grad_dtype == AV_BF16;
+  auto occ_of = [&](bool full, int split, int nr) {
+    return dev->occ[p.var][form_index(full, split, nr)][gb ? 1 : 0][tp.tm ? 1 : 0];
+  };
   // The fast form needs every on-chip slot filled (in each half, when split)
   // and the default on-chip split.
-  const long long rowvecs = split ? part : p.nvec;
-  const bool full = onchip_limit == 0 && rowvecs >= (long long)(nr_max + nl_max) * slot;
-  const bool gb = grad_zq && grad_dtype == AV_BF16;
-  const int occ = dev->occ[p.var][form_index(full, split, nr_max)][gb ? 1 : 0][tp.tm ? 1 : 0];
-  if (occ < 1 || lds > kMaxDynLds) return AV_EUNSUPPORTED;
+  const bool row_full = onchip_limit == 0 && p.nvec >= (long long)(nr_row + nl_max) * slot;
+
+  int split = 1, nwhole = 0;
+  if (wide && p.nvec >= 2 && split_mode == 2) {
+    split = 2;
+  } else if (wide && p.nvec >= 2 && p.ragged && split_mode == 3) {
+    split = 3;  // test form: the first half of the rows whole, the rest in halves
+    nwhole = R / 2;
+  } else if (wide && p.ragged && split_mode == 0 && row_full &&
+             part >= (long long)(avk::kPairRegs + nl_max) * slot) {
+    // Split tail: the rows of a last, partial round go in halves when their
+    // halves fill at most one round (otherwise that round would take longer
+    // than the whole rows it replaces).  Only for rows long enough that both
+    // the rows and their halves fill the fast form's on-chip slots: shorter
+    // rows are dominated by per-row fixed costs, which halves pay twice.
+    const long long grid3 = (long long)occ_of(row_full, 3, nr_row) * dev->cus;
+    if (grid3 >= 2) {
+      const long long rem = R % grid3;
+      if (rem > 0 && 2 * rem <= grid3) {
+        split = 3;
+        nwhole = (int)(R - rem);
+      }
+    }
+  }
+  if (split == 2 && onchip_limit == 0 && part < (long long)(nr_max + nl_max) * slot &&
+      part >= (long long)(avk::kPairRegs + nl_max) * slot)
+    nr_max = avk::kPairRegs;  // fast form with fewer register slots
+  int nr = nr_max, nl = nl_max;
+  if (onchip_limit > 0) {
+    nr = onchip_limit & 0xff;
+    nl = (onchip_limit >> 8) & 0xff;
+    if (nr > nr_max) nr = nr_max;
+    if (nl > nl_max) nl = nl_max;
+  }
+  // split 3 in the fast form needs both the rows and their halves full
+  const long long rowvecs = split == 2 ? part : p.nvec;
+  bool full = onchip_limit == 0 && rowvecs >= (long long)(nr_max + nl_max) * slot;
+  if (split == 3 && part < (long long)(avk::kPairRegs + nl_max) * slot) full = false;
+  const int occ = occ_of(full, split, nr_max);
+  if (occ < 1) return AV_EUNSUPPORTED;
   long long grid = (long long)occ * dev->cus;
-  if (split) {
+  if (split == 2) {
     // pairs of co-resident workgroups; no more pairs than rows
     if (grid > 2LL * R) grid = 2LL * R;
     grid &= ~1LL;
     if (grid < 2) return AV_EUNSUPPORTED;
-  } else if (grid > R) {
-    grid = R;
+  } else {
+    const long long items = split == 3 ? 2LL * R - nwhole : (long long)R;
+    if (grid > items) grid = items;
   }
 
   char* ws = (char*)workspace;
@@ -416,8 +455,9 @@ int verify_opd_fwd_impl(int dtype, int B, int k, int V, int R, const int32_t* ro
   a.nl = nl;
   a.ragged = p.ragged ? 1 : 0;
   a.lpt = lpt ? 1 : 0;
-  a.split = split ? 2 : 1;
-  a.pv0 = split ? pv0 : 0;
+  a.split = split;
+  a.pv0 = split > 1 ? pv0 : 0;
+  a.nwhole = nwhole;
   a.gbf16 = gb ? 1 : 0;
   a.tm = tp.tm ? 1 : 0;
   a.lam = lambda;

@@ -96,8 +96,11 @@ struct FwdArgs {
   int nr, nl;    // vectors per thread held in registers / in LDS
   int ragged;
   int lpt;       // dense layout, rows handed out longest first (unverified rows in halves)
-  int split;     // 2: rows in halves on workgroup pairs (2p, 2p+1), each half kept on chip
-  int pv0;       // split: first vector of the second half
+  int split;     // 1: whole rows; 2: rows in halves on workgroup pairs (2p, 2p+1), each
+                 // half kept on chip; 3: rows 0 .. nwhole-1 whole, the rest in halves
+                 // (ragged layout), all claimed from the dispenser
+  int pv0;       // split 2 and 3: first vector of the second half
+  int nwhole;    // split 3: rows taken whole
   int gbf16;     // gradient stored as bfloat16
   float lam, tau, gs;
   // temperature of the reverse-KL term
@@ -176,8 +179,10 @@ constexpr int kSpecChunkVecs = 512;
 // and the default on-chip split is used.
 // a.tm selects the tempered form of the kernels (fused and backward).
 // nr: register slots of the build (kRowRegs16, or kPairRegs for split rows).
+// a.split (1, 2 or 3) selects whole rows, split rows or whole rows with a
+// split tail.
 hipError_t launch_fused(Variant v, bool full, int nr, const FwdArgs& a, int grid, size_t lds, hipStream_t s);
-hipError_t fused_blocks_per_cu(Variant v, bool full, bool split, int nr, bool gbf16, bool tm, size_t lds, int* out);
+hipError_t fused_blocks_per_cu(Variant v, bool full, int split, int nr, bool gbf16, bool tm, size_t lds, int* out);
 hipError_t launch_bwd(Variant v, const BwdArgs& a, hipStream_t s);
 hipError_t launch_head(const HeadArgs& a, hipStream_t s);
 hipError_t launch_head_update(const HeadUpdArgs& a, hipStream_t s);

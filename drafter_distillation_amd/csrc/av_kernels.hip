@@ -1779,6 +1779,14 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
 // takes half h of each (unverified rows as the two halves of their argmax
 // scan).  Both halves of a verified row are therefore in progress together,
 // and a half only waits for its partner, which works through the same list.
+// SP = 3: a split tail (ragged layout, every row verified).  Items 0 ..
+// nwhole-1 are whole rows; then each remaining row is two consecutive items,
+// its halves.  Items are claimed from the dispenser in order, and every
+// workgroup of the launch is resident, so the partner of a claimed half is
+// either claimed already (and in progress) or the next item that any
+// workgroup claims when it finishes its current one: no half waits on a
+// half that cannot start.  The halves use kPairRegs register slots in the
+// fast form (FULL), the row's slot counts otherwise.
 template <int VAR, bool FULL, bool GB, bool TM, int NRT, int SP>
 __global__ __launch_bounds__(kRowBlock) void fused_kernel(FwdArgs a) {
   using S = typename Tr<VAR>::S;
@@ -1849,7 +1857,8 @@ __global__ __launch_bounds__(kRowBlock) void fused_kernel(FwdArgs a) {
   // counted twice (two halves each) unless rows are split (a pair takes both
   // halves of each of its rows).
   const uint32_t nitems =
-      (uint32_t)a.R + (SP == 1 && a.lpt ? (uint32_t)(a.R - sm.cum[a.k]) : 0u);
+      SP == 3 ? (uint32_t)(2 * a.R - a.nwhole)
+              : (uint32_t)a.R + (SP == 1 && a.lpt ? (uint32_t)(a.R - sm.cum[a.k]) : 0u);
   const int ph = SP == 2 ? (int)(blockIdx.x & 1u) : 0;
   const uint32_t pair = blockIdx.x >> 1, npairs = gridDim.x >> 1;
   for (int iter = 0;; ++iter) {
@@ -1863,9 +1872,17 @@ __global__ __launch_bounds__(kRowBlock) void fused_kernel(FwdArgs a) {
       __syncthreads();
       continue;
     }
+    if constexpr (SP == 3) {
+      const int h = (int)idx - a.nwhole;
+      if (h >= 0) {
+        const Item it = map_item(a, sm, s_off, order, key, a.nwhole + (h >> 1), false);
+        verified_row<VAR, FULL, GB, TM, FULL ? kPairRegs : NRT, 2>(a, sm, lp, lq, it, par, tag, h & 1);
+        continue;
+      }
+    }
     Item it = map_item(a, sm, s_off, order, key, (int)idx, SP == 2);
     if (SP == 2 && !it.verified) it.half = ph;
-    if (it.verified) verified_row<VAR, FULL, GB, TM, NRT, SP>(a, sm, lp, lq, it, par, tag, ph);
+    if (it.verified) verified_row<VAR, FULL, GB, TM, NRT, SP == 3 ? 1 : SP>(a, sm, lp, lq, it, par, tag, ph);
     else unverified_row<VAR, GB>(a, sm, it.row, par, it.half, tag);
   }
   // The workgroup that leaves last sums the request losses, reports the
@@ -2577,10 +2594,12 @@ __global__ __launch_bounds__(kBlock) void zero_kernel(uint64_t* p, size_t n) {
 
 // The kernel forms built: whole rows (every variant, general or fast form);
 // split rows for the 16-byte variants, in the general form or in the fast
-// form with kRowRegs16 or kPairRegs register slots.
-enum Form { kWholeGeneral, kWholeFast, kSplitGeneral, kSplitFast, kSplitFastPair };
-inline Form form_of(bool full, bool split, int nr) {
-  if (!split) return full ? kWholeFast : kWholeGeneral;
+// form with kRowRegs16 or kPairRegs register slots; whole rows with a split
+// tail for the 16-byte variants, general or fast.
+enum Form { kWholeGeneral, kWholeFast, kSplitGeneral, kSplitFast, kSplitFastPair, kTailGeneral, kTailFast };
+inline Form form_of(bool full, int split, int nr) {
+  if (split == 3) return full ? kTailFast : kTailGeneral;
+  if (split != 2) return full ? kWholeFast : kWholeGeneral;
   if (!full) return kSplitGeneral;
   return nr == kPairRegs ? kSplitFastPair : kSplitFast;
 }
@@ -2597,6 +2616,8 @@ const void* kernel_of(Form f) {
       case kSplitGeneral: return (const void*)fused_kernel<VAR, false, GB, TM, kRowRegs16, 2>;
       case kSplitFast: return (const void*)fused_kernel<VAR, true, GB, TM, kRowRegs16, 2>;
       case kSplitFastPair: return (const void*)fused_kernel<VAR, true, GB, TM, kPairRegs, 2>;
+      case kTailGeneral: return (const void*)fused_kernel<VAR, false, GB, TM, RowCfg<VAR>::NR, 3>;
+      case kTailFast: return (const void*)fused_kernel<VAR, true, GB, TM, RowCfg<VAR>::NR, 3>;
       default: break;
     }
   }
@@ -2630,14 +2651,14 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fused(Variant v, bool full, int nr, const FwdArgs& a, int grid, size_t lds, hipStream_t s) {
-  const void* k = fused_kernel_ptr(v, form_of(full, a.split == 2, nr), a.gbf16 != 0, a.tm != 0);
+  const void* k = fused_kernel_ptr(v, form_of(full, a.split, nr), a.gbf16 != 0, a.tm != 0);
   if (!k) return hipErrorInvalidDeviceFunction;
   FwdArgs arg = a;
   void* params[] = {&arg};
   return hipLaunchKernel(k, dim3(grid), dim3(kRowBlock), params, lds, s);
 }
 
-hipError_t fused_blocks_per_cu(Variant v, bool full, bool split, int nr, bool gb, bool tm, size_t lds, int* out) {
+hipError_t fused_blocks_per_cu(Variant v, bool full, int split, int nr, bool gb, bool tm, size_t lds, int* out) {
   const void* k = fused_kernel_ptr(v, form_of(full, split, nr), gb, tm);
   if (!k) {
     *out = 0;

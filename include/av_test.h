@@ -23,17 +23,22 @@ extern "C" {
  *                 pass keeps in registers and in LDS (each clamped to what
  *                 the build provides); the rest is read from HBM a second
  *                 time for the gradient.
- *   split_rows    0 = automatic (whole rows), 1 = whole rows, 2 = rows
- *                 split into halves on workgroup pairs: workgroups 2p and
- *                 2p+1 take the two halves of the same rows in a fixed order
- *                 and hand each other their first-sweep statistics and clip
- *                 corrections through the workspace (16-byte vector variants
- *                 only, V >= 2 vectors; ignored otherwise).  Both workgroups
- *                 of a pair are resident for the whole launch, so a half waits
- *                 only for its partner (bounded: AV_DEV_TIMEOUT if the device
- *                 is shared so heavily that a partner never runs).
+ *   split_rows    0 = automatic (as av_verify_opd_fwd), 1 = whole rows,
+ *                 2 = rows split into halves on workgroup pairs: workgroups
+ *                 2p and 2p+1 take the two halves of the same rows in a fixed
+ *                 order and hand each other their first-sweep statistics and
+ *                 clip corrections through the workspace (16-byte vector
+ *                 variants only, V >= 2 vectors; ignored otherwise).  Both
+ *                 workgroups of a pair are resident for the whole launch, so
+ *                 a half waits only for its partner (bounded: AV_DEV_TIMEOUT
+ *                 if the device is shared so heavily that a partner never
+ *                 runs).  3 = split tail, the form av_verify_opd_fwd picks
+ *                 for a ragged launch whose last round of rows is partial:
+ *                 here rows 0 .. R/2 - 1 whole and the rest as pairs of
+ *                 halves, all claimed from the work dispenser (ragged layout
+ *                 and 16-byte vector variants only; ignored otherwise).
  * Errors: as av_verify_opd_fwd; AV_EINVAL also for a negative onchip_limit
- * or a split_rows outside 0..2.
+ * or a split_rows outside 0..3.
  */
 int av_test_verify_opd_fwd(int dtype, int B, int k, int V, int R,
                            const int32_t* row_off, const void* zp, const void* zq,

@@ -215,6 +215,34 @@ def test_split_rows_ragged_and_ties(av, split):
     assert list(out["tgt_argmax"][:4]) == [cut - 1, 5, cut, 0]
 
 
+@pytest.mark.parametrize("dtype,V,vecs", [("bf16", 9000, 0), ("bf16", 5000, 1 | (1 << 8)), ("f32", 3001, 0),
+                                          ("f32", 4000, 2 | (1 << 8)), ("bf16", 151936, 0),
+                                          ("f32", 73728 + 4 * 100, 0)])
+def test_split_tail_forced(av, dtype, V, vecs):
+    """Split tail forced (half the rows whole, the rest as pairs of halves
+    claimed from the dispenser): small widths in the general form, and the
+    widths whose halves fill the fast form's slots."""
+    w = synth.make("ragged", B=7, V=V, dtype=dtype)
+    out = full_parity(av, w, None, 0.5, 0.1, gs=1.0 / w.R, vecs=vecs, split=3)
+    whole = run_fwd(av, gpu_inputs(w), w, bk=None, lam=0.5, tau=0.1, gs=1.0 / w.R, vecs=vecs, split=1)
+    assert np.array_equal(whole["tgt_argmax"], out["tgt_argmax"])
+    assert np.array_equal(whole["acc_len"], out["acc_len"])
+
+
+def test_split_tail_ties_across_halves(av):
+    # exact bf16 ties in tail rows, across the two halves: the first index wins
+    w = synth.make("ragged", B=4, V=12000, dtype="bf16")
+    zp = w.zp.copy()
+    big = synth.to_bf16_bits(np.array([40.0]))[0]
+    cut = 768 * 8  # first entry of the second half
+    last = w.R - 1  # a row of the split tail (rows R/2 .. R-1)
+    zp[last, cut - 1] = big
+    zp[last, cut] = big
+    w.zp = zp
+    out = full_parity(av, w, None, 0.5, 0.1, split=3)
+    assert out["tgt_argmax"][last] == cut - 1
+
+
 @pytest.mark.parametrize("lam", [0.0, 0.5, 1.0])
 @pytest.mark.parametrize("tau", [0.01, 0.05, 0.1, 1e9, float("inf")])
 def test_lambda_tau_branches(av, lam, tau):
