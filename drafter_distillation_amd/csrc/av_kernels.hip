@@ -482,7 +482,7 @@ struct RowAcc {
   float kq;      // sum exp(zq - mq) (zq - zp): the reverse KL, once normalised
   float sq1;     // tempered form: sum exp(zq - mq) at temperature 1 (the sums
                  // above then scale exponents by 1 / T; kq's difference does not)
-  float rp;      // temperature 1: reference of sp (sp = sum exp(zp - rp)), see kLazyGap
+  float rp;      // reference of sp (sp = sum exp((zp - rp) / T)), see kLazyGap
   float mq_on, mq_st;  // per region (on chip / streamed): max zq
   float pm_on, pm_st;  // per region: max exp(zq - mq) |zq - zp| (mq: running max)
 };
@@ -518,7 +518,8 @@ __device__ __forceinline__ int entry_index(int lo, int H, int e) {
 // scale every term of the thread by that error).
 template <int VAR, bool TM>
 __device__ __forceinline__ void acc_vec(const typename Tr<VAR>::S& xp, const typename Tr<VAR>::S& xq,
-                                        int lo, int H, RowAcc& A, bool onchip, float sL) {
+                                        int lo, int H, RowAcc& A, bool onchip, float sL,
+                                        float gp = kLazyGap, float gq = kLazyGap) {
   using T = Tr<VAR>;
   constexpr int VEC = T::VEC;
   const float L = TM ? sL : kLog2e;
@@ -582,24 +583,30 @@ __device__ __forceinline__ void acc_vec(const typename Tr<VAR>::S& xp, const typ
     }
     return;
   }
-  A.sp *= __builtin_amdgcn_exp2f((A.mp - np) * L);
+  // Tempered: the same lazy references, with gaps in logit units: gp keeps
+  // every term of sp and sq below exp(kLazyGap) (gp = kLazyGap T), gq also
+  // those of sq1, whose exponents are not scaled (gq = min(gp, kLazyGap)).
   A.mp = np;
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) A.sp += __builtin_amdgcn_exp2f((T::at(xp, e) - np) * L);
-  const float nq = fmaxf(A.mq, vq);
-  const float sc = __builtin_amdgcn_exp2f((A.mq - nq) * L);
-  A.sq *= sc;
-  A.kq *= sc;
-  A.sq1 *= __builtin_amdgcn_exp2f((A.mq - nq) * kLog2e);
-  const float scb = fmaxf(sc, kRescaleFloor);
-  A.pm_on *= scb;
-  A.pm_st *= scb;
-  A.mq = nq;
+  if (__builtin_expect(__any(vp > A.rp + gp || vq > A.mq + gq), 0)) {
+    A.sp *= __builtin_amdgcn_exp2f((A.rp - np) * L);
+    A.rp = np;
+    const float nq = fmaxf(A.mq, vq);
+    const float sc = __builtin_amdgcn_exp2f((A.mq - nq) * L);
+    A.sq *= sc;
+    A.kq *= sc;
+    A.sq1 *= __builtin_amdgcn_exp2f((A.mq - nq) * kLog2e);
+    const float scb = fmaxf(sc, kRescaleFloor);
+    A.pm_on *= scb;
+    A.pm_st *= scb;
+    A.mq = nq;
+  }
+  const float rp = A.rp, rq = A.mq;
   float pm = 0.0f;
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
     const float q = T::at(xq, e), p = T::at(xp, e);
-    const float dq = q - nq;
+    A.sp += __builtin_amdgcn_exp2f((p - rp) * L);
+    const float dq = q - rq;
     const float eq = __builtin_amdgcn_exp2f(dq * L);
     A.sq1 += __builtin_amdgcn_exp2f(dq * kLog2e);
     const float d = q - p;
@@ -629,35 +636,15 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float& k, float om
   k = k * fa + ok * fb;
 }
 
-// One butterfly step over the row statistics (not the per-thread bounds).
+// A wave's row statistics combined by one pass of maxima, one rescale of each
+// lane's sums and one pass of sums (instead of a log-sum-exp merge at each
+// butterfly level).  On entry sp is relative to mp; on exit every lane holds
+// the same bits: the wave's max of zp, its first index and the zq there, the
+// sums relative to the wave's maxima, and kq.  Lanes with empty sums
+// contribute nothing.  TM: sp, sq and kq scale exponents by L = log2(e) / T,
+// sq1 (temperature 1) does not.
 template <bool TM>
-__device__ __forceinline__ void merge_step(RowAcc& A, int o, float sL) {
-  const float L = TM ? sL : kLog2e;
-  const float omp = __shfl_xor(A.mp, o), osp = __shfl_xor(A.sp, o);
-  const int obi = __shfl_xor(A.bi, o);
-  const float oza = __shfl_xor(A.za, o);
-  const float omq = __shfl_xor(A.mq, o), osq = __shfl_xor(A.sq, o), okq = __shfl_xor(A.kq, o);
-  if (omp > A.mp || (omp == A.mp && obi < A.bi)) {
-    A.bi = obi;
-    A.za = oza;
-  }
-  if constexpr (TM) {  // before mq moves: same maxima, unscaled exponents
-    const float osq1 = __shfl_xor(A.sq1, o);
-    float m1 = A.mq, dummy = 0.0f;
-    lse_merge(m1, A.sq1, dummy, omq, osq1, 0.0f);
-  }
-  float dummy = 0.0f;
-  lse_merge(A.mp, A.sp, dummy, omp, osp, 0.0f, L);
-  lse_merge(A.mq, A.sq, A.kq, omq, osq, okq, L);
-}
-
-// Temperature 1: a wave's row statistics combined by one pass of maxima, one
-// rescale of each lane's sums and one pass of sums (instead of a log-sum-exp
-// merge at each butterfly level).  On entry sp is relative to mp; on exit
-// every lane holds the same bits: the wave's max of zp, its first index and
-// the zq there, the sums relative to the wave's maxima, and kq.  Lanes with
-// empty sums contribute nothing.
-__device__ __forceinline__ void wave_combine(RowAcc& W) {
+__device__ __forceinline__ void wave_combine(RowAcc& W, float L = kLog2e) {
   const float M = wmax(W.mp);
   int bi = (W.mp == M) ? W.bi : INT_MAX;
   float za = W.za;
@@ -670,9 +657,13 @@ __device__ __forceinline__ void wave_combine(RowAcc& W) {
       za = oza;
     }
   }
-  const float sp = (W.sp == 0.0f) ? 0.0f : W.sp * __builtin_amdgcn_exp2f((W.mp - M) * kLog2e);
+  const float sp = (W.sp == 0.0f) ? 0.0f : W.sp * __builtin_amdgcn_exp2f((W.mp - M) * L);
   const float Mq = wmax(W.mq);
-  const float f = (W.sq == 0.0f) ? 0.0f : __builtin_amdgcn_exp2f((W.mq - Mq) * kLog2e);
+  const float f = (W.sq == 0.0f) ? 0.0f : __builtin_amdgcn_exp2f((W.mq - Mq) * L);
+  if constexpr (TM) {
+    const float f1 = (W.sq1 == 0.0f) ? 0.0f : __builtin_amdgcn_exp2f((W.mq - Mq) * kLog2e);
+    W.sq1 = wsum(W.sq1 * f1);
+  }
   W.sp = wsum(sp);
   W.sq = wsum(W.sq * f);
   W.kq = wsum(W.kq * f);
@@ -1359,6 +1350,9 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   const bool tail = nfull >= von;      // the partial slot nfull (if any) is streamed
   const float tau = opaque_s(a.tau);
   const float sL = TM ? opaque_s(a.inv_tl) : kLog2e;
+  // lazy-rescale gaps of the tempered sums (see acc_vec): T kLazyGap, and at
+  // most kLazyGap for the unscaled sum
+  const float gp = TM ? kLazyGap * kLog2e / sL : kLazyGap, gq = fminf(gp, kLazyGap);
 
   // ---- sweep 1: read the row once; keep its on-chip slots, fold every
   // vector into the running statistics.  Fast form: the register slots and
@@ -1450,13 +1444,13 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
           if (io.has(nfullv)) {  // always: keeps one branch per register slot, as in the other forms
             rp[e] = io.lds(lp[2 * h + j], 64);
             rq[e] = io.lds(lq[2 * h + j], 64);
-            acc_vec<VAR, TM>(rp[e], rq[e], io.lo(e), io.H(64), A, true, sL);
+            acc_vec<VAR, TM>(rp[e], rq[e], io.lo(e), io.H(64), A, true, sL, gp, gq);
           }
         } else if (e < NR + nst) {
           const int sl = slot_of(e), nbv = io.nb(sl, nvec);
           if (io.has(nbv))
             acc_vec<VAR, TM>(io.lds(lp[2 * h + j], nbv), io.lds(lq[2 * h + j], nbv), io.lo(sl), io.H(nbv), A,
-                             false, sL);
+                             false, sL, gp, gq);
         }
       }
       wait_lds_reads();  // this half is free again
@@ -1472,7 +1466,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
           const int sl = slot_of(e), nbv = io.nb(sl, nvec);
           if (io.has(nbv))
             acc_vec<VAR, TM>(io.lds(lp[2 * h + j], nbv), io.lds(lq[2 * h + j], nbv), io.lo(sl), io.H(nbv), A,
-                             false, sL);
+                             false, sL, gp, gq);
         }
       }
       wait_lds_reads();
@@ -1486,13 +1480,13 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
 #pragma unroll AV_SU
     for (int s = von; s < nfull; ++s) {
       const S xp = io.template load<kAuxFirst>(rzp, s, 64), xq = io.template load<kAuxFirst>(rzq, s, 64);
-      acc_vec<VAR, TM>(xp, xq, io.lo(s), io.H(64), A, false, sL);
+      acc_vec<VAR, TM>(xp, xq, io.lo(s), io.H(64), A, false, sL, gp, gq);
     }
     if (tail) {
       const int nbv = io.nb(nfull, nvec);
       if (io.has(nbv)) {
         const S xp = io.template load<kAuxFirst>(rzp, nfull, nbv), xq = io.template load<kAuxFirst>(rzq, nfull, nbv);
-        acc_vec<VAR, TM>(xp, xq, io.lo(nfull), io.H(nbv), A, false, sL);
+        acc_vec<VAR, TM>(xp, xq, io.lo(nfull), io.H(nbv), A, false, sL, gp, gq);
       }
     }
   }
@@ -1504,7 +1498,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
     for (int v = 0; v < NR; ++v) {
       const int nbv = io.nb(v, nvec);
       if (v < nr && io.has(nbv))
-        acc_vec<VAR, TM>(rp[v], rq[v], io.lo(v), io.H(nbv), A, true, sL);
+        acc_vec<VAR, TM>(rp[v], rq[v], io.lo(v), io.H(nbv), A, true, sL, gp, gq);
     }
   }
   if constexpr (NL > 0) {
@@ -1514,20 +1508,18 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
     for (int l = 0; l < NL; ++l) {
       const int sl = nr + l, nbv = io.nb(sl, nvec);
       if (l < nl && io.has(nbv))
-        acc_vec<VAR, TM>(io.lds(lp[l], nbv), io.lds(lq[l], nbv), io.lo(sl), io.H(nbv), A, true, sL);
+        acc_vec<VAR, TM>(io.lds(lp[l], nbv), io.lds(lq[l], nbv), io.lo(sl), io.H(nbv), A, true, sL, gp, gq);
     }
   }
 
   // ---- combine the statistics of the 1024 threads: wave butterflies, then
   // every wave merges the 16 wave partials the same way ----
   RowAcc W = A;
-  if constexpr (!TM) {  // the merges take the zp sum relative to the running max
-    W.sp = (W.sp == 0.0f) ? 0.0f : W.sp * __builtin_amdgcn_exp2f((W.rp - W.mp) * kLog2e);
+  {  // the combine takes the zp sum relative to the running max
+    const float L = TM ? sL : kLog2e;
+    W.sp = (W.sp == 0.0f) ? 0.0f : W.sp * __builtin_amdgcn_exp2f((W.rp - W.mp) * L);
     W.rp = W.mp;
-    wave_combine(W);
-  } else {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) merge_step<TM>(W, o, sL);
+    wave_combine<TM>(W, L);
   }
   if (lane == 0) {
     sm.f[par][wid][0] = W.mp;
@@ -1552,12 +1544,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
     if constexpr (TM) W.sq1 = sm.f1[par][lane];
     W.bi = sm.i[par][lane];
   }
-  if constexpr (TM) {
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) merge_step<TM>(W, o, sL);
-  } else {
-    wave_combine(W);
-  }
+  wave_combine<TM>(W, TM ? sL : kLog2e);
   XRec xr{__shfl(W.mp, 0), __shfl(W.sp, 0), __shfl(W.mq, 0), __shfl(W.sq, 0), __shfl(W.kq, 0),
            __shfl(W.za, 0), TM ? __shfl(W.sq1, 0) : 0.0f, __shfl(W.bi, 0)};
   if constexpr (SP == 2) xr = xchange_stats<TM>(a, xr, row, ph, tag, sL);
