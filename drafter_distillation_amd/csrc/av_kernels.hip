@@ -381,24 +381,25 @@ __device__ __forceinline__ RowK row_consts(float lse_p, float lse_q, float tau, 
   k.sL = TM ? sL : kLog2e;
   return k;
 }
-// q_j = exp(s zq_j - lse_q); r_j = q_j (log q_j - log p_j), with the
-// log-ratio formed from the logits, s (zq_j - zp_j) - (lse_q - lse_p);
-// g_j = c_j (r_j + q_j) = c_j q_j (ell_j + 1).
+// q_j = exp(s zq_j - lse_q); r_j = q_j ell_j = q_j (log q_j - log p_j), with
+// the log-ratio ell_j formed from the logits, s (zq_j - zp_j) - (lse_q - lse_p).
 template <bool TM>
-__device__ __forceinline__ void opd_entry(float zp, float zq, const RowK& k, float& q, float& r,
-                                          float& g) {
+__device__ __forceinline__ void opd_entry(float zp, float zq, const RowK& k, float& q, float& ell,
+                                          float& r) {
   q = __builtin_amdgcn_exp2f(__builtin_fmaf(zq, TM ? k.sL : kLog2e, -k.lseqL));
-  const float ell = TM ? __builtin_fmaf(k.s, zq - zp, -k.delta) : (zq - zp) - k.delta;
+  ell = TM ? __builtin_fmaf(k.s, zq - zp, -k.delta) : (zq - zp) - k.delta;
   r = q * ell;
-  g = (__builtin_fabsf(r) <= k.tau) ? (r + q) : 0.0f;
 }
 
 // d loss / d zq_j = gs [lam (q1_j - [j = a]) + (1 - lam) s (g_j - S q_j)]
-// (q1 = softmax(zq); at T = 1, q1 = q and s = 1):
-//   T = 1:  A q_j + Bc g_j - [j = a] gs lam,  A = gs (lam - (1 - lam) S)
-//   TM:     C1 q1_j + A q_j + Bc g_j - [j = a] gs lam,  A = -gs (1 - lam) s S
+// (q1 = softmax(zq); at T = 1, q1 = q and s = 1) with g_j = q_j (ell_j + 1)
+// where |r_j| <= tau and 0 elsewhere, formed as
+//   T = 1:  q_j t_j - [j = a] gs lam,
+//   TM:     C1 q1_j + q_j t_j - [j = a] gs lam,
+//   t_j = A + B + B ell_j where |r_j| <= tau, A elsewhere,
+//   A = gs (lam - (1 - lam) S) (T = 1) or -gs (1 - lam) s S (TM), B = gs (1 - lam) s.
 struct GradK {
-  float a, b, fix, c1, l1L;
+  float a, ab, b, fix, c1, l1L;
 };
 template <bool TM>
 __device__ __forceinline__ GradK grad_consts(float lam, float gs, float S, float s, float lse1) {
@@ -414,15 +415,16 @@ __device__ __forceinline__ GradK grad_consts(float lam, float gs, float S, float
     g.c1 = 0.0f;
     g.l1L = 0.0f;
   }
+  g.ab = g.a + g.b;
   g.fix = gs * lam;
   return g;
 }
 template <bool TM>
-__device__ __forceinline__ float grad_entry(float q, float g, float zq, const GradK& c) {
-  const float kl = __builtin_fmaf(c.a, q, c.b * g);
+__device__ __forceinline__ float grad_entry(float q, float ell, float r, float zq, float tau, const GradK& c) {
+  const float t = (__builtin_fabsf(r) <= tau) ? __builtin_fmaf(c.b, ell, c.ab) : c.a;
   if constexpr (TM)
-    return __builtin_fmaf(c.c1, __builtin_amdgcn_exp2f(__builtin_fmaf(zq, kLog2e, -c.l1L)), kl);
-  return kl;
+    return __builtin_fmaf(c.c1, __builtin_amdgcn_exp2f(__builtin_fmaf(zq, kLog2e, -c.l1L)), q * t);
+  return q * t;
 }
 
 // ---------------------------------------------------------------------------
@@ -1103,9 +1105,9 @@ __device__ __forceinline__ void grad_vec(const typename Tr<VAR>::S& xp, const ty
   float out[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
-    float q, r, gg;
-    opd_entry<TM>(T::at(xp, e), T::at(xq, e), rk, q, r, gg);
-    out[e] = grad_entry<TM>(q, gg, T::at(xq, e), gk);
+    float q, ell, r;
+    opd_entry<TM>(T::at(xp, e), T::at(xq, e), rk, q, ell, r);
+    out[e] = grad_entry<TM>(q, ell, r, T::at(xq, e), rk.tau, gk);
   }
   const int lo = io.lo(s);
   int el = -1;  // entry that holds the label, if any
@@ -1140,10 +1142,9 @@ __device__ __forceinline__ void clip_vec(const typename Tr<VAR>::S& xp, const ty
 #pragma unroll
   for (int e = 0; e < T::VEC; ++e) {
     const float zp = T::at(xp, e), zq = T::at(xq, e);
-    float q, r, g;
-    opd_entry<TM>(zp, zq, rk, q, r, g);
+    float q, ell, r;
+    opd_entry<TM>(zp, zq, rk, q, ell, r);
     const float qf = __builtin_amdgcn_exp2f(__builtin_fmaf(zq - fk.mq, rk.sL, -fk.l2s));
-    const float ell = TM ? __builtin_fmaf(rk.s, zq - zp, -rk.delta) : (zq - zp) - rk.delta;
     const float rf = qf * ell;
     cs += (__builtin_fabsf(r) <= rk.tau) ? 0.0f : rf + qf;
     ck += rf - __builtin_amdgcn_fmed3f(rf, -rk.tau, rk.tau);
@@ -1991,9 +1992,9 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(BwdArgs a) {
         float out[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          float q, r, g;
-          opd_entry<TM>(T::at(xp[v], e), T::at(xq[v], e), rk, q, r, g);
-          out[e] = grad_entry<TM>(q, g, T::at(xq[v], e), gk);
+          float q, ell, r;
+          opd_entry<TM>(T::at(xp[v], e), T::at(xq[v], e), rk, q, ell, r);
+          out[e] = grad_entry<TM>(q, ell, r, T::at(xq[v], e), rk.tau, gk);
           if ((e < 4 ? e0 + e : e1 + (e - 4)) == (long long)A) out[e] = out[e] - gk.fix;
         }
         if constexpr (GB) {
@@ -2024,9 +2025,9 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(BwdArgs a) {
       float out[VEC];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        float q, r, g;
-        opd_entry<TM>(T::at(xp[v], e), T::at(xq[v], e), rk, q, r, g);
-        out[e] = grad_entry<TM>(q, g, T::at(xq[v], e), gk);
+        float q, ell, r;
+        opd_entry<TM>(T::at(xp[v], e), T::at(xq[v], e), rk, q, ell, r);
+        out[e] = grad_entry<TM>(q, ell, r, T::at(xq[v], e), rk.tau, gk);
         if (vi * VEC + e == A) out[e] = out[e] - gk.fix;
       }
       if constexpr (GB) store_vec_bf16<VEC>(gb_r, (unsigned)vi, out);
