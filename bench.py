@@ -54,10 +54,15 @@ KERNEL_SRC_DIR = os.path.join(ROOT, "drafter_distillation_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_concurrent_traffic.json")
 
 
+# Sources of the fused kernel and its launch (the LM-head GEMMs are not part of it).
+FUSED_SOURCES = ("av_api.hip", "av_internal.h", "av_kernels.hip")
+
+
 def kernel_sha() -> str:
-    """Hash of the kernel and launch sources: counter readings are stale once it changes."""
+    """Hash of the fused kernel's and its launch's sources: counter readings
+    are stale once it changes."""
     hsh = hashlib.sha256()
-    for name in sorted(os.listdir(KERNEL_SRC_DIR)):
+    for name in FUSED_SOURCES:
         with open(os.path.join(KERNEL_SRC_DIR, name), "rb") as f:
             hsh.update(name.encode() + b"\0" + f.read())
     return hsh.hexdigest()[:16]
