@@ -173,14 +173,23 @@ def _oracle_request(b: int) -> float:
 
     j = _ORACLE_JOB
     w, k = j["w"], j["w"].k
+
+    def decode(a):
+        return oracle.bf16_bits_to_f64(a) if w.dtype == "bf16" else a.astype(np.float64)
+
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        rows = slice(b * k, (b + 1) * k)
-        zp = oracle.bf16_bits_to_f64(w.zp[rows])
-        zq = oracle.bf16_bits_to_f64(w.zq[rows])
-        oracle.length_head(w.h[b:b + 1], w.w, w.bias, w.gamma, k)
-        oracle.verify_opd(zp, zq, w.draft[rows], k=k, lam=w.lam, tau=w.tau, grad_scale=1.0,
-                          bk=j["bk"][b:b + 1], temperature=j["temperature"])
+        if w.row_off is not None:  # ragged: the request's verified rows only, no length head
+            r0, r1 = int(w.row_off[b]), int(w.row_off[b + 1])
+            oracle.verify_opd(decode(w.zp[r0:r1]), decode(w.zq[r0:r1]), w.draft[r0:r1], k=k, lam=w.lam,
+                              tau=w.tau, grad_scale=1.0, row_off=np.array([0, r1 - r0]),
+                              temperature=j["temperature"])
+        else:
+            rows = slice(b * k, (b + 1) * k)
+            zp, zq = decode(w.zp[rows]), decode(w.zq[rows])
+            oracle.length_head(w.h[b:b + 1], w.w, w.bias, w.gamma, k)
+            oracle.verify_opd(zp, zq, w.draft[rows], k=k, lam=w.lam, tau=w.tau, grad_scale=1.0,
+                              bk=j["bk"][b:b + 1], temperature=j["temperature"])
         return time.perf_counter() - t0
 
 
@@ -197,7 +206,10 @@ def cpu_baseline(w, single_requests: int = 16, temperature: float = 1.0):
 
     import oracle
 
-    _, bk, _ = oracle.length_head(w.h, w.w, w.bias, w.gamma, w.k)
+    if w.row_off is None:
+        _, bk, _ = oracle.length_head(w.h, w.w, w.bias, w.gamma, w.k)
+    else:
+        bk = np.diff(w.row_off)
     cores = max(1, min(MAX_ORACLE_CORES, len(os.sched_getaffinity(0))))
     _ORACLE_JOB.update(w=w, bk=bk, temperature=temperature)
     try:
@@ -212,10 +224,12 @@ def cpu_baseline(w, single_requests: int = 16, temperature: float = 1.0):
     finally:
         _ORACLE_JOB.clear()
     Rv = int(np.clip(bk, 1, w.k).sum())
-    fused, head = algorithmic_bytes(w.B, w.k, w.V, w.H, w.R, Rv, lse1=temperature != 1.0)
+    ragged = w.row_off is not None
+    H = 0 if ragged else w.H  # the ragged workload runs no length head
+    fused, head = algorithmic_bytes(w.B, w.k, w.V, H, w.R, Rv, lse1=temperature != 1.0)
     bk1 = np.clip(bk[:single_requests], 1, w.k)
-    f1, h1 = algorithmic_bytes(single_requests, w.k, w.V, w.H, single_requests * w.k, int(bk1.sum()),
-                               lse1=temperature != 1.0)
+    r1 = int(bk1.sum()) if ragged else single_requests * w.k
+    f1, h1 = algorithmic_bytes(single_requests, w.k, w.V, H, r1, int(bk1.sum()), lse1=temperature != 1.0)
     return {
         "value": round((fused + head) / dt / 1e9, 4),
         "unit": "GB/s",
@@ -677,11 +691,14 @@ def bench_fused_other(args):
     import drafter_distillation_amd as dd
     import synth
 
+    name = "long" if args.workload == "long_sweep" else args.workload
+    w = synth.make(name, seed=args.seed)
+    # the oracle baseline runs first, in worker processes forked before this
+    # process touches the GPU
+    cpu_line = None if args.no_cpu_baseline else cpu_baseline(w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     dd.lib()
-    name = "long" if args.workload == "long_sweep" else args.workload
-    w = synth.make(name, seed=args.seed)
     B, k, V, R = w.B, w.k, w.V, w.R
     zp = torch.from_numpy(w.zp.view(np.int16)).view(torch.bfloat16).to(dev)
     zq = torch.from_numpy(w.zq.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -755,6 +772,8 @@ def bench_fused_other(args):
             "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
         }
+        if cpu_line is not None and (lam, tau) == (w.lam, w.tau):
+            line["cpu_baseline"] = cpu_line
         print(json.dumps(line), flush=True)
 
 
