@@ -690,8 +690,14 @@ __device__ __forceinline__ uint64_t claim(const FwdArgs& a) {
 
 // Counts one more completed row of a request; returns the new count.  The
 // counter word is {tag, count}: a word from an earlier launch counts as 0.
+// One fetch-and-add when the word already carries this launch's tag (every
+// arrival but a request's first); otherwise the add only touched a stale
+// word, which counts as 0 whatever it holds (a carry into its tag included),
+// and a compare-and-swap loop takes the word over.
 __device__ __forceinline__ uint32_t arrive(uint64_t* p, uint32_t tag) {
-  uint64_t old = tget(p);
+  uint64_t old = __hip_atomic_fetch_add(p, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tag_ok(old, tag)) return (uint32_t)old + 1u;
+  old = tget(p);
   for (;;) {
     const uint32_t n = tag_ok(old, tag) ? (uint32_t)old + 1u : 1u;
     const uint64_t nw = ((uint64_t)tag << 32) | (uint64_t)n;
