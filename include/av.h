@@ -264,8 +264,12 @@ int av_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
  *   status       [1] int32 out or NULL: 0, or AV_DEV_* bits found on device
  *   workspace    >= av_workspace_bytes(B, k, R) bytes, zeroed once by
  *                av_workspace_init before first use
- * Launch: one persistent 1024-thread workgroup per CU, whole rows taken
- * from a dispense counter in the workspace, longest first.
+ * Launch: one persistent 1024-thread workgroup per CU, rows taken from a
+ * dispense counter in the workspace, longest first.  A ragged launch of long
+ * rows (bfloat16 V >= 147456, float32 V >= 73728 with 16-byte rows) whose
+ * rows end in a partial round runs the full rounds as whole rows and the
+ * remaining rows as two halves each on two workgroups, which exchange their
+ * statistics through the workspace (each wait bounded: AV_DEV_TIMEOUT).
  * Errors (AV_EINVAL): NULL required pointer, B < 1, k < 1 or > AV_MAX_K,
  * V < 1, R inconsistent with the layout, lambda outside [0, 1] or NaN, tau
  * <= 0 or NaN, grad_scale non-finite, temperature not positive and finite,
