@@ -197,24 +197,77 @@ __device__ __forceinline__ void store_r(const Stage& st, uint16_t* lds) {
   }
 }
 
+// Row-contiguous operand kept as it lies, [k][row] in LDS (read back with
+// transposing fragment reads, frag_t): thread t loads row chunk t % 32 (8
+// rows, 16 bytes) of k-rows 8 (t / 32) .. + 7, so 32 lanes read one k-row's
+// 512 bytes and the 8 lanes of each 128-byte LDS write share a k-row.
+// k-row k's chunk c sits at position c ^ 4 (k % 4) (see gemm_dma_kernel).
+template <int MODE>
+__device__ __forceinline__ void load_rt(const Opnd& o, int r0, int k0, int kend, Stage& st) {
+  static_assert(MODE != kScalar, "16-byte rows only");
+  const int tid = threadIdx.x, c = tid & 31, kb = (tid >> 5) * 8;
+  const Rsrc r = rsrc_at(o.P, o.total, (long long)k0 * o.ld + r0);
+  const uint32_t vo = (uint32_t)((kb * o.ld + 8 * c) * 2), step = (uint32_t)(o.ld * 2);
+  const bool cin = MODE == kFast || r0 + 8 * c < o.rows;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (MODE == kFast || (cin && k0 + kb + i < kend))
+      st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, vo, i * step, 0);
+    else
+      st.v[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+__device__ __forceinline__ void store_rt(const Stage& st, uint16_t* lds) {
+  const int tid = threadIdx.x, c = tid & 31, kb = (tid >> 5) * 8;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int k = kb + i;
+    *(u32x4*)(lds + k * 256 + 8 * (c ^ (4 * (k & 3)))) = st.v[i];
+  }
+}
+
+template <int KS>
+__device__ __forceinline__ bf16x8 frag_t(const uint16_t* lds, int rb, int s) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const int l = threadIdx.x & 63, g = l >> 4, i = l & 15;
+  const int n = rb + 16 * (g & 1) + 4 * (i & 3);
+  s16x4 v[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int k = 16 * s + 8 * (g >> 1) + 4 * h + (i >> 2);
+    const uint16_t* p = lds + k * 256 + 8 * ((n >> 3) ^ (4 * (k & 3))) + (n & 7);
+    v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+  }
+  // k values 0..3 of the lane's 8, then 4..7
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // One K-step's products from LDS buffer `buf`: each wave's 128 x 128 quarter,
-// four 16-wide k steps of 4 x 4 matrix-core products.
+// four 16-wide k steps of 4 x 4 matrix-core products.  BT: B is held as
+// [k][col] (store_rt) and read with transposing reads.
+template <bool BT>
 __device__ __forceinline__ void products(const uint16_t (*buf)[kBM * kLdk], f32x16 (&acc)[4][4]) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   // lane l reads row l % 32 of a 32-row block, k values 8 (l / 32) .. + 7 of a
   // 16-wide k step
   const int frow = lane & 31, fk = (lane >> 5) * 8;
+  const int bn = (wid & 1) * 128;
   const uint16_t* As = buf[0] + ((wid >> 1) * 128 + frow) * kLdk + fk;
-  const uint16_t* Bs = buf[1] + ((wid & 1) * 128 + frow) * kLdk + fk;
+  const uint16_t* Bs = buf[1] + (bn + frow) * kLdk + fk;
+  auto bfrag = [&](int i, int s) {
+    if constexpr (BT) return frag_t<kBK>(buf[1], bn + 32 * i, s);
+    else return *(const bf16x8*)(Bs + i * 32 * kLdk + 16 * s);
+  };
+  constexpr int kReads = 4 + (BT ? 8 : 4);  // LDS reads of one 16-wide k step
   // fragments of 16-wide k step s + 1 are read while step s's products run:
   // the scheduler is told to alternate one product and one read
   bf16x8 a[2][4], b[2][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     a[0][i] = *(const bf16x8*)(As + i * 32 * kLdk);
-    b[0][i] = *(const bf16x8*)(Bs + i * 32 * kLdk);
+    b[0][i] = bfrag(i, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
 #pragma unroll
   for (int s = 0; s < kBK / 16; ++s) {
     const int c = s & 1;
@@ -222,7 +275,7 @@ __device__ __forceinline__ void products(const uint16_t (*buf)[kBM * kLdk], f32x
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         a[c ^ 1][i] = *(const bf16x8*)(As + i * 32 * kLdk + 16 * (s + 1));
-        b[c ^ 1][i] = *(const bf16x8*)(Bs + i * 32 * kLdk + 16 * (s + 1));
+        b[c ^ 1][i] = bfrag(i, s + 1);
       }
     }
 #pragma unroll
@@ -232,33 +285,36 @@ __device__ __forceinline__ void products(const uint16_t (*buf)[kBM * kLdk], f32x
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
     if (s + 1 < kBK / 16) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < kReads; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 16 - kReads, 0);
     } else {
       __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
     }
   }
 }
 
-template <bool AK, bool BK, int MODE>
+template <bool AK, bool BK, int MODE, bool BT = false>
 struct Loader {
   const Opnd& a;
   const Opnd& b;
   int m0, n0, kbeg, kend;
+  static constexpr bool kBT = BT;
   __device__ __forceinline__ void load(int t, Stage& sa, Stage& sb) const {
     const int k0 = kbeg + t * kBK;
     if constexpr (AK) load_k<MODE>(a, m0, k0, kend, sa);
     else load_r<MODE>(a, m0, k0, kend, sa);
     if constexpr (BK) load_k<MODE>(b, n0, k0, kend, sb);
+    else if constexpr (BT) load_rt<MODE>(b, n0, k0, kend, sb);
     else load_r<MODE>(b, n0, k0, kend, sb);
   }
   __device__ __forceinline__ static void store(uint16_t (*buf)[kBM * kLdk], const Stage& sa, const Stage& sb) {
     if constexpr (AK) store_k(sa, buf[0]);
     else store_r(sa, buf[0]);
     if constexpr (BK) store_k(sb, buf[1]);
+    else if constexpr (BT) store_rt(sb, buf[1]);
     else store_r(sb, buf[1]);
   }
 };
@@ -267,8 +323,8 @@ struct Loader {
 // through the two LDS buffers.  Global loads run two K-steps ahead of the
 // products: step t + 2 is requested while step t's products run, and step
 // t + 1 (requested one step earlier) is written to LDS after them.
-template <bool AK, bool BK, int MODE>
-__device__ __forceinline__ void k_loop2(const Loader<AK, BK, MODE>& L, uint16_t (*lds)[2][kBM * kLdk],
+template <bool AK, bool BK, int MODE, bool BT>
+__device__ __forceinline__ void k_loop2(const Loader<AK, BK, MODE, BT>& L, uint16_t (*lds)[2][kBM * kLdk],
                                         f32x16 (&acc)[4][4]) {
   const int nk = (L.kend - L.kbeg + kBK - 1) / kBK;
   if (nk <= 0) return;
@@ -285,20 +341,20 @@ __device__ __forceinline__ void k_loop2(const Loader<AK, BK, MODE>& L, uint16_t 
   int t = 0;
   for (; t + 1 < nk; t += 2) {
     L.load(min(t + 2, last), s0a, s0b);
-    products(lds[0], acc);
+    products<BT>(lds[0], acc);
     L.store(lds[1], s1a, s1b);
     __syncthreads();
     L.load(min(t + 3, last), s1a, s1b);
-    products(lds[1], acc);
+    products<BT>(lds[1], acc);
     L.store(lds[0], s0a, s0b);
     __syncthreads();
   }
-  if (t < nk) products(lds[0], acc);  // odd step count: the last step
+  if (t < nk) products<BT>(lds[0], acc);  // odd step count: the last step
 }
 
 // The same with loads one K-step ahead (element-wise loads: fewer registers).
-template <bool AK, bool BK, int MODE>
-__device__ __forceinline__ void k_loop1(const Loader<AK, BK, MODE>& L, uint16_t (*lds)[2][kBM * kLdk],
+template <bool AK, bool BK, int MODE, bool BT>
+__device__ __forceinline__ void k_loop1(const Loader<AK, BK, MODE, BT>& L, uint16_t (*lds)[2][kBM * kLdk],
                                         f32x16 (&acc)[4][4]) {
   const int nk = (L.kend - L.kbeg + kBK - 1) / kBK;
   if (nk <= 0) return;
@@ -308,7 +364,7 @@ __device__ __forceinline__ void k_loop1(const Loader<AK, BK, MODE>& L, uint16_t 
   __syncthreads();
   for (int t = 0; t < nk; ++t) {
     if (t + 1 < nk) L.load(t + 1, sa, sb);
-    products(lds[t & 1], acc);
+    products<BT>(lds[t & 1], acc);
     if (t + 1 < nk) L.store(lds[(t + 1) & 1], sa, sb);
     __syncthreads();
   }
@@ -354,15 +410,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
   const Opnd oa{g.A, g.lda, g.a_total, g.M}, ob{g.B, g.ldb, g.b_total, g.N};
+  // 16-byte rows: a row-contiguous B stays as it lies in LDS and is read
+  // with transposing reads (no register transposes)
+  constexpr bool BT = !BK;
   if (!g.vec) {
     k_loop1(Loader<AK, BK, kScalar>{oa, ob, m0, n0, kbeg, kend}, lds, acc);
   } else if (m0 + kBM <= g.M && n0 + kBN <= g.N) {
     // whole K-steps unchecked, then the partial last one (if any) checked
     const int kfull = kend > kbeg ? kbeg + (kend - kbeg) / kBK * kBK : kbeg;
-    k_loop2(Loader<AK, BK, kFast>{oa, ob, m0, n0, kbeg, kfull}, lds, acc);
-    if (kfull < kend) k_loop1(Loader<AK, BK, kEdge>{oa, ob, m0, n0, kfull, kend}, lds, acc);
+    k_loop2(Loader<AK, BK, kFast, BT>{oa, ob, m0, n0, kbeg, kfull}, lds, acc);
+    if (kfull < kend) k_loop1(Loader<AK, BK, kEdge, BT>{oa, ob, m0, n0, kfull, kend}, lds, acc);
   } else {
-    k_loop2(Loader<AK, BK, kEdge>{oa, ob, m0, n0, kbeg, kend}, lds, acc);
+    k_loop2(Loader<AK, BK, kEdge, BT>{oa, ob, m0, n0, kbeg, kend}, lds, acc);
   }
 
   store_tile(g, acc, m0, n0, sp);
@@ -448,22 +507,6 @@ __device__ __forceinline__ bf16x8 frag_k(const uint16_t* lds, int rb, int s) {
   const int l = threadIdx.x & 63, r = rb + (l & 31), kc = 2 * s + (l >> 5);
   return *(const bf16x8*)(lds + r * KS + 8 * (kc ^ KsGeom<KS>::swk(r)));
 }
-template <int KS>
-__device__ __forceinline__ bf16x8 frag_t(const uint16_t* lds, int rb, int s) {
-  typedef short s16x4 __attribute__((ext_vector_type(4)));
-  const int l = threadIdx.x & 63, g = l >> 4, i = l & 15;
-  const int n = rb + 16 * (g & 1) + 4 * (i & 3);
-  s16x4 v[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int k = 16 * s + 8 * (g >> 1) + 4 * h + (i >> 2);
-    const uint16_t* p = lds + k * 256 + 8 * ((n >> 3) ^ (4 * (k & 3))) + (n & 7);
-    v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
-  }
-  // k values 0..3 of the lane's 8, then 4..7
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
 template <bool AKC, bool BKC, int KS>
 __device__ __forceinline__ void dma_products(const uint16_t* As, const uint16_t* Bs, f32x16 (&acc)[4][4]) {
   const int wid = threadIdx.x >> 6, am = (wid >> 1) * 128, bn = (wid & 1) * 128;
