@@ -13,17 +13,14 @@
 // each wave a 128 x 128 quarter: 4 x 4 blocks of 32 x 32, 256 float32
 // accumulators per lane.  K advances 64 at a time through two LDS buffers.
 //
-// gemm_kernel (register-staged; d_hid, and any shape without 16-byte rows):
-//   both operands are held in LDS as [row][k] (k contiguous, rows padded to
-//   72 values so that the lanes of a 16-byte fragment read fall on distinct
-//   banks); global loads run two K-steps ahead into registers and are
-//   written to the free buffer after each step's products.  An operand that
-//   is not K-contiguous is loaded as 8 x 8 blocks (eight 16-byte rows along
-//   M or N) and transposed in registers with byte permutes.
-// gemm_dma_kernel (d_W): operands go from global memory straight into LDS
-//   and M- or N-contiguous operands are read back transposed (see the
-//   section below).
-//
+// Operands are staged through registers: global loads run two K-steps ahead
+// and are written to the free LDS buffer between the current step's products.
+// A K-contiguous operand is held in LDS as [row][k] (rows padded to 72 values
+// so that the lanes of a 16-byte fragment read fall on distinct banks); an M-
+// or N-contiguous one as [k][row], as it lies in memory, with an XOR swizzle of
+// its 16-byte chunks, and its fragments are read with the transposing LDS read
+// ds_read_b64_tr_b16 (see frag_t).  Shapes without 16-byte rows load element
+// by element and transpose 8 x 8 blocks in registers with byte permutes.
 // Long K (d_hid: K = V) is split over workgroups; the partial tiles go to
 // the workspace and reduce_kernel adds them in split order.  Tiles map to
 // workgroup ids so that the 32 workgroups that run together on one XCD (ids
@@ -46,7 +43,6 @@ constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kLdk = kBK + 8;  // LDS row length (bfloat16 values)
 constexpr int kThreads = 256;
 constexpr int kMaxSplits = 8;
-constexpr int kDmaKs = 64, kDmaStages = 2;  // K per LDS stage and stages of the DMA kernel
 constexpr int kMaxDim = 1 << 30;  // largest R (tile offsets stay in int)
 constexpr int kMaxLd = 1 << 22;   // largest V, H (per-thread buffer offsets stay in 31 bits)
 
@@ -143,15 +139,18 @@ __device__ __forceinline__ void load_k(const Opnd& o, int r0, int k0, int kend, 
       if (gr < o.rows)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (gk + e < kend) w[e >> 1] |= ld16(r, vo + 2 * e, q * step) << (16 * (e & 1));
+          if (gk + e < kend) w[e >> 1] |= ld16(r, vo + 2 * e + q * step, 0) << (16 * (e & 1));
       st.v[q] = u32x4{w[0], w[1], w[2], w[3]};
     }
   }
 }
-__device__ __forceinline__ void store_k(const Stage& st, uint16_t* lds) {
+__device__ __forceinline__ void store_k1(const Stage& st, uint16_t* lds, int q) {
   const int tid = threadIdx.x;
+  *(u32x4*)(lds + ((tid >> 3) + 32 * q) * kLdk + (tid & 7) * 8) = st.v[q];
+}
+__device__ __forceinline__ void store_k(const Stage& st, uint16_t* lds) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q) *(u32x4*)(lds + ((tid >> 3) + 32 * q) * kLdk + (tid & 7) * 8) = st.v[q];
+  for (int q = 0; q < 8; ++q) store_k1(st, lds, q);
 }
 
 // Row-contiguous operand, rows r0 .. r0+255, k0 .. k0+63: thread t loads the
@@ -175,7 +174,7 @@ __device__ __forceinline__ void load_r(const Opnd& o, int r0, int k0, int kend, 
       if (gk < kend)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (gr + e < o.rows) w[e >> 1] |= ld16(r, vo + 2 * e, i * step) << (16 * (e & 1));
+          if (gr + e < o.rows) w[e >> 1] |= ld16(r, vo + 2 * e + i * step, 0) << (16 * (e & 1));
       st.v[i] = u32x4{w[0], w[1], w[2], w[3]};
     }
   }
@@ -201,7 +200,8 @@ __device__ __forceinline__ void store_r(const Stage& st, uint16_t* lds) {
 // transposing fragment reads, frag_t): thread t loads row chunk t % 32 (8
 // rows, 16 bytes) of k-rows 8 (t / 32) .. + 7, so 32 lanes read one k-row's
 // 512 bytes and the 8 lanes of each 128-byte LDS write share a k-row.
-// k-row k's chunk c sits at position c ^ 4 (k % 4) (see gemm_dma_kernel).
+// k-row k's chunk c sits at position c ^ 4 (k % 4): the four k-rows that one
+// transposing read serves then start on different banks.
 template <int MODE>
 __device__ __forceinline__ void load_rt(const Opnd& o, int r0, int k0, int kend, Stage& st) {
   static_assert(MODE != kScalar, "16-byte rows only");
@@ -217,16 +217,22 @@ __device__ __forceinline__ void load_rt(const Opnd& o, int r0, int k0, int kend,
       st.v[i] = u32x4{0u, 0u, 0u, 0u};
   }
 }
+__device__ __forceinline__ void store_rt1(const Stage& st, uint16_t* lds, int i) {
+  const int tid = threadIdx.x, c = tid & 31, k = (tid >> 5) * 8 + i;
+  *(u32x4*)(lds + k * 256 + 8 * (c ^ (4 * (k & 3)))) = st.v[i];
+}
 __device__ __forceinline__ void store_rt(const Stage& st, uint16_t* lds) {
-  const int tid = threadIdx.x, c = tid & 31, kb = (tid >> 5) * 8;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int k = kb + i;
-    *(u32x4*)(lds + k * 256 + 8 * (c ^ (4 * (k & 3)))) = st.v[i];
-  }
+  for (int i = 0; i < 8; ++i) store_rt1(st, lds, i);
 }
 
-template <int KS>
+// Matrix-core fragment of rows rb .. rb + 31, 16-wide k step s (lane l: row
+// rb + l % 32, k values 8 (l / 32) .. + 7) from a [k][256] LDS block laid out
+// by store_rt.  ds_read_b64_tr_b16 hands lane i of each 16-lane group value
+// i % 4 of the 8-byte reads of lanes i / 4, 4 + i / 4, 8 + i / 4 and
+// 12 + i / 4 (a probe established this), so four lanes reading 4 consecutive
+// rows at 4 consecutive k give each lane 4 consecutive k of its own row; two
+// such reads make the lane's 8 values.
 __device__ __forceinline__ bf16x8 frag_t(const uint16_t* lds, int rb, int s) {
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   const int l = threadIdx.x & 63, g = l >> 4, i = l & 15;
@@ -242,29 +248,56 @@ __device__ __forceinline__ bf16x8 frag_t(const uint16_t* lds, int rb, int s) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// Scheduling of one 16-wide k step's 16 products: product q is followed by an
+// LDS read if q < NR (the next k step's fragments, read early) and by an LDS
+// write if q >= 16 - NW (the next K-step's operands, written late, so their
+// global loads have had the most time).
+template <int NR, int NW, int Q = 0>
+__device__ __forceinline__ void sched_products() {
+  if constexpr (Q < 16) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (Q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if constexpr (Q >= 16 - NW) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    sched_products<NR, NW, Q + 1>();
+  }
+}
+
 // One K-step's products from LDS buffer `buf`: each wave's 128 x 128 quarter,
-// four 16-wide k steps of 4 x 4 matrix-core products.  BT: B is held as
-// [k][col] (store_rt) and read with transposing reads.
-template <bool BT>
-__device__ __forceinline__ void products(const uint16_t (*buf)[kBM * kLdk], f32x16 (&acc)[4][4]) {
+// four 16-wide k steps of 4 x 4 matrix-core products.  AT, BT: A or B is
+// held as [k][row] (store_rt) and read with transposing reads.  IL: the next
+// K-step's operands (sa, sb: 8 pieces each, neither transposed in registers)
+// are written to LDS buffers `nxt` between the products, two pieces of each
+// per 16-wide k step.
+template <bool AT, bool BT, int IL = 0>
+__device__ __forceinline__ void products(const uint16_t (*buf)[kBM * kLdk], f32x16 (&acc)[4][4],
+                                         const Stage* sa = nullptr, const Stage* sb = nullptr,
+                                         uint16_t (*nxt)[kBM * kLdk] = nullptr) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   // lane l reads row l % 32 of a 32-row block, k values 8 (l / 32) .. + 7 of a
   // 16-wide k step
   const int frow = lane & 31, fk = (lane >> 5) * 8;
   const int bn = (wid & 1) * 128;
-  const uint16_t* As = buf[0] + ((wid >> 1) * 128 + frow) * kLdk + fk;
+  const int am = (wid >> 1) * 128;
+  const uint16_t* As = buf[0] + (am + frow) * kLdk + fk;
   const uint16_t* Bs = buf[1] + (bn + frow) * kLdk + fk;
+  auto afrag = [&](int i, int s) {
+    if constexpr (AT) return frag_t(buf[0], am + 32 * i, s);
+    else return *(const bf16x8*)(As + i * 32 * kLdk + 16 * s);
+  };
   auto bfrag = [&](int i, int s) {
-    if constexpr (BT) return frag_t<kBK>(buf[1], bn + 32 * i, s);
+    if constexpr (BT) return frag_t(buf[1], bn + 32 * i, s);
     else return *(const bf16x8*)(Bs + i * 32 * kLdk + 16 * s);
   };
-  constexpr int kReads = 4 + (BT ? 8 : 4);  // LDS reads of one 16-wide k step
-  // fragments of 16-wide k step s + 1 are read while step s's products run:
-  // the scheduler is told to alternate one product and one read
+  constexpr int kReads = (AT ? 8 : 4) + (BT ? 8 : 4);  // LDS reads of one 16-wide k step
+  // IL 1: two pieces of each operand after each 16-wide k step's products;
+  // IL 2: all sixteen after the last k step's (which reads nothing)
+  constexpr int kWrites = IL == 1 ? 4 : 0;
+  static_assert(kReads <= 16, "one read per product at most");
+  // fragments of 16-wide k step s + 1 are read while step s's products run
   bf16x8 a[2][4], b[2][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    a[0][i] = *(const bf16x8*)(As + i * 32 * kLdk);
+    a[0][i] = afrag(i, 0);
     b[0][i] = bfrag(i, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
@@ -274,8 +307,17 @@ __device__ __forceinline__ void products(const uint16_t (*buf)[kBM * kLdk], f32x
     if (s + 1 < kBK / 16) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        a[c ^ 1][i] = *(const bf16x8*)(As + i * 32 * kLdk + 16 * (s + 1));
+        a[c ^ 1][i] = afrag(i, s + 1);
         b[c ^ 1][i] = bfrag(i, s + 1);
+      }
+    }
+    if (IL == 1 || (IL == 2 && s + 1 == kBK / 16)) {
+#pragma unroll
+      for (int q = IL == 1 ? 2 * s : 0; q < (IL == 1 ? 2 * s + 2 : 8); ++q) {
+        if constexpr (AT) store_rt1(*sa, nxt[0], q);
+        else store_k1(*sa, nxt[0], q);
+        if constexpr (BT) store_rt1(*sb, nxt[1], q);
+        else store_k1(*sb, nxt[1], q);
       }
     }
 #pragma unroll
@@ -283,28 +325,20 @@ __device__ __forceinline__ void products(const uint16_t (*buf)[kBM * kLdk], f32x
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
-    if (s + 1 < kBK / 16) {
-#pragma unroll
-      for (int q = 0; q < kReads; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 16 - kReads, 0);
-    } else {
-      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-    }
+    if (s + 1 < kBK / 16) sched_products<kReads, kWrites>();
+    else sched_products<0, IL == 2 ? 16 : kWrites>();
   }
 }
 
-template <bool AK, bool BK, int MODE, bool BT = false>
+template <bool AK, bool BK, int MODE, bool AT = false, bool BT = false>
 struct Loader {
   const Opnd& a;
   const Opnd& b;
   int m0, n0, kbeg, kend;
-  static constexpr bool kBT = BT;
   __device__ __forceinline__ void load(int t, Stage& sa, Stage& sb) const {
     const int k0 = kbeg + t * kBK;
     if constexpr (AK) load_k<MODE>(a, m0, k0, kend, sa);
+    else if constexpr (AT) load_rt<MODE>(a, m0, k0, kend, sa);
     else load_r<MODE>(a, m0, k0, kend, sa);
     if constexpr (BK) load_k<MODE>(b, n0, k0, kend, sb);
     else if constexpr (BT) load_rt<MODE>(b, n0, k0, kend, sb);
@@ -312,6 +346,7 @@ struct Loader {
   }
   __device__ __forceinline__ static void store(uint16_t (*buf)[kBM * kLdk], const Stage& sa, const Stage& sb) {
     if constexpr (AK) store_k(sa, buf[0]);
+    else if constexpr (AT) store_rt(sa, buf[0]);
     else store_r(sa, buf[0]);
     if constexpr (BK) store_k(sb, buf[1]);
     else if constexpr (BT) store_rt(sb, buf[1]);
@@ -322,9 +357,9 @@ struct Loader {
 // The K loop of one tile: acc += A[m0 .., kbeg .. kend) B[kbeg .. kend), n0 ..],
 // through the two LDS buffers.  Global loads run two K-steps ahead of the
 // products: step t + 2 is requested while step t's products run, and step
-// t + 1 (requested one step earlier) is written to LDS after them.
-template <bool AK, bool BK, int MODE, bool BT>
-__device__ __forceinline__ void k_loop2(const Loader<AK, BK, MODE, BT>& L, uint16_t (*lds)[2][kBM * kLdk],
+// t + 1 (requested one step earlier) is written to LDS between them.
+template <bool AK, bool BK, int MODE, bool AT, bool BT>
+__device__ __forceinline__ void k_loop2(const Loader<AK, BK, MODE, AT, BT>& L, uint16_t (*lds)[2][kBM * kLdk],
                                         f32x16 (&acc)[4][4]) {
   const int nk = (L.kend - L.kbeg + kBK - 1) / kBK;
   if (nk <= 0) return;
@@ -338,23 +373,27 @@ __device__ __forceinline__ void k_loop2(const Loader<AK, BK, MODE, BT>& L, uint1
   __syncthreads();
   // two steps per trip, so that each register stage is a fixed set of registers;
   // at the top of a trip LDS buffer 0 holds step t and stage 1 step t + 1
+  // Where the next step's LDS writes go among the products (measured at
+  // R=2048, V=151936, H=4096): with one K-contiguous operand (d_hid, 12
+  // fragment reads per 16-wide k step) spread over the k steps, 1255 against
+  // 1180 TFLOP/s when written after the products; with none (d_W, 16 reads)
+  // after the last k step's products, which read nothing.
+  constexpr int IL = AK || BK ? 1 : 2;
   int t = 0;
   for (; t + 1 < nk; t += 2) {
     L.load(min(t + 2, last), s0a, s0b);
-    products<BT>(lds[0], acc);
-    L.store(lds[1], s1a, s1b);
+    products<AT, BT, IL>(lds[0], acc, &s1a, &s1b, lds[1]);
     __syncthreads();
     L.load(min(t + 3, last), s1a, s1b);
-    products<BT>(lds[1], acc);
-    L.store(lds[0], s0a, s0b);
+    products<AT, BT, IL>(lds[1], acc, &s0a, &s0b, lds[0]);
     __syncthreads();
   }
-  if (t < nk) products<BT>(lds[0], acc);  // odd step count: the last step
+  if (t < nk) products<AT, BT>(lds[0], acc);  // odd step count: the last step
 }
 
 // The same with loads one K-step ahead (element-wise loads: fewer registers).
-template <bool AK, bool BK, int MODE, bool BT>
-__device__ __forceinline__ void k_loop1(const Loader<AK, BK, MODE, BT>& L, uint16_t (*lds)[2][kBM * kLdk],
+template <bool AK, bool BK, int MODE, bool AT, bool BT>
+__device__ __forceinline__ void k_loop1(const Loader<AK, BK, MODE, AT, BT>& L, uint16_t (*lds)[2][kBM * kLdk],
                                         f32x16 (&acc)[4][4]) {
   const int nk = (L.kend - L.kbeg + kBK - 1) / kBK;
   if (nk <= 0) return;
@@ -364,7 +403,7 @@ __device__ __forceinline__ void k_loop1(const Loader<AK, BK, MODE, BT>& L, uint1
   __syncthreads();
   for (int t = 0; t < nk; ++t) {
     if (t + 1 < nk) L.load(t + 1, sa, sb);
-    products<BT>(lds[t & 1], acc);
+    products<AT, BT>(lds[t & 1], acc);
     if (t + 1 < nk) L.store(lds[(t + 1) & 1], sa, sb);
     __syncthreads();
   }
@@ -410,202 +449,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
   const Opnd oa{g.A, g.lda, g.a_total, g.M}, ob{g.B, g.ldb, g.b_total, g.N};
-  // 16-byte rows: a row-contiguous B stays as it lies in LDS and is read
-  // with transposing reads (no register transposes)
-  constexpr bool BT = !BK;
+  // 16-byte rows: an operand that is not K-contiguous stays as it lies in
+  // LDS and is read with transposing reads (no register transposes)
+  constexpr bool AT = !AK, BT = !BK;
   if (!g.vec) {
     k_loop1(Loader<AK, BK, kScalar>{oa, ob, m0, n0, kbeg, kend}, lds, acc);
   } else if (m0 + kBM <= g.M && n0 + kBN <= g.N) {
     // whole K-steps unchecked, then the partial last one (if any) checked
     const int kfull = kend > kbeg ? kbeg + (kend - kbeg) / kBK * kBK : kbeg;
-    k_loop2(Loader<AK, BK, kFast, BT>{oa, ob, m0, n0, kbeg, kfull}, lds, acc);
-    if (kfull < kend) k_loop1(Loader<AK, BK, kEdge, BT>{oa, ob, m0, n0, kfull, kend}, lds, acc);
+    k_loop2(Loader<AK, BK, kFast, AT, BT>{oa, ob, m0, n0, kbeg, kfull}, lds, acc);
+    if (kfull < kend) k_loop1(Loader<AK, BK, kEdge, AT, BT>{oa, ob, m0, n0, kfull, kend}, lds, acc);
   } else {
-    k_loop2(Loader<AK, BK, kEdge, BT>{oa, ob, m0, n0, kbeg, kend}, lds, acc);
+    k_loop2(Loader<AK, BK, kEdge, AT, BT>{oa, ob, m0, n0, kbeg, kend}, lds, acc);
   }
 
-  store_tile(g, acc, m0, n0, sp);
-}
-
-// ---------------------------------------------------------------------------
-// The main kernel: operands go from global memory straight into LDS
-// ---------------------------------------------------------------------------
-//
-// Each K-step of KS values is written to LDS by 16-byte buffer loads with the
-// LDS destination (lane l of a wave writes bytes 16 l .. 16 l + 15 of a 1 KB
-// block), so nothing passes through registers and no LDS store instruction
-// runs; ST buffers let the loads for step t + ST - 1 run while step t's
-// products do.  Within a 1 KB block the layout is fixed by the lane order, so
-// bank conflicts are avoided by choosing which global 16-byte chunk each lane
-// fetches (an XOR swizzle), and the fragment reads undo it:
-//  - K-contiguous operand, LDS [256 rows][KS k]: row r's chunk c (8 k values)
-//    sits at chunk position c ^ swk(r), which spreads the 16 rows that one
-//    16-byte fragment read serves at a time over all 64 banks;
-//  - row-contiguous operand, LDS [KS k][256 rows]: k-row k's chunk c (8 rows
-//    of the tile) sits at position c ^ 4 (k % 4); the fragments are read with
-//    ds_read_b64_tr_b16, which hands each lane of a 16-lane group one value
-//    from each of four lanes' 8-byte reads (lane i gets value i % 4 of the
-//    reads of lanes i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4), so four lanes
-//    reading 4 consecutive rows at 4 consecutive k give each lane 4
-//    consecutive k of its own row: half of a matrix-core operand fragment.
-// Loads that fall outside M, N or K take an offset past the buffer
-// resource's extent, which makes them write zeros.
-
-__device__ __forceinline__ void dma16(Rsrc r, const uint16_t* lds_block, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_block, 16, voff, 0, 0, 0);
-}
-
-constexpr uint32_t kOutside = 0x80000000u;  // an offset past every resource's extent
-
-template <int KS>
-struct KsGeom {
-  static constexpr int kCpr = KS / 8;            // 16-byte chunks per row of a K-contiguous tile
-  static constexpr int kRpb = 1024 / (2 * KS);   // its rows per 1 KB block
-  static constexpr int kRp256 = 128 / KS;        // its rows per 256 bytes (one pass over the banks)
-  static constexpr int kBlocks = KS / 2;         // 1 KB blocks per operand per step (either layout)
-  static constexpr int kBlocksPerWave = KS / 8;
-  __device__ static int swk(int r) { return (r / kRp256) % kCpr; }
-};
-
-// Per-lane offsets of one operand's DMA pieces for a step, relative to the
-// step's corner of the tile (the resource's base).  EDGE: pieces outside the
-// operand get kOutside.
-template <bool KC, int KS, bool EDGE>
-__device__ __forceinline__ void dma_offsets(const Opnd& o, int r0, int k0, int kend, uint32_t (&vo)[KS / 8]) {
-  using G = KsGeom<KS>;
-  const int L = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int q = 0; q < G::kBlocksPerWave; ++q) {
-    const int u = w * G::kBlocksPerWave + q;
-    if constexpr (KC) {
-      const int r = u * G::kRpb + L / G::kCpr, c = (L % G::kCpr) ^ G::swk(r);
-      vo[q] = (uint32_t)((r * o.ld + 8 * c) * 2);
-      if (EDGE && (r0 + r >= o.rows || k0 + 8 * c >= kend)) vo[q] = kOutside;
-    } else {
-      const int k = 2 * u + (L >> 5), c = (L & 31) ^ (4 * (k & 3));
-      vo[q] = (uint32_t)((k * o.ld + 8 * c) * 2);
-      if (EDGE && (k0 + k >= kend || r0 + 8 * c >= o.rows)) vo[q] = kOutside;
-    }
-  }
-}
-
-template <bool KC, int KS, bool EDGE>
-__device__ __forceinline__ void dma_step(const Opnd& o, int r0, int k0, int kend, const uint16_t* lds) {
-  using G = KsGeom<KS>;
-  uint32_t vo[KS / 8];
-  dma_offsets<KC, KS, EDGE>(o, r0, k0, kend, vo);
-  const Rsrc r = rsrc_at(o.P, o.total, KC ? (long long)r0 * o.ld + k0 : (long long)k0 * o.ld + r0);
-  const int w = threadIdx.x >> 6;
-#pragma unroll
-  for (int q = 0; q < G::kBlocksPerWave; ++q) dma16(r, lds + (w * G::kBlocksPerWave + q) * 512, vo[q]);
-}
-
-// Fragment of rows rb .. rb + 31, 16-wide k step s (lane l: row rb + l % 32,
-// k values 8 (l / 32) .. + 7).
-template <int KS>
-__device__ __forceinline__ bf16x8 frag_k(const uint16_t* lds, int rb, int s) {
-  const int l = threadIdx.x & 63, r = rb + (l & 31), kc = 2 * s + (l >> 5);
-  return *(const bf16x8*)(lds + r * KS + 8 * (kc ^ KsGeom<KS>::swk(r)));
-}
-template <bool AKC, bool BKC, int KS>
-__device__ __forceinline__ void dma_products(const uint16_t* As, const uint16_t* Bs, f32x16 (&acc)[4][4]) {
-  const int wid = threadIdx.x >> 6, am = (wid >> 1) * 128, bn = (wid & 1) * 128;
-#pragma unroll
-  for (int s = 0; s < KS / 16; ++s) {
-    bf16x8 a[4], b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a[i] = AKC ? frag_k<KS>(As, am + 32 * i, s) : frag_t<KS>(As, am + 32 * i, s);
-      b[i] = BKC ? frag_k<KS>(Bs, bn + 32 * i, s) : frag_t<KS>(Bs, bn + 32 * i, s);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-  }
-}
-
-// s_waitcnt with only the vector-memory count set (the others at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// LDS of the main kernel: one array per stage, so that the compiler can tell
-// a stage being loaded from the one being read (it then does not make the
-// reads wait for the loads).
-template <int KS>
-struct DmaLds {
-  uint16_t* a[4];  // A operand of each stage
-  uint16_t* b[4];  // B operand of each stage
-};
-
-template <bool AKC, bool BKC, int KS, int ST, bool EDGE>
-__device__ __forceinline__ void dma_loop(const GemmArgs& g, const DmaLds<KS>& L, int m0, int n0, int kbeg,
-                                         int kend, f32x16 (&acc)[4][4]) {
-  constexpr int kD = 2 * KsGeom<KS>::kBlocksPerWave;  // DMA instructions per wave per step
-  const Opnd oa{g.A, g.lda, g.a_total, g.M}, ob{g.B, g.ldb, g.b_total, g.N};
-  const int nk = (kend - kbeg + KS - 1) / KS;
-  auto issue = [&](int t, int stage) {
-    const int k0 = kbeg + t * KS;
-    dma_step<AKC, KS, EDGE>(oa, m0, k0, kend, L.a[stage]);
-    dma_step<BKC, KS, EDGE>(ob, n0, k0, kend, L.b[stage]);
-  };
-#pragma unroll
-  for (int p = 0; p < ST - 1; ++p)
-    if (p < nk) issue(p, p);
-  // ST steps per trip, so that each step's stage is known at compile time
-  for (int t0 = 0; t0 < nk; t0 += ST) {
-#pragma unroll
-    for (int p = 0; p < ST; ++p) {
-      const int t = t0 + p;
-      if (t < nk) {
-        // step t's loads (this wave's) have landed when at most the later
-        // steps' loads are still in flight
-        const int later = min(ST - 2, nk - 1 - t);
-        if constexpr (ST >= 4) {
-          if (later >= 2) wait_vm<2 * kD>();
-          else if (later == 1) wait_vm<kD>();
-          else wait_vm<0>();
-        } else if constexpr (ST == 3) {
-          if (later >= 1) wait_vm<kD>();
-          else wait_vm<0>();
-        } else {
-          wait_vm<0>();
-        }
-        // every wave's loads of step t are in LDS, and every wave is done
-        // with the stage that step t + ST - 1 overwrites
-        __syncthreads();
-        if (t + ST - 1 < nk) issue(t + ST - 1, (p + ST - 1) % ST);
-        dma_products<AKC, BKC, KS>(L.a[p], L.b[p], acc);
-      }
-    }
-  }
-}
-
-template <bool AKC, bool BKC, int KS, int ST>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_dma_kernel(GemmArgs g) {
-  static_assert(ST >= 2 && ST <= 4, "stages");
-  constexpr int kOp = 256 * KS;  // bf16 values per operand per stage
-  __shared__ __attribute__((aligned(1024))) uint16_t a0[kOp], b0[kOp], a1[kOp], b1[kOp];
-  __shared__ __attribute__((aligned(1024))) uint16_t a2[ST > 2 ? kOp : 8], b2[ST > 2 ? kOp : 8];
-  __shared__ __attribute__((aligned(1024))) uint16_t a3[ST > 3 ? kOp : 8], b3[ST > 3 ? kOp : 8];
-  const DmaLds<KS> L{{a0, a1, a2, a3}, {b0, b1, b2, b3}};
-  int tm, tn, sp;
-  if (!tile_of(g, blockIdx.x, tm, tn, sp)) return;
-  const int m0 = tm * kBM, n0 = tn * kBN;
-  const int kbeg = sp * g.kchunk, kend = min(g.K, kbeg + g.kchunk);
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-  if (m0 + kBM <= g.M && n0 + kBN <= g.N && (kend - kbeg) % KS == 0)
-    dma_loop<AKC, BKC, KS, ST, false>(g, L, m0, n0, kbeg, kend, acc);
-  else
-    dma_loop<AKC, BKC, KS, ST, true>(g, L, m0, n0, kbeg, kend, acc);
-  wait_vm<0>();
   store_tile(g, acc, m0, n0, sp);
 }
 
@@ -625,13 +482,7 @@ hipError_t launch_gemm(GemmArgs& g, bool vec, hipStream_t s) {
   g.per_xcd = (int)((tiles + 7) / 8);
   const dim3 grid((unsigned)(8LL * g.per_xcd));
   g.vec = vec;
-  // Measured on MI355X at R=2048, V=151936, H=4096: with a row-contiguous A
-  // (d_W) the DMA kernel's transposing reads beat the register transposes
-  // (940 against 700 TFLOP/s); with a K-contiguous A and the long K of d_hid
-  // the register-staged kernel, whose loads run two steps ahead, beats the
-  // two-stage DMA pipeline, which drains at every step (1050 against 880).
-  if (vec && !AK) hipLaunchKernelGGL((gemm_dma_kernel<AK, BK, kDmaKs, kDmaStages>), grid, dim3(kThreads), 0, s, g);
-  else hipLaunchKernelGGL((gemm_kernel<AK, BK>), grid, dim3(kThreads), 0, s, g);
+  hipLaunchKernelGGL((gemm_kernel<AK, BK>), grid, dim3(kThreads), 0, s, g);
   return hipGetLastError();
 }
 

@@ -3,13 +3,16 @@ hazards the compiler does not guard against on this target:
 
 * wide-store data: a store of more than 8 bytes (buffer/global/flat/scratch
   dwordx3/x4) keeps reading its data registers after it issues; any VALU
-  write to one of them must come at least two wait states later;
+  write to one of them must come at least two wait states later, on every
+  path through the branches that follow (a function's end within that
+  window also counts as a problem);
 * lane loops: a wave-uniform scalar operand that the compiler could not prove
   uniform makes it loop over lanes (readfirstlane / compare / saveexec around
   the instruction), which is slow and has clobbered store data.
 
 Usage: python -m drafter_distillation_amd.isa_check [file.s]
-(without a file, compiles the kernels to assembly with the build flags).
+(without a file, compiles the library's kernel sources to assembly with the
+build flags).
 """
 
 from __future__ import annotations
@@ -81,23 +84,48 @@ def functions(asm: str):
         body.append(s)
 
 
+def _follow(body: list, labels: dict, start: int, data: set, waited: int, seen: set):
+    """Walks every path from body[start] until MIN_WAIT_STATES have passed;
+    returns the first instruction on a path that writes `data` too early (or
+    leaves the function), else None."""
+    i = start
+    while i < len(body) and waited < MIN_WAIT_STATES:
+        if (i, waited) in seen:
+            return None
+        seen.add((i, waited))
+        nxt = body[i]
+        if nxt.endswith(":"):
+            i += 1
+            continue
+        if nxt.startswith(("s_setpc", "s_endpgm")):
+            return nxt
+        if nxt.startswith(("s_branch", "s_cbranch")):
+            tgt = nxt.split()[-1]
+            if tgt not in labels:
+                return nxt
+            hit = _follow(body, labels, labels[tgt], data, waited + 1, seen)
+            if hit or nxt.startswith("s_branch"):
+                return hit
+            waited += 1
+            i += 1
+            continue
+        if _valu_dst(nxt) & data:
+            return nxt
+        waited += _wait_states(nxt)
+        i += 1
+    return None
+
+
 def check(asm: str) -> list:
     problems = []
     for fn, body in functions(asm):
+        labels = {ins[:-1]: j for j, ins in enumerate(body) if ins.endswith(":")}
         for i, ins in enumerate(body):
             if WIDE_STORE.match(ins):
-                data = _store_data(ins)
-                waited = 0
-                for nxt in body[i + 1:]:
-                    if waited >= MIN_WAIT_STATES:
-                        break
-                    if nxt.endswith(":") or nxt.startswith(("s_branch", "s_cbranch", "s_setpc", "s_endpgm")):
-                        problems.append(f"{fn}: '{ins}' reaches '{nxt}' after {waited} wait states")
-                        break
-                    if _valu_dst(nxt) & data:
-                        problems.append(f"{fn}: '{ins}' data overwritten by '{nxt}' after {waited} wait states")
-                        break
-                    waited += _wait_states(nxt)
+                hit = _follow(body, labels, i + 1, _store_data(ins), 0, set())
+                if hit:
+                    problems.append(f"{fn}: '{ins}' data may be overwritten by '{hit}' within "
+                                    f"{MIN_WAIT_STATES} wait states")
             if ins.startswith("v_readfirstlane_b32"):
                 sreg = ins.split()[1].rstrip(",")
                 window = body[i + 1:i + 5]
@@ -127,7 +155,7 @@ def main(argv=None) -> int:
     else:
         from . import build as B
 
-        asm = compile_asm(os.path.join(B.CSRC, "av_kernels.hip"))
+        asm = "\n".join(compile_asm(os.path.join(B.CSRC, f)) for f in ("av_kernels.hip", "av_lmhead.hip"))
     probs = check(asm)
     for p in probs:
         print(p)

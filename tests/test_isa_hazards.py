@@ -12,11 +12,11 @@ from drafter_distillation_amd import build as B
 from drafter_distillation_amd import isa_check as C
 
 
-@pytest.fixture(scope="module")
-def asm():
+@pytest.fixture(scope="module", params=["av_kernels.hip", "av_lmhead.hip"])
+def asm(request):
     if not os.path.exists(B._hipcc()) and shutil.which(B._hipcc()) is None:
         pytest.skip("hipcc not available")
-    return C.compile_asm(os.path.join(B.CSRC, "av_kernels.hip"))
+    return C.compile_asm(os.path.join(B.CSRC, request.param))
 
 
 def test_no_wide_store_or_lane_loop_hazards(asm):
@@ -50,3 +50,24 @@ def test_checker_flags_a_lane_loop():
         ".Lfunc_end0:",
     ])
     assert any("lane loop" in p for p in C.check(loop))
+
+
+def test_checker_follows_branches():
+    """The window after a wide store is followed into both successors of a
+    conditional branch: a write at the branch target one wait state after the
+    branch is flagged, two are not."""
+    def prog(target_pad):
+        return "\n".join([
+            "_Zplanted:",
+            "\tscratch_store_dwordx4 off, v[4:7], off offset:16",
+            "\ts_cbranch_execz .LBB0_2",
+            "\ts_nop 1",
+            "\tv_mov_b32_e32 v4, 0",
+            ".LBB0_2:",
+            *target_pad,
+            "\tv_mov_b32_e32 v5, 0",
+            "\ts_endpgm",
+            ".Lfunc_end0:",
+        ])
+    assert len(C.check(prog([]))) == 1
+    assert C.check(prog(["\ts_or_b64 exec, exec, s[2:3]"])) == []
