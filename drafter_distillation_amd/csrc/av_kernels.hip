@@ -2123,11 +2123,13 @@ __global__ __launch_bounds__(kBlock) void head_grad_kernel(HeadUpdArgs a) {
 }
 
 // One AdamW step on one parameter held in float32 (arithmetic in float64):
-// decoupled weight decay, then bias-corrected moments.
-__device__ __forceinline__ void adamw(float* th, float* m, float* v, double g, const HeadUpdArgs& a) {
-  const double mm = a.beta1 * (double)*m + (1.0 - a.beta1) * g;
-  const double vv = a.beta2 * (double)*v + (1.0 - a.beta2) * g * g;
-  double t = (double)*th * (1.0 - a.lr * a.wd);
+// decoupled weight decay, then bias-corrected moments.  th0, m0, v0: the
+// values before the step.
+__device__ __forceinline__ void adamw_from(float* th, float* m, float* v, float th0, float m0, float v0, double g,
+                                          const HeadUpdArgs& a) {
+  const double mm = a.beta1 * (double)m0 + (1.0 - a.beta1) * g;
+  const double vv = a.beta2 * (double)v0 + (1.0 - a.beta2) * g * g;
+  double t = (double)th0 * (1.0 - a.lr * a.wd);
   t -= (a.lr / a.bc1) * mm / (sqrt(vv) / a.sqrt_bc2 + a.eps);
   *th = (float)t;
   *m = (float)mm;
@@ -2142,62 +2144,99 @@ __device__ __forceinline__ void adamw(float* th, float* m, float* v, double g, c
 // Wave 0 of workgroup 0 also sums g_bias and the loss (per lane in request
 // order, then lanes by a fixed butterfly) and steps the bias.
 constexpr int kStepWaves = 8, kStepCols = 64, kStepChunk = 1024;
+
+// Workgroup barrier for LDS data only: global stores still in flight are not
+// waited for (nothing in the workgroup reads them back).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __global__ __launch_bounds__(kStepWaves * 64) void head_step_kernel(HeadUpdArgs a) {
+  constexpr int kG = 16;  // requests of a wave whose loads go out together
   __shared__ double part[kStepWaves][kStepCols];
   __shared__ double sdz[kStepChunk];
+  __shared__ double ssq[kStepChunk];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int j = blockIdx.x * kStepCols + lane;
   const bool in = j < a.H;
-  const double wj = in ? (double)a.w[j] : 0.0;
-  double g = 0.0;
+  const bool bias_wg = blockIdx.x == 0;
+  // Everything the step reads is requested up front (the weight, its moments,
+  // the bias state, the first group of h values) and every value is taken
+  // into registers before the first store of d loss / d h: a wait for a load
+  // issued before a store also waits for that store.
+  float w0 = 0.0f, m0 = 0.0f, v0 = 0.0f, b0v = 0.0f, mb = 0.0f, vb = 0.0f;
+  if (in) {
+    w0 = a.w[j];
+    m0 = a.m_w[j];
+    v0 = a.v_w[j];
+  }
+  if (bias_wg && tid == 0) {
+    b0v = a.bias[0];
+    mb = a.m_b[0];
+    vb = a.v_b[0];
+  }
+  const double wj = (double)w0;
+  double g = 0.0, gb = 0.0, sq = 0.0;
   for (int b0 = 0; b0 < a.B; b0 += kStepChunk) {
     const int nb = min(kStepChunk, a.B - b0);
-    __syncthreads();
-    for (int i = tid; i < nb; i += kStepWaves * 64) sdz[i] = a.ws[b0 + i];
-    __syncthreads();
-    if (in) {
-      const float* hj = a.h + (long long)b0 * a.H + j;
-      float* gh = a.grad_h ? a.grad_h + (long long)b0 * a.H + j : nullptr;
-      // groups of 16 of the wave's requests: every load of a group goes out
-      // before its first product (same order of the sum as one at a time)
-      constexpr int kG = 16;
-      for (int i0 = wid; i0 < nb; i0 += kG * kStepWaves) {
-        float x[kG];
+    const float* hj = a.h + (long long)b0 * a.H + j;
+    float x[kG];
+    auto load_group = [&](int i0) {
+#pragma unroll
+      for (int u = 0; u < kG; ++u) {
+        const int i = i0 + u * kStepWaves;
+        x[u] = (in && i < nb) ? hj[(long long)i * a.H] : 0.0f;
+      }
+    };
+    load_group(wid);
+    if (b0 > 0) lds_barrier();  // the previous chunk's readers are done
+    for (int i = tid; i < nb; i += kStepWaves * 64) {
+      sdz[i] = a.ws[b0 + i];
+      if (bias_wg) ssq[i] = a.ws[a.B + b0 + i];
+    }
+    lds_barrier();
+    for (int i0 = wid; i0 < nb; i0 += kG * kStepWaves) {
+      if (i0 != wid) load_group(i0);
+      double d[kG];
+#pragma unroll
+      for (int u = 0; u < kG; ++u) {
+        const int i = i0 + u * kStepWaves;
+        d[u] = i < nb ? sdz[i] : 0.0;
+        if (i < nb) g = fma(d[u], (double)x[u], g);
+      }
+      asm volatile("" : "+v"(m0), "+v"(v0), "+v"(b0v), "+v"(mb), "+v"(vb));
+      if (in && a.grad_h) {
 #pragma unroll
         for (int u = 0; u < kG; ++u) {
           const int i = i0 + u * kStepWaves;
-          x[u] = i < nb ? hj[(long long)i * a.H] : 0.0f;
+          if (i < nb) a.grad_h[(long long)(b0 + i) * a.H + j] = (float)(d[u] * wj);
         }
-#pragma unroll
-        for (int u = 0; u < kG; ++u) {
-          const int i = i0 + u * kStepWaves;
-          if (i < nb) {
-            const double d = sdz[i];
-            g = fma(d, (double)x[u], g);
-            if (gh) gh[(long long)i * a.H] = (float)(d * wj);
-          }
-        }
+      }
+    }
+    // workgroup 0, wave 0: g_bias and the squared errors, per lane in
+    // request order
+    if (bias_wg && wid == 0) {
+      for (int i = lane; i < nb; i += 64) {
+        gb += sdz[i];
+        sq += ssq[i];
       }
     }
   }
   part[wid][lane] = g;
-  __syncthreads();
+  lds_barrier();
   if (wid == 0) {
     double t = 0.0;
 #pragma unroll
     for (int w = 0; w < kStepWaves; ++w) t += part[w][lane];
-    if (in) adamw(a.w + j, a.m_w + j, a.v_w + j, t, a);
-    if (blockIdx.x == 0) {
-      double gb = 0.0, sq = 0.0;
-      for (int b = lane; b < a.B; b += 64) {
-        gb += a.ws[b];
-        sq += a.ws[a.B + b];
-      }
+    if (in) adamw_from(a.w + j, a.m_w + j, a.v_w + j, w0, m0, v0, t, a);
+    if (bias_wg) {
       gb = wsumd(gb);
       sq = wsumd(sq);
       if (lane == 0) {
         if (a.loss) a.loss[0] = (float)(sq / (double)a.B);
-        adamw(a.bias, a.m_b, a.v_b, gb, a);
+        adamw_from(a.bias, a.m_b, a.v_b, b0v, mb, vb, gb, a);
       }
     }
   }

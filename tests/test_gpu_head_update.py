@@ -96,7 +96,11 @@ def test_concurrent_head_three_steps(av):
     run_steps(av, w.h, _accs(rng, bk, 3), [bk] * 3, w.k, w.w, w.bias, nsteps=3)
 
 
-@pytest.mark.parametrize("B,H", [(1, 1), (3, 300), (1500, 70), (7, 257), (128, 5120)])
+# (1, 1), (3, 300), (7, 257): one or a few 64-column workgroups, ragged last
+# one; (1500, 70), (5000, 24): more requests than one pass of the step
+# kernel's shared-memory chunk of d loss / d z (1024); (128, 5120): 80
+# workgroups.
+@pytest.mark.parametrize("B,H", [(1, 1), (3, 300), (1500, 70), (7, 257), (128, 5120), (5000, 24)])
 def test_shapes(av, B, H):
     rng = np.random.default_rng(B * 1000 + H)
     h = rng.normal(0, 1, (B, H)).astype(np.float32)
