@@ -269,7 +269,9 @@ int av_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
  * rows (bfloat16 V >= 147456, float32 V >= 73728 with 16-byte rows) whose
  * rows end in a partial round runs the full rounds as whole rows and the
  * remaining rows as two halves each on two workgroups, which exchange their
- * statistics through the workspace (each wait bounded: AV_DEV_TIMEOUT).
+ * statistics through the workspace (each wait bounded: AV_DEV_TIMEOUT); a
+ * dense launch of such rows with at most half as many rows as CUs runs every
+ * row in halves.
  * Errors (AV_EINVAL): NULL required pointer, B < 1, k < 1 or > AV_MAX_K,
  * V < 1, R inconsistent with the layout, lambda outside [0, 1] or NaN, tau
  * <= 0 or NaN, grad_scale non-finite, temperature not positive and finite,
