@@ -364,7 +364,7 @@ int verify_opd_fwd_impl(int dtype, int B, int k, int V, int R, const int32_t* ro
   const bool lpt = !p.ragged && B <= avk::kMaxLptRequests;
   size_t lds = 0;
   if (p.ragged) lds = (size_t)(B + 1) * sizeof(int32_t);
-  else if (lpt) lds = ((size_t)B * 3 + 3) & ~(size_t)3;
+  else if (lpt) lds = (((size_t)B + 7) & ~(size_t)7) + (((size_t)B * 2 + 3) & ~(size_t)3);
   if (lds > kMaxDynLds) return AV_EUNSUPPORTED;
   const bool gb = grad_zq && grad_dtype == AV_BF16;
   auto occ_of = [&](bool full, int split, int nr) {

@@ -692,6 +692,12 @@ __device__ __forceinline__ double wsumd16(double v) {
 }
 
 // Claims the next dispense index; the high half carries the launch's status.
+// Number of zero bytes of x (exact: no carry crosses a byte).
+__device__ __forceinline__ int zero_bytes(uint64_t x) {
+  const uint64_t t = ((x & 0x7f7f7f7f7f7f7f7full) + 0x7f7f7f7f7f7f7f7full) | x;
+  return __popcll(~t & 0x8080808080808080ull);
+}
+
 __device__ __forceinline__ uint64_t claim(const FwdArgs& a) {
   return __hip_atomic_fetch_add(a.ctl, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1825,17 +1831,20 @@ __global__ __launch_bounds__(kRowBlock) void fused_kernel(FwdArgs a) {
   __shared__ S lp[NLA][kRowBlock];
   __shared__ S lq[NLA][kRowBlock];
   __shared__ RowSmem sm;
-  // ragged: row offsets [B + 1]; dense longest-first: order [B] (uint16), b_k [B] (uint8)
+  // ragged: row offsets [B + 1]; dense longest-first: b_k [B] (uint8, padded
+  // to 8 bytes), then order [B] (uint16)
   extern __shared__ int s_dyn[];
   const int* s_off = s_dyn;
-  uint16_t* order = (uint16_t*)s_dyn;
-  uint8_t* key = (uint8_t*)(order + (a.lpt ? a.B : 0));
+  uint8_t* key = (uint8_t*)s_dyn;
+  uint16_t* order = (uint16_t*)(key + (a.lpt ? (a.B + 7) & ~7 : 0));
   const int tid = threadIdx.x;
   if (tid == 0) {
+    // both requests in flight at once (the launch boundary already orders
+    // this launch after the previous one's writes)
     const uint32_t epoch =
-        (uint32_t)__hip_atomic_load(a.ctl + 1, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-    sm.tag = epoch + 1u;  // epochs stay below 0xFFFFFFFF, so tags are never 0
+        (uint32_t)__hip_atomic_load(a.ctl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sm.item[0] = claim(a);  // split rows: only its status bits are used
+    sm.tag = epoch + 1u;  // epochs stay below 0xFFFFFFFF, so tags are never 0
   }
   int bad = 0;
   if (a.ragged) {
@@ -1851,6 +1860,7 @@ __global__ __launch_bounds__(kRowBlock) void fused_kernel(FwdArgs a) {
     if (bad && tid == 0) raise_status(a.ctl, AV_DEV_BAD_OFFSETS);
   } else if (a.lpt) {  // counting sort of the requests by b_k, descending
     if (tid <= a.k) sm.hist[tid] = 0;
+    if (tid < 8) key[((a.B + 7) & ~7) - 1 - tid] = 0;  // padding (no b_k is 0)
     __syncthreads();
     for (int b = tid; b < a.B; b += kRowBlock) {
       const int kb = min(max(a.bk[b], 1), a.k);
@@ -1877,8 +1887,16 @@ __global__ __launch_bounds__(kRowBlock) void fused_kernel(FwdArgs a) {
     }
     for (int b = tid; b < a.B; b += kRowBlock) {  // stable: rank among equal b_k
       const int kb = key[b];
+      // requests j < b with the same b_k, eight keys per LDS read: a byte of
+      // x is 0 exactly where key[j] == kb
+      const uint64_t* k8 = (const uint64_t*)key;
+      const uint64_t pat = 0x0101010101010101ull * (uint64_t)kb;
       int rank = 0;
-      for (int j = 0; j < b; ++j) rank += key[j] == kb;
+      for (int q = 0; q < (b >> 3); ++q) rank += zero_bytes(k8[q] ^ pat);
+      if (b & 7) {  // bytes of the last word at j >= b count as different
+        const uint64_t keep = (1ull << (8 * (b & 7))) - 1ull;
+        rank += zero_bytes((k8[b >> 3] ^ pat) | ~keep);
+      }
       order[sm.cnt[kb] + rank] = (uint16_t)b;
     }
   }
