@@ -465,6 +465,9 @@ int verify_opd_fwd_impl(int dtype, int B, int k, int V, int R, const int32_t* ro
   a.split = split;
   a.pv0 = split > 1 ? pv0 : 0;
   a.nwhole = nwhole;
+  // The last unverified rows of a longest-first launch go in quarters, so
+  // that its last items are short: one round of the device's workgroups.
+  a.nquart = (split == 1 && lpt && full) ? (int)grid : 0;
   a.gbf16 = gb ? 1 : 0;
   a.tm = tp.tm ? 1 : 0;
   a.lam = lambda;

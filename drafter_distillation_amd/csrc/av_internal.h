@@ -18,8 +18,9 @@ constexpr int kMaxChunks = 64;   // chunks per row of the standalone backward
 //   rowres   [R][2]   per-row target argmax and loss (tagged)
 //   reqres   [B][2]   per-request loss sum, float64 halves (tagged)
 //   arrive   [B]      per-request count of completed verified rows (tagged)
-//   halfres  [R][2][2] per half of an unverified row: max of zp, its index (tagged)
-//   harrive  [R]      per-row count of completed halves (tagged)
+//   halfres  [R][4][2] per part (half or quarter) of an unverified row: max
+//                     of zp, its index (tagged)
+//   harrive  [R]      per-row count of completed parts (tagged)
 //   xres     [R][2][12] split rows: what each half of a verified row hands its
 //                     partner (tagged): 8 words of first-sweep statistics, then
 //                     4 words of clip corrections
@@ -30,7 +31,7 @@ inline size_t ws_rowres_off() { return kCtlBytes; }
 inline size_t ws_reqres_off(int R) { return ws_rowres_off() + (size_t)R * 16; }
 inline size_t ws_arrive_off(int B, int R) { return ws_reqres_off(R) + (size_t)B * 16; }
 inline size_t ws_halfres_off(int B, int R) { return ws_arrive_off(B, R) + (size_t)B * 8; }
-inline size_t ws_harrive_off(int B, int R) { return ws_halfres_off(B, R) + (size_t)R * 32; }
+inline size_t ws_harrive_off(int B, int R) { return ws_halfres_off(B, R) + (size_t)R * 64; }
 inline size_t ws_xres_off(int B, int R) { return ws_harrive_off(B, R) + (size_t)R * 8; }
 inline size_t ws_total(int B, int R) {
   size_t n = ws_xres_off(B, R) + (size_t)R * 2 * kXWords * 8;
@@ -101,6 +102,8 @@ struct FwdArgs {
                  // (ragged layout), all claimed from the dispenser
   int pv0;       // split 2 and 3: first vector of the second half
   int nwhole;    // split 3: rows taken whole
+  int nquart;    // longest-first dense layout, split 1: at most this many of the
+                 // last unverified rows are handed out in quarters (the rest in halves)
   int gbf16;     // gradient stored as bfloat16
   float lam, tau, gs;
   // temperature of the reverse-KL term

@@ -724,21 +724,23 @@ __device__ __forceinline__ uint32_t arrive(uint64_t* p, uint32_t tag) {
 // Work item: a row, its request, and whether it is verified.
 struct Item {
   int row, req, r0, bkb;  // r0: first row of the request; bkb: its verified rows
-  int half;               // unverified rows of the longest-first order: 0 or 1; else -1
+  int half;               // unverified rows in parts: the part (0 .. nparts-1); else -1
+  int nparts;             // 2 (halves) or 4 (quarters)
   bool verified;
 };
 
 // Dense layout, longest first: verified rows position-major (position p holds
 // the cnt[p] requests with b_k > p, which lead `order`, sorted by b_k
 // descending), then unverified rows position-major (the requests with
-// b_k <= p, which trail `order`), each as two halves, so that the last work
-// items of a launch are short.
+// b_k <= p, which trail `order`), each as two halves and the last nq of them
+// as four quarters, so that the last work items of a launch are short.
 // whole: unverified rows are one item each (split rows: the pair's two
 // workgroups take their halves).
 __device__ __forceinline__ Item map_item(const FwdArgs& a, const RowSmem& sm, const int* s_off,
                                          const uint16_t* order, const uint8_t* key, int idx,
-                                         bool whole) {
+                                         bool whole, int nq = 0) {
   Item m;
+  m.nparts = 2;
   if (a.ragged) {
     int lo = 0, hi = opaque_s(a.B) - 1;  // last request whose first row is <= idx
     while (lo < hi) {
@@ -766,8 +768,19 @@ __device__ __forceinline__ Item map_item(const FwdArgs& a, const RowSmem& sm, co
       m.half = -1;
       m.verified = true;
     } else {
-      const int u = whole ? idx - rv : (idx - rv) >> 1;
-      m.half = whole ? 0 : (idx - rv) & 1;
+      int u;
+      const int nh = 2 * (opaque_s(a.R) - rv - nq);  // items of the halved unverified rows
+      if (whole) {
+        u = idx - rv;
+        m.half = 0;
+      } else if (idx - rv < nh) {
+        u = (idx - rv) >> 1;
+        m.half = (idx - rv) & 1;
+      } else {
+        u = (nh >> 1) + ((idx - rv - nh) >> 2);
+        m.half = (idx - rv - nh) & 3;
+        m.nparts = 4;
+      }
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (sm.cumu[mid] <= u) lo = mid;
@@ -1022,13 +1035,14 @@ __device__ __forceinline__ void zero_slots(const FwdArgs& a, long long rowv, int
   }
 }
 
-// Unverified row (half < 0) or half of one: target argmax only, zero
-// gradient.  Half h covers the first / second half of the row's vector slots
-// and of its gradient's 16-byte slots; the half that completes the row second
-// merges the two maxima (the lower index wins ties) and writes the results.
+// Unverified row (half < 0) or part `half` of np parts of one: target argmax
+// only, zero gradient.  Part h covers the h-th of np runs of the row's vector
+// slots and of its gradient's 16-byte slots; the part that completes the row
+// last merges the np maxima (the lower index wins ties) and writes the
+// results.
 template <int VAR, bool GB>
 __device__ __forceinline__ void unverified_row(const FwdArgs& a, RowSmem& sm, int row, int par, int half,
-                                               uint32_t tag) {
+                                               int np, uint32_t tag) {
   using T = Tr<VAR>;
   constexpr int VEC = T::VEC;
   int tid = threadIdx.x;
@@ -1046,10 +1060,10 @@ __device__ __forceinline__ void unverified_row(const FwdArgs& a, RowSmem& sm, in
   const int gs = (gpieces + kRowBlock - 1) / kRowBlock;    // gradient slots
   int s0 = 0, s1 = ns, g0 = 0, g1 = gs;
   if (half >= 0) {
-    s0 = half ? ns / 2 : 0;
-    s1 = half ? ns : ns / 2;
-    g0 = half ? gs / 2 : 0;
-    g1 = half ? gs : gs / 2;
+    s0 = ns * half / np;
+    s1 = ns * (half + 1) / np;
+    g0 = gs * half / np;
+    g1 = gs * (half + 1) / np;
   }
   const int full_end = min(s1, nvec / kRowBlock);  // slots in which every thread has a vector
   float m = -INFINITY;
@@ -1079,27 +1093,36 @@ __device__ __forceinline__ void unverified_row(const FwdArgs& a, RowSmem& sm, in
     }
     wargmax(M, I);
     bool write = half < 0;
-    if (half >= 0) {  // publish this half; the second half to finish merges
+    if (half >= 0) {  // publish this part; the last part to finish merges
       const KArgs K = cold_args();
       uint32_t n = 0;
       if (lane == 0) {
-        uint64_t* hr = K->halfres + 4 * (long long)row + 2 * half;
+        uint64_t* hr = K->halfres + 8 * (long long)row + 2 * half;
         tput(hr, tag, __float_as_uint(M));
         tput(hr + 1, tag, (uint32_t)I);
         n = arrive(K->harrive + row, tag);
       }
       n = __shfl(n, 0);
-      if (n == 2u) {
-        uint64_t* ho = K->halfres + 4 * (long long)row + 2 * (half ^ 1);
+      if (n == (uint32_t)np) {  // lane o < np reads part o's words
         uint64_t w0 = 0, w1 = 0;
-        Waiter wt(a.ctl, K->timeout_ticks);
-        for (;;) {
-          w0 = tget(ho);
-          w1 = tget(ho + 1);
-          if (tag_ok(w0, tag) && tag_ok(w1, tag)) break;
-          if (!wt.keep_going()) break;
+        if (lane < np && lane != half) {
+          uint64_t* ho = K->halfres + 8 * (long long)row + 2 * lane;
+          Waiter wt(a.ctl, K->timeout_ticks);
+          for (;;) {
+            w0 = tget(ho);
+            w1 = tget(ho + 1);
+            if (tag_ok(w0, tag) && tag_ok(w1, tag)) break;
+            if (!wt.keep_going()) break;
+          }
         }
-        amax_merge(M, I, lo_f(w0), (int)(uint32_t)w1);
+        float Mo = -INFINITY;
+        int Io = INT_MAX;
+        if (lane < np && lane != half) {
+          Mo = lo_f(w0);
+          Io = (int)(uint32_t)w1;
+        }
+#pragma unroll
+        for (int o = 0; o < 4; ++o) amax_merge(M, I, __shfl(Mo, o), __shfl(Io, o));
         write = true;
       }
     }
@@ -1905,9 +1928,11 @@ __global__ __launch_bounds__(kRowBlock) void fused_kernel(FwdArgs a) {
   // Work items: rows, with the unverified rows of the longest-first order
   // counted twice (two halves each) unless rows are split (a pair takes both
   // halves of each of its rows).
+  // (unverified rows in quarters count four times: the last nq of them)
+  const int nq = SP == 1 && a.lpt ? min(a.nquart, a.R - sm.cum[a.k]) : 0;
   const uint32_t nitems =
       SP == 3 ? (uint32_t)(2 * a.R - a.nwhole)
-              : (uint32_t)a.R + (SP == 1 && a.lpt ? (uint32_t)(a.R - sm.cum[a.k]) : 0u);
+              : (uint32_t)a.R + (SP == 1 && a.lpt ? (uint32_t)(a.R - sm.cum[a.k] + 2 * nq) : 0u);
   const int ph = SP == 2 ? (int)(blockIdx.x & 1u) : 0;
   const uint32_t pair = blockIdx.x >> 1, npairs = gridDim.x >> 1;
   for (int iter = 0;; ++iter) {
@@ -1929,10 +1954,10 @@ __global__ __launch_bounds__(kRowBlock) void fused_kernel(FwdArgs a) {
         continue;
       }
     }
-    Item it = map_item(a, sm, s_off, order, key, (int)idx, SP == 2);
+    Item it = map_item(a, sm, s_off, order, key, (int)idx, SP == 2, nq);
     if (SP == 2 && !it.verified) it.half = ph;
     if (it.verified) verified_row<VAR, FULL, GB, TM, NRT, SP == 3 ? 1 : SP>(a, sm, lp, lq, it, par, tag, ph);
-    else unverified_row<VAR, GB>(a, sm, it.row, par, it.half, tag);
+    else unverified_row<VAR, GB>(a, sm, it.row, par, it.half, it.nparts, tag);
   }
   // The workgroup that leaves last sums the request losses, reports the
   // status, resets the dispenser and the done count, and advances the epoch.

@@ -296,7 +296,7 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R,
  * array of AV_NOALLOC_SCRATCH_BYTES bytes per GPU, resident until the process
  * ends; the call allocates nothing.  Limits and behaviour:
  *  - av_workspace_bytes(B, k, R) must not exceed AV_NOALLOC_SCRATCH_BYTES
- *    (4 MiB: B = 128 requests of 16 rows need 0.5 MiB; about 16000 rows in
+ *    (4 MiB: B = 128 requests of 16 rows need 0.6 MiB; about 14900 rows in
  *    all), else AV_EUNSUPPORTED before anything is enqueued;
  *  - the array is looked up and zeroed synchronously on the first call on a
  *    device (or by av_init); make that first call, or av_init, outside graph
