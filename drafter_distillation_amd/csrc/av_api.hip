@@ -24,21 +24,23 @@ int hip_fail(hipError_t e) {
 struct DeviceInfo {
   int cus = 0;
   long long ticks_per_ms = 0;  // wall-clock counter rate
-  int occ[4][7][2][2] = {};    // fused-kernel workgroups per CU, per variant, kernel form
+  int occ[4][8][2][2] = {};    // fused-kernel workgroups per CU, per variant, kernel form
                                // (see kForms), gradient type and plain/tempered form, with
                                // the most dynamic LDS a launch uses
 };
 // Kernel forms: {fast form, split (1 whole rows, 2 split rows, 3 split
-// tail), register slots of the build}.
+// tail, 4 rows in quarters), register slots of the build}.
 struct FormDesc {
   bool full;
   int split, nr;
 };
-constexpr int kNumForms = 7;
+constexpr int kNumForms = 8;
 constexpr FormDesc kForms[kNumForms] = {{false, 1, 0}, {true, 1, 0}, {false, 2, avk::kRowRegs16},
                                         {true, 2, avk::kRowRegs16}, {true, 2, avk::kPairRegs},
-                                        {false, 3, avk::kRowRegs16}, {true, 3, avk::kRowRegs16}};
+                                        {false, 3, avk::kRowRegs16}, {true, 3, avk::kRowRegs16},
+                                        {false, 4, avk::kRowRegs16}};
 int form_index(bool full, int split, int nr) {
+  if (split == 4) return 7;
   if (split == 3) return full ? 6 : 5;
   if (split != 2) return full ? 1 : 0;
   if (!full) return 2;
@@ -331,7 +333,7 @@ int verify_opd_fwd_impl(int dtype, int B, int k, int V, int R, const int32_t* ro
   Plan p;
   int rc = plan_rows(dtype, B, k, V, R, row_off, zp, zq, grad_zq, &p);
   if (rc != AV_OK) return rc;
-  if (onchip_limit < 0 || split_mode < 0 || split_mode > 3) return AV_EINVAL;
+  if (onchip_limit < 0 || split_mode < 0 || split_mode > 4) return AV_EINVAL;
   if (p.ragged && B + 1 > 4096) return AV_EUNSUPPORTED;  // offsets are cached in LDS
   if (workspace_bytes < avk::ws_total(B, R)) return AV_EINVAL;
 
@@ -375,7 +377,9 @@ int verify_opd_fwd_impl(int dtype, int B, int k, int V, int R, const int32_t* ro
   const bool row_full = onchip_limit == 0 && p.nvec >= (long long)(nr_row + nl_max) * slot;
 
   int split = 1, nwhole = 0;
-  if (wide && p.nvec >= 2 && split_mode == 2) {
+  if (wide && p.nvec >= 4 && split_mode == 4) {
+    split = 4;
+  } else if (wide && p.nvec >= 2 && split_mode == 2) {
     split = 2;
   } else if (wide && p.nvec >= 2 && p.ragged && split_mode == 3) {
     split = 3;  // test form: the first half of the rows whole, the rest in halves
@@ -395,6 +399,10 @@ int verify_opd_fwd_impl(int dtype, int B, int k, int V, int R, const int32_t* ro
         nwhole = (int)(R - rem);
       }
     }
+  } else if (wide && !p.ragged && split_mode == 0 && row_full && 4LL * R <= (long long)dev->cus) {
+    // A dense launch whose rows, in quarters, fit one round with a CU each:
+    // every row in quarters.
+    split = 4;
   } else if (wide && !p.ragged && split_mode == 0 && row_full &&
              part >= (long long)(avk::kPairRegs + nl_max) * slot && 2LL * R <= (long long)dev->cus) {
     // A dense launch whose rows, in halves, fit one round with a CU each (a
@@ -405,6 +413,7 @@ int verify_opd_fwd_impl(int dtype, int B, int k, int V, int R, const int32_t* ro
   if (split == 2 && onchip_limit == 0 && part < (long long)(nr_max + nl_max) * slot &&
       part >= (long long)(avk::kPairRegs + nl_max) * slot)
     nr_max = avk::kPairRegs;  // fast form with fewer register slots
+  if (split == 4) nr_max = avk::kPairRegs;  // quarters: 5 register slots (4.6 slots at V = 151936 bf16)
   int nr = nr_max, nl = nl_max;
   if (onchip_limit > 0) {
     nr = onchip_limit & 0xff;
@@ -413,17 +422,18 @@ int verify_opd_fwd_impl(int dtype, int B, int k, int V, int R, const int32_t* ro
     if (nl > nl_max) nl = nl_max;
   }
   // split 3 in the fast form needs both the rows and their halves full
-  const long long rowvecs = split == 2 ? part : p.nvec;
+  const long long rowvecs = split == 2 ? part : split == 4 ? p.nvec / 4 : p.nvec;
   bool full = onchip_limit == 0 && rowvecs >= (long long)(nr_max + nl_max) * slot;
   if (split == 3 && part < (long long)(avk::kPairRegs + nl_max) * slot) full = false;
+  if (split == 4) full = false;  // quarters: general form only
   const int occ = occ_of(full, split, nr_max);
   if (occ < 1) return AV_EUNSUPPORTED;
   long long grid = (long long)occ * dev->cus;
-  if (split == 2) {
-    // pairs of co-resident workgroups; no more pairs than rows
-    if (grid > 2LL * R) grid = 2LL * R;
-    grid &= ~1LL;
-    if (grid < 2) return AV_EUNSUPPORTED;
+  if (split == 2 || split == 4) {
+    // teams of co-resident workgroups; no more teams than rows
+    if (grid > (long long)split * R) grid = (long long)split * R;
+    grid -= grid % split;
+    if (grid < split) return AV_EUNSUPPORTED;
   } else {
     const long long items = split == 3 ? 2LL * R - nwhole : (long long)R;
     if (grid > items) grid = items;

@@ -21,11 +21,12 @@ constexpr int kMaxChunks = 64;   // chunks per row of the standalone backward
 //   halfres  [R][4][2] per part (half or quarter) of an unverified row: max
 //                     of zp, its index (tagged)
 //   harrive  [R]      per-row count of completed parts (tagged)
-//   xres     [R][2][12] split rows: what each half of a verified row hands its
-//                     partner (tagged): 8 words of first-sweep statistics, then
-//                     4 words of clip corrections
+//   xres     [R][4][12] split rows: what each part (half or quarter) of a
+//                     verified row hands the others (tagged): 8 words of
+//                     first-sweep statistics, then 4 words of clip corrections
 constexpr size_t kCtlBytes = 256;
-constexpr int kXWords = 12;  // exchange words per half-row
+constexpr int kXWords = 12;  // exchange words per part of a row
+constexpr int kMaxParts = 4;  // parts of a split row
 
 inline size_t ws_rowres_off() { return kCtlBytes; }
 inline size_t ws_reqres_off(int R) { return ws_rowres_off() + (size_t)R * 16; }
@@ -34,7 +35,7 @@ inline size_t ws_halfres_off(int B, int R) { return ws_arrive_off(B, R) + (size_
 inline size_t ws_harrive_off(int B, int R) { return ws_halfres_off(B, R) + (size_t)R * 64; }
 inline size_t ws_xres_off(int B, int R) { return ws_harrive_off(B, R) + (size_t)R * 8; }
 inline size_t ws_total(int B, int R) {
-  size_t n = ws_xres_off(B, R) + (size_t)R * 2 * kXWords * 8;
+  size_t n = ws_xres_off(B, R) + (size_t)R * kMaxParts * kXWords * 8;
   return (n + 255) & ~(size_t)255;
 }
 
@@ -99,7 +100,8 @@ struct FwdArgs {
   int lpt;       // dense layout, rows handed out longest first (unverified rows in halves)
   int split;     // 1: whole rows; 2: rows in halves on workgroup pairs (2p, 2p+1), each
                  // half kept on chip; 3: rows 0 .. nwhole-1 whole, the rest in halves
-                 // (ragged layout), all claimed from the dispenser
+                 // (ragged layout), all claimed from the dispenser; 4: rows in
+                 // quarters on teams of four workgroups (4t .. 4t+3)
   int pv0;       // split 2 and 3: first vector of the second half
   int nwhole;    // split 3: rows taken whole
   int nquart;    // longest-first dense layout, split 1: at most this many of the
@@ -182,8 +184,8 @@ constexpr int kSpecChunkVecs = 512;
 // and the default on-chip split is used.
 // a.tm selects the tempered form of the kernels (fused and backward).
 // nr: register slots of the build (kRowRegs16, or kPairRegs for split rows).
-// a.split (1, 2 or 3) selects whole rows, split rows or whole rows with a
-// split tail.
+// a.split (1, 2, 3 or 4) selects whole rows, rows in halves, whole rows with
+// a split tail, or rows in quarters.
 hipError_t launch_fused(Variant v, bool full, int nr, const FwdArgs& a, int grid, size_t lds, hipStream_t s);
 hipError_t fused_blocks_per_cu(Variant v, bool full, int split, int nr, bool gbf16, bool tm, size_t lds, int* out);
 hipError_t launch_bwd(Variant v, const BwdArgs& a, hipStream_t s);

@@ -1282,7 +1282,7 @@ struct XRec {
 // Word i of a half's record, for lanes 0..n-1 (the others get 0): lane i
 // publishes or reads word i.
 __device__ __forceinline__ uint64_t* xrec(const FwdArgs& a, int row, int h) {
-  return cold_args()->xres + ((long long)row * 2 + h) * kXWords;
+  return cold_args()->xres + ((long long)row * kMaxParts + h) * kXWords;
 }
 
 // Publishes n words (lane i: word i) of this half's record and returns, in
@@ -1305,6 +1305,31 @@ __device__ __forceinline__ uint32_t xswap(const FwdArgs& a, uint64_t* mine, uint
     if (!__all(wt.keep_going())) break;
   }
   return (uint32_t)w;
+}
+
+// Four parts: publishes n words (lane i < n: word i, at offset `off` of this
+// part's record) and returns, in lane l < 4 n, word l % n of part l / n's
+// record (this part's own words included), once each carries this launch's
+// tag (bounded wait as above).  Called by every wave with the same values.
+__device__ __forceinline__ uint32_t xgather4(const FwdArgs& a, int row, int ph, int off, uint32_t v, int n,
+                                             uint32_t tag) {
+  const int lane = threadIdx.x & 63;
+  if ((threadIdx.x >> 6) == kLastWave && lane < n) tput(xrec(a, row, ph) + off + lane, tag, v);
+  const int o = lane / n, i = lane - o * n;
+  const uint32_t own = (uint32_t)__shfl((int)v, i);
+  const bool theirs = lane < n * 4 && o != ph;
+  uint64_t w = 0;
+  Waiter wt(a.ctl, cold_args()->timeout_ticks);
+  for (;;) {
+    bool ok = true;
+    if (theirs) {
+      w = tget(xrec(a, row, o) + off + i);
+      ok = tag_ok(w, tag);
+    }
+    if (__all(ok)) break;
+    if (!__all(wt.keep_going())) break;
+  }
+  return theirs ? (uint32_t)w : own;
 }
 
 // The statistics of the whole row from those of its halves, merged in a
@@ -1335,7 +1360,9 @@ __device__ __forceinline__ XRec xmerge(const XRec& A, const XRec& B, float sL) {
   return o;
 }
 
-template <bool TM>
+// The statistics of the whole row from those of its NP parts (2 or 4),
+// merged in part order, so every part gets the same bits.
+template <bool TM, int NP>
 __device__ __forceinline__ XRec xchange_stats(const FwdArgs& a, const XRec& mine, int row, int ph,
                                               uint32_t tag, float sL) {
   const int lane = threadIdx.x & 63;
@@ -1351,21 +1378,33 @@ __device__ __forceinline__ XRec xchange_stats(const FwdArgs& a, const XRec& mine
     case 7: v = (uint32_t)mine.bi; break;
     default: break;
   }
-  const uint32_t w = xswap(a, xrec(a, row, ph), xrec(a, row, ph ^ 1), v, 8, tag);
-  XRec o;
-  o.mp = __uint_as_float(__shfl(w, 0));
-  o.sp = __uint_as_float(__shfl(w, 1));
-  o.mq = __uint_as_float(__shfl(w, 2));
-  o.sq = __uint_as_float(__shfl(w, 3));
-  o.kq = __uint_as_float(__shfl(w, 4));
-  o.za = __uint_as_float(__shfl(w, 5));
-  o.sq1 = __uint_as_float(__shfl(w, 6));
-  o.bi = (int)__shfl(w, 7);
-  return ph == 0 ? xmerge<TM>(mine, o, sL) : xmerge<TM>(o, mine, sL);
+  const uint32_t w = NP == 2 ? xswap(a, xrec(a, row, ph), xrec(a, row, ph ^ 1), v, 8, tag)
+                             : xgather4(a, row, ph, 0, v, 8, tag);
+  auto rec = [&](int o) {
+    XRec r;
+    r.mp = __uint_as_float(__shfl(w, 8 * o + 0));
+    r.sp = __uint_as_float(__shfl(w, 8 * o + 1));
+    r.mq = __uint_as_float(__shfl(w, 8 * o + 2));
+    r.sq = __uint_as_float(__shfl(w, 8 * o + 3));
+    r.kq = __uint_as_float(__shfl(w, 8 * o + 4));
+    r.za = __uint_as_float(__shfl(w, 8 * o + 5));
+    r.sq1 = __uint_as_float(__shfl(w, 8 * o + 6));
+    r.bi = (int)__shfl(w, 8 * o + 7);
+    return r;
+  };
+  if constexpr (NP == 2) {
+    const XRec o = rec(0);  // the partner's
+    return ph == 0 ? xmerge<TM>(mine, o, sL) : xmerge<TM>(o, mine, sL);
+  } else {
+    XRec m = rec(0);
+    for (int o = 1; o < NP; ++o) m = xmerge<TM>(m, rec(o), sL);
+    return m;
+  }
 }
 
-// Clip corrections of the whole row: this half's plus its partner's (a sum
-// of two float64 values: the same bits in either order).
+// Clip corrections of the whole row: the parts' float64 values added in part
+// order (the same bits in every part; for two parts either order gives them).
+template <int NP>
 __device__ __forceinline__ void xchange_clip(const FwdArgs& a, double& cs, double& ck, int row, int ph,
                                              uint32_t tag) {
   const int lane = threadIdx.x & 63;
@@ -1378,11 +1417,24 @@ __device__ __forceinline__ void xchange_clip(const FwdArgs& a, double& cs, doubl
     case 3: v = (uint32_t)bk; break;
     default: break;
   }
-  const uint32_t w = xswap(a, xrec(a, row, ph) + 8, xrec(a, row, ph ^ 1) + 8, v, 4, tag);
-  const uint64_t os = ((uint64_t)__shfl(w, 0) << 32) | (uint64_t)__shfl(w, 1);
-  const uint64_t ok = ((uint64_t)__shfl(w, 2) << 32) | (uint64_t)__shfl(w, 3);
-  cs = cs + __longlong_as_double((long long)os);
-  ck = ck + __longlong_as_double((long long)ok);
+  if constexpr (NP == 2) {
+    const uint32_t w = xswap(a, xrec(a, row, ph) + 8, xrec(a, row, ph ^ 1) + 8, v, 4, tag);
+    const uint64_t os = ((uint64_t)__shfl(w, 0) << 32) | (uint64_t)__shfl(w, 1);
+    const uint64_t ok = ((uint64_t)__shfl(w, 2) << 32) | (uint64_t)__shfl(w, 3);
+    cs = cs + __longlong_as_double((long long)os);
+    ck = ck + __longlong_as_double((long long)ok);
+  } else {
+    const uint32_t w = xgather4(a, row, ph, 8, v, 4, tag);
+    double ts = 0.0, tk = 0.0;
+    for (int o = 0; o < NP; ++o) {
+      const uint64_t os = ((uint64_t)__shfl(w, 4 * o + 0) << 32) | (uint64_t)__shfl(w, 4 * o + 1);
+      const uint64_t ok = ((uint64_t)__shfl(w, 4 * o + 2) << 32) | (uint64_t)__shfl(w, 4 * o + 3);
+      ts = o == 0 ? __longlong_as_double((long long)os) : ts + __longlong_as_double((long long)os);
+      tk = o == 0 ? __longlong_as_double((long long)ok) : tk + __longlong_as_double((long long)ok);
+    }
+    cs = ts;
+    ck = tk;
+  }
 }
 
 // Verified row: statistics, loss, and (optionally) the gradient.
@@ -1396,6 +1448,8 @@ __device__ __forceinline__ void xchange_clip(const FwdArgs& a, double& cs, doubl
 // [0, pv0) or [pv0, nvec)) and its partner the other half, each on its own
 // CU; the halves hand each other their first-sweep statistics and then their
 // clip corrections, so both continue with the statistics of the whole row.
+// SP = 4: the same with four parts of the row (boundaries on 64-vector
+// multiples near the quarters), for launches with very few rows.
 template <int VAR, bool FULL, bool GB, bool TM, int NRT, int SP>
 __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
                                              typename Tr<VAR>::S (*lp)[kRowBlock],
@@ -1409,9 +1463,20 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   int tid = opaque(threadIdx.x);
   const int lane = tid & 63, wid = tid >> 6;
   const int row = it.row;
-  const int pv0 = SP == 2 ? opaque_s(a.pv0) : 0;
-  const int vbase = (SP == 2 && ph) ? pv0 : 0;  // first vector of this part
-  const int nvec = SP == 2 ? (ph ? opaque_s(a.nvec) - pv0 : pv0) : opaque_s(a.nvec);
+  int vbase = 0, nvec = opaque_s(a.nvec);  // first vector and vectors of this part
+  if constexpr (SP == 2) {
+    const int pv0 = opaque_s(a.pv0);
+    vbase = ph ? pv0 : 0;
+    nvec = ph ? nvec - pv0 : pv0;
+  } else if constexpr (SP == 4) {
+    const long long N = nvec;
+    auto bnd = [&](int i) {
+      const long long b = ((N * i + 3) / 4 + 63) & ~63LL;
+      return (int)(b < N ? b : N);
+    };
+    vbase = bnd(ph);
+    nvec = (ph == 3 ? (int)N : bnd(ph + 1)) - vbase;
+  }
   const int ebase = vbase * IO::VEC;              // row index of the part's first entry
   const long long rowv = (long long)row * a.nvec + vbase;
   const uint32_t rbytes = (uint32_t)nvec * (uint32_t)(IO::VEC * T::EB);
@@ -1620,7 +1685,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   wave_combine<TM>(W, TM ? sL : kLog2e);
   XRec xr{__shfl(W.mp, 0), __shfl(W.sp, 0), __shfl(W.mq, 0), __shfl(W.sq, 0), __shfl(W.kq, 0),
            __shfl(W.za, 0), TM ? __shfl(W.sq1, 0) : 0.0f, __shfl(W.bi, 0)};
-  if constexpr (SP == 2) xr = xchange_stats<TM>(a, xr, row, ph, tag, sL);
+  if constexpr (SP == 2 || SP == 4) xr = xchange_stats<TM, SP>(a, xr, row, ph, tag, sL);
   const float mp = xr.mp, sp = xr.sp;
   const float mq = xr.mq, sq = xr.sq, kq = xr.kq;
   const float zqa = xr.za;
@@ -1700,8 +1765,8 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   __syncthreads();
   double tcs = wsumd16((lane < kRowWaves) ? sm.d[par][lane][0] : 0.0);
   double tck = wsumd16((lane < kRowWaves) ? sm.d[par][lane][1] : 0.0);
-  if constexpr (SP == 2) {
-    if (tau < INFINITY) xchange_clip(a, tcs, tck, row, ph, tag);  // with tau = inf both are 0
+  if constexpr (SP == 2 || SP == 4) {
+    if (tau < INFINITY) xchange_clip<SP>(a, tcs, tck, row, ph, tag);  // with tau = inf all are 0
   }
   const double S64 = (KL + 1.0) - tcs, KLc64 = KL - tck;
   const float S32 = (float)S64;
@@ -1933,12 +1998,15 @@ __global__ __launch_bounds__(kRowBlock) void fused_kernel(FwdArgs a) {
   const uint32_t nitems =
       SP == 3 ? (uint32_t)(2 * a.R - a.nwhole)
               : (uint32_t)a.R + (SP == 1 && a.lpt ? (uint32_t)(a.R - sm.cum[a.k] + 2 * nq) : 0u);
-  const int ph = SP == 2 ? (int)(blockIdx.x & 1u) : 0;
-  const uint32_t pair = blockIdx.x >> 1, npairs = gridDim.x >> 1;
+  // split rows: teams of SP consecutive workgroups, one part of a row each
+  constexpr int NPT = SP == 4 ? 4 : 2;
+  constexpr bool TEAM = SP == 2 || SP == 4;
+  const int ph = TEAM ? (int)(blockIdx.x % NPT) : 0;
+  const uint32_t pair = blockIdx.x / NPT, npairs = gridDim.x / NPT;
   for (int iter = 0;; ++iter) {
     const int par = iter & 1;
     const uint64_t w = sm.item[par];
-    const uint32_t idx = SP == 2 ? pair + (uint32_t)iter * npairs : __builtin_amdgcn_readfirstlane((uint32_t)w);
+    const uint32_t idx = TEAM ? pair + (uint32_t)iter * npairs : __builtin_amdgcn_readfirstlane((uint32_t)w);
     const uint32_t stat = __builtin_amdgcn_readfirstlane((uint32_t)(w >> 32));
     if (idx >= nitems) break;
     if (bad || stat != 0u) {  // failed launch: drain without work
@@ -1954,8 +2022,11 @@ __global__ __launch_bounds__(kRowBlock) void fused_kernel(FwdArgs a) {
         continue;
       }
     }
-    Item it = map_item(a, sm, s_off, order, key, (int)idx, SP == 2, nq);
-    if (SP == 2 && !it.verified) it.half = ph;
+    Item it = map_item(a, sm, s_off, order, key, (int)idx, TEAM, nq);
+    if (TEAM && !it.verified) {
+      it.half = ph;
+      it.nparts = NPT;
+    }
     if (it.verified) verified_row<VAR, FULL, GB, TM, NRT, SP == 3 ? 1 : SP>(a, sm, lp, lq, it, par, tag, ph);
     else unverified_row<VAR, GB>(a, sm, it.row, par, it.half, it.nparts, tag);
   }
@@ -2708,9 +2779,13 @@ __global__ __launch_bounds__(kBlock) void zero_kernel(uint64_t* p, size_t n) {
 // The kernel forms built: whole rows (every variant, general or fast form);
 // split rows for the 16-byte variants, in the general form or in the fast
 // form with kRowRegs16 or kPairRegs register slots; whole rows with a split
-// tail for the 16-byte variants, general or fast.
-enum Form { kWholeGeneral, kWholeFast, kSplitGeneral, kSplitFast, kSplitFastPair, kTailGeneral, kTailFast };
+// tail for the 16-byte variants, general or fast; rows in four parts for the
+// 16-byte variants, general form.
+enum Form {
+  kWholeGeneral, kWholeFast, kSplitGeneral, kSplitFast, kSplitFastPair, kTailGeneral, kTailFast, kQuartGeneral
+};
 inline Form form_of(bool full, int split, int nr) {
+  if (split == 4) return kQuartGeneral;
   if (split == 3) return full ? kTailFast : kTailGeneral;
   if (split != 2) return full ? kWholeFast : kWholeGeneral;
   if (!full) return kSplitGeneral;
@@ -2731,6 +2806,7 @@ const void* kernel_of(Form f) {
       case kSplitFastPair: return (const void*)fused_kernel<VAR, true, GB, TM, kPairRegs, 2>;
       case kTailGeneral: return (const void*)fused_kernel<VAR, false, GB, TM, RowCfg<VAR>::NR, 3>;
       case kTailFast: return (const void*)fused_kernel<VAR, true, GB, TM, RowCfg<VAR>::NR, 3>;
+      case kQuartGeneral: return (const void*)fused_kernel<VAR, false, GB, TM, kPairRegs, 4>;
       default: break;
     }
   }

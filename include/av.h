@@ -271,7 +271,9 @@ int av_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
  * remaining rows as two halves each on two workgroups, which exchange their
  * statistics through the workspace (each wait bounded: AV_DEV_TIMEOUT); a
  * dense launch of such rows with at most half as many rows as CUs runs every
- * row in halves.
+ * row in halves.  A dense launch with at most a quarter as many rows as CUs
+ * (rows of bfloat16 V >= 106496, float32 V >= 53248 with 16-byte rows) runs
+ * every row in quarters, each on its own workgroup of a team of four.
  * Errors (AV_EINVAL): NULL required pointer, B < 1, k < 1 or > AV_MAX_K,
  * V < 1, R inconsistent with the layout, lambda outside [0, 1] or NaN, tau
  * <= 0 or NaN, grad_scale non-finite, temperature not positive and finite,
@@ -296,7 +298,7 @@ int av_verify_opd_fwd(int dtype, int B, int k, int V, int R,
  * array of AV_NOALLOC_SCRATCH_BYTES bytes per GPU, resident until the process
  * ends; the call allocates nothing.  Limits and behaviour:
  *  - av_workspace_bytes(B, k, R) must not exceed AV_NOALLOC_SCRATCH_BYTES
- *    (4 MiB: B = 128 requests of 16 rows need 0.6 MiB; about 14900 rows in
+ *    (4 MiB: B = 128 requests of 16 rows need 0.93 MiB; about 8800 rows in
  *    all), else AV_EUNSUPPORTED before anything is enqueued;
  *  - the array is looked up and zeroed synchronously on the first call on a
  *    device (or by av_init); make that first call, or av_init, outside graph

@@ -37,8 +37,11 @@ extern "C" {
  *                 here rows 0 .. R/2 - 1 whole and the rest as pairs of
  *                 halves, all claimed from the work dispenser (ragged layout
  *                 and 16-byte vector variants only; ignored otherwise).
+ *                 4 = rows split into four parts on teams of four workgroups
+ *                 (4t .. 4t+3), as 2 otherwise (16-byte vector variants, V
+ *                 >= 4 vectors; ignored otherwise).
  * Errors: as av_verify_opd_fwd; AV_EINVAL also for a negative onchip_limit
- * or a split_rows outside 0..3.
+ * or a split_rows outside 0..4.
  */
 int av_test_verify_opd_fwd(int dtype, int B, int k, int V, int R,
                            const int32_t* row_off, const void* zp, const void* zq,

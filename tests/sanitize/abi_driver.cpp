@@ -72,7 +72,7 @@ int main() {
                                 nullptr, F, nullptr, P, 0, nullptr, P, big, -1, 0, nullptr),
          AV_EINVAL);
   EXPECT(av_test_verify_opd_fwd(1, 2, 4, 64, 8, nullptr, P, P, I, I, 0.5f, 0.1f, 1.f, 1.f, I, I, F, nullptr,
-                                nullptr, F, nullptr, P, 0, nullptr, P, big, 0, 4, nullptr),
+                                nullptr, F, nullptr, P, 0, nullptr, P, big, 0, 5, nullptr),
          AV_EINVAL);
   EXPECT(av_verify_opd_fwd_noalloc(1, 2048, 16, 64, 2048 * 16, nullptr, P, P, I, I, 0.5f, 0.1f, 1.f, 1.f, I, I,
                                    F, nullptr, nullptr, nullptr, nullptr, P, 0, nullptr, nullptr),

@@ -102,7 +102,7 @@ def fwd(**kw):
     (dict(temp=float("inf")), dd.AV_EINVAL),
     (dict(ws_bytes=256), dd.AV_EINVAL),                  # workspace too small
     (dict(vecs=-1), dd.AV_EINVAL),                       # test hook: knob out of range
-    (dict(vecs=0, split=4), dd.AV_EINVAL),
+    (dict(vecs=0, split=5), dd.AV_EINVAL),
     (dict(vecs=0, split=-1), dd.AV_EINVAL),
     (dict(vecs=0, split=2, zp=NULL), dd.AV_EINVAL),      # the hook validates as the entry point
     (dict(stats=ctypes.c_void_p(0x10004)), dd.AV_EINVAL),  # row_stats not 16-byte aligned

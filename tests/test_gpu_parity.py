@@ -170,10 +170,12 @@ SPLIT_V = [16, 64, 1000, 10000, 10008, 65544]
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("V", SPLIT_V)
 @pytest.mark.parametrize("vecs", [0, 1 | (1 << 8)])
-def test_split_rows_small_shapes(av, dtype, V, vecs):
+@pytest.mark.parametrize("split", [2, 4])
+def test_split_rows_small_shapes(av, dtype, V, vecs, split):
+    # split 4 at V = 16 (f32: 4 vectors) leaves three of the four parts empty
     w = synth.make("concurrent", B=3, V=V, dtype=dtype)
     bk = np.array([1, 16, 7])
-    full_parity(av, w, bk, 0.5, 0.1, gs=0.25, vecs=vecs, split=2)
+    full_parity(av, w, bk, 0.5, 0.1, gs=0.25, vecs=vecs, split=split)
 
 
 SPLIT_FAST_BF16 = [147456, 151936, 163840, 212992 - 8, 212992, 262144]
@@ -198,21 +200,42 @@ def test_split_rows_fast_forms(av, dtype, V):
     np.testing.assert_allclose(whole["row_loss"], out["row_loss"], rtol=1e-5, atol=1e-6)
 
 
-@pytest.mark.parametrize("split", [1, 2])
+@pytest.mark.parametrize("split", [1, 2, 4])
 def test_split_rows_ragged_and_ties(av, split):
     w = synth.make("ragged", B=10, V=9000)
     full_parity(av, w, None, 0.5, 0.1, gs=1.0 / w.R, split=split)
-    # exact bf16 ties across the two halves: the first half's index wins
+    # exact bf16 ties across the parts: the first part's index wins
     w = synth.make("concurrent", B=1, V=12000, dtype="bf16")
     zp = w.zp.copy()
     big = synth.to_bf16_bits(np.array([40.0]))[0]
-    cut = 768 * 8  # first entry of the second half (64-vector boundary past the middle)
+    # first entry of the second half (64-vector boundary past the middle),
+    # also the first entry of the third quarter (quarters: 384, 768, 1152 vectors)
+    cut = 768 * 8
     for i, (j1, j2) in enumerate([(cut - 1, cut), (5, cut + 3), (cut, 11999), (0, 11999)]):
         zp[i, j1] = big
         zp[i, j2] = big
     w.zp = zp
     out = full_parity(av, w, np.array([16]), 0.5, 0.1, split=split)
     assert list(out["tgt_argmax"][:4]) == [cut - 1, 5, cut, 0]
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 151936), ("f32", 73728 + 4 * 100), ("bf16", 40000)])
+def test_quarter_rows(av, dtype, V):
+    """Rows in quarters on teams of four workgroups: oracle parity, the
+    backward from the saved statistics bit for bit, and the same argmax,
+    acceptance and losses (to rounding) as whole rows."""
+    w = synth.make("concurrent", B=2, V=V, dtype=dtype)
+    bk = np.array([16, 5])
+    out = full_parity(av, w, bk, 0.5, 0.1, gs=0.25, split=4)
+    inp = gpu_inputs(w)
+    g = av.av_verify_opd_bwd(inp["zp"], inp["zq"], torch.from_numpy(out["tgt_argmax"]).cuda(),
+                             torch.from_numpy(out["row_stats"]).cuda(), k=w.k, lam=0.5, tau=0.1,
+                             grad_scale=0.25, bk=torch.from_numpy(bk.astype(np.int32)).cuda())
+    assert np.array_equal(g.cpu().numpy().view(np.uint32), out["grad"].view(np.uint32))
+    whole = run_fwd(av, inp, w, bk=bk, lam=0.5, tau=0.1, gs=0.25, split=1)
+    assert np.array_equal(whole["tgt_argmax"], out["tgt_argmax"])
+    assert np.array_equal(whole["acc_len"], out["acc_len"])
+    np.testing.assert_allclose(whole["row_loss"], out["row_loss"], rtol=1e-5, atol=1e-6)
 
 
 @pytest.mark.parametrize("dtype,V,vecs", [("bf16", 9000, 0), ("bf16", 5000, 1 | (1 << 8)), ("f32", 3001, 0),
