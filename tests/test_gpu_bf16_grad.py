@@ -28,9 +28,9 @@ def bits(t):
     return t.contiguous().view(torch.int16)
 
 
-def compare(av, w, bk, vecs=0, lam=0.5, tau=0.1, gs=0.5, every=1):
+def compare(av, w, bk, vecs=0, lam=0.5, tau=0.1, gs=0.5, every=1, split=0):
     inp = gpu_inputs(w)
-    kw = dict(k=w.k, lam=lam, tau=tau, grad_scale=gs, onchip_limit=vecs)
+    kw = dict(k=w.k, lam=lam, tau=tau, grad_scale=gs, onchip_limit=vecs, split_rows=split)
     if w.row_off is not None:
         kw["row_off"] = inp["row_off"]
     else:
@@ -54,7 +54,7 @@ def compare(av, w, bk, vecs=0, lam=0.5, tau=0.1, gs=0.5, every=1):
     for key in ("tgt_argmax", "acc_len", "row_loss", "req_loss", "total_loss", "row_stats", "status"):
         assert torch.equal(a[key], b[key]), key
     # the standalone backward writes the same bits
-    kwb = {k: v for k, v in kw.items() if k not in ("onchip_limit",)}
+    kwb = {k: v for k, v in kw.items() if k not in ("onchip_limit", "split_rows")}
     g = av.av_verify_opd_bwd(inp["zp"], inp["zq"], b["tgt_argmax"], b["row_stats"],
                              grad_dtype=torch.bfloat16, **kwb)
     torch.cuda.synchronize()
@@ -71,6 +71,17 @@ def test_small_shapes(av, dtype, V, vecs):
 
 def test_ragged(av):
     compare(av, synth.make("ragged", B=10, V=5000), None)
+
+
+@pytest.mark.parametrize("name,kw,split", [
+    ("concurrent", dict(B=2, V=151936), 2),
+    ("concurrent", dict(B=2, V=151936), 4),
+    ("ragged", dict(B=10, V=9000), 3),
+])
+def test_split_forms(av, name, kw, split):
+    """Rows in halves or quarters write the bfloat16 gradient of their part."""
+    w = synth.make(name, **kw)
+    compare(av, w, None if w.row_off is not None else np.array([16, 5]), split=split)
 
 
 def test_full_concurrent(av):

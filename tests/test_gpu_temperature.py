@@ -38,11 +38,11 @@ def head_bk(w):
     return bk
 
 
-def parity(av, w, bk, lam, tau, T, gs=1.0, vecs=0, rows=None, inp=None):
+def parity(av, w, bk, lam, tau, T, gs=1.0, vecs=0, rows=None, inp=None, split=0):
     say(f"tempered parity {w.name} B={w.B} k={w.k} V={w.V} {w.dtype} {w.layout} T={T} lam={lam} "
-        f"tau={tau} vecs={vecs}")
+        f"tau={tau} vecs={vecs} split={split}")
     inp = inp or gpu_inputs(w)
-    out = run_fwd(av, inp, w, bk=bk, lam=lam, tau=tau, gs=gs, vecs=vecs, temperature=T)
+    out = run_fwd(av, inp, w, bk=bk, lam=lam, tau=tau, gs=gs, vecs=vecs, temperature=T, split=split)
     assert out.get("lse_q1") is not None
     errors = check_workload(out, w, bk, lam, tau, gs, rows=rows, temperature=T)
     assert not errors, "\n".join(errors[:10])
@@ -71,6 +71,33 @@ def test_small_shapes(av, T, dtype, V, vecs):
     out = parity(av, w, bk, 0.5, 0.05, T, gs=0.5, vecs=vecs)
     ref = oracle_reductions(w, bk, 0.5, 0.05, 0.5, temperature=T)
     np.testing.assert_allclose(out["req_loss"], ref["req_loss"], rtol=1e-3, atol=1e-4)
+
+
+@pytest.mark.parametrize("T", [0.5, 2.0])
+@pytest.mark.parametrize("name,kw,split", [
+    ("concurrent", dict(B=2, V=151936), 2),   # rows in halves, fast form with 5 register slots
+    ("concurrent", dict(B=2, V=151936), 4),   # rows in quarters
+    ("concurrent", dict(B=2, V=40000), 4),    # quarters, general form, some slots streamed
+    ("ragged", dict(B=10, V=9000), 3),        # split tail: half the rows whole, the rest in halves
+])
+def test_split_forms(av, T, name, kw, split):
+    """Rows in parts exchange the tempered statistics (and the plain log-sum-exp
+    of zq) through the workspace: oracle parity, and the standalone backward
+    reproduces the gradient bit for bit from what the pass saved."""
+    w = synth.make(name, **kw)
+    bk = None if w.row_off is not None else np.array([16, 5])
+    inp = gpu_inputs(w)
+    out = parity(av, w, bk, 0.5, 0.1, T, gs=0.25, inp=inp, split=split)
+    kwb = dict(k=w.k, lam=0.5, tau=0.1, grad_scale=0.25, temperature=T,
+               lse_q1=torch.from_numpy(out["lse_q1"]).cuda())
+    if w.row_off is not None:
+        kwb["row_off"] = inp["row_off"]
+    else:
+        kwb["bk"] = torch.from_numpy(bk.astype(np.int32)).cuda()
+    g = av.av_verify_opd_bwd(inp["zp"], inp["zq"], torch.from_numpy(out["tgt_argmax"]).cuda(),
+                             torch.from_numpy(out["row_stats"]).cuda(), **kwb)
+    torch.cuda.synchronize()
+    assert np.array_equal(g.cpu().numpy().view(np.uint32), out["grad"].view(np.uint32))
 
 
 @pytest.mark.parametrize("T", [0.25, 0.7, 3.0])

@@ -53,7 +53,7 @@ def both(av, w, bk):
         assert torch.equal(a.view(torch.int32), b.view(torch.int32)), key
 
 
-@pytest.mark.parametrize("order", ["large_then_small", "ragged_then_dense"])
+@pytest.mark.parametrize("order", ["large_then_small", "ragged_then_dense", "halves_then_quarters"])
 def test_noalloc_matches_workspace_entry_point(av, order):
     print(f"no-alloc entry point: {order}", flush=True)
     if order == "large_then_small":
@@ -61,6 +61,12 @@ def test_noalloc_matches_workspace_entry_point(av, order):
         both(av, big, np.array([16, 1, 8, 3, 16, 5, 2, 9]))
         small = synth.make("concurrent", B=3, V=20000)
         both(av, small, np.array([2, 16, 7]))
+    elif order == "halves_then_quarters":
+        # 128 rows of 151936 run in halves on 256 CUs, 32 rows in quarters
+        halves = synth.make("concurrent", B=8, V=151936, seed=1)
+        both(av, halves, np.array([3, 16, 9, 1, 12, 16, 7, 2]))
+        quarters = synth.make("concurrent", B=2, V=151936, seed=2)
+        both(av, quarters, np.array([16, 6]))
     else:
         rg = synth.make("ragged", B=12, V=30000)
         both(av, rg, None)
