@@ -151,9 +151,13 @@ __device__ __forceinline__ float opaque_s(float x) {
 // wave64 reductions (xor butterflies: every lane ends with the same bits)
 // ---------------------------------------------------------------------------
 
+// O0: the first butterfly distance (32: the whole wave; 8: lanes 0-15 hold
+// the values and the other lanes only identities, which the steps 32 and 16
+// would add without changing a bit).
+template <int O0 = 32>
 __device__ __forceinline__ float wsum(float v) {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  for (int o = O0; o >= 1; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
 __device__ __forceinline__ double wsumd(double v) {
@@ -161,9 +165,10 @@ __device__ __forceinline__ double wsumd(double v) {
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
+template <int O0 = 32>
 __device__ __forceinline__ float wmax(float v) {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  for (int o = O0; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
 }
 // (value desc, index asc): the first index of the largest value.
@@ -173,9 +178,10 @@ __device__ __forceinline__ void amax_merge(float& v, int& i, float ov, int oi) {
     i = oi;
   }
 }
+template <int O0 = 32>
 __device__ __forceinline__ void wargmax(float& v, int& i) {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
+  for (int o = O0; o >= 1; o >>= 1) {
     const float ov = __shfl_xor(v, o);
     const int oi = __shfl_xor(i, o);
     amax_merge(v, i, ov, oi);
@@ -440,6 +446,7 @@ __device__ __forceinline__ float grad_entry_inside(float q, float ell, float zq,
 // ---------------------------------------------------------------------------
 
 constexpr int kRowWaves = kRowBlock / 64;
+static_assert(kRowWaves == 16, "the second-level reductions take 16 wave partials in lanes 0-15");
 constexpr int kLastWave = kRowWaves - 1;  // publishes rows and finishes requests
 // Floor of the factor that rescales the clip-bound maxima when a thread's
 // running max of zq grows: keeps them upper bounds instead of letting them
@@ -653,13 +660,14 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float& k, float om
 // sums relative to the wave's maxima, and kq.  Lanes with empty sums
 // contribute nothing.  TM: sp, sq and kq scale exponents by L = log2(e) / T,
 // sq1 (temperature 1) does not.
-template <bool TM>
+// O0 = 8: only lanes 0-15 hold partials (the others are empty).
+template <bool TM, int O0 = 32>
 __device__ __forceinline__ void wave_combine(RowAcc& W, float L = kLog2e) {
-  const float M = wmax(W.mp);
+  const float M = wmax<O0>(W.mp);
   int bi = (W.mp == M) ? W.bi : INT_MAX;
   float za = W.za;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
+  for (int o = O0; o >= 1; o >>= 1) {
     const int obi = __shfl_xor(bi, o);
     const float oza = __shfl_xor(za, o);
     if (obi < bi) {
@@ -668,15 +676,15 @@ __device__ __forceinline__ void wave_combine(RowAcc& W, float L = kLog2e) {
     }
   }
   const float sp = (W.sp == 0.0f) ? 0.0f : W.sp * __builtin_amdgcn_exp2f((W.mp - M) * L);
-  const float Mq = wmax(W.mq);
+  const float Mq = wmax<O0>(W.mq);
   const float f = (W.sq == 0.0f) ? 0.0f : __builtin_amdgcn_exp2f((W.mq - Mq) * L);
   if constexpr (TM) {
     const float f1 = (W.sq1 == 0.0f) ? 0.0f : __builtin_amdgcn_exp2f((W.mq - Mq) * kLog2e);
-    W.sq1 = wsum(W.sq1 * f1);
+    W.sq1 = wsum<O0>(W.sq1 * f1);
   }
-  W.sp = wsum(sp);
-  W.sq = wsum(W.sq * f);
-  W.kq = wsum(W.kq * f);
+  W.sp = wsum<O0>(sp);
+  W.sq = wsum<O0>(W.sq * f);
+  W.kq = wsum<O0>(W.kq * f);
   W.mp = M;
   W.rp = M;
   W.bi = bi;
@@ -684,11 +692,25 @@ __device__ __forceinline__ void wave_combine(RowAcc& W, float L = kLog2e) {
   W.mq = Mq;
 }
 
-// Sum of the first 16 lanes, in a fixed order, broadcast from lane 0.
+// Lane 0's value in every lane, through a scalar register (every lane of
+// the wave must be active, so that lane 0 is the first active one).
+__device__ __forceinline__ uint32_t bcast0(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
+__device__ __forceinline__ int bcast0(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ float bcast0(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+__device__ __forceinline__ double bcast0(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = bcast0((uint32_t)b), hi = bcast0((uint32_t)(b >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Sum of the first 16 lanes, in a fixed order, broadcast from lane 0 (all
+// lanes active).
 __device__ __forceinline__ double wsumd16(double v) {
 #pragma unroll
   for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return __shfl(v, 0);
+  return bcast0(v);
 }
 
 // Claims the next dispense index; the high half carries the launch's status.
@@ -1091,7 +1113,7 @@ __device__ __forceinline__ void unverified_row(const FwdArgs& a, RowSmem& sm, in
       M = sm.f[par][lane][0];
       I = sm.i[par][lane];
     }
-    wargmax(M, I);
+    wargmax<8>(M, I);  // the 16 wave partials sit in lanes 0-15
     bool write = half < 0;
     if (half >= 0) {  // publish this part; the last part to finish merges
       const KArgs K = cold_args();
@@ -1102,7 +1124,7 @@ __device__ __forceinline__ void unverified_row(const FwdArgs& a, RowSmem& sm, in
         tput(hr + 1, tag, (uint32_t)I);
         n = arrive(K->harrive + row, tag);
       }
-      n = __shfl(n, 0);
+      n = bcast0(n);
       if (n == (uint32_t)np) {  // lane o < np reads part o's words
         uint64_t w0 = 0, w1 = 0;
         if (lane < np && lane != half) {
@@ -1682,9 +1704,17 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
     if constexpr (TM) W.sq1 = sm.f1[par][lane];
     W.bi = sm.i[par][lane];
   }
-  wave_combine<TM>(W, TM ? sL : kLog2e);
-  XRec xr{__shfl(W.mp, 0), __shfl(W.sp, 0), __shfl(W.mq, 0), __shfl(W.sq, 0), __shfl(W.kq, 0),
-           __shfl(W.za, 0), TM ? __shfl(W.sq1, 0) : 0.0f, __shfl(W.bi, 0)};
+  wave_combine<TM, 8>(W, TM ? sL : kLog2e);  // the 16 wave partials sit in lanes 0-15
+  // (the tempered form keeps them in vector registers: through scalar
+  // registers it measured slower, 0.8-1.2% at T = 0.5 and 2)
+  XRec xr;
+  if constexpr (TM) {
+    xr = XRec{__shfl(W.mp, 0), __shfl(W.sp, 0), __shfl(W.mq, 0), __shfl(W.sq, 0), __shfl(W.kq, 0),
+              __shfl(W.za, 0), __shfl(W.sq1, 0), __shfl(W.bi, 0)};
+  } else {
+    xr = XRec{bcast0(W.mp), bcast0(W.sp), bcast0(W.mq), bcast0(W.sq), bcast0(W.kq), bcast0(W.za), 0.0f,
+              bcast0(W.bi)};
+  }
   if constexpr (SP == 2 || SP == 4) xr = xchange_stats<TM, SP>(a, xr, row, ph, tag, sL);
   const float mp = xr.mp, sp = xr.sp;
   const float mq = xr.mq, sq = xr.sq, kq = xr.kq;
@@ -1763,8 +1793,14 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
     sm.d[par][wid][1] = dck;
   }
   __syncthreads();
-  double tcs = wsumd16((lane < kRowWaves) ? sm.d[par][lane][0] : 0.0);
-  double tck = wsumd16((lane < kRowWaves) ? sm.d[par][lane][1] : 0.0);
+  // (no wave with a correction: every partial is zero, and so are the sums)
+  const double pcs = (lane < kRowWaves) ? sm.d[par][lane][0] : 0.0;
+  const double pck = (lane < kRowWaves) ? sm.d[par][lane][1] : 0.0;
+  double tcs = 0.0, tck = 0.0;
+  if (__any(pcs != 0.0 || pck != 0.0)) {
+    tcs = wsumd16(pcs);
+    tck = wsumd16(pck);
+  }
   if constexpr (SP == 2 || SP == 4) {
     if (tau < INFINITY) xchange_clip<SP>(a, tcs, tck, row, ph, tag);  // with tau = inf all are 0
   }
@@ -1790,7 +1826,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
       tput(K->rowres + 2 * (long long)row + 1, tag, __float_as_uint(loss));
       n = arrive(K->arrive + it.req, tag);
     }
-    n = __shfl(n, 0);
+    n = bcast0(n);
     if (n == (uint32_t)it.bkb) finish_request(a, it.req, it.r0, it.bkb, tag);
   }
 
