@@ -151,13 +151,9 @@ __device__ __forceinline__ float opaque_s(float x) {
 // wave64 reductions (xor butterflies: every lane ends with the same bits)
 // ---------------------------------------------------------------------------
 
-// O0: the first butterfly distance (32: the whole wave; 8: lanes 0-15 hold
-// the values and the other lanes only identities, which the steps 32 and 16
-// would add without changing a bit).
-template <int O0 = 32>
 __device__ __forceinline__ float wsum(float v) {
 #pragma unroll
-  for (int o = O0; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
 __device__ __forceinline__ double wsumd(double v) {
@@ -165,10 +161,9 @@ __device__ __forceinline__ double wsumd(double v) {
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
-template <int O0 = 32>
 __device__ __forceinline__ float wmax(float v) {
 #pragma unroll
-  for (int o = O0; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
 }
 // (value desc, index asc): the first index of the largest value.
@@ -176,15 +171,6 @@ __device__ __forceinline__ void amax_merge(float& v, int& i, float ov, int oi) {
   if (ov > v || (ov == v && oi < i)) {
     v = ov;
     i = oi;
-  }
-}
-template <int O0 = 32>
-__device__ __forceinline__ void wargmax(float& v, int& i) {
-#pragma unroll
-  for (int o = O0; o >= 1; o >>= 1) {
-    const float ov = __shfl_xor(v, o);
-    const int oi = __shfl_xor(i, o);
-    amax_merge(v, i, ov, oi);
   }
 }
 
@@ -653,45 +639,6 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float& k, float om
   k = k * fa + ok * fb;
 }
 
-// A wave's row statistics combined by one pass of maxima, one rescale of each
-// lane's sums and one pass of sums (instead of a log-sum-exp merge at each
-// butterfly level).  On entry sp is relative to mp; on exit every lane holds
-// the same bits: the wave's max of zp, its first index and the zq there, the
-// sums relative to the wave's maxima, and kq.  Lanes with empty sums
-// contribute nothing.  TM: sp, sq and kq scale exponents by L = log2(e) / T,
-// sq1 (temperature 1) does not.
-// O0 = 8: only lanes 0-15 hold partials (the others are empty).
-template <bool TM, int O0 = 32>
-__device__ __forceinline__ void wave_combine(RowAcc& W, float L = kLog2e) {
-  const float M = wmax<O0>(W.mp);
-  int bi = (W.mp == M) ? W.bi : INT_MAX;
-  float za = W.za;
-#pragma unroll
-  for (int o = O0; o >= 1; o >>= 1) {
-    const int obi = __shfl_xor(bi, o);
-    const float oza = __shfl_xor(za, o);
-    if (obi < bi) {
-      bi = obi;
-      za = oza;
-    }
-  }
-  const float sp = (W.sp == 0.0f) ? 0.0f : W.sp * __builtin_amdgcn_exp2f((W.mp - M) * L);
-  const float Mq = wmax<O0>(W.mq);
-  const float f = (W.sq == 0.0f) ? 0.0f : __builtin_amdgcn_exp2f((W.mq - Mq) * L);
-  if constexpr (TM) {
-    const float f1 = (W.sq1 == 0.0f) ? 0.0f : __builtin_amdgcn_exp2f((W.mq - Mq) * kLog2e);
-    W.sq1 = wsum<O0>(W.sq1 * f1);
-  }
-  W.sp = wsum<O0>(sp);
-  W.sq = wsum<O0>(W.sq * f);
-  W.kq = wsum<O0>(W.kq * f);
-  W.mp = M;
-  W.rp = M;
-  W.bi = bi;
-  W.za = za;
-  W.mq = Mq;
-}
-
 // Lane 0's value in every lane, through a scalar register (every lane of
 // the wave must be active, so that lane 0 is the first active one).
 __device__ __forceinline__ uint32_t bcast0(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
@@ -704,14 +651,162 @@ __device__ __forceinline__ double bcast0(double v) {
   const uint32_t lo = bcast0((uint32_t)b), hi = bcast0((uint32_t)(b >> 32));
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
-
-// Sum of the first 16 lanes, in a fixed order, broadcast from lane 0 (all
-// lanes active).
-__device__ __forceinline__ double wsumd16(double v) {
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return bcast0(v);
+// Lane l's value, through a scalar register.
+__device__ __forceinline__ int lane_of(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ float lane_of(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
+__device__ __forceinline__ double lane_of(double v, int l) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Reductions of the fused row kernel, in two stages.  Inside each row of 16
+// lanes, four DPP moves pair every lane with another (neighbours, pairs of a
+// quad, mirror images in 8 lanes, mirror images in 16) and each step combines
+// the two values with a commutative operation, so after the four steps every
+// lane of a row holds the row's result with the same bits.  The four rows'
+// results are then read into scalar registers and combined in row order.
+// NL = 16: only lanes 0-15 hold values, and the result is row 0's.  Every
+// lane of the wave must be active.
+constexpr int kDppSwap1 = 0xB1;     // quad_perm [1, 0, 3, 2]
+constexpr int kDppSwap2 = 0x4E;     // quad_perm [2, 3, 0, 1]
+constexpr int kDppMirror8 = 0x141;  // row_half_mirror
+constexpr int kDppMirror16 = 0x140; // row_mirror
+template <int C>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, C, 0xF, 0xF, false);
+}
+template <int C>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(dpp<C>(__float_as_int(v)));
+}
+template <int C>
+__device__ __forceinline__ double dpp(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)dpp<C>((int)(uint32_t)b), hi = (uint32_t)dpp<C>((int)(uint32_t)(b >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+template <class T>
+__device__ __forceinline__ T row_sum(T v) {
+  v += dpp<kDppSwap1>(v);
+  v += dpp<kDppSwap2>(v);
+  v += dpp<kDppMirror8>(v);
+  v += dpp<kDppMirror16>(v);
+  return v;
+}
+__device__ __forceinline__ float row_max(float v) {
+  v = fmaxf(v, dpp<kDppSwap1>(v));
+  v = fmaxf(v, dpp<kDppSwap2>(v));
+  v = fmaxf(v, dpp<kDppMirror8>(v));
+  v = fmaxf(v, dpp<kDppMirror16>(v));
+  return v;
+}
+template <int NL, class T>
+__device__ __forceinline__ T xsum(T v) {
+  v = row_sum(v);
+  if constexpr (NL == 16) return bcast0(v);
+  else return (lane_of(v, 0) + lane_of(v, 16)) + (lane_of(v, 32) + lane_of(v, 48));
+}
+template <int NL>
+__device__ __forceinline__ float xmax(float v) {
+  v = row_max(v);
+  if constexpr (NL == 16) return bcast0(v);
+  else return fmaxf(fmaxf(lane_of(v, 0), lane_of(v, 16)), fmaxf(lane_of(v, 32), lane_of(v, 48)));
+}
+// Smallest index, with the value that goes with it.
+template <int C>
+__device__ __forceinline__ void min_step(int& i, float& z) {
+  const int oi = dpp<C>(i);
+  const float oz = dpp<C>(z);
+  if (oi < i) {
+    i = oi;
+    z = oz;
+  }
+}
+template <int NL>
+__device__ __forceinline__ void xminidx(int& i, float& z) {
+  min_step<kDppSwap1>(i, z);
+  min_step<kDppSwap2>(i, z);
+  min_step<kDppMirror8>(i, z);
+  min_step<kDppMirror16>(i, z);
+  if constexpr (NL == 16) {
+    i = bcast0(i);
+    z = bcast0(z);
+  } else {
+    int bi = lane_of(i, 0);
+    float bz = lane_of(z, 0);
+#pragma unroll
+    for (int r = 1; r < 4; ++r) {
+      const int oi = lane_of(i, 16 * r);
+      const float oz = lane_of(z, 16 * r);
+      if (oi < bi) {
+        bi = oi;
+        bz = oz;
+      }
+    }
+    i = bi;
+    z = bz;
+  }
+}
+// (value desc, index asc): the first index of the largest value.
+template <int C>
+__device__ __forceinline__ void amax_step(float& v, int& i) {
+  amax_merge(v, i, dpp<C>(v), dpp<C>(i));
+}
+template <int NL>
+__device__ __forceinline__ void xargmax(float& v, int& i) {
+  amax_step<kDppSwap1>(v, i);
+  amax_step<kDppSwap2>(v, i);
+  amax_step<kDppMirror8>(v, i);
+  amax_step<kDppMirror16>(v, i);
+  if constexpr (NL == 16) {
+    v = bcast0(v);
+    i = bcast0(i);
+  } else {
+    float bv = lane_of(v, 0);
+    int bi = lane_of(i, 0);
+#pragma unroll
+    for (int r = 1; r < 4; ++r) amax_merge(bv, bi, lane_of(v, 16 * r), lane_of(i, 16 * r));
+    v = bv;
+    i = bi;
+  }
+}
+
+// A wave's row statistics combined by one pass of maxima, one rescale of each
+// lane's sums and one pass of sums (instead of a log-sum-exp merge at each
+// reduction step).  On entry sp is relative to mp; on exit every lane holds
+// the same bits: the wave's max of zp, its first index and the zq there, the
+// sums relative to the wave's maxima, and kq.  Lanes with empty sums
+// contribute nothing.  TM: sp, sq and kq scale exponents by L = log2(e) / T,
+// sq1 (temperature 1) does not.  NL = 16: only lanes 0-15 hold partials.
+template <bool TM, int NL = 64>
+__device__ __forceinline__ void wave_combine(RowAcc& W, float L = kLog2e) {
+  const float M = xmax<NL>(W.mp);
+  int bi = (W.mp == M) ? W.bi : INT_MAX;
+  float za = W.za;
+  xminidx<NL>(bi, za);
+  const float sp = (W.sp == 0.0f) ? 0.0f : W.sp * __builtin_amdgcn_exp2f((W.mp - M) * L);
+  const float Mq = xmax<NL>(W.mq);
+  const float f = (W.sq == 0.0f) ? 0.0f : __builtin_amdgcn_exp2f((W.mq - Mq) * L);
+  if constexpr (TM) {
+    const float f1 = (W.sq1 == 0.0f) ? 0.0f : __builtin_amdgcn_exp2f((W.mq - Mq) * kLog2e);
+    W.sq1 = xsum<NL>(W.sq1 * f1);
+  }
+  W.sp = xsum<NL>(sp);
+  W.sq = xsum<NL>(W.sq * f);
+  W.kq = xsum<NL>(W.kq * f);
+  W.mp = M;
+  W.rp = M;
+  W.bi = bi;
+  W.za = za;
+  W.mq = Mq;
+}
+
+// Sum of the first 16 lanes, the same bits in every lane (all lanes active).
+__device__ __forceinline__ double wsumd16(double v) { return xsum<16>(v); }
 
 // Claims the next dispense index; the high half carries the launch's status.
 // Number of zero bytes of x (exact: no carry crosses a byte).
@@ -864,7 +959,7 @@ __device__ __forceinline__ void finish_request(const FwdArgs& a, int req, int r0
   const uint64_t mism = __ballot(inb && !match);
   const int acc = mism ? (__ffsll((unsigned long long)mism) - 1) : bkb;
   double v = inb ? (double)lo_f(w1) : 0.0;
-  v = wsumd(v);
+  v = xsum<64>(v);
   if (lane == 0) {
     K->acc[req] = acc;
     if (K->req_loss) K->req_loss[req] = (float)v;
@@ -895,7 +990,7 @@ __device__ __forceinline__ bool finish_total(const FwdArgs& a, RowSmem& sm, uint
     }
     part += __longlong_as_double((long long)(((uint64_t)(uint32_t)h << 32) | (uint32_t)l));
   }
-  part = wsumd(part);
+  part = xsum<64>(part);
   if (lane == 0) sm.d[0][wid][0] = part;
   ok = __syncthreads_and(ok);
   if (wid == 0) {
@@ -1099,7 +1194,7 @@ __device__ __forceinline__ void unverified_row(const FwdArgs& a, RowSmem& sm, in
   for (int s = max(full_end, s0); s < s1; ++s)
     if (s * kRowBlock + tid < nvec)
       argmax_vec<VAR>(T::template bload<kAuxOnce>(rzp, voff, (uint32_t)s * SIN), s * kRowBlock + tid, m, bi);
-  wargmax(m, bi);
+  xargmax<64>(m, bi);
   if (lane == 0) {
     sm.f[par][wid][0] = m;
     sm.i[par][wid] = bi;
@@ -1113,7 +1208,7 @@ __device__ __forceinline__ void unverified_row(const FwdArgs& a, RowSmem& sm, in
       M = sm.f[par][lane][0];
       I = sm.i[par][lane];
     }
-    wargmax<8>(M, I);  // the 16 wave partials sit in lanes 0-15
+    xargmax<16>(M, I);  // the 16 wave partials sit in lanes 0-15
     bool write = half < 0;
     if (half >= 0) {  // publish this part; the last part to finish merges
       const KArgs K = cold_args();
@@ -1704,7 +1799,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
     if constexpr (TM) W.sq1 = sm.f1[par][lane];
     W.bi = sm.i[par][lane];
   }
-  wave_combine<TM, 8>(W, TM ? sL : kLog2e);  // the 16 wave partials sit in lanes 0-15
+  wave_combine<TM, 16>(W, TM ? sL : kLog2e);  // the 16 wave partials sit in lanes 0-15
   // (the tempered form keeps them in vector registers: through scalar
   // registers it measured slower, 0.8-1.2% at T = 0.5 and 2)
   XRec xr;
@@ -1785,8 +1880,8 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   }
   double dcs = 0.0, dck = 0.0;
   if (__any(flag_on || flag_st)) {
-    dcs = wsumd((double)cs);
-    dck = wsumd((double)ck);
+    dcs = xsum<64>((double)cs);
+    dck = xsum<64>((double)ck);
   }
   if (lane == 0) {
     sm.d[par][wid][0] = dcs;
