@@ -390,11 +390,14 @@ __device__ __forceinline__ void opd_entry(float zp, float zq, const RowK& k, flo
 //   TM:     C1 q1_j + q_j t_j - [j = a] gs lam,
 //   t_j = A + B + B ell_j where |r_j| <= tau, A elsewhere,
 //   A = gs (lam - (1 - lam) S) (T = 1) or -gs (1 - lam) s S (TM), B = gs (1 - lam) s.
+// With ell_j = s d_j - delta (d_j = zq_j - zp_j, delta = lse_q - lse_p), the
+// inside value is taken as t_j = Bs d_j + C0 (Bs = B s at T != 1, B at T = 1;
+// C0 = A + B - B delta, rounded once): one operation fewer per entry.
 struct GradK {
-  float a, ab, b, fix, c1, l1L;
+  float a, ab, b, fix, c1, l1L, bd, c0;
 };
 template <bool TM>
-__device__ __forceinline__ GradK grad_consts(float lam, float gs, float S, float s, float lse1) {
+__device__ __forceinline__ GradK grad_consts(float lam, float gs, float S, float s, float lse1, float delta) {
   GradK g;
   if constexpr (TM) {
     g.b = gs * (1.0f - lam) * s;
@@ -409,19 +412,21 @@ __device__ __forceinline__ GradK grad_consts(float lam, float gs, float S, float
   }
   g.ab = g.a + g.b;
   g.fix = gs * lam;
+  g.bd = TM ? g.b * s : g.b;
+  g.c0 = __builtin_fmaf(-g.b, delta, g.ab);
   return g;
 }
 template <bool TM>
-__device__ __forceinline__ float grad_entry(float q, float ell, float r, float zq, float tau, const GradK& c) {
-  const float t = (__builtin_fabsf(r) <= tau) ? __builtin_fmaf(c.b, ell, c.ab) : c.a;
+__device__ __forceinline__ float grad_entry(float q, float d, float r, float zq, float tau, const GradK& c) {
+  const float t = (__builtin_fabsf(r) <= tau) ? __builtin_fmaf(c.bd, d, c.c0) : c.a;
   if constexpr (TM)
     return __builtin_fmaf(c.c1, __builtin_amdgcn_exp2f(__builtin_fmaf(zq, kLog2e, -c.l1L)), q * t);
   return q * t;
 }
 // The same for an entry known to lie inside the clip interval.
 template <bool TM>
-__device__ __forceinline__ float grad_entry_inside(float q, float ell, float zq, const GradK& c) {
-  const float t = __builtin_fmaf(c.b, ell, c.ab);
+__device__ __forceinline__ float grad_entry_inside(float q, float d, float zq, const GradK& c) {
+  const float t = __builtin_fmaf(c.bd, d, c.c0);
   if constexpr (TM)
     return __builtin_fmaf(c.c1, __builtin_amdgcn_exp2f(__builtin_fmaf(zq, kLog2e, -c.l1L)), q * t);
   return q * t;
@@ -1273,14 +1278,14 @@ __device__ __forceinline__ void grad_vec(const typename Tr<VAR>::S& xp, const ty
     for (int e = 0; e < VEC; ++e) {
       float q, ell, r;
       opd_entry<TM>(T::at(xp, e), T::at(xq, e), rk, q, ell, r);
-      out[e] = grad_entry<TM>(q, ell, r, T::at(xq, e), rk.tau, gk);
+      out[e] = grad_entry<TM>(q, T::at(xq, e) - T::at(xp, e), r, T::at(xq, e), rk.tau, gk);
     }
   } else {
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
       float q, ell, r;
       opd_entry<TM>(T::at(xp, e), T::at(xq, e), rk, q, ell, r);
-      out[e] = grad_entry_inside<TM>(q, ell, T::at(xq, e), gk);
+      out[e] = grad_entry_inside<TM>(q, T::at(xq, e) - T::at(xp, e), T::at(xq, e), gk);
     }
   }
   const int lo = io.lo(s);
@@ -1928,7 +1933,7 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
   // ---- sweep 2: the gradient; streamed vectors are read a second time
   // (fast form: through the LDS slots once their resident data is done) ----
   if (a.grad) {
-    const GradK gk = grad_consts<TM>(opaque_s(a.lam), opaque_s(a.gs), S32, st, lse_q1);
+    const GradK gk = grad_consts<TM>(opaque_s(a.lam), opaque_s(a.gs), S32, st, lse_q1, rk.delta);
     const Rsrc rg = grad_rsrc<GB, IO::VEC>(a.grad, rowv, nvec * IO::VEC);
     if constexpr (RING) {
       // Each LDS half's resident slots' gradient frees the half; the streamed
@@ -2254,7 +2259,7 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(BwdArgs a) {
   const f32x4 st = *(const f32x4*)(a.stats + 4 * (long long)row);
   const int A = a.tgt[row];
   const RowK rk = row_consts<TM>(st[0], st[1], a.tau, a.inv_t, a.inv_tl);
-  const GradK gk = grad_consts<TM>(a.lam, a.gs, st[2], a.inv_t, TM ? a.lse1[row] : 0.0f);
+  const GradK gk = grad_consts<TM>(a.lam, a.gs, st[2], a.inv_t, TM ? a.lse1[row] : 0.0f, rk.delta);
   S xp[NVMAX], xq[NVMAX];
   if constexpr (kHalves) {
     const char* pb = (const char*)zp_r;
@@ -2282,7 +2287,7 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(BwdArgs a) {
         for (int e = 0; e < VEC; ++e) {
           float q, ell, r;
           opd_entry<TM>(T::at(xp[v], e), T::at(xq[v], e), rk, q, ell, r);
-          out[e] = grad_entry<TM>(q, ell, r, T::at(xq[v], e), rk.tau, gk);
+          out[e] = grad_entry<TM>(q, T::at(xq[v], e) - T::at(xp[v], e), r, T::at(xq[v], e), rk.tau, gk);
           if ((e < 4 ? e0 + e : e1 + (e - 4)) == (long long)A) out[e] = out[e] - gk.fix;
         }
         if constexpr (GB) {
@@ -2315,7 +2320,7 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(BwdArgs a) {
       for (int e = 0; e < VEC; ++e) {
         float q, ell, r;
         opd_entry<TM>(T::at(xp[v], e), T::at(xq[v], e), rk, q, ell, r);
-        out[e] = grad_entry<TM>(q, ell, r, T::at(xq[v], e), rk.tau, gk);
+        out[e] = grad_entry<TM>(q, T::at(xq[v], e) - T::at(xp[v], e), r, T::at(xq[v], e), rk.tau, gk);
         if (vi * VEC + e == A) out[e] = out[e] - gk.fix;
       }
       if constexpr (GB) store_vec_bf16<VEC>(gb_r, (unsigned)vi, out);
