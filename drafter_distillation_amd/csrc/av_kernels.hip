@@ -148,7 +148,8 @@ __device__ __forceinline__ float opaque_s(float x) {
 }
 
 // ---------------------------------------------------------------------------
-// wave64 reductions (xor butterflies: every lane ends with the same bits)
+// wave64 reductions (xor butterflies: every lane ends with the same bits);
+// the fused row kernel uses the DPP row reductions further down
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ float wsum(float v) {
@@ -1772,8 +1773,8 @@ __device__ __forceinline__ void verified_row(const FwdArgs& a, RowSmem& sm,
     }
   }
 
-  // ---- combine the statistics of the 1024 threads: wave butterflies, then
-  // every wave merges the 16 wave partials the same way ----
+  // ---- combine the statistics of the 1024 threads: row reductions inside
+  // each wave, then every wave merges the 16 wave partials the same way ----
   RowAcc W = A;
   {  // the combine takes the zp sum relative to the running max
     const float L = TM ? sL : kLog2e;
