@@ -2779,6 +2779,26 @@ __device__ __forceinline__ void race_merge(RaceBest& R, const RaceBest& O) {
   race_keep(O.rk, O.ri, R.rk, R.ri);
   race_keep(O.pk, O.pi, R.pk, R.pi);
 }
+// The wave's best residual and p draws in every lane: DPP steps inside each
+// row of 16 lanes, then the four rows in order (a selection under a total
+// order, so the result is the same whatever the pairing; all lanes active).
+template <int C>
+__device__ __forceinline__ void race_step(RaceBest& R) {
+  const RaceBest O{dpp<C>(R.rk), dpp<C>(R.pk), dpp<C>(R.ri), dpp<C>(R.pi)};
+  race_merge(R, O);
+}
+__device__ __forceinline__ void race_wave(RaceBest& R) {
+  race_step<kDppSwap1>(R);
+  race_step<kDppSwap2>(R);
+  race_step<kDppMirror8>(R);
+  race_step<kDppMirror16>(R);
+  RaceBest B{lane_of(R.rk, 0), lane_of(R.pk, 0), lane_of(R.ri, 0), lane_of(R.pi, 0)};
+#pragma unroll
+  for (int r = 1; r < 4; ++r)
+    race_merge(B, RaceBest{lane_of(R.rk, 16 * r), lane_of(R.pk, 16 * r), lane_of(R.ri, 16 * r),
+                           lane_of(R.pi, 16 * r)});
+  R = B;
+}
 
 // The accepted length of request b: the first verified position whose test
 // failed (n if none).  Run by one wave; every lane gets the result.
@@ -2847,15 +2867,7 @@ __global__ __launch_bounds__(kBlock) void spec_race_kernel(SpecArgs a) {
       }
     }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    RaceBest O;
-    O.rk = __shfl_xor(R.rk, o);
-    O.ri = __shfl_xor(R.ri, o);
-    O.pk = __shfl_xor(R.pk, o);
-    O.pi = __shfl_xor(R.pi, o);
-    race_merge(R, O);
-  }
+  race_wave(R);
   if (lane == 0) s_r[wid] = R;
   __syncthreads();
   if (tid == 0) {
